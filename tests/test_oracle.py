@@ -1,0 +1,409 @@
+"""Pins for the fp64 oracle: every function is checked against something other than
+itself -- numbers the pages print (tests/golden), closed forms, invariants, textbook
+special cases and brute force -- chosen so that a dropped term, a wrong sign or index,
+or a transposed operand fails at least one test. CPU only.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_worked_examples.json")))
+
+
+def textbook_fwht(v):
+    """In-place radix-2 Walsh-Hadamard butterflies (a, b) -> (a + b, a - b), natural order.
+    Written independently of the oracle's explicit Sylvester product."""
+    v = np.array(v, dtype=np.float64)
+    n = v.shape[-1]
+    h = 1
+    while h < n:
+        w = v.reshape(v.shape[:-1] + (n // (2 * h), 2, h))
+        a = w[..., 0, :].copy()
+        b = w[..., 1, :].copy()
+        w[..., 0, :] = a + b
+        w[..., 1, :] = a - b
+        v = w.reshape(v.shape)
+        h *= 2
+    return v
+
+
+def popcount(x):
+    return bin(int(x)).count("1")
+
+
+# ------------------------------------------------------------------ Hadamard matrices
+
+
+def test_sylvester_small_matches_page():
+    g = GOLDEN["sylvester_small"]
+    for n, key in ((1, "H1"), (2, "H2"), (4, "H4")):
+        assert np.array_equal(oracle.sylvester(n), np.array(g[key], dtype=np.float64))
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048])
+def test_sylvester_orthogonal_symmetric_popcount(n):
+    h = oracle.sylvester(n)
+    assert h.shape == (n, n)
+    assert np.array_equal(h, h.T)
+    assert np.array_equal(h @ h.T, n * np.eye(n))  # integer sums: exact in fp64
+    if n <= 1024:
+        assert np.array_equal(h, oracle.hadamard_popcount(n))
+
+
+def test_sylvester_entry_closed_form_spot_checks_large():
+    rng = np.random.default_rng(7)
+    for n in (4096, 16384):
+        for c0 in (0, n // 2, n - 1024):
+            blk = oracle.hadamard_column_block(n, c0, 1024)
+            rows = rng.integers(0, n, 64)
+            cols = rng.integers(0, 1024, 64)
+            for r, c in zip(rows, cols):
+                assert blk[r, c] == (-1.0) ** popcount(int(r) & int(c0 + c))
+
+
+def test_column_block_equals_full_matrix():
+    n = 4096
+    h = oracle.sylvester(n)
+    for c0 in range(0, n, 512):
+        assert np.array_equal(oracle.hadamard_column_block(n, c0, 512), h[:, c0:c0 + 512])
+
+
+def test_rejects_non_power_of_two():
+    for bad in (0, 3, 6, 12, 100):
+        with pytest.raises(ValueError):
+            oracle.sylvester(bad)
+        with pytest.raises(ValueError):
+            oracle.rotate(np.ones((1, bad)))
+
+
+# ------------------------------------------------------------------ rotation
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
+def test_rotation_equals_textbook_fwht_exactly(n):
+    rng = np.random.default_rng(n)
+    x = rng.integers(-1000, 1000, size=(9, n)).astype(np.float64)
+    got = oracle.rotate(x, normalize=False)
+    assert np.array_equal(got, textbook_fwht(x))
+    # and the normalized map is that divided by sqrt(n)
+    assert np.allclose(oracle.rotate(x), textbook_fwht(x) / math.sqrt(n), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [128, 4096, 8192])
+def test_rotation_matches_fwht_larger(n):
+    x = workloads.to_float64(workloads.gen_rows(1, 4, n, "bfloat16"), "bfloat16")
+    got = oracle.rotate(x)
+    ref = textbook_fwht(x) / math.sqrt(n)
+    scale = np.max(np.abs(x))
+    assert np.max(np.abs(got - ref)) <= 1e-12 * scale * math.sqrt(n)
+
+
+@pytest.mark.parametrize("n", [128, 4096, 16384])
+def test_rotation_preserves_norm(n):
+    rows = 2 if n == 16384 else 8
+    x = workloads.to_float64(workloads.gen_rows(2, rows, n, "bfloat16", kind="swiglu", n_outliers=8, factor=200), "bfloat16")
+    y = oracle.rotate(x)
+    nx = np.linalg.norm(x, axis=1)
+    ny = np.linalg.norm(y, axis=1)
+    assert np.all(np.abs(ny - nx) <= 1e-12 * nx)
+
+
+def test_rotation_is_involution():
+    # (H/sqrt n)^2 = I because H is symmetric and orthogonal after normalisation
+    x = workloads.gen_rows(3, 3, 1024, "float32").astype(np.float64)
+    back = oracle.rotate(oracle.rotate(x))
+    assert np.max(np.abs(back - x)) <= 1e-12 * np.max(np.abs(x))
+
+
+def test_single_spike_spreads_exactly():
+    # page: one non-zero entry a -> every output has magnitude |a|/sqrt(n); worked
+    # example: 60 in one of 4096 channels -> 60/64 = 0.9375 (printed as ~0.94)
+    g = GOLDEN["hidden_state_example"]
+    n, a, ch = g["n"], g["outlier"], GOLDEN["config_1_outlier_channel"]["channel"]
+    x = np.zeros((1, n))
+    x[0, ch] = a
+    y = oracle.rotate(x)[0]
+    assert round(a / math.sqrt(n), g["printed_spread_decimals"]) == g["printed_spread"]
+    signs = np.array([(-1.0) ** popcount(i & ch) for i in range(n)])
+    assert np.array_equal(y, signs * 0.9375)
+    # transposed operand would read row `ch` of H instead of column: same by symmetry,
+    # so also check a non-symmetric use: two spikes with different magnitudes
+    x2 = np.zeros((1, 8))
+    x2[0, 1] = 3.0
+    x2[0, 6] = 5.0
+    y2 = oracle.rotate(x2, normalize=False)[0]
+    want = [3.0 * (-1) ** popcount(i & 1) + 5.0 * (-1) ** popcount(i & 6) for i in range(8)]
+    assert np.array_equal(y2, np.array(want))
+
+
+# ------------------------------------------------------------------ quantizer
+
+
+def test_outlier_curse_figure_scale():
+    g = GOLDEN["outlier_curse_figure"]
+    x = np.array([g["activations"]])
+    s = oracle.absmax_scale(x)[0]
+    assert round(s, g["printed_scale_decimals"]) == g["printed_scale"]
+    q = oracle.quantize_codes(x, np.array([s]))[0]
+    i0 = g["activations"].index(g["value_that_rounds_to_zero"])
+    assert q[i0] == 0
+    assert q[1] == 7  # the outlier lands on the top level
+    assert (oracle.QMIN, oracle.QMAX) == tuple(g["int4_range"])
+
+
+def test_widget_and_hidden_state_steps():
+    w = GOLDEN["widget"]
+    s = oracle.absmax_scale(np.array([[1.0, -0.5, w["outlier"], 0.25]]))[0]
+    assert round(s, w["printed_step_decimals"]) == w["printed_step"]
+    # 15 levels are reachable from a symmetric absmax scale: -7..7
+    assert oracle.QMAX - (-oracle.QMAX) + 1 == w["levels"]
+    h = GOLDEN["hidden_state_example"]
+    s2 = oracle.absmax_scale(np.array([[h["outlier"], 1.0, -1.0]]))[0]
+    assert round(s2, h["printed_step_decimals"]) == h["printed_step_unrotated"]
+
+
+def test_round_half_even_ties_without_rotation():
+    # absmax 7 -> scale exactly 1, so y/s is y itself and ties are exact
+    row = np.array([[7.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, -3.5, 6.5, -6.5]])
+    r = oracle.hadamard_quant_int4(row, scale_dtype="float32", packed=False, rotate_input=False)
+    assert r["s_stored"][0] == 1.0
+    assert r["q"][0].tolist() == [7, 2, 4, -2, 0, 2, 0, -4, 6, -6]
+
+
+def test_clamp_then_round_equals_round_then_clamp():
+    rng = np.random.default_rng(11)
+    t = np.concatenate([rng.uniform(-20, 20, 100000), np.arange(-12, 12, 0.5)])
+    a = np.rint(np.clip(t, -8, 7))
+    b = np.clip(np.rint(t), -8, 7)
+    assert np.array_equal(a, b)
+    q = oracle.quantize_codes(t[None, :], np.array([1.0]))[0]
+    assert np.array_equal(q, b)
+
+
+def test_pack_layout_known_bytes():
+    q = np.array([[-8, 7, 0, -1, 1, -7, 3, 5]], dtype=np.int8)
+    b = oracle.pack_nibbles(q)
+    # byte j = low nibble q[2j], high nibble q[2j+1], two's complement nibbles
+    assert b[0].tolist() == [0x78, 0xF0, 0x91, 0x53]
+    assert np.array_equal(oracle.unpack_nibbles(b), q)
+    allq = np.array(np.meshgrid(np.arange(-8, 8), np.arange(-8, 8))).reshape(2, -1).T.reshape(1, -1)
+    assert np.array_equal(oracle.unpack_nibbles(oracle.pack_nibbles(allq)), allq.astype(np.int8))
+
+
+def test_scale_dtype_rounding_and_zero_rows():
+    s = np.array([1.0 / 3.0, 1e-8, 6.0e-5, 5.0e-8])
+    s16, raw16 = oracle.round_scale(s, "float16")
+    assert raw16.dtype == np.float16
+    assert s16[0] == float(np.float16(1.0 / 3.0))
+    assert s16[1] == 0.0  # 1e-8 underflows fp16
+    s32, raw32 = oracle.round_scale(s, "float32")
+    assert raw32.dtype == np.float32 and s32[1] == float(np.float32(1e-8))
+    z = np.zeros((2, 16))
+    r16 = oracle.hadamard_quant_int4(z, "float16")
+    assert np.all(r16["q"] == 0) and np.all(r16["s_stored"] == 0.0)
+    r32 = oracle.hadamard_quant_int4(z, "float32")
+    assert np.all(r32["q"] == 0) and np.allclose(r32["s_stored"], 1e-8, rtol=1e-7)
+
+
+def test_tiny_rows_clamp_against_brute_force():
+    # fp16 subnormal scales round far from max/7, so |y/s| can exceed 7.5 and clamp
+    rng = np.random.default_rng(5)
+    y = rng.uniform(-1, 1, (64, 32)) * rng.uniform(1e-7, 1e-3, (64, 1))
+    r = oracle.hadamard_quant_int4(y, "float16", packed=False, rotate_input=False)
+    for i in range(y.shape[0]):
+        s = max(np.max(np.abs(y[i])) / 7.0, 1e-8)
+        sh = float(np.float16(s))
+        for j in range(y.shape[1]):
+            want = 0 if sh == 0 else min(7, max(-8, int(round_half_even(y[i, j] / sh))))
+            assert r["q"][i, j] == want
+    assert np.any(r["q"] == -8) or np.any(np.abs(r["q"]) == 7)
+
+
+def round_half_even(t):
+    f = math.floor(t)
+    d = t - f
+    if d > 0.5:
+        return f + 1
+    if d < 0.5:
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+def test_codes_brute_force_small():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, 8)) * 3
+    r = oracle.hadamard_quant_int4(x, "float32", packed=True)
+    for i in range(6):
+        y = [sum(x[i, j] * (-1) ** popcount(k & j) for j in range(8)) / math.sqrt(8) for k in range(8)]
+        m = max(abs(v) for v in y)
+        s = float(np.float32(max(m / 7.0, 1e-8)))
+        q = [min(7, max(-8, round_half_even(v / s))) for v in y]
+        assert r["q"][i].tolist() == q
+        packed = [(q[2 * j] & 15) | ((q[2 * j + 1] & 15) << 4) for j in range(4)]
+        assert r["codes"][i].tolist() == packed
+
+
+def test_invariants_on_rotated_rows():
+    x = workloads.to_float64(workloads.gen_rows(4, 64, 2048, "bfloat16", kind="swiglu", n_outliers=4, factor=200), "bfloat16")
+    r = oracle.hadamard_quant_int4(x, "float16", packed=True)
+    assert not np.any(r["q"] == -8)  # |y/s| <= 7 * s/s_stored < 7.5 for normal fp16 scales
+    assert np.all(np.max(np.abs(r["q"]), axis=1) == 7)
+    assert np.array_equal(oracle.unpack_nibbles(r["codes"]), r["q"])
+    # dequantization error is within half a step everywhere
+    deq = oracle.dequantize(r["q"], r["s_stored"])
+    assert np.all(np.abs(deq - r["y"]) <= 0.5 * r["s_stored"][:, None] * (1 + 1e-12))
+
+
+# ------------------------------------------------------------------ worked example
+
+
+def test_worked_example_unrotated_and_rotated():
+    g = GOLDEN["hidden_state_example"]
+    x = workloads.gen_worked_example(seed=0).astype(np.float64)
+    ch = GOLDEN["config_1_outlier_channel"]["channel"]
+    direct = oracle.hadamard_quant_int4(x, "float32", packed=False, rotate_input=False)
+    step = direct["s_stored"]
+    assert np.allclose(step, 60.0 / 7.0, rtol=1e-7)
+    assert np.all(direct["q"][:, ch] == 7)
+    assert np.allclose(direct["q"][:, ch] * step, 60.0, rtol=1e-6)
+    small = np.abs(x) < 30.0 / 7.0
+    small[:, ch] = False
+    assert np.all(direct["q"][small] == 0)  # everything ordinary collapses to 0
+    rot = oracle.hadamard_quant_int4(x, "float32", packed=False)
+    m = np.max(np.abs(rot["y"]), axis=1)
+    assert np.all((m > 2.0) & (m < 10.0))  # "a few units, not 60"
+    assert np.all(step / rot["s_stored"] > 8.0)  # the step shrinks by about an order of magnitude
+    mse_direct = oracle.mse(x, oracle.dequantize(direct["q"], direct["s_stored"]))
+    y_hat = oracle.dequantize(rot["q"], rot["s_stored"])
+    mse_rot = oracle.mse(x, oracle.rotate(y_hat))  # rotate back (H/sqrt n is its own inverse)
+    assert abs(mse_rot - oracle.mse(rot["y"], y_hat)) <= 1e-9 * mse_rot
+    assert mse_rot / mse_direct < 1.0 - GOLDEN["noise_analysis"]["variance_reduction_at_least"]
+    # noise model: rounding error per coordinate ~ step^2 / 12
+    assert 0.7 < mse_rot / np.mean(rot["s_stored"] ** 2 / 12.0) < 1.3
+
+
+def test_spike_codes_and_bytes_end_to_end():
+    n, ch = 4096, 142
+    x = np.zeros((1, n))
+    x[0, ch] = 60.0
+    for dtype in ("float32", "float16"):
+        r = oracle.hadamard_quant_int4(x, dtype, packed=True)
+        assert r["s"][0] == 0.9375 / 7.0
+        signs = np.array([(-1) ** popcount(i & ch) for i in range(n)])
+        assert np.array_equal(r["q"][0], 7 * signs)
+        lo = np.where(signs[0::2] > 0, 0x7, 0x9)
+        hi = np.where(signs[1::2] > 0, 0x7, 0x9)
+        assert np.array_equal(r["codes"][0], (lo | (hi << 4)).astype(np.uint8))
+
+
+# ------------------------------------------------------------------ invariance pins
+
+
+def test_rmsnorm_commutes_with_rotation_on_page_example():
+    g = GOLDEN["rmsnorm_rotation"]
+    h = np.array(g["h"])
+    r90 = np.array([[0.0, -1.0], [1.0, 0.0]])
+    assert np.array_equal(r90 @ h, np.array(g["rotated"]))
+    assert np.linalg.norm(r90 @ h) == g["length"]
+    for div in ("norm", "rms"):
+        assert np.array_equal(oracle.rmsnorm(r90 @ h, div), r90 @ oracle.rmsnorm(h, div))
+        hh = oracle.sylvester(2) / math.sqrt(2)
+        assert np.allclose(oracle.rmsnorm(hh @ h, div), hh @ oracle.rmsnorm(h, div), rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rmsnorm(h, "norm"), h / 5.0)
+
+
+def test_computational_invariance_through_rotation():
+    # W x = (W Q^T)(Q x) with Q = H/sqrt(n); rows of W rotated by the same oracle call
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((5, 64))
+    x = rng.standard_normal((3, 64))
+    lhs = x @ w.T
+    rhs = oracle.rotate(x) @ oracle.rotate(w).T
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-12)
+
+
+def test_round_to_bf16_matches_bit_rounding():
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(20000) * 10.0).astype(np.float32)
+    v = np.concatenate([v, np.array([1.00390625, 1.01171875, -1.00390625, 3.0], dtype=np.float32)])
+    want = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(v)).astype(np.float64)
+    assert np.array_equal(oracle.round_to_bf16(v.astype(np.float64)), want)
+
+
+# ------------------------------------------------------------------ GEMM
+
+
+def test_int_gemm_brute_force():
+    rng = np.random.default_rng(4)
+    for (m, n, k) in ((1, 1, 2), (3, 5, 8), (7, 4, 16)):
+        qa = rng.integers(-8, 8, (m, k))
+        qw = rng.integers(-8, 8, (n, k))
+        acc = oracle.int_gemm(qa, qw)
+        for i in range(m):
+            for j in range(n):
+                assert acc[i, j] == sum(int(qa[i, t]) * int(qw[j, t]) for t in range(k))
+        sa = rng.uniform(0.01, 1, m).astype(np.float16)
+        sw = rng.uniform(0.01, 1, n).astype(np.float16)
+        acc2, out = oracle.w4a4_gemm(qa, sa, qw, sw)
+        assert np.array_equal(acc, acc2)
+        for i in range(m):
+            for j in range(n):
+                assert out[i, j] == acc[i, j] * float(sa[i]) * float(sw[j])
+
+
+def test_int_gemm_extremes_exact_and_orientation():
+    k = 4096
+    qa = np.full((2, k), -8)
+    qw = np.full((3, k), -8)
+    assert np.all(oracle.int_gemm(qa, qw) == 64 * k)
+    # non-square operands catch a transposed operand
+    qa = np.arange(6).reshape(2, 3) - 3
+    qw = np.arange(12).reshape(4, 3) % 5 - 2
+    assert np.array_equal(oracle.int_gemm(qa, qw), qa @ qw.T)
+    with pytest.raises(ValueError):
+        oracle.int_gemm(qa, qw.T)
+
+
+def test_rotated_gemm_approximates_float_product():
+    # the end-to-end point of the path: quantized rotated operands reproduce W x
+    a_bits, w, _ = workloads.gen_gemm_inputs(seed=0, m=64, n=96, k=512)
+    a = workloads.to_float64(a_bits, "bfloat16")
+    w = w.astype(np.float64)
+    ra = oracle.hadamard_quant_int4(a, "float16", packed=False)
+    rw = oracle.hadamard_quant_int4(w, "float16", packed=False)
+    _, out = oracle.w4a4_gemm(ra["q"], ra["s_stored"], rw["q"], rw["s_stored"])
+    ref = a @ w.T
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    da = oracle.hadamard_quant_int4(a, "float16", packed=False, rotate_input=False)
+    dw = oracle.hadamard_quant_int4(w, "float16", packed=False, rotate_input=False)
+    _, out_direct = oracle.w4a4_gemm(da["q"], da["s_stored"], dw["q"], dw["s_stored"])
+    rel_direct = np.linalg.norm(out_direct - ref) / np.linalg.norm(ref)
+    assert rel < 0.25 and rel < 0.5 * rel_direct
+
+
+# ------------------------------------------------------------------ R3 wrapper
+
+
+def test_kv_rotate_quant_per_head_spike():
+    d = 128
+    q = np.zeros((1, 2, 3, d))
+    k = np.zeros((1, 2, 3, d))
+    q[0, 1, 2, 5] = 8.0
+    k[0, 0, 1, 77] = -16.0
+    out = oracle.kv_rotate_quant(q, k)
+    yq = out["q"]["y"][0, 1, 2]
+    assert np.allclose(np.abs(yq), 8.0 / math.sqrt(d), rtol=1e-15)
+    assert np.all(out["q"]["q"][0, 1, 2] * np.sign(yq) == 7)
+    assert np.all(out["q"]["q"][0, 0] == 0) and np.all(out["q"]["s_stored"][0, 0] == 0)
+    yk = out["k"]["y"][0, 0, 1]
+    assert np.allclose(yk, [-16.0 / math.sqrt(d) * (-1) ** popcount(i & 77) for i in range(d)], rtol=1e-15)
+    assert out["k"]["codes"].shape == (1, 2, 3, d // 2)
+    rot_only = oracle.kv_rotate_quant(q, k, q_rotate_only=True)
+    assert np.allclose(np.abs(rot_only["q_rot"][0, 1, 2]), 0.70703125)  # bf16(8/sqrt(128))
