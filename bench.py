@@ -1,0 +1,310 @@
+"""Benchmark of the online-rotation hot path on one MI355X.
+
+One step is one pass over every hot-path call, each on its full workload:
+  * kv_rotate_quant   -- R3 on post-RoPE Q and K, bf16 [16, 32, 2048, 128] each;
+  * hadamard_quant_int4 -- R4 on the down-projection input, bf16 [8192, 16384], n = 16384;
+  * w4a4_gemm         -- A [4096, 4096] x W [11008, 4096] packed INT4, bf16 output.
+Inputs are seeded synthetic tensors (workloads.py) already resident in HBM; four input
+sets (more than the 256 MB last-level cache per call) are rotated so the timed reads come
+from HBM. Each launch is bracketed by HIP events on the stream it runs on.
+
+The headline value is the fused Hadamard + INT4 quantizer's throughput at n = 16384 in
+algorithmic GB/s (bf16 input read once, packed codes and fp16 scales written once); the
+GEMM's TOPS and the per-call times are reported beside it, with the fp64 oracle timed on
+a bounded sample on the host cores as a baseline.
+
+usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (no sparsity)
+NSETS = 4
+
+R4_TOKENS, R4_N = 8192, 16384
+KV_SHAPE = (16, 32, 2048, 128)
+GEMM_M, GEMM_N, GEMM_K = 4096, 11008, 4096
+
+R4_BYTES = R4_TOKENS * R4_N * 2 + R4_TOKENS * R4_N // 2 + R4_TOKENS * 2
+KV_ROWS = KV_SHAPE[0] * KV_SHAPE[1] * KV_SHAPE[2]
+KV_BYTES = 2 * (KV_ROWS * KV_SHAPE[3] * 2 + KV_ROWS * KV_SHAPE[3] // 2 + KV_ROWS * 2)
+GEMM_OPS = 2 * GEMM_M * GEMM_N * GEMM_K
+GEMM_BYTES = GEMM_M * GEMM_K // 2 + GEMM_N * GEMM_K // 2 + GEMM_M * 2 + GEMM_N * 2 + GEMM_M * GEMM_N * 2
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "rotation_bit_quantization_fwht_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+FWHT_SOURCES = ("common.h", "plan.h", "fwht_engine.h", "devctx.h", "fwht_kernels.hip")
+GEMM_SOURCES = ("common.h", "w4a4_gemm.hip")
+
+
+def load_traffic(name, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    e = d.get(name)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline():
+    """The oracle as it stands, on a bounded sample of the n=16384 workload."""
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing or no BLAS info
+        cores = os.cpu_count() or 1
+    rows = 16
+    xb, _ = workloads.gen_ffn(seed=7, tokens=rows, n=R4_N)
+    x64 = workloads.to_float64(xb, "bfloat16")
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.hadamard_quant_int4(x64, "float16", packed=True)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 8:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    sample_bytes = rows * (R4_N * 2 + R4_N // 2 + 2)
+    return {
+        "value": round(sample_bytes / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{rows} rows of the bf16 [8192, 16384] R4 workload, explicit fp64 Sylvester "
+                  f"multiply + quantizer, {reps} repetitions, {dt:.2f} s each",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm"], default="all",
+                    help="restrict the step (for profiling one kernel)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rotation_bit_quantization_fwht_amd as rbq
+    import workloads
+
+    if not os.path.exists(rbq.library_path()):
+        from rotation_bit_quantization_fwht_amd.build import build
+
+        build()
+    rbq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    run_r4 = args.only in ("all", "r4")
+    run_kv = args.only in ("all", "kv")
+    run_gemm = args.only in ("all", "gemm")
+
+    # ---- inputs: one seeded set from workloads.py, further sets are row rotations of it
+    sets = {}
+    if run_r4:
+        xb, _ = workloads.gen_ffn(seed=0)
+        x0 = to_dev16(xb)
+        del xb
+        sets["r4_x"] = [x0] + [torch.roll(x0, shifts=97 * i, dims=0).contiguous() for i in range(1, NSETS)]
+        sets["r4_codes"] = [torch.empty((R4_TOKENS, R4_N // 2), dtype=torch.uint8, device=dev) for _ in range(NSETS)]
+        sets["r4_scales"] = [torch.empty((R4_TOKENS,), dtype=torch.float16, device=dev) for _ in range(NSETS)]
+    if run_kv:
+        qb, kb, _ = workloads.gen_kv(seed=0)
+        q0, k0 = to_dev16(qb), to_dev16(kb)
+        del qb, kb
+        sets["kv_q"] = [q0] + [torch.roll(q0, shifts=31 * i, dims=2).contiguous() for i in range(1, NSETS)]
+        sets["kv_k"] = [k0] + [torch.roll(k0, shifts=31 * i, dims=2).contiguous() for i in range(1, NSETS)]
+        B, H, S, D = KV_SHAPE
+        sets["kv_out"] = [
+            {
+                "q_codes": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev),
+                "q_scales": torch.empty((B, H, S), dtype=torch.float16, device=dev),
+                "k_codes": torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev),
+                "k_scales": torch.empty((B, H, S), dtype=torch.float16, device=dev),
+            }
+            for _ in range(NSETS)
+        ]
+    gemm_ok = False
+    if run_gemm:
+        ab, w, _ = workloads.gen_gemm_inputs(seed=0)
+        a0 = to_dev16(ab)
+        w0 = torch.from_numpy(w).to(dev)
+        del ab, w
+        qa, sa = rbq.hadamard_quant_int4(a0)                     # activations, online rotation
+        qw, sw = rbq.hadamard_quant_int4(w0)                     # weights, offline rotation
+        out = torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=dev)
+        try:
+            rbq.w4a4_gemm(qa, sa, qw, sw, out=out)
+            gemm_ok = True
+        except rbq.RBQError as e:
+            if e.status != rbq.RBQ_ENOTSUP:
+                raise
+        del a0, w0
+    torch.cuda.synchronize()
+
+    def step(i, ev):
+        s = i % NSETS
+        j = 0
+        if run_kv:
+            ev[j].record()
+            o = sets["kv_out"][s]
+            rbq.kv_rotate_quant(sets["kv_q"][s], sets["kv_k"][s], **o)
+            j += 1
+        if run_r4:
+            ev[j].record()
+            rbq.hadamard_quant_int4(sets["r4_x"][s], codes=sets["r4_codes"][s], scales=sets["r4_scales"][s])
+            j += 1
+        if run_gemm and gemm_ok:
+            ev[j].record()
+            rbq.w4a4_gemm(qa, sa, qw, sw, out=out)
+            j += 1
+        ev[j].record()
+
+    nk = int(run_kv) + int(run_r4) + int(run_gemm and gemm_ok)
+    for i in range(args.warmup):
+        step(i, [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)])
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = []
+    if run_kv:
+        names.append("kv_rotate_quant")
+    if run_r4:
+        names.append("hadamard_quant_int4")
+    if run_gemm and gemm_ok:
+        names.append("w4a4_gemm")
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    step_ms = [ev[0].elapsed_time(ev[-1]) for ev in events]
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    med = {n: float(np.median(v)) for n, v in per.items()}
+
+    kernels = {}
+    fwht_hash = kernel_source_hash(FWHT_SOURCES)
+    if "hadamard_quant_int4" in avg:
+        t = avg["hadamard_quant_int4"] * 1e-3
+        kernels["hadamard_quant_int4"] = {
+            "workload": "R4 bf16 [8192, 16384], n=16384, packed INT4 + fp16 scales",
+            "avg_us": round(t * 1e6, 3), "median_us": round(med["hadamard_quant_int4"] * 1e3, 3),
+            "algorithmic_bytes": R4_BYTES, "GB_s": round(R4_BYTES / t / 1e9, 2),
+            "frac_hbm_peak": round(R4_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if "kv_rotate_quant" in avg:
+        t = avg["kv_rotate_quant"] * 1e-3
+        kernels["kv_rotate_quant"] = {
+            "workload": "R3 bf16 Q and K [16, 32, 2048, 128], packed INT4 + fp16 scales",
+            "avg_us": round(t * 1e6, 3), "median_us": round(med["kv_rotate_quant"] * 1e3, 3),
+            "algorithmic_bytes": KV_BYTES, "GB_s": round(KV_BYTES / t / 1e9, 2),
+            "frac_hbm_peak": round(KV_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if "w4a4_gemm" in avg:
+        t = avg["w4a4_gemm"] * 1e-3
+        kernels["w4a4_gemm"] = {
+            "workload": "A [4096, 4096] x W [11008, 4096] packed INT4, bf16 out",
+            "avg_us": round(t * 1e6, 3), "median_us": round(med["w4a4_gemm"] * 1e3, 3),
+            "algorithmic_ops": GEMM_OPS, "TOPS": round(GEMM_OPS / t / 1e12, 2),
+            "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4),
+        }
+
+    headline = kernels.get("hadamard_quant_int4")
+    value = headline["GB_s"] if headline else None
+    roofline = None
+    if headline:
+        roofline = {
+            "kernel": "hadamard_quant_int4 (fwht_quant_kernel<14, bf16>)",
+            "bound": "hbm", "achieved": headline["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": headline["frac_hbm_peak"],
+            "traffic": load_traffic("hadamard_quant_int4", fwht_hash),
+        }
+    extra_roofline = {}
+    if "kv_rotate_quant" in kernels:
+        k = kernels["kv_rotate_quant"]
+        extra_roofline["kv_rotate_quant"] = {
+            "bound": "hbm", "achieved": k["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": k["frac_hbm_peak"], "traffic": load_traffic("kv_rotate_quant", fwht_hash)}
+    if "w4a4_gemm" in kernels:
+        k = kernels["w4a4_gemm"]
+        extra_roofline["w4a4_gemm"] = {
+            "bound": "mfma", "achieved": k["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": k["frac_int8_mfma_peak"],
+            "traffic": load_traffic("w4a4_gemm", kernel_source_hash(GEMM_SOURCES))}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "Hadamard+INT4 quant GB/s & %HBM peak at n=16384; W4A4 GEMM TOPS & %MFMA",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in / fp32 transform / int4 codes; int8 MFMA int32 accumulate",
+        "data": "synthetic (seeded, workloads.py)",
+        "config": {
+            "workload": "R4 down_proj input bf16 [8192, 16384] (n=16384) fused Hadamard + INT4 quant; "
+                        "step also runs R3 Q/K [16,32,2048,128] and the W4A4 GEMM 4096x11008x4096",
+            "tokens": R4_TOKENS, "n": R4_N, "input_sets_rotated": NSETS,
+        },
+        "gemm": kernels.get("w4a4_gemm"),
+        "kernels": kernels,
+        "roofline": roofline,
+        "roofline_other": extra_roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

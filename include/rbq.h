@@ -1,0 +1,142 @@
+/*
+ * rbq.h -- C ABI of the online-rotation hot path for MI355X (gfx950).
+ *
+ * What it computes (all three calls, restated from the pages):
+ *
+ *  - A fixed Sylvester-Hadamard rotation y = H_n x / sqrt(n) per row
+ *    ("Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices";
+ *    computed as an O(n log n) fast transform per the same page's section "Why it's
+ *    free: computational invariance"), fused with
+ *  - per-row symmetric INT4 absmax quantization: scale s = max(max|y| / 7, 1e-8)
+ *    stored in the scale dtype (round to nearest even), codes
+ *    q = round_half_even(clamp(y / s_stored, -8, 7))
+ *    ("SpinQuant Guide: Learned Rotations for 4-Bit LLMs", outlier-curse figure,
+ *    step-size equation and the uniform_quantize_int4 listing), packed two per byte
+ *    (element 2j in the low nibble, element 2j+1 in the high nibble, two's complement);
+ *  - R3: the same op per (batch, head, token) vector of post-RoPE Q and K over head_dim
+ *    ("SpinQuant, when rotations are worth learning", section "Four rotation sites");
+ *  - the W4A4 GEMM that consumes packed codes: out[m,n] = sA[m] sW[n] sum_k qA[m,k] qW[n,k]
+ *    ("SpinQuant: rotate before you round", section "Deployment implications";
+ *    "SpinQuant Guide...", section "The Orthogonal Invariance Principle").
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the library never
+ *    allocates, frees or synchronizes, keeps no global state and is thread-safe.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the default stream).
+ *  - Arguments are validated on the host before any HIP call. On a non-OK status
+ *    nothing is launched and no output is written.
+ *  - Inputs must be finite; NaN/Inf inputs are outside the contract.
+ *  - Sizes are element counts unless stated otherwise.
+ */
+#ifndef RBQ_H
+#define RBQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RBQ_OK = 0,      /* success (also for an empty problem, which launches nothing) */
+  RBQ_EINVAL = 1,  /* invalid argument: NULL pointer, bad size, misalignment, bad dtype */
+  RBQ_ENOTSUP = 2, /* valid but unsupported combination (e.g. K % 128 != 0 in the GEMM) */
+  RBQ_EHIP = 3     /* the HIP launch failed (hipGetLastError after the launch) */
+} rbq_status;
+
+typedef enum { RBQ_F32 = 0, RBQ_BF16 = 1, RBQ_F16 = 2 } rbq_dtype;
+
+enum {
+  RBQ_PACKED = 1u << 0,        /* codes two per byte; otherwise one int8 per element */
+  RBQ_NO_ROTATE = 1u << 1,     /* quantize x itself (no Hadamard, no 1/sqrt(n)) */
+  RBQ_Q_ROTATE_ONLY = 1u << 2  /* kv_rotate_quant: write Q rotated (bf16), do not quantize Q */
+};
+
+/*
+ * hadamard_quant_int4 -- rotate each of `tokens` rows of length n by H_n / sqrt(n)
+ * (natural Sylvester order), then quantize each row to INT4 with one absmax scale.
+ * This is the R4 path (down-projection input) and the offline weight rotation
+ * (rows of W rotated along K, which equals W H^T / sqrt(K) because H is symmetric).
+ *
+ *  x            [tokens, n] row-major with row stride `x_row_stride` (elements, >= n),
+ *               dtype x_dtype (F32, BF16, F16). The start of every row must be aligned
+ *               to min(16, n * element size) bytes.
+ *  n            power of two, 2 <= n <= 32768 (the pages' K-cache path likewise
+ *               requires a power-of-two size for the fast transform).
+ *  tokens       number of rows, >= 0; 0 returns RBQ_OK without launching.
+ *  codes        RBQ_PACKED: uint8 [tokens, n/2], contiguous; else int8 [tokens, n].
+ *               16-byte aligned.
+ *  scales       [tokens] contiguous, scale_dtype F32 or F16 (stored scale s_stored).
+ *               Rows whose stored scale is 0 (fp16 underflow) get all-zero codes.
+ *  rotated      optional float [tokens, n] contiguous, 16-byte aligned: y = H x / sqrt(n)
+ *               as computed (or x itself with RBQ_NO_ROTATE); NULL skips it.
+ *  flags        RBQ_PACKED, RBQ_NO_ROTATE.
+ * Errors: RBQ_EINVAL for NULL x/codes/scales (when tokens > 0), n not a power of two
+ * in [2, 32768], tokens < 0, x_row_stride < n, misaligned pointers/strides, a bad dtype
+ * or unknown flag bits; RBQ_EHIP if the launch fails.
+ */
+rbq_status hadamard_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
+                               int64_t x_row_stride, void *codes, void *scales,
+                               rbq_dtype scale_dtype, float *rotated, unsigned flags,
+                               hipStream_t stream);
+
+/*
+ * kv_rotate_quant -- R3: rotate every head_dim vector of post-RoPE Q and K by
+ * H_d / sqrt(d) and quantize it to INT4 with one scale per (batch, head, token).
+ * Q and K are processed in one launch.
+ *
+ *  q, k         [batch, heads, seq, head_dim], dtype BF16 or F16, element strides
+ *               q_strides[4] / k_strides[4] in (b, h, s, d) order; the d stride must be 1
+ *               and every vector start 16-byte aligned (head_dim * 2 >= 16).
+ *  head_dim     power of two, 8 <= head_dim <= 32768; a layout whose vectors are not
+ *               equally spaced (non-flattenable strides) needs head_dim 64, 128 or 256
+ *               (else RBQ_ENOTSUP).
+ *  q_codes, k_codes   uint8 [batch, heads, seq, head_dim/2] contiguous, 16-byte aligned.
+ *  q_scales, k_scales [batch, heads, seq] contiguous, scale_dtype (F16 or F32).
+ *  q_rotated    with RBQ_Q_ROTATE_ONLY: bf16/f16 (same dtype as q) [batch, heads, seq,
+ *               head_dim] contiguous, receives H q / sqrt(d) rounded to nearest even;
+ *               q_codes and q_scales are then not written and may be NULL.
+ *  flags        RBQ_Q_ROTATE_ONLY (codes are always packed two per byte).
+ * Errors: RBQ_EINVAL for NULL required pointers, non-positive/inconsistent sizes,
+ * head_dim not a power of two in range, a d stride != 1, misalignment, bad dtypes or
+ * flags; an empty problem (any of batch, heads, seq == 0) returns RBQ_OK.
+ */
+rbq_status kv_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_t batch,
+                           int64_t heads, int64_t seq, int64_t head_dim,
+                           const int64_t q_strides[4], const int64_t k_strides[4],
+                           uint8_t *q_codes, void *q_scales, uint8_t *k_codes, void *k_scales,
+                           rbq_dtype scale_dtype, void *q_rotated, unsigned flags,
+                           hipStream_t stream);
+
+/*
+ * w4a4_gemm -- out[m, n] = bf16( sA[m] * sW[n] * sum_k qA[m, k] * qW[n, k] ).
+ * Codes are the packed INT4 produced above (two per byte, low nibble = even k).
+ * The integer sum is exact (int32 accumulation on int8 matrix cores).
+ *
+ *  qA     uint8 [M, K/2] row-major (K-contiguous), 16-byte aligned.
+ *  sA     [M] scale_dtype (F16 or F32).
+ *  qW     uint8 [N, K/2] row-major (K-contiguous), 16-byte aligned.
+ *  sW     [N] scale_dtype.
+ *  out_bf16  bf16 [M, N] row-major, 16-byte aligned (round to nearest even).
+ *  acc    optional int32 [M, N] row-major: the exact integer sums; NULL skips it.
+ *  M, N   >= 0 (0 returns RBQ_OK); K > 0, K % 128 == 0 (else RBQ_ENOTSUP),
+ *         K <= 131072; N % 8 == 0 (16-byte output rows; else RBQ_ENOTSUP).
+ * Errors: RBQ_EINVAL for NULL pointers, negative sizes, odd K, misalignment or a bad
+ * scale dtype; RBQ_ENOTSUP as above; RBQ_EHIP if the launch fails.
+ */
+rbq_status w4a4_gemm(const uint8_t *qA, const void *sA, const uint8_t *qW, const void *sW,
+                     rbq_dtype scale_dtype, int64_t M, int64_t N, int64_t K, void *out_bf16,
+                     int32_t *acc, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *rbq_status_string(rbq_status s);
+
+/* Library version string (static). */
+const char *rbq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBQ_H */

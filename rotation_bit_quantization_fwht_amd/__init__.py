@@ -1,0 +1,244 @@
+"""Thin Python binding of librbq.so, the C-ABI HIP library for MI355X (gfx950).
+
+The three calls have the same names and meaning as the C functions declared in
+``include/rbq.h``:
+
+* ``hadamard_quant_int4`` -- Sylvester-Hadamard rotation per row fused with per-row
+  symmetric INT4 absmax quantization (round half to even), codes packed two per byte;
+* ``kv_rotate_quant`` -- the same per (batch, head, token) vector of post-RoPE Q and K;
+* ``w4a4_gemm`` -- the W4A4 GEMM on packed codes with int32 accumulation and a bf16
+  dequantization epilogue.
+
+This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
+memory, allocates outputs with torch when the caller does not pass them, and hands raw
+device pointers and the current HIP stream to the library. Every step of the computation
+runs in the library's kernels. If the library is missing the calls raise; there is no
+fallback.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "RBQError",
+    "LibraryMissing",
+    "lib",
+    "library_path",
+    "hadamard_quant_int4",
+    "kv_rotate_quant",
+    "w4a4_gemm",
+    "RBQ_OK",
+    "RBQ_EINVAL",
+    "RBQ_ENOTSUP",
+    "RBQ_EHIP",
+    "RBQ_F32",
+    "RBQ_BF16",
+    "RBQ_F16",
+    "RBQ_PACKED",
+    "RBQ_NO_ROTATE",
+    "RBQ_Q_ROTATE_ONLY",
+    "EXPORTED_SYMBOLS",
+]
+
+RBQ_OK, RBQ_EINVAL, RBQ_ENOTSUP, RBQ_EHIP = 0, 1, 2, 3
+RBQ_F32, RBQ_BF16, RBQ_F16 = 0, 1, 2
+RBQ_PACKED, RBQ_NO_ROTATE, RBQ_Q_ROTATE_ONLY = 1, 2, 4
+
+EXPORTED_SYMBOLS = (
+    "hadamard_quant_int4",
+    "kv_rotate_quant",
+    "w4a4_gemm",
+    "rbq_status_string",
+    "rbq_version",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.environ.get("RBQ_LIBRARY", os.path.join(_HERE, "librbq.so"))
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class RBQError(RuntimeError):
+    def __init__(self, func, status, message):
+        super().__init__(f"{func}: {message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load librbq.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise LibraryMissing(
+            f"{path} is not built; run rotation_bit_quantization_fwht_amd.build.build() "
+            "(hipcc --offload-arch=gfx950). There is no CPU fallback."
+        )
+    L = ctypes.CDLL(path)
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    L.hadamard_quant_int4.argtypes = [vp, ci, i64, i64, i64, vp, vp, ci, vp, cu, vp]
+    L.hadamard_quant_int4.restype = ci
+    L.kv_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, vp, vp, ci, vp, cu, vp]
+    L.kv_rotate_quant.restype = ci
+    L.w4a4_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
+    L.w4a4_gemm.restype = ci
+    L.rbq_status_string.argtypes = [ci]
+    L.rbq_status_string.restype = ctypes.c_char_p
+    L.rbq_version.argtypes = []
+    L.rbq_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(func, status):
+    if status != RBQ_OK:
+        msg = lib().rbq_status_string(status).decode()
+        raise RBQError(func, status, msg)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    m = {torch.float32: RBQ_F32, torch.bfloat16: RBQ_BF16, torch.float16: RBQ_F16}
+    if t not in m:
+        raise TypeError(f"unsupported dtype {t}")
+    return m[t]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("rbq kernels take GPU tensors only")
+
+
+def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=None, scales=None,
+                        rotated=None, return_rotated=False, stream=None):
+    """Rotate every row of ``x`` [tokens, n] (last dim contiguous) by H_n / sqrt(n) and
+    quantize it to INT4 with one absmax scale per row.
+
+    Returns ``(codes, scales)`` -- codes uint8 [tokens, n/2] (packed) or int8
+    [tokens, n]; scales [tokens] in ``scale_dtype`` (default float16) -- plus the float
+    rotated rows when ``return_rotated`` (or a ``rotated`` buffer) is given.
+    """
+    torch = _torch()
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with a contiguous last dimension")
+    tokens, n = x.shape
+    scale_dtype = torch.float16 if scale_dtype is None else scale_dtype
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((tokens, n // 2 if packed else n), dtype=torch.uint8 if packed else torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty((tokens,), dtype=scale_dtype, device=dev)
+    if rotated is None and return_rotated:
+        rotated = torch.empty((tokens, n), dtype=torch.float32, device=dev)
+    _require_cuda(codes, scales, rotated)
+    flags = (RBQ_PACKED if packed else 0) | (0 if rotate else RBQ_NO_ROTATE)
+    st = lib().hadamard_quant_int4(
+        _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
+        _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), flags, _stream(stream, dev),
+    )
+    _check("hadamard_quant_int4", st)
+    if rotated is not None:
+        return codes, scales, rotated
+    return codes, scales
+
+
+def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None, q_scales=None,
+                    k_codes=None, k_scales=None, q_rotated=None, stream=None):
+    """R3 on post-RoPE ``q`` and ``k`` [B, H, S, D] (bf16/fp16, D contiguous): rotate every
+    head vector by H_D / sqrt(D) and quantize it to packed INT4 with one scale per vector.
+
+    Returns a dict with ``k_codes`` [B,H,S,D/2], ``k_scales`` [B,H,S] and either
+    ``q_codes``/``q_scales`` or, with ``q_rotate_only``, ``q_rotated`` [B,H,S,D].
+    """
+    torch = _torch()
+    _require_cuda(q, k)
+    if q.dim() != 4 or k.shape != q.shape or k.dtype != q.dtype:
+        raise ValueError("q and k must be [B, H, S, D] tensors of one shape and dtype")
+    B, H, S, D = q.shape
+    scale_dtype = torch.float16 if scale_dtype is None else scale_dtype
+    dev = q.device
+    out = {}
+    if q_rotate_only:
+        if q_rotated is None:
+            q_rotated = torch.empty((B, H, S, D), dtype=q.dtype, device=dev)
+        out["q_rotated"] = q_rotated
+    else:
+        if q_codes is None:
+            q_codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
+        if q_scales is None:
+            q_scales = torch.empty((B, H, S), dtype=scale_dtype, device=dev)
+        out["q_codes"], out["q_scales"] = q_codes, q_scales
+    if k_codes is None:
+        k_codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
+    if k_scales is None:
+        k_scales = torch.empty((B, H, S), dtype=scale_dtype, device=dev)
+    out["k_codes"], out["k_scales"] = k_codes, k_scales
+    qs = (ctypes.c_int64 * 4)(*q.stride())
+    ks = (ctypes.c_int64 * 4)(*k.stride())
+    sdt = _dtype_code(k_scales.dtype)
+    st = lib().kv_rotate_quant(
+        _ptr(q), _ptr(k), _dtype_code(q.dtype), B, H, S, D, qs, ks,
+        _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), sdt, _ptr(q_rotated),
+        RBQ_Q_ROTATE_ONLY if q_rotate_only else 0, _stream(stream, dev),
+    )
+    _check("kv_rotate_quant", st)
+    return out
+
+
+def w4a4_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=None):
+    """out[m, n] = bf16(sa[m] * sw[n] * sum_k qa[m, k] qw[n, k]) on packed INT4 codes.
+
+    qa uint8 [M, K/2], qw uint8 [N, K/2] (contiguous), sa [M], sw [N] (fp16 or fp32, same
+    dtype). Returns ``out`` (bf16 [M, N]), plus the int32 accumulators when requested.
+    """
+    torch = _torch()
+    _require_cuda(qa, sa, qw, sw)
+    if qa.dim() != 2 or qw.dim() != 2 or qa.shape[1] != qw.shape[1]:
+        raise ValueError("qa must be [M, K/2] and qw [N, K/2]")
+    if not (qa.is_contiguous() and qw.is_contiguous() and sa.is_contiguous() and sw.is_contiguous()):
+        raise ValueError("operands must be contiguous")
+    if sa.dtype != sw.dtype:
+        raise ValueError("sa and sw must share a dtype")
+    M, N, K = qa.shape[0], qw.shape[0], 2 * qa.shape[1]
+    dev = qa.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if acc is None and return_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    st = lib().w4a4_gemm(
+        _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _dtype_code(sa.dtype), M, N, K, _ptr(out), _ptr(acc),
+        _stream(stream, dev),
+    )
+    _check("w4a4_gemm", st)
+    if acc is not None:
+        return out, acc
+    return out

@@ -1,0 +1,469 @@
+// Workgroup body of the fused Walsh-Hadamard rotation + INT4 quantizer.
+//
+// One workgroup owns 2^r rows of length n = 2^k (see plan.h for the data layouts):
+//   load (global -> registers, widen to fp32; for 16-bit inputs the first butterfly is
+//   fused into the widening with a 2-term dot product against (1, 1) and (1, -1))
+//   -> register butterflies -> LDS transpose -> register butterflies [-> transpose ->
+//   butterflies] -> per-row absmax (registers, lane shuffles, LDS across waves)
+//   -> scale, round half to even, clamp, nibble packing -> coalesced stores.
+//
+// Math (restated from the pages): y = H_n x / sqrt(n) with the Sylvester H_n
+// ("Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices");
+// s = max(max|y| / 7, 1e-8) rounded to the scale dtype; q = RNE(clamp(y / s, -8, 7))
+// ("SpinQuant Guide: Learned Rotations for 4-Bit LLMs", step-size equation and
+// quantizer listing). The 1/sqrt(n) is folded into the per-row multiplier: the kernel
+// keeps u = H_n x and uses q = RNE(u * (1 / (s * sqrt(n)))).
+//
+// The body is written against a small context object (lane/wave ids, LDS, barriers,
+// lane shuffles, global loads/stores) so the same code runs in the HIP kernel and in
+// the host-side layout emulator used by the CPU tests.
+#pragma once
+
+#include "common.h"
+#include "plan.h"
+
+namespace rbq {
+
+enum InKind : int { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
+
+enum : uint32_t {
+  MODE_QUANT = 1u,  // write codes + scales
+  MODE_ROT32 = 2u,  // write the rotated row as float
+  MODE_ROT16 = 4u   // write the rotated row in the input's 16-bit format
+};
+enum : uint32_t { OPT_PACKED = 1u, OPT_SCALE_F16 = 2u };
+
+struct TensorArgs {
+  const void* x;
+  int64_t row_stride;      // 2-D addressing: elements between consecutive rows
+  int64_t sb, sh, ss;      // 4-D addressing: element strides of (batch, head, seq)
+  FastDiv div_s, div_h;    // 4-D: row -> (b, h, s)
+  uint32_t seq, heads;
+  void* codes;             // uint8 [rows, n/2] (packed) or int8 [rows, n]
+  void* scales;            // [rows] fp16 or fp32
+  float* rot32;            // [rows, n] float
+  uint16_t* rot16;         // [rows, n] bf16/fp16 bits
+  uint32_t mode;
+};
+
+struct KArgs {
+  TensorArgs t[2];
+  int64_t rows;       // rows per tensor
+  uint32_t blocks0;   // workgroups for tensor 0 (the rest process tensor 1)
+  uint32_t opts;
+};
+
+constexpr int popcount_c(uint32_t x) { int c = 0; while (x) { c += x & 1u; x >>= 1; } return c; }
+
+// gather the bits of x selected by mask into the low bits
+constexpr uint32_t pext_c(uint32_t x, uint32_t mask) {
+  uint32_t out = 0; int o = 0;
+  for (int b = 0; b < 32; ++b) if ((mask >> b) & 1u) { if ((x >> b) & 1u) out |= 1u << o; ++o; }
+  return out;
+}
+// scatter the low bits of x to the positions selected by mask
+constexpr uint32_t pdep_c(uint32_t x, uint32_t mask) {
+  uint32_t out = 0; int o = 0;
+  for (int b = 0; b < 32; ++b) if ((mask >> b) & 1u) { if ((x >> o) & 1u) out |= 1u << b; ++o; }
+  return out;
+}
+
+constexpr float sqrt_pow2(int k) {
+  float p = (float)(1u << (k / 2));
+  return (k & 1) ? 1.41421356237309504880f * p : p;
+}
+
+// element-space index contributed by the lane and wave ids in phase PH, with the bits
+// of RM squeezed out (every bit's destination is a compile-time constant)
+template <int K, int PH, uint32_t RM = 0u>
+RBQ_HD uint32_t lane_part(uint32_t lane, uint32_t wave) {
+  uint32_t idx = 0;
+  static_for<0, 6>([&](auto I) {
+    constexpr uint32_t bit = compress(1u << PlanOf<K>::value.lane[PH][I.value], RM);
+    idx |= ((lane >> I.value) & 1u) ? bit : 0u;
+  });
+  static_for<0, PlanOf<K>::value.w>([&](auto I) {
+    constexpr uint32_t bit = compress(1u << PlanOf<K>::value.wave[PH][I.value], RM);
+    idx |= ((wave >> I.value) & 1u) ? bit : 0u;
+  });
+  return idx;
+}
+
+template <bool FOURD>
+RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
+  if constexpr (FOURD) {
+    uint32_t r = (uint32_t)row;
+    uint32_t bh = fastdiv(r, t.div_s);
+    uint32_t s = r - bh * t.seq;
+    uint32_t b = fastdiv(bh, t.div_h);
+    uint32_t h = bh - b * t.heads;
+    return (int64_t)b * t.sb + (int64_t)h * t.sh + (int64_t)s * t.ss;
+  } else {
+    return row * t.row_stride;
+  }
+}
+
+// ------------------------------------------------------------------ load (phase 0)
+
+template <int K, int IN, bool ROT, bool FOURD, class Ctx>
+RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
+                        float (&v)[1 << PlanOf<K>::value.e]) {
+  constexpr int C0 = run_log(PlanOf<K>::value, 0);
+  constexpr int L = 1 << C0;
+  constexpr int NRUN = (1 << PlanOf<K>::value.e) / L;
+  constexpr int ESZ = (IN == IN_F32) ? 4 : 2;
+  constexpr int BYTES = L * ESZ;
+  const uint32_t lp = lane_part<K, 0>(c.lane, c.wave);
+  static_for<0, NRUN>([&](auto J) {
+    constexpr uint32_t rb = (uint32_t)J.value << C0;
+    constexpr uint32_t rp = reg_part(PlanOf<K>::value, 0, rb);
+    const uint32_t idx = lp | rp;
+    const int64_t row = row0 + (int64_t)(idx >> K);
+    const uint32_t el = idx & ((1u << K) - 1u);
+    uint32_t w[BYTES / 4];
+    if (row < rows) {
+      const char* src = (const char*)t.x + (row_offset<FOURD>(t, row) + (int64_t)el) * ESZ;
+      if constexpr (BYTES >= 16) {
+        static_for<0, BYTES / 16>([&](auto Q) {
+          u32x4 q4 = c.template load<u32x4>(src + 16 * Q.value);
+          w[4 * Q.value + 0] = q4.x; w[4 * Q.value + 1] = q4.y;
+          w[4 * Q.value + 2] = q4.z; w[4 * Q.value + 3] = q4.w;
+        });
+      } else if constexpr (BYTES == 8) {
+        u32x2 q2 = c.template load<u32x2>(src);
+        w[0] = q2.x; w[1] = q2.y;
+      } else {
+        w[0] = c.template load<uint32_t>(src);
+      }
+    } else {
+      static_for<0, BYTES / 4>([&](auto Q) { w[Q.value] = 0u; });
+    }
+    if constexpr (IN == IN_F32) {
+      static_for<0, L>([&](auto I) { v[rb + I.value] = bits_f32(w[I.value]); });
+    } else {
+      static_for<0, L / 2>([&](auto I) {
+        float a, b;
+        if constexpr (ROT) c.template widen_butterfly<IN>(w[I.value], a, b);
+        else c.template widen<IN>(w[I.value], a, b);
+        v[rb + 2 * I.value] = a;
+        v[rb + 2 * I.value + 1] = b;
+      });
+    }
+  });
+}
+
+// ------------------------------------------------------------------ register butterflies
+
+template <int K, int PH, bool SKIP_R0>
+RBQ_HD void stages(float (&v)[1 << PlanOf<K>::value.e]) {
+  constexpr uint32_t M = stage_mask(PlanOf<K>::value, PH) & (SKIP_R0 ? ~1u : ~0u);
+  static_for<0, PlanOf<K>::value.e>([&](auto J) {
+    if constexpr ((M >> J.value) & 1u) {
+      constexpr int S = 1 << J.value;
+      static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+        if constexpr ((R.value & S) == 0) {
+          const float a = v[R.value];
+          const float b = v[R.value + S];
+          v[R.value] = a + b;
+          v[R.value + S] = a - b;
+        }
+      });
+    }
+  });
+}
+
+// ------------------------------------------------------------------ LDS transpose
+
+template <int K, int T, class Ctx>
+RBQ_HD void transpose(Ctx& c, float (&v)[1 << PlanOf<K>::value.e]) {
+  constexpr int SR = PlanOf<K>::value.sr[T];
+  constexpr uint32_t RM = sub_mask(PlanOf<K>::value, T);
+  constexpr bool WL = transpose_is_wave_local(PlanOf<K>::value, T);
+  constexpr uint32_t SMASK = (1u << SR) - 1u;
+  const uint32_t wbase = lds_pad(lane_part<K, T, RM>(c.lane, c.wave));
+  const uint32_t rbase = lds_pad(lane_part<K, T + 1, RM>(c.lane, c.wave));
+  if constexpr (!WL) c.barrier();
+  static_for<0, (1 << SR)>([&](auto S) {
+    static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+      if constexpr ((R.value & SMASK) == (uint32_t)S.value) {
+        constexpr uint32_t off = lds_pad(compress(reg_part(PlanOf<K>::value, T, R.value), RM));
+        c.lds_store(wbase + off, v[R.value]);
+      }
+    });
+    if constexpr (WL) c.wave_sync(); else c.barrier();
+    static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+      if constexpr ((R.value & SMASK) == (uint32_t)S.value) {
+        constexpr uint32_t off = lds_pad(compress(reg_part(PlanOf<K>::value, T + 1, R.value), RM));
+        v[R.value] = c.lds_load(rbase + off);
+      }
+    });
+    if constexpr (WL) c.wave_sync(); else c.barrier();
+  });
+}
+
+// ------------------------------------------------------------------ quantize + pack
+
+// Rounding by the float adder: for |t| < 2^22, fma(u, mul, 1.5*2^23 + OFF) is
+// 1.5*2^23 + OFF + RNE(u*mul), so the low mantissa bits hold RNE(u*mul) + OFF as an
+// unsigned integer (single rounding of the exact product: round half to even).
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
+
+// Horner-combine m magic floats (each 0x4B400000 + t_i, 0 <= t_i < 2^bits) into
+// sum t_i << (bits*i), then remove the constant and flip the offset-binary sign bit of
+// every field to get two's complement fields.
+template <int M, int BITS>
+RBQ_HD uint32_t combine_fields(const float* f) {
+  uint32_t acc = 0;
+  static_for<0, M>([&](auto I) {
+    acc = (acc << BITS) + f32_bits(f[M - 1 - I.value]);
+  });
+  constexpr uint32_t ones = [] {
+    uint32_t s = 0;
+    for (int i = 0; i < M; ++i) s += 1u << (BITS * i);
+    return s;
+  }();
+  constexpr uint32_t C = 0x4B400000u * ones;
+  constexpr uint32_t X = (BITS == 4 ? 8u : 0x80u) * ones;
+  return (acc - C) ^ X;
+}
+
+// Round u / d half to even exactly, given mk ~= 1/d (d > 0, or mk == 0 for a zero
+// scale). The product u * mk can sit on the other side of a half-integer than the exact
+// quotient; the sign of u - b*d at the nearest boundary b, computed exactly by a fused
+// multiply-add, settles it. Used where exact ties are frequent: quantizing the input as
+// is, and rows of length 4, 16 or 64, whose transform is usually exact in float and
+// whose sqrt(n) is a power of two (for odd log2 n the quotient is irrational).
+RBQ_HD float round_quotient_exact(float u, float mk, float d) {
+  const float t = u * mk;
+  const float q0 = rintf(t);
+  if (mk == 0.0f) return 0.0f;
+  const float dl = t - q0;
+  const float b = q0 + (dl >= 0.0f ? 0.5f : -0.5f);
+  const float e = fmaf(-b, d, u);  // sign(u/d - b), exact
+  const bool odd = (((int)q0) & 1) != 0;
+  if (dl >= 0.0f) {
+    if (e > 0.0f || (e == 0.0f && odd)) return q0 + 1.0f;
+  } else {
+    if (e < 0.0f || (e == 0.0f && odd)) return q0 - 1.0f;
+  }
+  return q0;
+}
+
+template <int K, int PH, bool ROT, int IN, class Ctx>
+RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
+                   float (&v)[1 << PlanOf<K>::value.e]) {
+  constexpr int E = 1 << PlanOf<K>::value.e;
+  constexpr uint32_t RRM = reg_row_mask(PlanOf<K>::value, PH);
+  constexpr int NRR = popcount_c(RRM);
+  constexpr int NC = 1 << NRR;
+  constexpr uint32_t LEM = lane_elem_mask(PlanOf<K>::value, PH);
+  constexpr uint32_t WEM = wave_elem_mask(PlanOf<K>::value, PH);
+  constexpr int N = 1 << K;
+  constexpr float SQRTN = ROT ? sqrt_pow2(K) : 1.0f;
+  constexpr float SEVEN_SQRTN = 7.0f * SQRTN;
+  constexpr float INV_SQRTN = ROT ? 1.0f / sqrt_pow2(K) : 1.0f;
+  // exact rounding decisions where the quotient is exact often enough to tie
+  constexpr bool EXACT = !ROT || (K <= 6 && (K % 2) == 0);
+
+  // ---- per-row absmax of |u|
+  float m[NC];
+  static_for<0, NC>([&](auto C) { m[C.value] = 0.0f; });
+  static_for<0, E>([&](auto R) {
+    constexpr int ci = (int)pext_c(R.value, RRM);
+    m[ci] = fmaxf(m[ci], fabsf(v[R.value]));
+  });
+  static_for<0, 6>([&](auto B) {
+    if constexpr ((LEM >> B.value) & 1u) {
+      static_for<0, NC>([&](auto C) {
+        m[C.value] = fmaxf(m[C.value], c.shfl_xor(m[C.value], 1 << B.value));
+      });
+    }
+  });
+  if constexpr (WEM != 0) {
+    static_assert(NC == 1, "cross-wave reduction assumes one row per workgroup");
+    constexpr uint32_t RED = lds_words(PlanOf<K>::value);
+    if (c.lane == 0) c.lds_store(RED + c.wave, m[0]);
+    c.barrier();
+    float mm = 0.0f;
+    static_for<0, (1 << PlanOf<K>::value.w)>([&](auto W) { mm = fmaxf(mm, c.lds_load(RED + W.value)); });
+    m[0] = mm;
+  }
+
+  // ---- per-row scale and multiplier
+  const uint32_t mode = t.mode;
+  const bool scale_f16 = (a.opts & OPT_SCALE_F16) != 0;
+  const uint32_t lp = lane_part<K, PH>(c.lane, c.wave);
+  const bool leader = ((c.lane & LEM) == 0) && ((c.wave & WEM) == 0);
+  float mul[NC];
+  float divv[NC];
+  bool clampv[NC];
+  static_for<0, NC>([&](auto C) {
+    const float mu = m[C.value];
+    float s = mu / SEVEN_SQRTN;
+    s = fmaxf(s, 1e-8f);
+    float s_st;
+    uint32_t h16 = 0;
+    if (scale_f16) { h16 = f32_to_f16(s); s_st = f16_to_f32(h16); }
+    else s_st = s;
+    const float mk = (s_st == 0.0f) ? 0.0f : 1.0f / (s_st * SQRTN);
+    mul[C.value] = mk;
+    divv[C.value] = s_st * SQRTN;
+    clampv[C.value] = (mu * mk) > 7.25f;
+    if (mode & MODE_QUANT) {
+      constexpr uint32_t rp = reg_part(PlanOf<K>::value, PH, pdep_c((uint32_t)C.value, RRM));
+      const int64_t row = row0 + (int64_t)((lp | rp) >> K);
+      if (leader && row < a.rows) {
+        if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + row, (uint16_t)h16);
+        else c.template store<float>((float*)t.scales + row, s_st);
+      }
+    }
+  });
+
+  // ---- codes and optional rotated output, one contiguous run of L elements at a time
+  constexpr int CF = run_log(PlanOf<K>::value, PH);
+  constexpr int L = 1 << CF;
+  constexpr int NRUN = E / L;
+  const bool packed = (a.opts & OPT_PACKED) != 0;
+  static_for<0, NRUN>([&](auto J) {
+    constexpr uint32_t rb = (uint32_t)J.value << CF;
+    constexpr uint32_t rp = reg_part(PlanOf<K>::value, PH, rb);
+    constexpr int ci = (int)pext_c(rb, RRM);
+    const uint32_t idx = lp | rp;
+    const int64_t row = row0 + (int64_t)(idx >> K);
+    const uint32_t el = idx & (uint32_t)(N - 1);
+    if (row >= a.rows) return;
+    if (mode & MODE_QUANT) {
+      const float mk = mul[ci];
+      if (packed) {
+        constexpr int NW = (L >= 8) ? L / 8 : 1;   // output dwords (or one short field)
+        constexpr int PER = (L >= 8) ? 8 : L;
+        uint32_t out[NW];
+        auto quant = [&](auto CL) {
+          constexpr bool CLAMP = decltype(CL)::value != 0;
+          static_for<0, NW>([&](auto D) {
+            float f[PER];
+            static_for<0, PER>([&](auto I) {
+              float q;
+              if constexpr (EXACT) {
+                q = round_quotient_exact(v[rb + PER * D.value + I.value], mk, divv[ci]) + (kMagic + 8.0f);
+              } else {
+                q = fmaf(v[rb + PER * D.value + I.value], mk, kMagic + 8.0f);
+              }
+              if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic), kMagic + 15.0f);
+              f[I.value] = q;
+            });
+            out[D.value] = combine_fields<PER, 4>(f);
+          });
+        };
+        if (clampv[ci]) quant(IC<1>{}); else quant(IC<0>{});
+        uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)(N / 2) + el / 2;
+        if constexpr (L >= 32) {
+          static_for<0, L / 32>([&](auto Q) {
+            c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
+          });
+        } else if constexpr (L == 16) {
+          c.template store<u32x2>(dst, u32x2{out[0], out[1]});
+        } else if constexpr (L == 8) {
+          c.template store<uint32_t>(dst, out[0]);
+        } else if constexpr (L == 4) {
+          c.template store<uint16_t>(dst, (uint16_t)out[0]);
+        } else {
+          c.template store<uint8_t>(dst, (uint8_t)out[0]);
+        }
+      } else {
+        constexpr int NW = (L >= 4) ? L / 4 : 1;
+        constexpr int PER = (L >= 4) ? 4 : L;
+        uint32_t out[NW];
+        auto quant = [&](auto CL) {
+          constexpr bool CLAMP = decltype(CL)::value != 0;
+          static_for<0, NW>([&](auto D) {
+            float f[PER];
+            static_for<0, PER>([&](auto I) {
+              float q;
+              if constexpr (EXACT) {
+                q = round_quotient_exact(v[rb + PER * D.value + I.value], mk, divv[ci]) + (kMagic + 128.0f);
+              } else {
+                q = fmaf(v[rb + PER * D.value + I.value], mk, kMagic + 128.0f);
+              }
+              if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic + 120.0f), kMagic + 135.0f);
+              f[I.value] = q;
+            });
+            out[D.value] = combine_fields<PER, 8>(f);
+          });
+        };
+        if (clampv[ci]) quant(IC<1>{}); else quant(IC<0>{});
+        uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)N + el;
+        if constexpr (L >= 16) {
+          static_for<0, L / 16>([&](auto Q) {
+            c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
+          });
+        } else if constexpr (L == 8) {
+          c.template store<u32x2>(dst, u32x2{out[0], out[1]});
+        } else if constexpr (L == 4) {
+          c.template store<uint32_t>(dst, out[0]);
+        } else {
+          c.template store<uint16_t>(dst, (uint16_t)out[0]);
+        }
+      }
+    }
+    if (mode & MODE_ROT32) {
+      float* dst = t.rot32 + row * (int64_t)N + el;
+      if constexpr (L >= 4) {
+        static_for<0, L / 4>([&](auto Q) {
+          constexpr int o = 4 * Q.value;
+          c.template store<f32x4>(dst + o, f32x4{v[rb + o] * INV_SQRTN, v[rb + o + 1] * INV_SQRTN, v[rb + o + 2] * INV_SQRTN, v[rb + o + 3] * INV_SQRTN});
+        });
+      } else {
+        static_for<0, L>([&](auto I) { c.template store<float>(dst + I.value, v[rb + I.value] * INV_SQRTN); });
+      }
+    }
+    if (mode & MODE_ROT16) {
+      uint16_t* dst = t.rot16 + row * (int64_t)N + el;
+      constexpr int NW = (L >= 2) ? L / 2 : 1;
+      uint32_t out[NW];
+      static_for<0, NW>([&](auto D) {
+        const float y0 = v[rb + 2 * D.value] * INV_SQRTN;
+        const float y1 = v[rb + 2 * D.value + 1] * INV_SQRTN;
+        if constexpr (IN == IN_F16) out[D.value] = f32_to_f16(y0) | (f32_to_f16(y1) << 16);
+        else out[D.value] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
+      });
+      if constexpr (L >= 8) {
+        static_for<0, L / 8>([&](auto Q) {
+          c.template store<u32x4>((char*)dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
+        });
+      } else if constexpr (L == 4) {
+        c.template store<u32x2>(dst, u32x2{out[0], out[1]});
+      } else {
+        c.template store<uint32_t>(dst, out[0]);
+      }
+    }
+  });
+}
+
+// ------------------------------------------------------------------ the workgroup body
+
+template <int K, int IN, bool ROT, bool FOURD, class Ctx>
+RBQ_HD void fwht_quant_wg(Ctx& c, const KArgs& a, uint32_t block) {
+  const bool second = block >= a.blocks0;
+  const TensorArgs& t = second ? a.t[1] : a.t[0];
+  const uint32_t blk = second ? block - a.blocks0 : block;
+  const int64_t row0 = (int64_t)blk << PlanOf<K>::value.r;
+  float v[1 << PlanOf<K>::value.e];
+  load_phase0<K, IN, ROT, FOURD>(c, t, a.rows, row0, v);
+  if constexpr (ROT) {
+    stages<K, 0, IN != IN_F32>(v);
+    if constexpr (PlanOf<K>::value.nph >= 2) {
+      transpose<K, 0>(c, v);
+      stages<K, 1, false>(v);
+    }
+    if constexpr (PlanOf<K>::value.nph >= 3) {
+      transpose<K, 1>(c, v);
+      stages<K, 2, false>(v);
+    }
+    finish<K, PlanOf<K>::value.nph - 1, true, IN>(c, t, a, row0, v);
+  } else {
+    finish<K, 0, false, IN>(c, t, a, row0, v);
+  }
+}
+
+}  // namespace rbq

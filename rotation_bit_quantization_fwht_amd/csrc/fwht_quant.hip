@@ -1,0 +1,133 @@
+// HIP kernels and C-ABI entry points for the fused Hadamard rotation + INT4 quantizer:
+// hadamard_quant_int4 (rows of any length 2..32768; the R4 down-projection path and
+// offline weight rotation) and kv_rotate_quant (R3 on post-RoPE Q and K per head).
+// The workgroup body lives in fwht_engine.h, the gfx950 context in devctx.h and the
+// kernel instantiations (one translation unit per row length) in fwht_kernels.hip; this
+// file validates arguments, fills the kernel arguments and dispatches on log2 n.
+#include <hip/hip_runtime.h>
+
+#include "../../include/rbq.h"
+#include "fwht_engine.h"
+#include "validate.h"
+
+namespace rbq {
+
+template <int K>
+hipError_t fwht_launch(const KArgs& a, uint32_t grid, int in, bool rot, bool fourd, hipStream_t s);
+
+static hipError_t dispatch(int k, const KArgs& a, uint32_t grid, int in, bool rot, bool fourd,
+                           hipStream_t s) {
+  switch (k) {
+    case 1: return fwht_launch<1>(a, grid, in, rot, fourd, s);
+    case 2: return fwht_launch<2>(a, grid, in, rot, fourd, s);
+    case 3: return fwht_launch<3>(a, grid, in, rot, fourd, s);
+    case 4: return fwht_launch<4>(a, grid, in, rot, fourd, s);
+    case 5: return fwht_launch<5>(a, grid, in, rot, fourd, s);
+    case 6: return fwht_launch<6>(a, grid, in, rot, fourd, s);
+    case 7: return fwht_launch<7>(a, grid, in, rot, fourd, s);
+    case 8: return fwht_launch<8>(a, grid, in, rot, fourd, s);
+    case 9: return fwht_launch<9>(a, grid, in, rot, fourd, s);
+    case 10: return fwht_launch<10>(a, grid, in, rot, fourd, s);
+    case 11: return fwht_launch<11>(a, grid, in, rot, fourd, s);
+    case 12: return fwht_launch<12>(a, grid, in, rot, fourd, s);
+    case 13: return fwht_launch<13>(a, grid, in, rot, fourd, s);
+    case 14: return fwht_launch<14>(a, grid, in, rot, fourd, s);
+    case 15: return fwht_launch<15>(a, grid, in, rot, fourd, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+static int rows_log(int k) {
+  switch (k) {
+    case 1: return PlanOf<1>::value.r;   case 2: return PlanOf<2>::value.r;
+    case 3: return PlanOf<3>::value.r;   case 4: return PlanOf<4>::value.r;
+    case 5: return PlanOf<5>::value.r;   case 6: return PlanOf<6>::value.r;
+    case 7: return PlanOf<7>::value.r;   case 8: return PlanOf<8>::value.r;
+    case 9: return PlanOf<9>::value.r;   case 10: return PlanOf<10>::value.r;
+    case 11: return PlanOf<11>::value.r; case 12: return PlanOf<12>::value.r;
+    case 13: return PlanOf<13>::value.r; case 14: return PlanOf<14>::value.r;
+    default: return PlanOf<15>::value.r;
+  }
+}
+
+static int in_kind(rbq_dtype d) { return d == RBQ_F32 ? IN_F32 : (d == RBQ_BF16 ? IN_BF16 : IN_F16); }
+
+}  // namespace rbq
+
+using namespace rbq;
+
+extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int64_t n,
+                                          int64_t tokens, int64_t x_row_stride, void* codes,
+                                          void* scales, rbq_dtype scale_dtype, float* rotated,
+                                          unsigned flags, hipStream_t stream) {
+  const HqCheck chk = check_hadamard_quant(x, x_dtype, n, tokens, x_row_stride, codes, scales,
+                                           scale_dtype, rotated, flags);
+  if (chk.status != RBQ_OK || tokens == 0) return chk.status;
+  const int rl = rows_log(chk.k);
+  const int64_t blocks = (tokens + (int64_t{1} << rl) - 1) >> rl;
+  if (blocks > 0x7FFFFFFF) return RBQ_EINVAL;
+  KArgs a{};
+  TensorArgs& t = a.t[0];
+  t.x = x;
+  t.row_stride = x_row_stride;
+  t.codes = codes;
+  t.scales = scales;
+  t.rot32 = rotated;
+  t.mode = MODE_QUANT | (rotated ? MODE_ROT32 : 0u);
+  a.t[1] = t;
+  a.rows = tokens;
+  a.blocks0 = (uint32_t)blocks;
+  a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
+  const bool rot = (flags & RBQ_NO_ROTATE) == 0;
+  if (dispatch(chk.k, a, (uint32_t)blocks, in_kind(x_dtype), rot, false, stream) != hipSuccess)
+    return RBQ_EHIP;
+  return RBQ_OK;
+}
+
+extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dtype, int64_t batch,
+                                      int64_t heads, int64_t seq, int64_t head_dim,
+                                      const int64_t q_strides[4], const int64_t k_strides[4],
+                                      uint8_t* q_codes, void* q_scales, uint8_t* k_codes,
+                                      void* k_scales, rbq_dtype scale_dtype, void* q_rotated,
+                                      unsigned flags, hipStream_t stream) {
+  const KvCheck chk = check_kv(q, k, dtype, batch, heads, seq, head_dim, q_strides, k_strides,
+                               q_codes, q_scales, k_codes, k_scales, scale_dtype, q_rotated, flags);
+  if (chk.status != RBQ_OK) return chk.status;
+  if (batch == 0 || heads == 0 || seq == 0) return RBQ_OK;
+  if (!chk.flat && (chk.k < 6 || chk.k > 8)) return RBQ_ENOTSUP;  // strided only for d in {64,128,256}
+  const int64_t rows = batch * heads * seq;
+  const int rl = rows_log(chk.k);
+  const int64_t blocks = (rows + (int64_t{1} << rl) - 1) >> rl;
+  if (2 * blocks > 0x7FFFFFFF) return RBQ_EINVAL;
+  KArgs a{};
+  const bool rot_only = (flags & RBQ_Q_ROTATE_ONLY) != 0;
+  const void* src[2] = {q, k};
+  const int64_t* st[2] = {q_strides, k_strides};
+  const int64_t rs[2] = {chk.q_rs, chk.k_rs};
+  for (int i = 0; i < 2; ++i) {
+    TensorArgs& t = a.t[i];
+    t.x = src[i];
+    t.row_stride = rs[i];
+    t.sb = st[i][0];
+    t.sh = st[i][1];
+    t.ss = st[i][2];
+    t.seq = (uint32_t)seq;
+    t.heads = (uint32_t)heads;
+    t.div_s = make_fastdiv((uint32_t)seq);
+    t.div_h = make_fastdiv((uint32_t)heads);
+  }
+  a.t[0].codes = q_codes;
+  a.t[0].scales = q_scales;
+  a.t[0].rot16 = (uint16_t*)q_rotated;
+  a.t[0].mode = rot_only ? MODE_ROT16 : MODE_QUANT;
+  a.t[1].codes = k_codes;
+  a.t[1].scales = k_scales;
+  a.t[1].mode = MODE_QUANT;
+  a.rows = rows;
+  a.blocks0 = (uint32_t)blocks;
+  a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
+  if (dispatch(chk.k, a, (uint32_t)(2 * blocks), in_kind(dtype), true, !chk.flat, stream) !=
+      hipSuccess)
+    return RBQ_EHIP;
+  return RBQ_OK;
+}

@@ -1,0 +1,199 @@
+// Host execution of the fused Hadamard + INT4 quantizer's workgroup body (the same
+// template code the HIP kernel runs), one std::thread per GPU lane, with LDS, workgroup
+// barriers, wave-level synchronisation and lane shuffles emulated, and every global and
+// LDS access bounds-checked. Used by tests/test_host_emulator.py to validate the data
+// layouts and index arithmetic on the CPU before anything runs on a GPU.
+//
+// usage: fwht_emu K IN ROT FOURD rows opts mode0 x.bin x_elems row_stride
+//                 codes.bin scales.bin [B H S sb sh ss]
+// (the rotated output, when requested by mode0, is written to codes.bin + ".rot")
+#include <barrier>
+#include <cstdio>
+#include <cstdlib>
+#include <memory>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../rotation_bit_quantization_fwht_amd/csrc/fwht_engine.h"
+
+using namespace rbq;
+
+struct Buf { const char* lo; const char* hi; const char* name; };
+static std::vector<Buf> g_bufs;
+
+static void check_ptr(const void* p, size_t n, const char* what) {
+  const char* c = (const char*)p;
+  for (auto& b : g_bufs)
+    if (c >= b.lo && c + n <= b.hi) return;
+  fprintf(stderr, "OUT OF BOUNDS %s access at %p (+%zu)\n", what, p, n);
+  std::abort();
+}
+
+struct WgShared {
+  std::vector<float> lds;
+  std::barrier<> wg;
+  std::vector<std::unique_ptr<std::barrier<>>> wave_bar;
+  std::vector<std::vector<float>> shfl;
+  WgShared(size_t lds_words, int nthreads, int nwaves)
+      : lds(lds_words, -12345.0f), wg(nthreads) {
+    for (int w = 0; w < nwaves; ++w) {
+      wave_bar.emplace_back(new std::barrier<>(64));
+      shfl.emplace_back(64, 0.0f);
+    }
+  }
+};
+
+struct HostCtx {
+  uint32_t lane, wave;
+  WgShared* s;
+  void barrier() { s->wg.arrive_and_wait(); }
+  void wave_sync() { s->wave_bar[wave]->arrive_and_wait(); }
+  float shfl_xor(float v, int m) {
+    s->shfl[wave][lane] = v;
+    s->wave_bar[wave]->arrive_and_wait();
+    float r = s->shfl[wave][lane ^ (uint32_t)m];
+    s->wave_bar[wave]->arrive_and_wait();
+    return r;
+  }
+  template <class T> T load(const void* p) {
+    check_ptr(p, sizeof(T), "load");
+    if ((uintptr_t)p % alignof(T)) { fprintf(stderr, "MISALIGNED load\n"); std::abort(); }
+    T v; memcpy(&v, p, sizeof(T)); return v;
+  }
+  template <class T> void store(void* p, T v) {
+    check_ptr(p, sizeof(T), "store");
+    if ((uintptr_t)p % alignof(T)) { fprintf(stderr, "MISALIGNED store\n"); std::abort(); }
+    memcpy(p, &v, sizeof(T));
+  }
+  void lds_store(uint32_t i, float v) {
+    if (i >= s->lds.size()) { fprintf(stderr, "LDS OOB store %u/%zu\n", i, s->lds.size()); std::abort(); }
+    s->lds[i] = v;
+  }
+  float lds_load(uint32_t i) {
+    if (i >= s->lds.size()) { fprintf(stderr, "LDS OOB load %u/%zu\n", i, s->lds.size()); std::abort(); }
+    return s->lds[i];
+  }
+  template <int IN> void widen(uint32_t w, float& a, float& b) {
+    if (IN == IN_BF16) { a = bf16_to_f32(w & 0xFFFFu); b = bf16_to_f32(w >> 16); }
+    else { a = f16_to_f32(w & 0xFFFFu); b = f16_to_f32(w >> 16); }
+  }
+  template <int IN> void widen_butterfly(uint32_t w, float& a, float& b) {
+    float x0, x1;
+    widen<IN>(w, x0, x1);
+    a = x0 + x1;
+    b = x0 - x1;
+  }
+};
+
+template <int K, int IN, bool ROT, bool FOURD>
+static void run(const KArgs& a, uint32_t grid) {
+  constexpr const Plan& P = PlanOf<K>::value;
+  const int nthreads = 64 << P.w;
+  for (uint32_t blk = 0; blk < grid; ++blk) {
+    WgShared sh(lds_words(P) + (1u << P.w) + 1, nthreads, 1 << P.w);
+    std::vector<std::thread> th;
+    for (int t = 0; t < nthreads; ++t)
+      th.emplace_back([&, t] {
+        HostCtx c{(uint32_t)(t & 63), (uint32_t)(t >> 6), &sh};
+        fwht_quant_wg<K, IN, ROT, FOURD>(c, a, blk);
+      });
+    for (auto& x : th) x.join();
+  }
+}
+
+template <int K>
+static void run_k(const KArgs& a, uint32_t grid, int in, bool rot, bool fourd) {
+  if (fourd) {
+    if (in == IN_BF16) run<K, IN_BF16, true, true>(a, grid);
+    else run<K, IN_F16, true, true>(a, grid);
+    return;
+  }
+  if (in == IN_F32) { if (rot) run<K, IN_F32, true, false>(a, grid); else run<K, IN_F32, false, false>(a, grid); }
+  else if (in == IN_BF16) { if (rot) run<K, IN_BF16, true, false>(a, grid); else run<K, IN_BF16, false, false>(a, grid); }
+  else { if (rot) run<K, IN_F16, true, false>(a, grid); else run<K, IN_F16, false, false>(a, grid); }
+}
+
+static std::vector<char> read_file(const char* path) {
+  FILE* f = fopen(path, "rb");
+  if (!f) { perror(path); std::exit(2); }
+  fseek(f, 0, SEEK_END); long n = ftell(f); fseek(f, 0, SEEK_SET);
+  std::vector<char> v(n);
+  if (n && fread(v.data(), 1, n, f) != (size_t)n) { perror("read"); std::exit(2); }
+  fclose(f);
+  return v;
+}
+
+static void write_file(const char* path, const void* p, size_t n) {
+  FILE* f = fopen(path, "wb");
+  if (!f) { perror(path); std::exit(2); }
+  if (n) fwrite(p, 1, n, f);
+  fclose(f);
+}
+
+int main(int argc, char** argv) {
+  if (argc < 13) { fprintf(stderr, "bad args\n"); return 2; }
+  const int K = atoi(argv[1]), in = atoi(argv[2]), rot = atoi(argv[3]), fourd = atoi(argv[4]);
+  const long long rows = atoll(argv[5]);
+  const unsigned opts = (unsigned)atoi(argv[6]), mode0 = (unsigned)atoi(argv[7]);
+  std::vector<char> x = read_file(argv[8]);
+  const long long row_stride = atoll(argv[10]);
+  const long long n = 1ll << K;
+  const int esz = in == IN_F32 ? 4 : 2;
+  // 16-byte aligned copies with exact-size registration (bounds checks are tight)
+  auto alloc = [](size_t bytes) { return (char*)aligned_alloc(64, ((bytes + 63) / 64) * 64 + 64); };
+  char* xb = alloc(x.size());
+  memcpy(xb, x.data(), x.size());
+  const size_t code_bytes = (size_t)rows * ((opts & OPT_PACKED) ? n / 2 : n);
+  const size_t scale_bytes = (size_t)rows * ((opts & OPT_SCALE_F16) ? 2 : 4);
+  const size_t rot_bytes = (size_t)rows * n * ((mode0 & MODE_ROT16) ? 2 : 4);
+  char* codes = alloc(code_bytes);
+  char* scales = alloc(scale_bytes);
+  char* rotb = alloc(rot_bytes);
+  memset(codes, 0xEE, code_bytes); memset(scales, 0xEE, scale_bytes); memset(rotb, 0xEE, rot_bytes);
+  g_bufs.push_back({xb, xb + x.size(), "x"});
+  g_bufs.push_back({codes, codes + code_bytes, "codes"});
+  g_bufs.push_back({scales, scales + scale_bytes, "scales"});
+  g_bufs.push_back({rotb, rotb + rot_bytes, "rot"});
+  KArgs a{};
+  TensorArgs& t = a.t[0];
+  t.x = xb;
+  t.row_stride = row_stride;
+  t.codes = codes; t.scales = scales;
+  t.rot32 = (mode0 & MODE_ROT32) ? (float*)rotb : nullptr;
+  t.rot16 = (mode0 & MODE_ROT16) ? (uint16_t*)rotb : nullptr;
+  t.mode = mode0;
+  if (argc >= 19) {
+    const long long B = atoll(argv[13]), H = atoll(argv[14]), S = atoll(argv[15]);
+    t.sb = atoll(argv[16]); t.sh = atoll(argv[17]); t.ss = atoll(argv[18]);
+    t.seq = (uint32_t)S; t.heads = (uint32_t)H;
+    t.div_s = make_fastdiv((uint32_t)S); t.div_h = make_fastdiv((uint32_t)H);
+    (void)B;
+  }
+  a.t[1] = t;
+  a.rows = rows;
+  int rl = 0;
+  switch (K) {
+#define RL(k) case k: rl = PlanOf<k>::value.r; break;
+    RL(1) RL(2) RL(3) RL(4) RL(5) RL(6) RL(7) RL(8) RL(9) RL(10) RL(11) RL(12) RL(13) RL(14) RL(15)
+#undef RL
+  }
+  const uint32_t grid = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
+  a.blocks0 = grid;
+  a.opts = opts;
+  (void)esz;
+  switch (K) {
+#define RK(k) case k: run_k<k>(a, grid, in, rot != 0, fourd != 0); break;
+    RK(1) RK(2) RK(3) RK(4) RK(5) RK(6) RK(7) RK(8) RK(9) RK(10) RK(11) RK(12) RK(13) RK(14) RK(15)
+#undef RK
+    default: return 2;
+  }
+  write_file(argv[11], codes, code_bytes);
+  write_file(argv[12], scales, scale_bytes);
+  // rotated output goes next to the codes file with suffix ".rot"
+  if (mode0 & (MODE_ROT32 | MODE_ROT16)) {
+    std::string p = std::string(argv[11]) + ".rot";
+    write_file(p.c_str(), rotb, rot_bytes);
+  }
+  return 0;
+}

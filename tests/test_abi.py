@@ -1,0 +1,136 @@
+"""CPU tests of the C ABI: the library loads, exports every function include/rbq.h
+declares, and rejects invalid arguments on the host (before any HIP call, so these run
+without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rotation_bit_quantization_fwht_amd as rbq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rbq.h")
+
+
+@pytest.fixture(scope="session")
+def L():
+    if not os.path.exists(rbq.library_path()):
+        from rotation_bit_quantization_fwht_amd.build import build
+
+        build()
+    return rbq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(rbq.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", rbq.library_path()], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings_and_version(L):
+    assert L.rbq_status_string(rbq.RBQ_OK) == b"RBQ_OK"
+    for s in (rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP, rbq.RBQ_EHIP):
+        assert L.rbq_status_string(s).startswith(b"RBQ_E")
+    assert L.rbq_status_string(99) == b"RBQ_UNKNOWN"
+    assert b"gfx950" in L.rbq_version()
+
+
+A16 = ctypes.c_void_p(0x10000)  # a 16-byte aligned fake device address (never dereferenced)
+A16b = ctypes.c_void_p(0x20000)
+A16c = ctypes.c_void_p(0x30000)
+NULL = None
+
+
+def hq(L, x=A16, dt=rbq.RBQ_BF16, n=4096, tokens=8, stride=4096, codes=A16b, scales=A16c,
+       sdt=rbq.RBQ_F16, rot=NULL, flags=rbq.RBQ_PACKED):
+    return L.hadamard_quant_int4(x, dt, n, tokens, stride, codes, scales, sdt, rot, flags, NULL)
+
+
+def test_hadamard_quant_validation(L):
+    E = rbq.RBQ_EINVAL
+    assert hq(L, tokens=0) == rbq.RBQ_OK
+    assert hq(L, x=NULL, codes=NULL, scales=NULL, tokens=0) == rbq.RBQ_OK
+    for n in (0, 1, 3, 6, 4095, 65536, -4):
+        assert hq(L, n=n, stride=max(n, 1)) == E, n
+    assert hq(L, tokens=-1) == E
+    assert hq(L, x=NULL) == E
+    assert hq(L, codes=NULL) == E
+    assert hq(L, scales=NULL) == E
+    assert hq(L, stride=4095) == E
+    assert hq(L, stride=4100) == E  # 8200-byte rows are not 16-byte aligned
+    assert hq(L, x=ctypes.c_void_p(0x10008)) == E
+    assert hq(L, codes=ctypes.c_void_p(0x20004)) == E
+    assert hq(L, rot=ctypes.c_void_p(0x40004)) == E
+    assert hq(L, dt=7) == E
+    assert hq(L, sdt=rbq.RBQ_BF16) == E
+    assert hq(L, flags=0x80) == E
+    assert hq(L, flags=rbq.RBQ_Q_ROTATE_ONLY) == E
+    # tiny rows only need element alignment of the row size
+    assert hq(L, n=2, stride=2, x=ctypes.c_void_p(0x10004), tokens=0) == rbq.RBQ_OK
+
+
+def kv(L, q=A16, k=A16b, dt=rbq.RBQ_BF16, B=2, H=4, S=16, D=128, qs=None, ks=None, qc=A16c, qsc=A16c,
+       kc=A16c, ksc=A16c, sdt=rbq.RBQ_F16, qrot=NULL, flags=0):
+    def st(v):
+        return (ctypes.c_int64 * 4)(*v) if v is not None else (ctypes.c_int64 * 4)(H * S * D, S * D, D, 1)
+    return L.kv_rotate_quant(q, k, dt, B, H, S, D, st(qs), st(ks), qc, qsc, kc, ksc, sdt, qrot, flags, NULL)
+
+
+def test_kv_validation(L):
+    E = rbq.RBQ_EINVAL
+    assert kv(L, S=0) == rbq.RBQ_OK
+    assert kv(L, D=96) == E
+    assert kv(L, D=4) == E
+    assert kv(L, dt=rbq.RBQ_F32) == E
+    assert kv(L, B=-1) == E
+    assert kv(L, q=NULL) == E
+    assert kv(L, kc=NULL) == E
+    assert kv(L, qc=NULL) == E
+    assert kv(L, qc=NULL, qsc=NULL, flags=rbq.RBQ_Q_ROTATE_ONLY) == E  # needs q_rotated
+    assert kv(L, qs=(4 * 16 * 128, 16 * 128, 128, 2)) == E  # d stride must be 1
+    assert kv(L, qs=(4 * 16 * 128, 16 * 128, 132, 1)) == E  # vector starts not 16-byte aligned
+    assert kv(L, flags=rbq.RBQ_PACKED) == E
+    # a non-flattenable layout needs head_dim 64/128/256
+    assert kv(L, D=512, qs=(16 * 4 * 512, 512, 4 * 512, 1), ks=(16 * 4 * 512, 512, 4 * 512, 1)) == rbq.RBQ_ENOTSUP
+
+
+def test_gemm_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+
+    def g(qa=A16, sa=A16b, qw=A16c, sw=A16b, sdt=rbq.RBQ_F16, M=64, N=64, K=4096, out=A16, acc=NULL):
+        return L.w4a4_gemm(qa, sa, qw, sw, sdt, M, N, K, out, acc, NULL)
+
+    assert g(M=0) == rbq.RBQ_OK
+    assert g(N=0, out=NULL) == rbq.RBQ_OK
+    assert g(K=0) == E
+    assert g(K=4097) == E
+    assert g(M=-1) == E
+    assert g(qa=NULL) == E
+    assert g(out=NULL) == E
+    assert g(sdt=rbq.RBQ_BF16) == E
+    assert g(qa=ctypes.c_void_p(0x10001)) == E
+    assert g(K=4000) == NS
+    assert g(N=60) == NS
+    assert g(K=262144) == NS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("RBQ_LIBRARY", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(rbq, "_lib", None)
+    with pytest.raises(rbq.LibraryMissing):
+        rbq.lib()

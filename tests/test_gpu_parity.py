@@ -1,0 +1,237 @@
+"""GPU parity of the fused Hadamard + INT4 quantizer (hadamard_quant_int4) and the R3
+per-head op (kv_rotate_quant) against the fp64 oracle, through the C ABI.
+
+Small cases are checked element by element; the full workload sizes, in the launch
+configuration the benchmark times, are checked on sampled rows the oracle computes one
+by one plus properties that hold for every row.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import check_quant
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rbq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotation_bit_quantization_fwht_amd as m
+
+    m.lib()  # raises if the library is missing: no fallback
+    return m
+
+
+def to_dev(x, dtype):
+    if dtype == "float32":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+        t = t.view(torch.bfloat16 if dtype == "bfloat16" else torch.float16)
+    return t.cuda()
+
+
+def unpack(codes_dev):
+    return oracle.unpack_nibbles(codes_dev.cpu().numpy())
+
+
+ROWS = {1: 8200, 2: 4100, 3: 2050, 4: 1030, 5: 515, 6: 260, 7: 131, 8: 70, 9: 35, 10: 17, 11: 9, 12: 5,
+        13: 3, 14: 3, 15: 2}
+
+
+@pytest.mark.parametrize("k", list(range(1, 16)))
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32", "float16"])
+def test_rotate_quant_all_sizes(rbq, k, dtype):
+    n, rows = 1 << k, ROWS[k]
+    print(f"case hadamard_quant_int4 k={k} dtype={dtype} rows={rows}", flush=True)
+    x = workloads.gen_rows(k, rows, n, dtype, kind="swiglu", n_outliers=1, factor=150)
+    codes, scales, rot = rbq.hadamard_quant_int4(to_dev(x, dtype), return_rotated=True)
+    torch.cuda.synchronize()
+    x64 = workloads.to_float64(x, dtype)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64, y_gpu=rot.cpu().numpy())
+
+
+@pytest.mark.parametrize("k", [1, 4, 7, 12, 14, 15])
+def test_no_rotate_exact(rbq, k):
+    n, rows = 1 << k, ROWS[k]
+    print(f"case no-rotate k={k}", flush=True)
+    x = workloads.gen_rows(100 + k, rows, n, "bfloat16", n_outliers=1, factor=60)
+    codes, scales, rot = rbq.hadamard_quant_int4(to_dev(x, "bfloat16"), rotate=False, return_rotated=True)
+    x64 = workloads.to_float64(x, "bfloat16")
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, rotate_input=False)
+    st = check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64, rotate=False, y_gpu=rot.cpu().numpy())
+    assert st["code_flips"] == 0
+
+
+def test_edge_token_counts(rbq):
+    for k in (7, 12, 14):
+        n = 1 << k
+        for rows in (0, 1, 3):
+            print(f"case tokens={rows} k={k}", flush=True)
+            x = workloads.gen_rows(500 + rows, max(rows, 1), n, "bfloat16")[:rows]
+            codes, scales = rbq.hadamard_quant_int4(to_dev(x, "bfloat16"))
+            torch.cuda.synchronize()
+            assert codes.shape == (rows, n // 2)
+            if rows:
+                x64 = workloads.to_float64(x, "bfloat16")
+                ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+                check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64)
+
+
+def test_strided_rows_and_output_bounds(rbq):
+    k, n = 12, 4096
+    full = workloads.gen_rows(9, 33, n + 128, "bfloat16", n_outliers=2, factor=90)
+    xd = to_dev(full, "bfloat16")[:, :n]
+    assert xd.stride(0) == n + 128
+    # guard bytes around the outputs must stay untouched
+    codes_buf = torch.full((33 * n // 2 + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    codes = codes_buf[:33 * n // 2].view(33, n // 2)
+    codes, scales = rbq.hadamard_quant_int4(xd, codes=codes)
+    torch.cuda.synchronize()
+    assert torch.all(codes_buf[33 * n // 2:] == 0xA5)
+    x64 = workloads.to_float64(full[:, :n], "bfloat16")
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64)
+
+
+def test_spike_bit_exact(rbq):
+    n, ch = 4096, 142
+    x = np.zeros((3, n), dtype=np.float32)
+    x[0, ch] = 60.0
+    x[1, ch] = -60.0
+    codes, scales, rot = rbq.hadamard_quant_int4(to_dev(x, "float32"), return_rotated=True)
+    ref = oracle.hadamard_quant_int4(x.astype(np.float64), "float16", packed=True)
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref["s_stored"])
+    assert np.array_equal(rot.cpu().numpy().astype(np.float64), ref["y"])
+
+
+def test_worked_example_config_full(rbq):
+    """64 x 4096 fp32, channel 142 = 60: int8 codes + fp32 scales, and the MSE of the
+    dequantized result with and without rotation."""
+    print("case worked example 64x4096", flush=True)
+    x = workloads.gen_worked_example(seed=0)
+    xd = to_dev(x, "float32")
+    codes, scales, rot = rbq.hadamard_quant_int4(xd, scale_dtype=torch.float32, packed=False, return_rotated=True)
+    dcodes, dscales = rbq.hadamard_quant_int4(xd, scale_dtype=torch.float32, packed=False, rotate=False)
+    x64 = x.astype(np.float64)
+    ref = oracle.hadamard_quant_int4(x64, "float32", packed=False)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), ref, "float32", x64, y_gpu=rot.cpu().numpy())
+    dref = oracle.hadamard_quant_int4(x64, "float32", packed=False, rotate_input=False)
+    st = check_quant(dcodes.cpu().numpy(), dscales.cpu().numpy(), dref, "float32", x64, rotate=False)
+    assert st["code_flips"] == 0
+    # MSE from the GPU outputs vs from the oracle (dequantize + rotate back on the host)
+    q, s = codes.cpu().numpy().astype(np.float64), scales.cpu().numpy().astype(np.float64)
+    mse_gpu = oracle.mse(x64, oracle.rotate(q * s[:, None]))
+    mse_ref = oracle.mse(x64, oracle.rotate(oracle.dequantize(ref["q"], ref["s_stored"])))
+    dq, ds = dcodes.cpu().numpy().astype(np.float64), dscales.cpu().numpy().astype(np.float64)
+    mse_direct_gpu = oracle.mse(x64, dq * ds[:, None])
+    mse_direct_ref = oracle.mse(x64, oracle.dequantize(dref["q"], dref["s_stored"]))
+    assert abs(mse_gpu / mse_ref - 1) < 1e-3
+    assert abs(mse_direct_gpu / mse_direct_ref - 1) < 1e-3
+    assert mse_gpu < 0.1 * mse_direct_gpu
+
+
+def test_ffn_config_full_size(rbq):
+    """R4 at the full workload: bf16 [8192, 16384], packed codes, fp16 scales; sampled rows
+    against the oracle, every row against the invariants."""
+    print("case R4 full size 8192x16384", flush=True)
+    xbits, ch = workloads.gen_ffn(seed=0)
+    xd = to_dev(xbits, "bfloat16")
+    codes, scales = rbq.hadamard_quant_int4(xd)
+    codes2, scales2 = rbq.hadamard_quant_int4(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)  # deterministic
+    rows = np.unique(np.concatenate([[0, 1, 8191], np.random.default_rng(3).integers(0, 8192, 29)]))
+    x64 = workloads.to_float64(xbits[rows], "bfloat16")
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    c = codes.cpu().numpy()
+    check_quant(oracle.unpack_nibbles(c[rows]), scales.cpu().numpy()[rows], ref, "float16", x64)
+    # every row: the absmax element lands on +-7, no code is -8, the scale is positive
+    q_all = oracle.unpack_nibbles(c)
+    assert np.all(np.max(np.abs(q_all), axis=1) == 7)
+    assert not np.any(q_all == -8)
+    assert np.all(scales.cpu().numpy().astype(np.float64) > 0)
+
+
+@pytest.mark.parametrize("tokens", workloads.DECODE_TOKENS)
+@pytest.mark.parametrize("n", workloads.DECODE_N)
+def test_decode_sweep_points(rbq, tokens, n):
+    print(f"case decode T={tokens} n={n}", flush=True)
+    xbits, _ = workloads.gen_decode(seed=0, tokens=tokens, n=n)
+    codes, scales = rbq.hadamard_quant_int4(to_dev(xbits, "bfloat16"))
+    sample = np.arange(tokens) if tokens * n <= 64 * 8192 else np.unique(np.linspace(0, tokens - 1, 8).astype(int))
+    x64 = workloads.to_float64(xbits[sample], "bfloat16")
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    check_quant(unpack(codes)[sample], scales.cpu().numpy()[sample], ref, "float16", x64)
+
+
+# ------------------------------------------------------------------ R3: kv_rotate_quant
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "bshd_view"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_kv_small(rbq, layout, D):
+    B, H, S = 2, 3, 45
+    print(f"case kv small D={D} layout={layout}", flush=True)
+    q_bits, k_bits, _ = workloads.gen_kv(seed=D, batch=B, heads=H, seq=S, head_dim=D)
+    if layout == "contiguous":
+        qd, kd = to_dev(q_bits, "bfloat16"), to_dev(k_bits, "bfloat16")
+    else:
+        qd = to_dev(np.ascontiguousarray(q_bits.transpose(0, 2, 1, 3)), "bfloat16").permute(0, 2, 1, 3)
+        kd = to_dev(np.ascontiguousarray(k_bits.transpose(0, 2, 1, 3)), "bfloat16").permute(0, 2, 1, 3)
+    out = rbq.kv_rotate_quant(qd, kd)
+    ref = oracle.kv_rotate_quant(workloads.to_float64(q_bits, "bfloat16"), workloads.to_float64(k_bits, "bfloat16"))
+    for name in ("q", "k"):
+        rows = B * H * S
+        x64 = workloads.to_float64(q_bits if name == "q" else k_bits, "bfloat16").reshape(rows, D)
+        r = {key: ref[name][key].reshape(rows, -1) if ref[name][key].ndim == 4 else ref[name][key].reshape(rows)
+             for key in ("y", "q", "s", "s_stored")}
+        got_q = oracle.unpack_nibbles(out[f"{name}_codes"].cpu().numpy().reshape(rows, D // 2))
+        check_quant(got_q, out[f"{name}_scales"].cpu().numpy().reshape(rows), r, "float16", x64)
+
+
+def test_kv_q_rotate_only(rbq):
+    B, H, S, D = 1, 4, 33, 128
+    q_bits, k_bits, _ = workloads.gen_kv(seed=1, batch=B, heads=H, seq=S, head_dim=D)
+    out = rbq.kv_rotate_quant(to_dev(q_bits, "bfloat16"), to_dev(k_bits, "bfloat16"), q_rotate_only=True)
+    got = out["q_rotated"].float().cpu().numpy().astype(np.float64)
+    want = oracle.round_to_bf16(oracle.rotate(workloads.to_float64(q_bits, "bfloat16")))
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7)
+    assert np.mean(got == want) > 0.999
+    rows = B * H * S
+    x64 = workloads.to_float64(k_bits, "bfloat16").reshape(rows, D)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    check_quant(oracle.unpack_nibbles(out["k_codes"].cpu().numpy().reshape(rows, D // 2)),
+                out["k_scales"].cpu().numpy().reshape(rows), ref, "float16", x64)
+
+
+def test_kv_config_full_size(rbq):
+    """R3 at the full workload: Q and K [16, 32, 2048, 128] bf16 in one call."""
+    print("case R3 full size", flush=True)
+    q_bits, k_bits, ch = workloads.gen_kv(seed=0)
+    qd, kd = to_dev(q_bits, "bfloat16"), to_dev(k_bits, "bfloat16")
+    out = rbq.kv_rotate_quant(qd, kd)
+    out2 = rbq.kv_rotate_quant(qd, kd)
+    torch.cuda.synchronize()
+    for key in out:
+        assert torch.equal(out[key], out2[key])
+    rows_all = 16 * 32 * 2048
+    sample = np.unique(np.concatenate([[0, rows_all - 1], np.random.default_rng(4).integers(0, rows_all, 4000)]))
+    for name, bits in (("q", q_bits), ("k", k_bits)):
+        x64 = workloads.to_float64(bits.reshape(rows_all, 128)[sample], "bfloat16")
+        ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+        c = out[f"{name}_codes"].view(rows_all, 64).cpu().numpy()
+        s = out[f"{name}_scales"].view(rows_all).cpu().numpy()
+        check_quant(oracle.unpack_nibbles(c[sample]), s[sample], ref, "float16", x64)
+        q_all = oracle.unpack_nibbles(c[::97])
+        assert np.all(np.max(np.abs(q_all), axis=1) == 7) and not np.any(q_all == -8)
