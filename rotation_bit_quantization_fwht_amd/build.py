@@ -42,7 +42,9 @@ def _hipcc():
 def _units():
     units = []
     for k in range(KMIN, KMAX + 1):
-        units.append((os.path.join(CSRC, "fwht_kernels.hip"), f"fwht_k{k}.o", [f"-DRBQ_K={k}"]))
+        # the 32-point factor's MFMA results go straight to VGPRs (no AGPR copies)
+        units.append((os.path.join(CSRC, "fwht_kernels.hip"), f"fwht_k{k}.o",
+                      [f"-DRBQ_K={k}", "-mllvm", "-amdgpu-mfma-vgpr-form"]))
     units.append((os.path.join(CSRC, "fwht_quant.hip"), "fwht_quant.o", []))
     units.append((os.path.join(CSRC, "w4a4_gemm.hip"), "w4a4_gemm.o", []))
     units.append((os.path.join(CSRC, "status.cpp"), "status.o", ["-x", "hip"]))

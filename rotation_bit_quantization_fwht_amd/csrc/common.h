@@ -92,6 +92,15 @@ RBQ_HD uint32_t f32_to_f16(float f) {
   return sign | keep;
 }
 
+// Funnel shift: low 32 bits of ({hi, lo} >> s), 0 <= s < 32 (one v_alignbit_b32).
+RBQ_HD uint32_t alignbit(uint32_t hi, uint32_t lo, uint32_t s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_alignbit(hi, lo, s);
+#else
+  return (uint32_t)((((uint64_t)hi << 32) | lo) >> s);
+#endif
+}
+
 // Unsigned division by a runtime constant d >= 1 for numerators n < 2^31, by a
 // multiply-high and a shift (round-up reciprocal method): with l = ceil(log2 d) and
 // mul = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, mul) + n) >> l.

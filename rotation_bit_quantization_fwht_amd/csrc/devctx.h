@@ -1,6 +1,7 @@
 // gfx950 execution context for the workgroup bodies: LDS, barriers, lane shuffles,
-// global memory access and the 2-term dot products that widen a packed pair of 16-bit
-// values to float and apply the first radix-2 butterfly in one instruction each.
+// global memory access, the 2-term dot products that widen a packed pair of 16-bit
+// values to float and apply the first radix-2 butterfly in one instruction each, and the
+// 16x16x32 MFMA pair that applies the 32-point Hadamard factor to 16-bit inputs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,10 +12,41 @@ namespace rbq {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// +-1 weights of the 32-point factor in MFMA operand-A layout (see plan.h)
+__constant__ HadamardA kHadamardA = make_hadamard_a();
 
 struct DevCtx {
   uint32_t lane, wave;
   float* lds;
+  u32x4_t ha[2];  // operand A of the two MFMAs for this lane (matrix plans only)
+
+  template <int IN>
+  __device__ __forceinline__ void load_hadamard_a() {
+    const int f = (IN == IN_F16) ? 1 : 0;
+    ha[0] = *(const u32x4_t*)&kHadamardA.w[f][0][lane][0];
+    ha[1] = *(const u32x4_t*)&kHadamardA.w[f][1][lane][0];
+  }
+
+  // d = rows {j + 4m + 8 (lane / 16)} of H_32 times this wave's 16 groups of 32 inputs
+  // (operand B: lane l holds elements 8 (l / 16) .. + 7 of group l mod 16)
+  template <int IN>
+  __device__ __forceinline__ void hadamard32(const uint32_t (&b)[4], int m, float (&d)[4]) const {
+    const u32x4_t bv = {b[0], b[1], b[2], b[3]};
+    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t r;
+    if constexpr (IN == IN_F16)
+      r = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ha[m]),
+                                                 __builtin_bit_cast(f16x8_t, bv), z, 0, 0, 0);
+    else
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ha[m]),
+                                                  __builtin_bit_cast(bf16x8_t, bv), z, 0, 0, 0);
+    d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
+  }
 
   __device__ __forceinline__ void barrier() const { __syncthreads(); }
   // LDS operations of one wave execute in program order; this only keeps the

@@ -1,8 +1,10 @@
 // Workgroup body of the fused Walsh-Hadamard rotation + INT4 quantizer.
 //
 // One workgroup owns 2^r rows of length n = 2^k (see plan.h for the data layouts):
-//   load (global -> registers, widen to fp32; for 16-bit inputs the first butterfly is
-//   fused into the widening with a 2-term dot product against (1, 1) and (1, -1))
+//   load (global -> registers) and the first transform factor: for 16-bit inputs with
+//   k >= 7 a pair of 16x16x32 MFMAs multiplies every 32-element group by H_32 (exact:
+//   16-bit inputs, +-1 weights, fp32 accumulation); otherwise widen to fp32, fusing the
+//   first butterfly into the widening of 16-bit pairs with a 2-term dot product
 //   -> register butterflies -> LDS transpose -> register butterflies [-> transpose ->
 //   butterflies] -> per-row absmax (registers, lane shuffles, LDS across waves)
 //   -> scale, round half to even, clamp, nibble packing -> coalesced stores.
@@ -15,8 +17,8 @@
 // keeps u = H_n x and uses q = RNE(u * (1 / (s * sqrt(n)))).
 //
 // The body is written against a small context object (lane/wave ids, LDS, barriers,
-// lane shuffles, global loads/stores) so the same code runs in the HIP kernel and in
-// the host-side layout emulator used by the CPU tests.
+// lane shuffles, global loads/stores, the MFMA pair) so the same code runs in the HIP
+// kernel and in the host-side emulator used by the CPU tests.
 #pragma once
 
 #include "common.h"
@@ -53,6 +55,15 @@ struct KArgs {
   uint32_t opts;
 };
 
+// plan of a kernel instantiation: matrix plans for 16-bit rotated inputs with k >= 7
+constexpr bool use_matrix_plan(int k, int in, bool rot) { return rot && in != IN_F32 && k >= 7; }
+
+#define RBQ_PLAN PlanOf<K, MF>::value
+
+// the per-lane register file of one workgroup slot: 2^e values
+template <int K, bool MF>
+using Regs = float[1 << PlanOf<K, MF>::value.e];
+
 constexpr int popcount_c(uint32_t x) { int c = 0; while (x) { c += x & 1u; x >>= 1; } return c; }
 
 // gather the bits of x selected by mask into the low bits
@@ -75,16 +86,33 @@ constexpr float sqrt_pow2(int k) {
 
 // element-space index contributed by the lane and wave ids in phase PH, with the bits
 // of RM squeezed out (every bit's destination is a compile-time constant)
-template <int K, int PH, uint32_t RM = 0u>
+// compressed destination bit of slot bit i (lane bits 0..5, then wave bits 6..)
+constexpr int slot_dest(const Plan& p, int ph, int i, uint32_t rm) {
+  const int b = i < 6 ? p.lane[ph][i] : p.wave[ph][i - 6];
+  int pos = 0;
+  while ((compress(1u << b, rm) >> pos) != 1u) ++pos;
+  return pos;
+}
+// length of the run of slot bits starting at i whose destinations are consecutive (0 if
+// bit i continues a run started earlier)
+constexpr int slot_run(const Plan& p, int ph, int i, uint32_t rm) {
+  const int end = i < 6 ? 6 : 6 + p.w;
+  if (i != 0 && i != 6 && slot_dest(p, ph, i - 1, rm) + 1 == slot_dest(p, ph, i, rm)) return 0;
+  int len = 1;
+  while (i + len < end && slot_dest(p, ph, i + len, rm) == slot_dest(p, ph, i, rm) + len) ++len;
+  return len;
+}
+
+template <int K, bool MF, int PH, uint32_t RM = 0u>
 RBQ_HD uint32_t lane_part(uint32_t lane, uint32_t wave) {
   uint32_t idx = 0;
-  static_for<0, 6>([&](auto I) {
-    constexpr uint32_t bit = compress(1u << PlanOf<K>::value.lane[PH][I.value], RM);
-    idx |= ((lane >> I.value) & 1u) ? bit : 0u;
-  });
-  static_for<0, PlanOf<K>::value.w>([&](auto I) {
-    constexpr uint32_t bit = compress(1u << PlanOf<K>::value.wave[PH][I.value], RM);
-    idx |= ((wave >> I.value) & 1u) ? bit : 0u;
+  static_for<0, 6 + RBQ_PLAN.w>([&](auto I) {
+    constexpr int len = slot_run(RBQ_PLAN, PH, I.value, RM);
+    if constexpr (len > 0) {
+      constexpr int dst = slot_dest(RBQ_PLAN, PH, I.value, RM);
+      const uint32_t src = (I.value < 6) ? (lane >> I.value) : (wave >> (I.value - 6));
+      idx |= (src & ((1u << len) - 1u)) << dst;
+    }
   });
   return idx;
 }
@@ -105,23 +133,23 @@ RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
 
 // ------------------------------------------------------------------ load (phase 0)
 
-template <int K, int IN, bool ROT, bool FOURD, class Ctx>
+template <int K, bool MF, int IN, bool ROT, bool FOURD, class Ctx>
 RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
-                        float (&v)[1 << PlanOf<K>::value.e]) {
-  constexpr int C0 = run_log(PlanOf<K>::value, 0);
+                        Regs<K, MF>& v) {
+  constexpr int C0 = run_log(RBQ_PLAN, 0);
   constexpr int L = 1 << C0;
-  constexpr int NRUN = (1 << PlanOf<K>::value.e) / L;
+  constexpr int NRUN = (1 << RBQ_PLAN.e) / L;
   constexpr int ESZ = (IN == IN_F32) ? 4 : 2;
   constexpr int BYTES = L * ESZ;
-  const uint32_t lp = lane_part<K, 0>(c.lane, c.wave);
+  const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
   static_for<0, NRUN>([&](auto J) {
     constexpr uint32_t rb = (uint32_t)J.value << C0;
-    constexpr uint32_t rp = reg_part(PlanOf<K>::value, 0, rb);
+    constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, rb);
     const uint32_t idx = lp | rp;
     const int64_t row = row0 + (int64_t)(idx >> K);
     const uint32_t el = idx & ((1u << K) - 1u);
     uint32_t w[BYTES / 4];
-    if (row < rows) {
+    if (RBQ_PLAN.r == 0 || row < rows) {
       const char* src = (const char*)t.x + (row_offset<FOURD>(t, row) + (int64_t)el) * ESZ;
       if constexpr (BYTES >= 16) {
         static_for<0, BYTES / 16>([&](auto Q) {
@@ -152,15 +180,44 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
   });
 }
 
+// matrix plans: every load instruction brings 512 consecutive elements per wave, one
+// 16-byte vector per lane, which is operand B of the MFMA pair
+template <int K, bool MF, int IN, bool FOURD, class Ctx>
+RBQ_HD void load_phase0_matrix(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
+                               Regs<K, MF>& v) {
+  constexpr int NIT = (1 << RBQ_PLAN.e) / 8;
+  const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
+  static_for<0, NIT>([&](auto J) {
+    constexpr uint32_t rb = (uint32_t)J.value << 3;
+    constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, rb);
+    const uint32_t idx = lp | rp;
+    const int64_t row = row0 + (int64_t)(idx >> K);
+    const uint32_t el = idx & ((1u << K) - 1u);
+    uint32_t b[4] = {0u, 0u, 0u, 0u};
+    if (RBQ_PLAN.r == 0 || row < rows) {
+      const char* src = (const char*)t.x + (row_offset<FOURD>(t, row) + (int64_t)el) * 2;
+      const u32x4 q4 = c.template load<u32x4>(src);
+      b[0] = q4.x; b[1] = q4.y; b[2] = q4.z; b[3] = q4.w;
+    }
+    float d0[4], d1[4];
+    c.template hadamard32<IN>(b, 0, d0);
+    c.template hadamard32<IN>(b, 1, d1);
+    static_for<0, 4>([&](auto R) {
+      v[rb + R.value] = d0[R.value];
+      v[rb + 4 + R.value] = d1[R.value];
+    });
+  });
+}
+
 // ------------------------------------------------------------------ register butterflies
 
-template <int K, int PH, bool SKIP_R0>
-RBQ_HD void stages(float (&v)[1 << PlanOf<K>::value.e]) {
-  constexpr uint32_t M = stage_mask(PlanOf<K>::value, PH) & (SKIP_R0 ? ~1u : ~0u);
-  static_for<0, PlanOf<K>::value.e>([&](auto J) {
+template <int K, bool MF, int PH, bool SKIP_R0>
+RBQ_HD void stages(Regs<K, MF>& v) {
+  constexpr uint32_t M = stage_mask(RBQ_PLAN, PH) & (SKIP_R0 ? ~1u : ~0u);
+  static_for<0, RBQ_PLAN.e>([&](auto J) {
     if constexpr ((M >> J.value) & 1u) {
       constexpr int S = 1 << J.value;
-      static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+      static_for<0, (1 << RBQ_PLAN.e)>([&](auto R) {
         if constexpr ((R.value & S) == 0) {
           const float a = v[R.value];
           const float b = v[R.value + S];
@@ -174,26 +231,26 @@ RBQ_HD void stages(float (&v)[1 << PlanOf<K>::value.e]) {
 
 // ------------------------------------------------------------------ LDS transpose
 
-template <int K, int T, class Ctx>
-RBQ_HD void transpose(Ctx& c, float (&v)[1 << PlanOf<K>::value.e]) {
-  constexpr int SR = PlanOf<K>::value.sr[T];
-  constexpr uint32_t RM = sub_mask(PlanOf<K>::value, T);
-  constexpr bool WL = transpose_is_wave_local(PlanOf<K>::value, T);
+template <int K, bool MF, int T, class Ctx>
+RBQ_HD void transpose(Ctx& c, Regs<K, MF>& v) {
+  constexpr int SR = RBQ_PLAN.sr[T];
+  constexpr uint32_t RM = sub_mask(RBQ_PLAN, T);
+  constexpr bool WL = transpose_is_wave_local(RBQ_PLAN, T);
   constexpr uint32_t SMASK = (1u << SR) - 1u;
-  const uint32_t wbase = lds_pad(lane_part<K, T, RM>(c.lane, c.wave));
-  const uint32_t rbase = lds_pad(lane_part<K, T + 1, RM>(c.lane, c.wave));
+  const uint32_t wbase = lds_pad(RBQ_PLAN, T, lane_part<K, MF, T, RM>(c.lane, c.wave));
+  const uint32_t rbase = lds_pad(RBQ_PLAN, T, lane_part<K, MF, T + 1, RM>(c.lane, c.wave));
   if constexpr (!WL) c.barrier();
   static_for<0, (1 << SR)>([&](auto S) {
-    static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+    static_for<0, (1 << RBQ_PLAN.e)>([&](auto R) {
       if constexpr ((R.value & SMASK) == (uint32_t)S.value) {
-        constexpr uint32_t off = lds_pad(compress(reg_part(PlanOf<K>::value, T, R.value), RM));
+        constexpr uint32_t off = lds_pad(RBQ_PLAN, T, compress(reg_part(RBQ_PLAN, T, R.value), RM));
         c.lds_store(wbase + off, v[R.value]);
       }
     });
     if constexpr (WL) c.wave_sync(); else c.barrier();
-    static_for<0, (1 << PlanOf<K>::value.e)>([&](auto R) {
+    static_for<0, (1 << RBQ_PLAN.e)>([&](auto R) {
       if constexpr ((R.value & SMASK) == (uint32_t)S.value) {
-        constexpr uint32_t off = lds_pad(compress(reg_part(PlanOf<K>::value, T + 1, R.value), RM));
+        constexpr uint32_t off = lds_pad(RBQ_PLAN, T, compress(reg_part(RBQ_PLAN, T + 1, R.value), RM));
         v[R.value] = c.lds_load(rbase + off);
       }
     });
@@ -203,29 +260,11 @@ RBQ_HD void transpose(Ctx& c, float (&v)[1 << PlanOf<K>::value.e]) {
 
 // ------------------------------------------------------------------ quantize + pack
 
-// Rounding by the float adder: for |t| < 2^22, fma(u, mul, 1.5*2^23 + OFF) is
-// 1.5*2^23 + OFF + RNE(u*mul), so the low mantissa bits hold RNE(u*mul) + OFF as an
-// unsigned integer (single rounding of the exact product: round half to even).
+// Rounding by the float adder: for |t| < 2^22, fma(u, mul, 1.5 * 2^23) equals
+// 1.5 * 2^23 + RNE(u * mul) (single rounding of the exact product, half to even), so the
+// low mantissa bits hold RNE(u * mul) as a two's complement integer; clamping the float
+// to [1.5 * 2^23 - 8, 1.5 * 2^23 + 7] clamps the code to [-8, 7].
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23, bit pattern 0x4B400000
-
-// Horner-combine m magic floats (each 0x4B400000 + t_i, 0 <= t_i < 2^bits) into
-// sum t_i << (bits*i), then remove the constant and flip the offset-binary sign bit of
-// every field to get two's complement fields.
-template <int M, int BITS>
-RBQ_HD uint32_t combine_fields(const float* f) {
-  uint32_t acc = 0;
-  static_for<0, M>([&](auto I) {
-    acc = (acc << BITS) + f32_bits(f[M - 1 - I.value]);
-  });
-  constexpr uint32_t ones = [] {
-    uint32_t s = 0;
-    for (int i = 0; i < M; ++i) s += 1u << (BITS * i);
-    return s;
-  }();
-  constexpr uint32_t C = 0x4B400000u * ones;
-  constexpr uint32_t X = (BITS == 4 ? 8u : 0x80u) * ones;
-  return (acc - C) ^ X;
-}
 
 // Round u / d half to even exactly, given mk ~= 1/d (d > 0, or mk == 0 for a zero
 // scale). The product u * mk can sit on the other side of a half-integer than the exact
@@ -249,21 +288,22 @@ RBQ_HD float round_quotient_exact(float u, float mk, float d) {
   return q0;
 }
 
-template <int K, int PH, bool ROT, int IN, class Ctx>
+template <int K, bool MF, int PH, bool ROT, int IN, class Ctx>
 RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
-                   float (&v)[1 << PlanOf<K>::value.e]) {
-  constexpr int E = 1 << PlanOf<K>::value.e;
-  constexpr uint32_t RRM = reg_row_mask(PlanOf<K>::value, PH);
+                   Regs<K, MF>& v) {
+  constexpr int E = 1 << RBQ_PLAN.e;
+  constexpr uint32_t RRM = reg_row_mask(RBQ_PLAN, PH);
   constexpr int NRR = popcount_c(RRM);
   constexpr int NC = 1 << NRR;
-  constexpr uint32_t LEM = lane_elem_mask(PlanOf<K>::value, PH);
-  constexpr uint32_t WEM = wave_elem_mask(PlanOf<K>::value, PH);
+  constexpr uint32_t LEM = lane_elem_mask(RBQ_PLAN, PH);
+  constexpr uint32_t WEM = wave_elem_mask(RBQ_PLAN, PH);
   constexpr int N = 1 << K;
   constexpr float SQRTN = ROT ? sqrt_pow2(K) : 1.0f;
   constexpr float SEVEN_SQRTN = 7.0f * SQRTN;
   constexpr float INV_SQRTN = ROT ? 1.0f / sqrt_pow2(K) : 1.0f;
   // exact rounding decisions where the quotient is exact often enough to tie
   constexpr bool EXACT = !ROT || (K <= 6 && (K % 2) == 0);
+  constexpr bool ONE_ROW = RBQ_PLAN.r == 0;  // the grid never runs past the last row
 
   // ---- per-row absmax of |u|
   float m[NC];
@@ -281,22 +321,22 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   });
   if constexpr (WEM != 0) {
     static_assert(NC == 1, "cross-wave reduction assumes one row per workgroup");
-    constexpr uint32_t RED = lds_words(PlanOf<K>::value);
+    constexpr uint32_t RED = lds_words(RBQ_PLAN);
     if (c.lane == 0) c.lds_store(RED + c.wave, m[0]);
     c.barrier();
     float mm = 0.0f;
-    static_for<0, (1 << PlanOf<K>::value.w)>([&](auto W) { mm = fmaxf(mm, c.lds_load(RED + W.value)); });
+    static_for<0, (1 << RBQ_PLAN.w)>([&](auto W) { mm = fmaxf(mm, c.lds_load(RED + W.value)); });
     m[0] = mm;
   }
 
   // ---- per-row scale and multiplier
   const uint32_t mode = t.mode;
   const bool scale_f16 = (a.opts & OPT_SCALE_F16) != 0;
-  const uint32_t lp = lane_part<K, PH>(c.lane, c.wave);
+  const uint32_t lp = lane_part<K, MF, PH>(c.lane, c.wave);
   const bool leader = ((c.lane & LEM) == 0) && ((c.wave & WEM) == 0);
   float mul[NC];
   float divv[NC];
-  bool clampv[NC];
+  bool any_clamp = false;
   static_for<0, NC>([&](auto C) {
     const float mu = m[C.value];
     float s = mu / SEVEN_SQRTN;
@@ -308,105 +348,87 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     const float mk = (s_st == 0.0f) ? 0.0f : 1.0f / (s_st * SQRTN);
     mul[C.value] = mk;
     divv[C.value] = s_st * SQRTN;
-    clampv[C.value] = (mu * mk) > 7.25f;
+    // subnormal fp16 scales can sit far below max/7: then codes need the clamp
+    any_clamp = any_clamp || ((mu * mk) > 7.25f);
     if (mode & MODE_QUANT) {
-      constexpr uint32_t rp = reg_part(PlanOf<K>::value, PH, pdep_c((uint32_t)C.value, RRM));
+      constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
       const int64_t row = row0 + (int64_t)((lp | rp) >> K);
-      if (leader && row < a.rows) {
+      if (leader && (ONE_ROW || row < a.rows)) {
         if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + row, (uint16_t)h16);
         else c.template store<float>((float*)t.scales + row, s_st);
       }
     }
   });
 
-  // ---- codes and optional rotated output, one contiguous run of L elements at a time
-  constexpr int CF = run_log(PlanOf<K>::value, PH);
+  // ---- one contiguous run of L elements at a time
+  constexpr int CF = run_log(RBQ_PLAN, PH);
   constexpr int L = 1 << CF;
   constexpr int NRUN = E / L;
-  const bool packed = (a.opts & OPT_PACKED) != 0;
-  static_for<0, NRUN>([&](auto J) {
-    constexpr uint32_t rb = (uint32_t)J.value << CF;
-    constexpr uint32_t rp = reg_part(PlanOf<K>::value, PH, rb);
-    constexpr int ci = (int)pext_c(rb, RRM);
-    const uint32_t idx = lp | rp;
-    const int64_t row = row0 + (int64_t)(idx >> K);
-    const uint32_t el = idx & (uint32_t)(N - 1);
-    if (row >= a.rows) return;
-    if (mode & MODE_QUANT) {
+
+  auto codes_pass = [&](auto PACKEDC, auto CL) {
+    constexpr bool PACKED = decltype(PACKEDC)::value != 0;
+    constexpr bool CLAMP = decltype(CL)::value != 0;
+    constexpr int FB = PACKED ? 4 : 8;            // bits per code field
+    constexpr int PER = PACKED ? 8 : 4;            // codes per dword
+    constexpr int G = (L >= PER) ? PER : L;        // codes per output word
+    constexpr int NW = (L >= PER) ? L / PER : 1;   // output words per run
+    static_for<0, NRUN>([&](auto J) {
+      constexpr uint32_t rb = (uint32_t)J.value << CF;
+      constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
+      constexpr int ci = (int)pext_c(rb, RRM);
+      const uint32_t idx = lp | rp;
+      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t el = idx & (uint32_t)(N - 1);
+      if (!ONE_ROW && row >= a.rows) return;
       const float mk = mul[ci];
-      if (packed) {
-        constexpr int NW = (L >= 8) ? L / 8 : 1;   // output dwords (or one short field)
-        constexpr int PER = (L >= 8) ? 8 : L;
-        uint32_t out[NW];
-        auto quant = [&](auto CL) {
-          constexpr bool CLAMP = decltype(CL)::value != 0;
-          static_for<0, NW>([&](auto D) {
-            float f[PER];
-            static_for<0, PER>([&](auto I) {
-              float q;
-              if constexpr (EXACT) {
-                q = round_quotient_exact(v[rb + PER * D.value + I.value], mk, divv[ci]) + (kMagic + 8.0f);
-              } else {
-                q = fmaf(v[rb + PER * D.value + I.value], mk, kMagic + 8.0f);
-              }
-              if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic), kMagic + 15.0f);
-              f[I.value] = q;
-            });
-            out[D.value] = combine_fields<PER, 4>(f);
-          });
-        };
-        if (clampv[ci]) quant(IC<1>{}); else quant(IC<0>{});
-        uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)(N / 2) + el / 2;
-        if constexpr (L >= 32) {
-          static_for<0, L / 32>([&](auto Q) {
-            c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
-          });
-        } else if constexpr (L == 16) {
-          c.template store<u32x2>(dst, u32x2{out[0], out[1]});
-        } else if constexpr (L == 8) {
-          c.template store<uint32_t>(dst, out[0]);
-        } else if constexpr (L == 4) {
-          c.template store<uint16_t>(dst, (uint16_t)out[0]);
-        } else {
-          c.template store<uint8_t>(dst, (uint8_t)out[0]);
-        }
+      uint32_t out[NW];
+      static_for<0, NW>([&](auto D) {
+        uint32_t acc = 0u;
+        static_for<0, G>([&](auto I) {
+          const float u = v[rb + G * D.value + I.value];
+          float q;
+          if constexpr (EXACT) q = round_quotient_exact(u, mk, divv[ci]) + kMagic;
+          else q = fmaf(u, mk, kMagic);
+          if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic - 8.0f), kMagic + 7.0f);
+          // insert the low FB bits of the field at the top, shifting earlier ones down
+          acc = alignbit(f32_bits(q), acc, FB);
+        });
+        out[D.value] = (G * FB < 32) ? (acc >> (32 - G * FB)) : acc;
+      });
+      constexpr int RUN_BYTES = PACKED ? L / 2 : L;
+      uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)(PACKED ? N / 2 : N) + (PACKED ? el / 2 : el);
+      if constexpr (RUN_BYTES >= 16) {
+        static_for<0, RUN_BYTES / 16>([&](auto Q) {
+          c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
+        });
+      } else if constexpr (RUN_BYTES == 8) {
+        c.template store<u32x2>(dst, u32x2{out[0], out[1]});
+      } else if constexpr (RUN_BYTES == 4) {
+        c.template store<uint32_t>(dst, out[0]);
+      } else if constexpr (RUN_BYTES == 2) {
+        c.template store<uint16_t>(dst, (uint16_t)out[0]);
       } else {
-        constexpr int NW = (L >= 4) ? L / 4 : 1;
-        constexpr int PER = (L >= 4) ? 4 : L;
-        uint32_t out[NW];
-        auto quant = [&](auto CL) {
-          constexpr bool CLAMP = decltype(CL)::value != 0;
-          static_for<0, NW>([&](auto D) {
-            float f[PER];
-            static_for<0, PER>([&](auto I) {
-              float q;
-              if constexpr (EXACT) {
-                q = round_quotient_exact(v[rb + PER * D.value + I.value], mk, divv[ci]) + (kMagic + 128.0f);
-              } else {
-                q = fmaf(v[rb + PER * D.value + I.value], mk, kMagic + 128.0f);
-              }
-              if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic + 120.0f), kMagic + 135.0f);
-              f[I.value] = q;
-            });
-            out[D.value] = combine_fields<PER, 8>(f);
-          });
-        };
-        if (clampv[ci]) quant(IC<1>{}); else quant(IC<0>{});
-        uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)N + el;
-        if constexpr (L >= 16) {
-          static_for<0, L / 16>([&](auto Q) {
-            c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
-          });
-        } else if constexpr (L == 8) {
-          c.template store<u32x2>(dst, u32x2{out[0], out[1]});
-        } else if constexpr (L == 4) {
-          c.template store<uint32_t>(dst, out[0]);
-        } else {
-          c.template store<uint16_t>(dst, (uint16_t)out[0]);
-        }
+        c.template store<uint8_t>(dst, (uint8_t)out[0]);
       }
+    });
+  };
+
+  if (mode & MODE_QUANT) {
+    const bool packed = (a.opts & OPT_PACKED) != 0;
+    if (packed) {
+      if (any_clamp) codes_pass(IC<1>{}, IC<1>{}); else codes_pass(IC<1>{}, IC<0>{});
+    } else {
+      if (any_clamp) codes_pass(IC<0>{}, IC<1>{}); else codes_pass(IC<0>{}, IC<0>{});
     }
-    if (mode & MODE_ROT32) {
+  }
+  if (mode & MODE_ROT32) {
+    static_for<0, NRUN>([&](auto J) {
+      constexpr uint32_t rb = (uint32_t)J.value << CF;
+      constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
+      const uint32_t idx = lp | rp;
+      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t el = idx & (uint32_t)(N - 1);
+      if (!ONE_ROW && row >= a.rows) return;
       float* dst = t.rot32 + row * (int64_t)N + el;
       if constexpr (L >= 4) {
         static_for<0, L / 4>([&](auto Q) {
@@ -416,8 +438,16 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       } else {
         static_for<0, L>([&](auto I) { c.template store<float>(dst + I.value, v[rb + I.value] * INV_SQRTN); });
       }
-    }
-    if (mode & MODE_ROT16) {
+    });
+  }
+  if (mode & MODE_ROT16) {
+    static_for<0, NRUN>([&](auto J) {
+      constexpr uint32_t rb = (uint32_t)J.value << CF;
+      constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
+      const uint32_t idx = lp | rp;
+      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t el = idx & (uint32_t)(N - 1);
+      if (!ONE_ROW && row >= a.rows) return;
       uint16_t* dst = t.rot16 + row * (int64_t)N + el;
       constexpr int NW = (L >= 2) ? L / 2 : 1;
       uint32_t out[NW];
@@ -436,34 +466,42 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       } else {
         c.template store<uint32_t>(dst, out[0]);
       }
-    }
-  });
+    });
+  }
 }
 
 // ------------------------------------------------------------------ the workgroup body
 
 template <int K, int IN, bool ROT, bool FOURD, class Ctx>
 RBQ_HD void fwht_quant_wg(Ctx& c, const KArgs& a, uint32_t block) {
+  constexpr bool MF = use_matrix_plan(K, IN, ROT);
   const bool second = block >= a.blocks0;
   const TensorArgs& t = second ? a.t[1] : a.t[0];
   const uint32_t blk = second ? block - a.blocks0 : block;
-  const int64_t row0 = (int64_t)blk << PlanOf<K>::value.r;
-  float v[1 << PlanOf<K>::value.e];
-  load_phase0<K, IN, ROT, FOURD>(c, t, a.rows, row0, v);
-  if constexpr (ROT) {
-    stages<K, 0, IN != IN_F32>(v);
-    if constexpr (PlanOf<K>::value.nph >= 2) {
-      transpose<K, 0>(c, v);
-      stages<K, 1, false>(v);
-    }
-    if constexpr (PlanOf<K>::value.nph >= 3) {
-      transpose<K, 1>(c, v);
-      stages<K, 2, false>(v);
-    }
-    finish<K, PlanOf<K>::value.nph - 1, true, IN>(c, t, a, row0, v);
+  const int64_t row0 = (int64_t)blk << RBQ_PLAN.r;
+  Regs<K, MF> v;
+  if constexpr (MF) {
+    load_phase0_matrix<K, MF, IN, FOURD>(c, t, a.rows, row0, v);
+    stages<K, MF, 0, false>(v);
   } else {
-    finish<K, 0, false, IN>(c, t, a, row0, v);
+    load_phase0<K, MF, IN, ROT, FOURD>(c, t, a.rows, row0, v);
+    if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
+  }
+  if constexpr (ROT) {
+    if constexpr (RBQ_PLAN.nph >= 2) {
+      transpose<K, MF, 0>(c, v);
+      stages<K, MF, 1, false>(v);
+    }
+    if constexpr (RBQ_PLAN.nph >= 3) {
+      transpose<K, MF, 1>(c, v);
+      stages<K, MF, 2, false>(v);
+    }
+    finish<K, MF, RBQ_PLAN.nph - 1, true, IN>(c, t, a, row0, v);
+  } else {
+    finish<K, MF, 0, false, IN>(c, t, a, row0, v);
   }
 }
+
+#undef RBQ_PLAN
 
 }  // namespace rbq

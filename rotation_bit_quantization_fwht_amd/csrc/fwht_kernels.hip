@@ -10,17 +10,24 @@
 
 namespace rbq {
 
+template <int K, int IN, bool ROT>
+using KPlan = PlanOf<K, use_matrix_plan(K, IN, ROT)>;
+
 template <int K, int IN, bool ROT, bool FOURD>
-__global__ __launch_bounds__(64 << PlanOf<K>::value.w) void fwht_quant_kernel(KArgs a) {
-  constexpr const Plan& P = PlanOf<K>::value;
+__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) void fwht_quant_kernel(KArgs a) {
+  constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   __shared__ float lds[lds_words(P) + (1 << P.w) + 1];
-  DevCtx c{threadIdx.x & 63u, threadIdx.x >> 6, lds};
+  DevCtx c;
+  c.lane = threadIdx.x & 63u;
+  c.wave = threadIdx.x >> 6;
+  c.lds = lds;
+  if constexpr (P.mfma) c.template load_hadamard_a<IN>();
   fwht_quant_wg<K, IN, ROT, FOURD>(c, a, blockIdx.x);
 }
 
 template <int K, int IN, bool ROT, bool FOURD>
 static hipError_t launch_one(const KArgs& a, uint32_t grid, hipStream_t stream) {
-  constexpr const Plan& P = PlanOf<K>::value;
+  constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD>), dim3(grid), dim3(64u << P.w), 0,
                      stream, a);
   return hipGetLastError();

@@ -37,18 +37,8 @@ static hipError_t dispatch(int k, const KArgs& a, uint32_t grid, int in, bool ro
   return hipErrorInvalidValue;
 }
 
-static int rows_log(int k) {
-  switch (k) {
-    case 1: return PlanOf<1>::value.r;   case 2: return PlanOf<2>::value.r;
-    case 3: return PlanOf<3>::value.r;   case 4: return PlanOf<4>::value.r;
-    case 5: return PlanOf<5>::value.r;   case 6: return PlanOf<6>::value.r;
-    case 7: return PlanOf<7>::value.r;   case 8: return PlanOf<8>::value.r;
-    case 9: return PlanOf<9>::value.r;   case 10: return PlanOf<10>::value.r;
-    case 11: return PlanOf<11>::value.r; case 12: return PlanOf<12>::value.r;
-    case 13: return PlanOf<13>::value.r; case 14: return PlanOf<14>::value.r;
-    default: return PlanOf<15>::value.r;
-  }
-}
+// rows per workgroup (log2) of the plan a launch will use
+static int rows_log(int k, int in, bool rot) { return make_plan(k, use_matrix_plan(k, in, rot)).r; }
 
 static int in_kind(rbq_dtype d) { return d == RBQ_F32 ? IN_F32 : (d == RBQ_BF16 ? IN_BF16 : IN_F16); }
 
@@ -63,7 +53,8 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   const HqCheck chk = check_hadamard_quant(x, x_dtype, n, tokens, x_row_stride, codes, scales,
                                            scale_dtype, rotated, flags);
   if (chk.status != RBQ_OK || tokens == 0) return chk.status;
-  const int rl = rows_log(chk.k);
+  const bool rot = (flags & RBQ_NO_ROTATE) == 0;
+  const int rl = rows_log(chk.k, in_kind(x_dtype), rot);
   const int64_t blocks = (tokens + (int64_t{1} << rl) - 1) >> rl;
   if (blocks > 0x7FFFFFFF) return RBQ_EINVAL;
   KArgs a{};
@@ -78,7 +69,6 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   a.rows = tokens;
   a.blocks0 = (uint32_t)blocks;
   a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
-  const bool rot = (flags & RBQ_NO_ROTATE) == 0;
   if (dispatch(chk.k, a, (uint32_t)blocks, in_kind(x_dtype), rot, false, stream) != hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
@@ -96,7 +86,7 @@ extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dt
   if (batch == 0 || heads == 0 || seq == 0) return RBQ_OK;
   if (!chk.flat && (chk.k < 6 || chk.k > 8)) return RBQ_ENOTSUP;  // strided only for d in {64,128,256}
   const int64_t rows = batch * heads * seq;
-  const int rl = rows_log(chk.k);
+  const int rl = rows_log(chk.k, in_kind(dtype), true);
   const int64_t blocks = (rows + (int64_t{1} << rl) - 1) >> rl;
   if (2 * blocks > 0x7FFFFFFF) return RBQ_EINVAL;
   KArgs a{};

@@ -35,14 +35,20 @@ struct WgShared {
   std::barrier<> wg;
   std::vector<std::unique_ptr<std::barrier<>>> wave_bar;
   std::vector<std::vector<float>> shfl;
+  std::vector<std::vector<float>> mfma_b;  // per wave: 64 lanes x 8 operand-B values
   WgShared(size_t lds_words, int nthreads, int nwaves)
       : lds(lds_words, -12345.0f), wg(nthreads) {
     for (int w = 0; w < nwaves; ++w) {
       wave_bar.emplace_back(new std::barrier<>(64));
       shfl.emplace_back(64, 0.0f);
+      mfma_b.emplace_back(64 * 8, 0.0f);
     }
   }
 };
+
+static constexpr HadamardA kHA = make_hadamard_a();
+
+static float half16(uint32_t h, int in) { return in == IN_F16 ? f16_to_f32(h) : bf16_to_f32(h); }
 
 struct HostCtx {
   uint32_t lane, wave;
@@ -78,6 +84,28 @@ struct HostCtx {
     if (IN == IN_BF16) { a = bf16_to_f32(w & 0xFFFFu); b = bf16_to_f32(w >> 16); }
     else { a = f16_to_f32(w & 0xFFFFu); b = f16_to_f32(w >> 16); }
   }
+  // emulation of the 16x16x32 MFMA with the constant operand A of plan.h:
+  // D[i][j] = sum_k A_m[i][k] B[k][j]; A: lane l = row l%16, k = 8 (l/16) + v;
+  // B: lane l = column l%16, k = 8 (l/16) + v; D: lane l, reg r = D[4 (l/16) + r][l%16]
+  template <int IN> void hadamard32(const uint32_t (&b)[4], int m, float (&d)[4]) {
+    std::vector<float>& buf = s->mfma_b[wave];
+    for (int v = 0; v < 8; ++v) buf[lane * 8 + v] = half16((b[v / 2] >> (16 * (v % 2))) & 0xFFFFu, IN);
+    s->wave_bar[wave]->arrive_and_wait();
+    const int fmt = (IN == IN_F16) ? 1 : 0;
+    const int j = (int)lane % 16;
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * ((int)lane / 16) + r;
+      float acc = 0.0f;
+      for (int g = 0; g < 4; ++g)
+        for (int v = 0; v < 8; ++v) {
+          const uint32_t aw = kHA.w[fmt][m][i + 16 * g][v / 2];
+          const float av = half16((aw >> (16 * (v % 2))) & 0xFFFFu, IN);
+          acc += av * buf[(j + 16 * g) * 8 + v];
+        }
+      d[r] = acc;
+    }
+    s->wave_bar[wave]->arrive_and_wait();
+  }
   template <int IN> void widen_butterfly(uint32_t w, float& a, float& b) {
     float x0, x1;
     widen<IN>(w, x0, x1);
@@ -88,7 +116,7 @@ struct HostCtx {
 
 template <int K, int IN, bool ROT, bool FOURD>
 static void run(const KArgs& a, uint32_t grid) {
-  constexpr const Plan& P = PlanOf<K>::value;
+  constexpr const Plan& P = PlanOf<K, use_matrix_plan(K, IN, ROT)>::value;
   const int nthreads = 64 << P.w;
   for (uint32_t blk = 0; blk < grid; ++blk) {
     WgShared sh(lds_words(P) + (1u << P.w) + 1, nthreads, 1 << P.w);
@@ -172,12 +200,7 @@ int main(int argc, char** argv) {
   }
   a.t[1] = t;
   a.rows = rows;
-  int rl = 0;
-  switch (K) {
-#define RL(k) case k: rl = PlanOf<k>::value.r; break;
-    RL(1) RL(2) RL(3) RL(4) RL(5) RL(6) RL(7) RL(8) RL(9) RL(10) RL(11) RL(12) RL(13) RL(14) RL(15)
-#undef RL
-  }
+  const int rl = make_plan(K, use_matrix_plan(K, in, rot != 0)).r;
   const uint32_t grid = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
   a.blocks0 = grid;
   a.opts = opts;
