@@ -110,14 +110,26 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm"], default="all",
-                    help="restrict the step (for profiling one kernel)")
+    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "copy"], default="all",
+                    help="restrict the step (for profiling one kernel); 'copy' runs a plain 1 GiB "
+                         "device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
+
+    if args.only == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": args.warmup + args.steps}))
+        return
 
     import rotation_bit_quantization_fwht_amd as rbq
     import workloads

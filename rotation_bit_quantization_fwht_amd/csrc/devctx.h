@@ -48,6 +48,11 @@ struct DevCtx {
     d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
   }
 
+  // Called at the top of every block iteration: makes the lane id opaque to the compiler
+  // so that per-lane address arithmetic is recomputed in each iteration instead of being
+  // hoisted out of the block loop (hoisting keeps dozens of registers live across it).
+  __device__ __forceinline__ void refresh_ids() { asm volatile("" : "+v"(lane)); }
+
   __device__ __forceinline__ void barrier() const { __syncthreads(); }
   // LDS operations of one wave execute in program order; this only keeps the
   // compiler from moving LDS accesses across the point.

@@ -51,8 +51,15 @@ struct TensorArgs {
 struct KArgs {
   TensorArgs t[2];
   int64_t rows;       // rows per tensor
-  uint32_t blocks0;   // workgroups for tensor 0 (the rest process tensor 1)
+  uint32_t blocks0;   // row blocks of tensor 0 (blocks past it belong to tensor 1)
+  uint32_t nblocks;   // row blocks in total; workgroups loop over them with a stride
   uint32_t opts;
+};
+
+// one block of rows: its tensor and first row
+struct Block {
+  const TensorArgs* t;
+  int64_t row0;
 };
 
 // plan of a kernel instantiation: matrix plans for 16-bit rotated inputs with k >= 7
@@ -117,6 +124,17 @@ RBQ_HD uint32_t lane_part(uint32_t lane, uint32_t wave) {
   return idx;
 }
 
+// the LDS padding of transpose T for a runtime index (shift amounts are constants)
+template <int K, bool MF, int T>
+RBQ_HD uint32_t lds_pad_rt(uint32_t i) {
+  constexpr int PA = RBQ_PLAN.pad[T][0];
+  constexpr int PB = RBQ_PLAN.pad[T][1];
+  uint32_t r = i;
+  if constexpr (PA > 0) r += i >> PA;
+  if constexpr (PB > 0) r += i >> PB;
+  return r;
+}
+
 template <bool FOURD>
 RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
   if constexpr (FOURD) {
@@ -133,6 +151,20 @@ RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
 
 // ------------------------------------------------------------------ load (phase 0)
 
+// address of element `el` of row `row0 + rw` (rw < 2^r): a uniform 64-bit block base plus
+// a 32-bit lane offset for 2-D tensors (the host checks 2^r * stride * esize < 2^31);
+// 4-D tensors decompose each row into (batch, head, token)
+template <int K, bool MF, int ESZ, bool FOURD>
+RBQ_HD const char* in_addr(const TensorArgs& t, int64_t row0, uint32_t rw, uint32_t el) {
+  if constexpr (FOURD) {
+    return (const char*)t.x + (row_offset<true>(t, row0 + rw) + (int64_t)el) * ESZ;
+  } else {
+    const char* base = (const char*)t.x + row0 * t.row_stride * ESZ;
+    if constexpr (RBQ_PLAN.r == 0) return base + el * (uint32_t)ESZ;
+    else return base + (rw * (uint32_t)t.row_stride + el) * (uint32_t)ESZ;
+  }
+}
+
 template <int K, bool MF, int IN, bool ROT, bool FOURD, class Ctx>
 RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                         Regs<K, MF>& v) {
@@ -146,11 +178,11 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
     constexpr uint32_t rb = (uint32_t)J.value << C0;
     constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, rb);
     const uint32_t idx = lp | rp;
-    const int64_t row = row0 + (int64_t)(idx >> K);
+    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : (idx >> K);
     const uint32_t el = idx & ((1u << K) - 1u);
     uint32_t w[BYTES / 4];
-    if (RBQ_PLAN.r == 0 || row < rows) {
-      const char* src = (const char*)t.x + (row_offset<FOURD>(t, row) + (int64_t)el) * ESZ;
+    if (RBQ_PLAN.r == 0 || row0 + rw < rows) {
+      const char* src = in_addr<K, MF, ESZ, FOURD>(t, row0, rw, el);
       if constexpr (BYTES >= 16) {
         static_for<0, BYTES / 16>([&](auto Q) {
           u32x4 q4 = c.template load<u32x4>(src + 16 * Q.value);
@@ -181,27 +213,36 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
 }
 
 // matrix plans: every load instruction brings 512 consecutive elements per wave, one
-// 16-byte vector per lane, which is operand B of the MFMA pair
-template <int K, bool MF, int IN, bool FOURD, class Ctx>
-RBQ_HD void load_phase0_matrix(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
-                               Regs<K, MF>& v) {
-  constexpr int NIT = (1 << RBQ_PLAN.e) / 8;
+// 16-byte vector per lane, which is operand B of the MFMA pair. The loads are issued
+// one block ahead (see fwht_quant_persistent), so they are split from the MFMAs.
+template <int K, bool MF>
+constexpr int kMatrixLoads = (1 << PlanOf<K, MF>::value.e) / 8;
+
+template <int K, bool MF, bool FOURD, class Ctx>
+RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
+                         uint32_t (&raw)[kMatrixLoads<K, MF>][4]) {
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
-  static_for<0, NIT>([&](auto J) {
-    constexpr uint32_t rb = (uint32_t)J.value << 3;
-    constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, rb);
+  static_for<0, kMatrixLoads<K, MF>>([&](auto J) {
+    constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, (uint32_t)J.value << 3);
     const uint32_t idx = lp | rp;
-    const int64_t row = row0 + (int64_t)(idx >> K);
+    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : (idx >> K);
     const uint32_t el = idx & ((1u << K) - 1u);
-    uint32_t b[4] = {0u, 0u, 0u, 0u};
-    if (RBQ_PLAN.r == 0 || row < rows) {
-      const char* src = (const char*)t.x + (row_offset<FOURD>(t, row) + (int64_t)el) * 2;
-      const u32x4 q4 = c.template load<u32x4>(src);
-      b[0] = q4.x; b[1] = q4.y; b[2] = q4.z; b[3] = q4.w;
+    if (RBQ_PLAN.r == 0 || row0 + rw < rows) {
+      const u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
+      raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
+    } else {
+      raw[J.value][0] = raw[J.value][1] = raw[J.value][2] = raw[J.value][3] = 0u;
     }
+  });
+}
+
+template <int K, bool MF, int IN, class Ctx>
+RBQ_HD void matrix_apply(Ctx& c, const uint32_t (&raw)[kMatrixLoads<K, MF>][4], Regs<K, MF>& v) {
+  static_for<0, kMatrixLoads<K, MF>>([&](auto J) {
+    constexpr uint32_t rb = (uint32_t)J.value << 3;
     float d0[4], d1[4];
-    c.template hadamard32<IN>(b, 0, d0);
-    c.template hadamard32<IN>(b, 1, d1);
+    c.template hadamard32<IN>(raw[J.value], 0, d0);
+    c.template hadamard32<IN>(raw[J.value], 1, d1);
     static_for<0, 4>([&](auto R) {
       v[rb + R.value] = d0[R.value];
       v[rb + 4 + R.value] = d1[R.value];
@@ -237,8 +278,8 @@ RBQ_HD void transpose(Ctx& c, Regs<K, MF>& v) {
   constexpr uint32_t RM = sub_mask(RBQ_PLAN, T);
   constexpr bool WL = transpose_is_wave_local(RBQ_PLAN, T);
   constexpr uint32_t SMASK = (1u << SR) - 1u;
-  const uint32_t wbase = lds_pad(RBQ_PLAN, T, lane_part<K, MF, T, RM>(c.lane, c.wave));
-  const uint32_t rbase = lds_pad(RBQ_PLAN, T, lane_part<K, MF, T + 1, RM>(c.lane, c.wave));
+  const uint32_t wbase = lds_pad_rt<K, MF, T>(lane_part<K, MF, T, RM>(c.lane, c.wave));
+  const uint32_t rbase = lds_pad_rt<K, MF, T>(lane_part<K, MF, T + 1, RM>(c.lane, c.wave));
   if constexpr (!WL) c.barrier();
   static_for<0, (1 << SR)>([&](auto S) {
     static_for<0, (1 << RBQ_PLAN.e)>([&](auto R) {
@@ -288,7 +329,9 @@ RBQ_HD float round_quotient_exact(float u, float mk, float d) {
   return q0;
 }
 
-template <int K, bool MF, int PH, bool ROT, int IN, class Ctx>
+// FAST: only packed codes and scales are written (no unpacked codes, no rotated rows), so
+// the kernel carries no registers for the other outputs
+template <int K, bool MF, int PH, bool ROT, int IN, bool FAST, class Ctx>
 RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
                    Regs<K, MF>& v) {
   constexpr int E = 1 << RBQ_PLAN.e;
@@ -350,12 +393,12 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     divv[C.value] = s_st * SQRTN;
     // subnormal fp16 scales can sit far below max/7: then codes need the clamp
     any_clamp = any_clamp || ((mu * mk) > 7.25f);
-    if (mode & MODE_QUANT) {
+    if (FAST || (mode & MODE_QUANT)) {
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
-      const int64_t row = row0 + (int64_t)((lp | rp) >> K);
-      if (leader && (ONE_ROW || row < a.rows)) {
-        if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + row, (uint16_t)h16);
-        else c.template store<float>((float*)t.scales + row, s_st);
+      const uint32_t rw = ONE_ROW ? 0u : ((lp | rp) >> K);
+      if (leader && (ONE_ROW || row0 + rw < a.rows)) {
+        if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + row0 + rw, (uint16_t)h16);
+        else c.template store<float>((float*)t.scales + row0 + rw, s_st);
       }
     }
   });
@@ -377,9 +420,9 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
       constexpr int ci = (int)pext_c(rb, RRM);
       const uint32_t idx = lp | rp;
-      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row >= a.rows) return;
+      if (!ONE_ROW && row0 + rw >= a.rows) return;
       const float mk = mul[ci];
       uint32_t out[NW];
       static_for<0, NW>([&](auto D) {
@@ -396,7 +439,8 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
         out[D.value] = (G * FB < 32) ? (acc >> (32 - G * FB)) : acc;
       });
       constexpr int RUN_BYTES = PACKED ? L / 2 : L;
-      uint8_t* dst = (uint8_t*)t.codes + row * (int64_t)(PACKED ? N / 2 : N) + (PACKED ? el / 2 : el);
+      constexpr uint32_t ROWB = PACKED ? N / 2 : N;
+      uint8_t* dst = (uint8_t*)t.codes + row0 * (int64_t)ROWB + (rw * ROWB + (PACKED ? el / 2 : el));
       if constexpr (RUN_BYTES >= 16) {
         static_for<0, RUN_BYTES / 16>([&](auto Q) {
           c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
@@ -413,6 +457,10 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     });
   };
 
+  if constexpr (FAST) {
+    if (any_clamp) codes_pass(IC<1>{}, IC<1>{}); else codes_pass(IC<1>{}, IC<0>{});
+    return;
+  }
   if (mode & MODE_QUANT) {
     const bool packed = (a.opts & OPT_PACKED) != 0;
     if (packed) {
@@ -426,10 +474,10 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       constexpr uint32_t rb = (uint32_t)J.value << CF;
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
       const uint32_t idx = lp | rp;
-      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row >= a.rows) return;
-      float* dst = t.rot32 + row * (int64_t)N + el;
+      if (!ONE_ROW && row0 + rw >= a.rows) return;
+      float* dst = t.rot32 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       if constexpr (L >= 4) {
         static_for<0, L / 4>([&](auto Q) {
           constexpr int o = 4 * Q.value;
@@ -445,10 +493,10 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       constexpr uint32_t rb = (uint32_t)J.value << CF;
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, rb);
       const uint32_t idx = lp | rp;
-      const int64_t row = row0 + (int64_t)(idx >> K);
+      const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row >= a.rows) return;
-      uint16_t* dst = t.rot16 + row * (int64_t)N + el;
+      if (!ONE_ROW && row0 + rw >= a.rows) return;
+      uint16_t* dst = t.rot16 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       constexpr int NW = (L >= 2) ? L / 2 : 1;
       uint32_t out[NW];
       static_for<0, NW>([&](auto D) {
@@ -470,23 +518,20 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   }
 }
 
-// ------------------------------------------------------------------ the workgroup body
+// ------------------------------------------------------------------ the workgroup loop
 
-template <int K, int IN, bool ROT, bool FOURD, class Ctx>
-RBQ_HD void fwht_quant_wg(Ctx& c, const KArgs& a, uint32_t block) {
-  constexpr bool MF = use_matrix_plan(K, IN, ROT);
-  const bool second = block >= a.blocks0;
-  const TensorArgs& t = second ? a.t[1] : a.t[0];
-  const uint32_t blk = second ? block - a.blocks0 : block;
-  const int64_t row0 = (int64_t)blk << RBQ_PLAN.r;
-  Regs<K, MF> v;
-  if constexpr (MF) {
-    load_phase0_matrix<K, MF, IN, FOURD>(c, t, a.rows, row0, v);
-    stages<K, MF, 0, false>(v);
-  } else {
-    load_phase0<K, MF, IN, ROT, FOURD>(c, t, a.rows, row0, v);
-    if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
-  }
+template <int K, bool MF>
+RBQ_HD Block block_of(const KArgs& a, uint32_t blk) {
+  const bool second = blk >= a.blocks0;
+  Block b;
+  b.t = second ? &a.t[1] : &a.t[0];
+  b.row0 = (int64_t)(second ? blk - a.blocks0 : blk) << RBQ_PLAN.r;
+  return b;
+}
+
+// the transform after phase 0, the reduction, the scale and the stores of one block
+template <int K, bool MF, int IN, bool ROT, bool FAST, class Ctx>
+RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v) {
   if constexpr (ROT) {
     if constexpr (RBQ_PLAN.nph >= 2) {
       transpose<K, MF, 0>(c, v);
@@ -496,9 +541,47 @@ RBQ_HD void fwht_quant_wg(Ctx& c, const KArgs& a, uint32_t block) {
       transpose<K, MF, 1>(c, v);
       stages<K, MF, 2, false>(v);
     }
-    finish<K, MF, RBQ_PLAN.nph - 1, true, IN>(c, t, a, row0, v);
+    finish<K, MF, RBQ_PLAN.nph - 1, true, IN, FAST>(c, *b.t, a, b.row0, v);
   } else {
-    finish<K, MF, 0, false, IN>(c, t, a, row0, v);
+    finish<K, MF, 0, false, IN, FAST>(c, *b.t, a, b.row0, v);
+  }
+}
+
+// Workgroup `first` processes blocks first, first + step, ... < a.nblocks. With matrix
+// plans the next block's loads are issued as soon as the MFMAs have consumed the
+// current block's, so they are in flight while the current block is transformed.
+template <int K, int IN, bool ROT, bool FOURD, bool FAST, class Ctx>
+RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32_t step) {
+  constexpr bool MF = use_matrix_plan(K, IN, ROT);
+  const uint32_t nb = a.nblocks;
+  if constexpr (MF) {
+    uint32_t raw[kMatrixLoads<K, MF>][4];
+    if (first < nb) {
+      const Block b = block_of<K, MF>(a, first);
+      matrix_issue<K, MF, FOURD>(c, *b.t, a.rows, b.row0, raw);
+    }
+    for (uint32_t blk = first; blk < nb; blk += step) {
+      c.refresh_ids();
+      const Block b = block_of<K, MF>(a, blk);
+      Regs<K, MF> v;
+      matrix_apply<K, MF, IN>(c, raw, v);
+      const uint32_t nxt = blk + step;
+      if (nxt < nb) {
+        const Block bn = block_of<K, MF>(a, nxt);
+        matrix_issue<K, MF, FOURD>(c, *bn.t, a.rows, bn.row0, raw);
+      }
+      stages<K, MF, 0, false>(v);
+      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+    }
+  } else {
+    for (uint32_t blk = first; blk < nb; blk += step) {
+      c.refresh_ids();
+      const Block b = block_of<K, MF>(a, blk);
+      Regs<K, MF> v;
+      load_phase0<K, MF, IN, ROT, FOURD>(c, *b.t, a.rows, b.row0, v);
+      if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
+      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+    }
   }
 }
 

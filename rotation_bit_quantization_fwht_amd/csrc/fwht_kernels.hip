@@ -13,45 +13,69 @@ namespace rbq {
 template <int K, int IN, bool ROT>
 using KPlan = PlanOf<K, use_matrix_plan(K, IN, ROT)>;
 
-template <int K, int IN, bool ROT, bool FOURD>
-__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) void fwht_quant_kernel(KArgs a) {
+// at least 3 waves per SIMD (<= 168 VGPRs): enough resident workgroups to overlap one
+// block's loads with another's arithmetic
+template <int K, int IN, bool ROT, bool FOURD, bool FAST>
+__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(3)))
+void fwht_quant_kernel(KArgs a) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   __shared__ float lds[lds_words(P) + (1 << P.w) + 1];
   DevCtx c;
   c.lane = threadIdx.x & 63u;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
   c.lds = lds;
   if constexpr (P.mfma) c.template load_hadamard_a<IN>();
-  fwht_quant_wg<K, IN, ROT, FOURD>(c, a, blockIdx.x);
+  fwht_quant_persistent<K, IN, ROT, FOURD, FAST>(c, a, blockIdx.x, gridDim.x);
 }
 
-template <int K, int IN, bool ROT, bool FOURD>
-static hipError_t launch_one(const KArgs& a, uint32_t grid, hipStream_t stream) {
+// Workgroups loop over the row blocks (see fwht_quant_persistent); the grid holds as many
+// workgroups as fit on the device at once, or fewer when there are fewer blocks.
+template <int K, int IN, bool ROT, bool FOURD, bool FAST = false>
+static hipError_t launch_one(const KArgs& a, hipStream_t stream) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
-  hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD>), dim3(grid), dim3(64u << P.w), 0,
-                     stream, a);
+  constexpr int threads = 64 << P.w;
+  static const int per_cu = [] {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fwht_quant_kernel<K, IN, ROT, FOURD, FAST>, threads, 0) !=
+            hipSuccess || o < 1)
+      o = 1;
+    return o;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return hipErrorInvalidDevice;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)cus;
+  const uint32_t grid = (uint32_t)(a.nblocks < cap ? a.nblocks : cap);
+  hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD, FAST>), dim3(grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
+// fast: packed codes and scales are the only outputs (no rotated rows, no int8 codes)
 template <int K>
-hipError_t fwht_launch(const KArgs& a, uint32_t grid, int in, bool rot, bool fourd,
-                       hipStream_t s) {
+hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, hipStream_t s) {
   if (fourd) {
     // strided [B, H, S, D] addressing is instantiated for head_dim 64, 128 and 256
     if constexpr (K >= 6 && K <= 8) {
-      if (in == IN_BF16) return launch_one<K, IN_BF16, true, true>(a, grid, s);
-      return launch_one<K, IN_F16, true, true>(a, grid, s);
+      if (in == IN_BF16)
+        return fast ? launch_one<K, IN_BF16, true, true, true>(a, s) : launch_one<K, IN_BF16, true, true>(a, s);
+      return fast ? launch_one<K, IN_F16, true, true, true>(a, s) : launch_one<K, IN_F16, true, true>(a, s);
     } else {
       return hipErrorNotSupported;
     }
   }
   switch (in) {
-    case IN_F32: return rot ? launch_one<K, IN_F32, true, false>(a, grid, s) : launch_one<K, IN_F32, false, false>(a, grid, s);
-    case IN_BF16: return rot ? launch_one<K, IN_BF16, true, false>(a, grid, s) : launch_one<K, IN_BF16, false, false>(a, grid, s);
-    default: return rot ? launch_one<K, IN_F16, true, false>(a, grid, s) : launch_one<K, IN_F16, false, false>(a, grid, s);
+    case IN_F32:
+      return rot ? launch_one<K, IN_F32, true, false>(a, s) : launch_one<K, IN_F32, false, false>(a, s);
+    case IN_BF16:
+      if (!rot) return launch_one<K, IN_BF16, false, false>(a, s);
+      return fast ? launch_one<K, IN_BF16, true, false, true>(a, s) : launch_one<K, IN_BF16, true, false>(a, s);
+    default:
+      if (!rot) return launch_one<K, IN_F16, false, false>(a, s);
+      return fast ? launch_one<K, IN_F16, true, false, true>(a, s) : launch_one<K, IN_F16, true, false>(a, s);
   }
 }
 
-template hipError_t fwht_launch<RBQ_K>(const KArgs&, uint32_t, int, bool, bool, hipStream_t);
+template hipError_t fwht_launch<RBQ_K>(const KArgs&, int, bool, bool, bool, hipStream_t);
 
 }  // namespace rbq

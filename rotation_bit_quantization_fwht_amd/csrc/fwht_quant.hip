@@ -6,6 +6,8 @@
 // file validates arguments, fills the kernel arguments and dispatches on log2 n.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../../include/rbq.h"
 #include "fwht_engine.h"
 #include "validate.h"
@@ -13,26 +15,26 @@
 namespace rbq {
 
 template <int K>
-hipError_t fwht_launch(const KArgs& a, uint32_t grid, int in, bool rot, bool fourd, hipStream_t s);
+hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, hipStream_t s);
 
-static hipError_t dispatch(int k, const KArgs& a, uint32_t grid, int in, bool rot, bool fourd,
+static hipError_t dispatch(int k, const KArgs& a, int in, bool rot, bool fourd, bool fast,
                            hipStream_t s) {
   switch (k) {
-    case 1: return fwht_launch<1>(a, grid, in, rot, fourd, s);
-    case 2: return fwht_launch<2>(a, grid, in, rot, fourd, s);
-    case 3: return fwht_launch<3>(a, grid, in, rot, fourd, s);
-    case 4: return fwht_launch<4>(a, grid, in, rot, fourd, s);
-    case 5: return fwht_launch<5>(a, grid, in, rot, fourd, s);
-    case 6: return fwht_launch<6>(a, grid, in, rot, fourd, s);
-    case 7: return fwht_launch<7>(a, grid, in, rot, fourd, s);
-    case 8: return fwht_launch<8>(a, grid, in, rot, fourd, s);
-    case 9: return fwht_launch<9>(a, grid, in, rot, fourd, s);
-    case 10: return fwht_launch<10>(a, grid, in, rot, fourd, s);
-    case 11: return fwht_launch<11>(a, grid, in, rot, fourd, s);
-    case 12: return fwht_launch<12>(a, grid, in, rot, fourd, s);
-    case 13: return fwht_launch<13>(a, grid, in, rot, fourd, s);
-    case 14: return fwht_launch<14>(a, grid, in, rot, fourd, s);
-    case 15: return fwht_launch<15>(a, grid, in, rot, fourd, s);
+    case 1: return fwht_launch<1>(a, in, rot, fourd, fast, s);
+    case 2: return fwht_launch<2>(a, in, rot, fourd, fast, s);
+    case 3: return fwht_launch<3>(a, in, rot, fourd, fast, s);
+    case 4: return fwht_launch<4>(a, in, rot, fourd, fast, s);
+    case 5: return fwht_launch<5>(a, in, rot, fourd, fast, s);
+    case 6: return fwht_launch<6>(a, in, rot, fourd, fast, s);
+    case 7: return fwht_launch<7>(a, in, rot, fourd, fast, s);
+    case 8: return fwht_launch<8>(a, in, rot, fourd, fast, s);
+    case 9: return fwht_launch<9>(a, in, rot, fourd, fast, s);
+    case 10: return fwht_launch<10>(a, in, rot, fourd, fast, s);
+    case 11: return fwht_launch<11>(a, in, rot, fourd, fast, s);
+    case 12: return fwht_launch<12>(a, in, rot, fourd, fast, s);
+    case 13: return fwht_launch<13>(a, in, rot, fourd, fast, s);
+    case 14: return fwht_launch<14>(a, in, rot, fourd, fast, s);
+    case 15: return fwht_launch<15>(a, in, rot, fourd, fast, s);
   }
   return hipErrorInvalidValue;
 }
@@ -57,6 +59,8 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   const int rl = rows_log(chk.k, in_kind(x_dtype), rot);
   const int64_t blocks = (tokens + (int64_t{1} << rl) - 1) >> rl;
   if (blocks > 0x7FFFFFFF) return RBQ_EINVAL;
+  // rows of one block are addressed with 32-bit offsets from the block's first row
+  if (rl > 0 && (x_row_stride * dtype_size(x_dtype) << rl) >= (int64_t{1} << 31)) return RBQ_ENOTSUP;
   KArgs a{};
   TensorArgs& t = a.t[0];
   t.x = x;
@@ -68,8 +72,10 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   a.t[1] = t;
   a.rows = tokens;
   a.blocks0 = (uint32_t)blocks;
+  a.nblocks = (uint32_t)blocks;
   a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
-  if (dispatch(chk.k, a, (uint32_t)blocks, in_kind(x_dtype), rot, false, stream) != hipSuccess)
+  const bool fast = (flags & RBQ_PACKED) && rotated == nullptr;
+  if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, stream) != hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
 }
@@ -88,6 +94,7 @@ extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dt
   const int64_t rows = batch * heads * seq;
   const int rl = rows_log(chk.k, in_kind(dtype), true);
   const int64_t blocks = (rows + (int64_t{1} << rl) - 1) >> rl;
+  if (chk.flat && (std::max(chk.q_rs, chk.k_rs) * 2 << rl) >= (int64_t{1} << 31)) return RBQ_ENOTSUP;
   if (2 * blocks > 0x7FFFFFFF) return RBQ_EINVAL;
   KArgs a{};
   const bool rot_only = (flags & RBQ_Q_ROTATE_ONLY) != 0;
@@ -115,8 +122,9 @@ extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dt
   a.t[1].mode = MODE_QUANT;
   a.rows = rows;
   a.blocks0 = (uint32_t)blocks;
+  a.nblocks = (uint32_t)(2 * blocks);
   a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
-  if (dispatch(chk.k, a, (uint32_t)(2 * blocks), in_kind(dtype), true, !chk.flat, stream) !=
+  if (dispatch(chk.k, a, in_kind(dtype), true, !chk.flat, !rot_only, stream) !=
       hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;

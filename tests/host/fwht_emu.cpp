@@ -53,6 +53,7 @@ static float half16(uint32_t h, int in) { return in == IN_F16 ? f16_to_f32(h) : 
 struct HostCtx {
   uint32_t lane, wave;
   WgShared* s;
+  void refresh_ids() {}
   void barrier() { s->wg.arrive_and_wait(); }
   void wave_sync() { s->wave_bar[wave]->arrive_and_wait(); }
   float shfl_xor(float v, int m) {
@@ -114,17 +115,20 @@ struct HostCtx {
   }
 };
 
+// workgroups run one after another; with fewer workgroups than blocks each one loops
+// over several blocks, as on the GPU
 template <int K, int IN, bool ROT, bool FOURD>
 static void run(const KArgs& a, uint32_t grid) {
   constexpr const Plan& P = PlanOf<K, use_matrix_plan(K, IN, ROT)>::value;
   const int nthreads = 64 << P.w;
-  for (uint32_t blk = 0; blk < grid; ++blk) {
+  for (uint32_t wg = 0; wg < grid; ++wg) {
     WgShared sh(lds_words(P) + (1u << P.w) + 1, nthreads, 1 << P.w);
     std::vector<std::thread> th;
     for (int t = 0; t < nthreads; ++t)
       th.emplace_back([&, t] {
         HostCtx c{(uint32_t)(t & 63), (uint32_t)(t >> 6), &sh};
-        fwht_quant_wg<K, IN, ROT, FOURD>(c, a, blk);
+        if (getenv("RBQ_EMU_FAST")) fwht_quant_persistent<K, IN, ROT, FOURD, true>(c, a, wg, grid);
+        else fwht_quant_persistent<K, IN, ROT, FOURD, false>(c, a, wg, grid);
       });
     for (auto& x : th) x.join();
   }
@@ -201,8 +205,13 @@ int main(int argc, char** argv) {
   a.t[1] = t;
   a.rows = rows;
   const int rl = make_plan(K, use_matrix_plan(K, in, rot != 0)).r;
-  const uint32_t grid = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
-  a.blocks0 = grid;
+  const uint32_t nblocks = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
+  a.blocks0 = nblocks;
+  a.nblocks = nblocks;
+  // a small grid so that workgroups loop over several blocks (RBQ_EMU_GRID overrides)
+  const char* g = getenv("RBQ_EMU_GRID");
+  const uint32_t want = g ? (uint32_t)atoi(g) : 3u;
+  const uint32_t grid = nblocks < want ? nblocks : want;
   a.opts = opts;
   (void)esz;
   switch (K) {

@@ -49,7 +49,7 @@ def emu():
 
 
 def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, mode=MODE_QUANT | MODE_ROT32,
-            row_stride=None, fourd=None):
+            row_stride=None, fourd=None, fast=False, grid=3):
     n = 1 << k
     xb = np.ascontiguousarray(x)
     xpath = str(tmp_path / "x.bin")
@@ -61,7 +61,10 @@ def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, m
             str(mode), xpath, str(xb.size), str(row_stride or n), cpath, spath]
     if fourd is not None:
         args += [str(v) for v in fourd]
-    r = subprocess.run(args, capture_output=True, text=True, timeout=600)
+    env = dict(os.environ, RBQ_EMU_GRID=str(grid))
+    if fast:
+        env["RBQ_EMU_FAST"] = "1"
+    r = subprocess.run(args, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, r.stderr
     codes = np.fromfile(cpath, dtype=np.uint8).reshape(rows, -1)
     scales = np.fromfile(spath, dtype=np.float16 if f16 else np.float32).astype(np.float64)
@@ -178,3 +181,17 @@ def test_q_rotate_only_bf16_output(emu, tmp_path):
     ulp = np.abs(want) * 2.0 ** -7
     assert np.all(np.abs(got - want) <= ulp)
     assert np.mean(got == want) > 0.999
+
+
+@pytest.mark.parametrize("k", [7, 8, 9, 12, 13, 14, 15])
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+def test_fast_variant_codes_only(emu, tmp_path, k, dtype):
+    """The codes-and-scales-only kernel variant (what the benchmark runs), with workgroups
+    looping over several blocks and prefetching the next one."""
+    rows = {7: 300, 8: 150, 9: 70, 12: 9, 13: 5, 14: 5, 15: 3}[k]
+    n = 1 << k
+    x = workloads.gen_rows(400 + k, rows, n, dtype, kind="swiglu", n_outliers=4, factor=200)
+    codes, scales, _ = run_emu(emu, tmp_path, x, dtype, k, rows, mode=MODE_QUANT, fast=True, grid=2)
+    x64 = workloads.to_float64(x, dtype)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+    check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", x64)
