@@ -120,8 +120,9 @@ rbq_status kv_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_
  *  sW     [N] scale_dtype.
  *  out_bf16  bf16 [M, N] row-major, 16-byte aligned (round to nearest even).
  *  acc    optional int32 [M, N] row-major: the exact integer sums; NULL skips it.
- *  M, N   >= 0 (0 returns RBQ_OK); K > 0, K % 128 == 0 (else RBQ_ENOTSUP),
- *         K <= 131072; N % 8 == 0 (16-byte output rows; else RBQ_ENOTSUP).
+ *  M, N   >= 0 (0 returns RBQ_OK); K > 0, K % 128 == 0 and K <= 65536 (else
+ *         RBQ_ENOTSUP: the int32 sums of 16x-scaled int8 products stay exact below that);
+ *         N % 8 == 0 (else RBQ_ENOTSUP).
  * Errors: RBQ_EINVAL for NULL pointers, negative sizes, odd K, misalignment or a bad
  * scale dtype; RBQ_ENOTSUP as above; RBQ_EHIP if the launch fails.
  */

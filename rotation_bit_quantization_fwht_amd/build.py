@@ -51,8 +51,8 @@ def _units():
     return units
 
 
-def _compile(hipcc, src, obj, extra):
-    cmd = [hipcc] + HIP_FLAGS + extra + ["-c", src, "-o", os.path.join(BUILD, obj)]
+def _compile(hipcc, src, obj, extra, build_dir):
+    cmd = [hipcc] + HIP_FLAGS + extra + ["-c", src, "-o", os.path.join(build_dir, obj)]
     t0 = time.time()
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     noise = "is not a recognized feature for this target"
@@ -60,16 +60,21 @@ def _compile(hipcc, src, obj, extra):
     return p.returncode, obj, time.time() - t0, log, cmd
 
 
-def build(verbose=False, jobs=None):
-    """Compile every translation unit for gfx950 and link librbq.so. Returns its path."""
+def build(verbose=False, jobs=None, defines=(), lib_path=None, build_dir=None):
+    """Compile every translation unit for gfx950 and link librbq.so. Returns its path.
+
+    defines/lib_path/build_dir build a variant library (tuning experiments) elsewhere.
+    """
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir = build_dir or BUILD
+    lib_path = lib_path or LIB
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or max(1, min(16, os.cpu_count() or 1))
-    units = _units()
+    units = [(s, o, e + [f"-D{d}" for d in defines]) for (s, o, e) in _units()]
     t0 = time.time()
     failed = []
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_compile, hipcc, s, o, e) for (s, o, e) in units]
+        futs = [ex.submit(_compile, hipcc, s, o, e, build_dir) for (s, o, e) in units]
         for f in concurrent.futures.as_completed(futs):
             rc, obj, dt, log, cmd = f.result()
             if verbose:
@@ -80,16 +85,16 @@ def build(verbose=False, jobs=None):
                 failed.append((obj, " ".join(cmd)))
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(o for o, _ in failed))
-    objs = [os.path.join(BUILD, o) for (_, o, _) in units]
-    tmp = LIB + ".tmp"
+    objs = [os.path.join(build_dir, o) for (_, o, _) in units]
+    tmp = lib_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if p.returncode != 0:
         raise RuntimeError("link failed:\n" + p.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"[build] {LIB} in {time.time() - t0:.1f}s", flush=True)
-    return LIB
+        print(f"[build] {lib_path} in {time.time() - t0:.1f}s", flush=True)
+    return lib_path
 
 
 if __name__ == "__main__":

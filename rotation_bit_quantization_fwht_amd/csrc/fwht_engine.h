@@ -547,14 +547,30 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
   }
 }
 
-// Workgroup `first` processes blocks first, first + step, ... < a.nblocks. With matrix
-// plans the next block's loads are issued as soon as the MFMAs have consumed the
-// current block's, so they are in flight while the current block is transformed.
+#ifndef RBQ_PREFETCH
+#define RBQ_PREFETCH 0
+#endif
+
+// Workgroup `first` processes blocks first, first + step, ... < a.nblocks. With
+// RBQ_PREFETCH and matrix plans the next block's loads are issued as soon as the MFMAs
+// have consumed the current block's, so they are in flight while the current block is
+// transformed.
 template <int K, int IN, bool ROT, bool FOURD, bool FAST, class Ctx>
 RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32_t step) {
   constexpr bool MF = use_matrix_plan(K, IN, ROT);
   const uint32_t nb = a.nblocks;
-  if constexpr (MF) {
+  if constexpr (MF && !RBQ_PREFETCH) {
+    for (uint32_t blk = first; blk < nb; blk += step) {
+      c.refresh_ids();
+      const Block b = block_of<K, MF>(a, blk);
+      uint32_t raw[kMatrixLoads<K, MF>][4];
+      matrix_issue<K, MF, FOURD>(c, *b.t, a.rows, b.row0, raw);
+      Regs<K, MF> v;
+      matrix_apply<K, MF, IN>(c, raw, v);
+      stages<K, MF, 0, false>(v);
+      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+    }
+  } else if constexpr (MF) {
     uint32_t raw[kMatrixLoads<K, MF>][4];
     if (first < nb) {
       const Block b = block_of<K, MF>(a, first);

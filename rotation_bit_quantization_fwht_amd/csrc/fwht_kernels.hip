@@ -13,10 +13,17 @@ namespace rbq {
 template <int K, int IN, bool ROT>
 using KPlan = PlanOf<K, use_matrix_plan(K, IN, ROT)>;
 
-// at least 3 waves per SIMD (<= 168 VGPRs): enough resident workgroups to overlap one
+#ifndef RBQ_WAVES_PER_EU
+#define RBQ_WAVES_PER_EU 4
+#endif
+#ifndef RBQ_RESIDENT_GRID
+#define RBQ_RESIDENT_GRID 0
+#endif
+
+// at least RBQ_WAVES_PER_EU waves per SIMD: enough resident workgroups to overlap one
 // block's loads with another's arithmetic
 template <int K, int IN, bool ROT, bool FOURD, bool FAST>
-__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(RBQ_WAVES_PER_EU)))
 void fwht_quant_kernel(KArgs a) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   __shared__ float lds[lds_words(P) + (1 << P.w) + 1];
@@ -45,7 +52,8 @@ static hipError_t launch_one(const KArgs& a, hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return hipErrorInvalidDevice;
-  const uint64_t cap = (uint64_t)per_cu * (uint64_t)cus;
+  // one workgroup per block, or (RBQ_RESIDENT_GRID) only as many as are resident at once
+  const uint64_t cap = RBQ_RESIDENT_GRID ? (uint64_t)per_cu * (uint64_t)cus : 0xFFFFFFFFull;
   const uint32_t grid = (uint32_t)(a.nblocks < cap ? a.nblocks : cap);
   hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD, FAST>), dim3(grid), dim3(threads), 0, stream, a);
   return hipGetLastError();

@@ -123,7 +123,7 @@ inline rbq_status check_gemm(const void* qA, const void* sA, const void* qW, con
   if (acc && !aligned(acc, 16)) return RBQ_EINVAL;
   const uint64_t ssz = (uint64_t)dtype_size((rbq_dtype)scale_dtype);
   if (!aligned(sA, ssz) || !aligned(sW, ssz)) return RBQ_EINVAL;
-  if (K % 128 != 0 || K > 131072 || N % 8 != 0) return RBQ_ENOTSUP;
+  if (K % 128 != 0 || K > 65536 || N % 8 != 0) return RBQ_ENOTSUP;
   if (M > (int64_t{1} << 30) || N > (int64_t{1} << 30)) return RBQ_ENOTSUP;
   return RBQ_OK;
 }

@@ -126,7 +126,7 @@ def test_gemm_validation(L):
     assert g(qa=ctypes.c_void_p(0x10001)) == E
     assert g(K=4000) == NS
     assert g(N=60) == NS
-    assert g(K=262144) == NS
+    assert g(K=131072) == NS
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

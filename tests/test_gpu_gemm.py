@@ -1,0 +1,97 @@
+"""GPU parity of w4a4_gemm against the oracle's exact integer GEMM, through the C ABI:
+int32 accumulators bit-exact, bf16 outputs within 1e-2 relative. Operands are oracle-made
+codes of the rotated workload (small sizes) or seeded random packed codes (any size)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rbq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotation_bit_quantization_fwht_amd as m
+
+    m.lib()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_out(acc_gpu, out_gpu, acc_ref, sa, sw):
+    assert np.array_equal(acc_gpu.astype(np.int64), acc_ref), "int32 accumulators differ"
+    ref = acc_ref.astype(np.float64) * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+    got = out_gpu.astype(np.float64)
+    zero = acc_ref == 0
+    assert np.all(got[zero] == 0.0)
+    rel = np.abs(got[~zero] - ref[~zero]) / np.abs(ref[~zero])
+    assert rel.size == 0 or float(rel.max()) <= 1e-2, f"bf16 output rel err {rel.max():.3g}"
+
+
+def run(rbq, qa, sa, qw, sw):
+    out, acc = rbq.w4a4_gemm(dev(qa), dev(sa), dev(qw), dev(sw), return_acc=True)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (64, 256, 128), (300, 264, 1024), (256, 512, 4096),
+                                   (513, 1032, 2048), (77, 11008 // 43, 4096)])
+@pytest.mark.parametrize("sdt", ["float16", "float32"])
+def test_gemm_random_codes(rbq, M, N, K, sdt):
+    print(f"case w4a4_gemm M={M} N={N} K={K} scales={sdt}", flush=True)
+    qa = workloads.gen_packed_codes(1, M, K)
+    qw = workloads.gen_packed_codes(2, N, K)
+    sa = workloads.gen_scales(3, M, sdt)
+    sw = workloads.gen_scales(4, N, sdt)
+    acc, out = run(rbq, qa, sa, qw, sw)
+    acc_ref = oracle.int_gemm(oracle.unpack_nibbles(qa), oracle.unpack_nibbles(qw))
+    check_out(acc, out, acc_ref, sa, sw)
+
+
+def test_gemm_extreme_codes(rbq):
+    # all codes -8: the largest magnitude sum, 64 * K per output
+    M, N, K = 64, 64, 65536
+    qa = np.full((M, K // 2), 0x88, dtype=np.uint8)
+    qw = np.full((N, K // 2), 0x88, dtype=np.uint8)
+    s = np.ones(M, dtype=np.float16)
+    acc, out = run(rbq, qa, s, qw, s[:N])
+    assert np.all(acc == 64 * K)
+
+
+def test_gemm_on_rotated_workload_codes(rbq):
+    """The path end to end at reduced size: rotated, quantized activations and weights."""
+    ab, w, _ = workloads.gen_gemm_inputs(seed=3, m=96, n=264, k=2048)
+    ra = oracle.hadamard_quant_int4(workloads.to_float64(ab, "bfloat16"), "float16", packed=True)
+    rw = oracle.hadamard_quant_int4(w.astype(np.float64), "float16", packed=True)
+    acc, out = run(rbq, ra["codes"], ra["scales"], rw["codes"], rw["scales"])
+    acc_ref, _ = oracle.w4a4_gemm(ra["q"], ra["s_stored"], rw["q"], rw["s_stored"])
+    check_out(acc, out, acc_ref, ra["s_stored"], rw["s_stored"])
+
+
+def test_gemm_full_size_sampled(rbq):
+    """The full workload shape, M=4096, N=11008, K=4096: sampled rows exactly, and row and
+    column sums of every accumulator against identities computable at any size."""
+    M, N, K = 4096, 11008, 4096
+    print("case w4a4_gemm full size", flush=True)
+    qa = workloads.gen_packed_codes(11, M, K)
+    qw = workloads.gen_packed_codes(12, N, K)
+    sa = workloads.gen_scales(13, M)
+    sw = workloads.gen_scales(14, N)
+    acc, out = run(rbq, qa, sa, qw, sw)
+    a_codes = oracle.unpack_nibbles(qa).astype(np.int64)
+    w_codes = oracle.unpack_nibbles(qw).astype(np.int64)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(5).integers(0, M, 28)]))
+    acc_ref = oracle.int_gemm(a_codes[rows], w_codes)
+    check_out(acc[rows], out[rows], acc_ref, sa[rows], sw)
+    # sum over n of acc[m, n] = a[m] . (sum_n w[n]);  sum over m = (sum_m a[m]) . w[n]
+    assert np.array_equal(acc.astype(np.int64).sum(axis=1), a_codes @ w_codes.sum(axis=0))
+    assert np.array_equal(acc.astype(np.int64).sum(axis=0), w_codes @ a_codes.sum(axis=0))

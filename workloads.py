@@ -163,3 +163,15 @@ def to_float64(x, dtype):
     if dtype == "float16":
         return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
     raise ValueError(dtype)
+
+
+def gen_packed_codes(seed, rows, k):
+    """Uniformly random packed INT4 codes: uint8 [rows, k/2], every nibble value -8..7
+    equally likely (stand-in operands for GEMM tests at any size)."""
+    return _rng(seed, 7, rows, k).integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+
+
+def gen_scales(seed, n, dtype="float16", lo=1e-3, hi=0.1):
+    """Positive per-row scales, log-uniform in [lo, hi], in the storage dtype."""
+    v = np.exp(_rng(seed, 8, n).uniform(np.log(lo), np.log(hi), size=n))
+    return v.astype(np.float16 if dtype == "float16" else np.float32)
