@@ -71,6 +71,8 @@ constexpr bool use_matrix_plan(int k, int in, bool rot) { return rot && in != IN
 template <int K, bool MF>
 using Regs = float[1 << PlanOf<K, MF>::value.e];
 
+RBQ_HD uint32_t min_u32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
 constexpr int popcount_c(uint32_t x) { int c = 0; while (x) { c += x & 1u; x >>= 1; } return c; }
 
 // gather the bits of x selected by mask into the low bits
@@ -174,14 +176,17 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
   constexpr int ESZ = (IN == IN_F32) ? 4 : 2;
   constexpr int BYTES = L * ESZ;
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
+  const uint32_t last = (uint32_t)(rows - 1 - row0);  // last valid row of the block
   static_for<0, NRUN>([&](auto J) {
     constexpr uint32_t rb = (uint32_t)J.value << C0;
     constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, rb);
     const uint32_t idx = lp | rp;
-    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : (idx >> K);
+    // rows past the end (last block only) re-read the last row: their results are never
+    // stored, and rows do not mix, so no branch is needed
+    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : min_u32(idx >> K, last);
     const uint32_t el = idx & ((1u << K) - 1u);
     uint32_t w[BYTES / 4];
-    if (RBQ_PLAN.r == 0 || row0 + rw < rows) {
+    {
       const char* src = in_addr<K, MF, ESZ, FOURD>(t, row0, rw, el);
       if constexpr (BYTES >= 16) {
         static_for<0, BYTES / 16>([&](auto Q) {
@@ -195,8 +200,6 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
       } else {
         w[0] = c.template load<uint32_t>(src);
       }
-    } else {
-      static_for<0, BYTES / 4>([&](auto Q) { w[Q.value] = 0u; });
     }
     if constexpr (IN == IN_F32) {
       static_for<0, L>([&](auto I) { v[rb + I.value] = bits_f32(w[I.value]); });
@@ -222,17 +225,15 @@ template <int K, bool MF, bool FOURD, class Ctx>
 RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                          uint32_t (&raw)[kMatrixLoads<K, MF>][4]) {
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
+  const uint32_t last = (uint32_t)(rows - 1 - row0);  // last valid row of the block
   static_for<0, kMatrixLoads<K, MF>>([&](auto J) {
     constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, (uint32_t)J.value << 3);
     const uint32_t idx = lp | rp;
-    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : (idx >> K);
+    // rows past the end re-read the last row (their results are never stored)
+    const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : min_u32(idx >> K, last);
     const uint32_t el = idx & ((1u << K) - 1u);
-    if (RBQ_PLAN.r == 0 || row0 + rw < rows) {
-      const u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
-      raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
-    } else {
-      raw[J.value][0] = raw[J.value][1] = raw[J.value][2] = raw[J.value][3] = 0u;
-    }
+    const u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
+    raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
   });
 }
 

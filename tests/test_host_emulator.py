@@ -43,8 +43,10 @@ def emu():
     os.makedirs(BUILD, exist_ok=True)
     exe = os.path.join(BUILD, "fwht_emu_" + _source_hash())
     if not os.path.exists(exe):
-        subprocess.run(["g++", "-std=c++20", "-O1", "-pthread", "-o", exe + ".tmp", SRC], check=True)
-        os.replace(exe + ".tmp", exe)
+        # a private temporary name: parallel test workers may build at the same time
+        tmp = "%s.%d.tmp" % (exe, os.getpid())
+        subprocess.run(["g++", "-std=c++20", "-O1", "-pthread", "-o", tmp, SRC], check=True)
+        os.replace(tmp, exe)
     return exe
 
 
