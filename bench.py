@@ -90,7 +90,7 @@ def cpu_baseline():
     while True:
         oracle.hadamard_quant_int4(x64, "float16", packed=True)
         reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 8:
+        if time.perf_counter() - t0 > 12.0 or reps >= 200:
             break
     dt = (time.perf_counter() - t0) / reps
     sample_bytes = rows * (R4_N * 2 + R4_N // 2 + 2)

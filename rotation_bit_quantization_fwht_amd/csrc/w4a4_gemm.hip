@@ -12,15 +12,23 @@
 // (d << 4) & 0xF0F0F0F0 gives the even codes and d & 0xF0F0F0F0 the odd codes, each as a
 // signed byte equal to 16 * code. Both operands carry the factor 16, so every product is
 // 256 times the code product and the sum is 256 times the integer dot product (exact:
-// |code| <= 8, so |sum| <= 256 * 64 * K < 2^31 for K <= 65536); it is shifted back by 8. The even/odd split permutes K
-// identically in both operands, which leaves the dot product unchanged.
+// |code| <= 8, so |sum| <= 256 * 64 * K < 2^31 for K <= 65536); it is shifted back by 8.
+// The even/odd split permutes K identically in both operands, which leaves the dot
+// product unchanged.
 //
-// Tiling: a 512-thread workgroup computes a 256 x 256 output tile. Each K step stages
-// 128 codes (64 packed bytes) of 256 A rows and 256 W rows in LDS (double buffered,
-// 16-byte chunks XOR-swizzled by row so the fragment reads hit distinct banks) while the
-// next step's global loads are in flight. The 8 waves form a 2 x 4 grid of 128 (m) x
-// 64 (n) wave tiles of 4 x 2 MFMA tiles; W rows are MFMA operand A and A rows operand B,
-// so each lane's accumulators hold four consecutive n of one m (8-byte bf16 stores).
+// Tiling: a 512-thread workgroup computes a 256 x 256 output tile. Each K step covers
+// 128 codes (64 packed bytes) of 256 A rows and 256 W rows, copied from global memory
+// straight into LDS (global_load_lds, 16 bytes per lane, no register staging) through a
+// four-stage ring: while step s is multiplied, step s + 1 is already published (its first
+// fragments are read before the step ends) and the copies for steps s + 2 and s + 3 are in
+// flight; one barrier per step publishes the next step and frees the oldest stage.
+// 16-byte chunks are XOR-swizzled by row so the fragment reads hit distinct banks; the
+// copy realises the swizzle by choosing which chunk each lane fetches. The 8 waves form a
+// 2 x 4 grid of 128 (m) x 64 (n) wave tiles of 4 x 2 MFMA tiles; W rows are MFMA operand
+// A and A rows operand B. Within a step the four 32-code sub-steps are software-pipelined:
+// the MFMAs of one sub-step overlap the widening of the next one's operands. The epilogue
+// stages each wave's bf16 tile through LDS so the output is written in whole 128-byte row
+// segments.
 #include <hip/hip_runtime.h>
 
 #include "../../include/rbq.h"
@@ -45,14 +53,24 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-constexpr int kBM = 256, kBN = 256;
+constexpr int kBM = 256, kBN = 256;                 // output tile (m x n)
+constexpr int kWavesN = kBN / 64;                   // wave grid: 2 (m) x kWavesN (n)
+constexpr int kThreads = 128 * kWavesN;
 constexpr int kStepBytes = 64;            // packed bytes of one row per K step (128 codes)
 constexpr int kChunks = kStepBytes / 16;  // 16-byte chunks per row per K step
-constexpr int kThreads = 512;
+constexpr int kStages = 4;
+constexpr int kSlotsA = kBM * kChunks;              // 16-byte slots of the A rows of a stage
+constexpr int kSlots = (kBM + kBN) * kChunks;       // slots per stage (A rows, then W rows)
+constexpr int kLoads = kSlots / kThreads;           // 16-byte copies per thread per step
+constexpr int kEpiStride = 144;                     // bytes per staged output row (128 + pad)
+static_assert(kSlots % kThreads == 0, "whole copies per thread");
+static_assert(2 * kWavesN * 64 * kEpiStride <= kStages * kSlots * 16, "epilogue staging must fit the ring");
 
-// 16-byte chunk j of row r is stored at chunk j ^ ((r >> 1) & 3): eight consecutive rows
-// reading the same chunk then cover all eight 16-byte bank groups
-__device__ __forceinline__ int swz(int r, int j) { return r * kChunks + (j ^ ((r >> 1) & 3)); }
+// chunk j of row r sits in slot r * 4 + (j ^ key(r)), key(r) = ((r >> 1) ^ (r >> 2)) & 3:
+// the 8 (and the 16) consecutive rows that one LDS cycle serves, reading the same chunk,
+// then cover 8 (16) distinct 16-byte bank groups
+__device__ __forceinline__ int swz_key(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int swz(int r, int j) { return r * kChunks + (j ^ swz_key(r)); }
 
 __device__ __forceinline__ v4i_t widen(uint32_t d0, uint32_t d1) {
   v4i_t r;
@@ -68,8 +86,16 @@ __device__ __forceinline__ float load_scale(const void* p, int i, int f16) {
   return ((const float*)p)[i];
 }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding (they
+// retire in issue order), then meet the other waves. The asm is a compiler memory
+// barrier as well, so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
-  __shared__ u32x4_g lds[2][2][kBM * kChunks];  // [stage][0: A rows, 1: W rows][chunk]
+  __shared__ u32x4_g lds[kStages * kSlots];
 
   // tile order: consecutive workgroups land on different XCDs; give each XCD a contiguous
   // range of tiles, n-major, so the W columns of a range stay in that XCD's L2
@@ -85,16 +111,29 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
   const int wm0 = (wave & 1) * 128, wn0 = (wave >> 1) * 64;
 
   const int rowbytes = g.K / 2;
-  // global -> LDS: 2 chunks of A rows and 2 of W rows per thread per K step
-  const int c0 = tid, c1 = tid + kThreads;
-  const int ra0 = c0 / kChunks, ja0 = c0 % kChunks, ra1 = c1 / kChunks, ja1 = c1 % kChunks;
-  const int am0 = min(m0 + ra0, g.M - 1), am1 = min(m0 + ra1, g.M - 1);
-  const int wn_0 = min(n0 + ra0, g.N - 1), wn_1 = min(n0 + ra1, g.N - 1);
-  const uint8_t* pa0 = g.qa + (int64_t)am0 * rowbytes + ja0 * 16;
-  const uint8_t* pa1 = g.qa + (int64_t)am1 * rowbytes + ja1 * 16;
-  const uint8_t* pw0 = g.qw + (int64_t)wn_0 * rowbytes + ja0 * 16;
-  const uint8_t* pw1 = g.qw + (int64_t)wn_1 * rowbytes + ja1 * 16;
-  const int sa0 = swz(ra0, ja0), sa1 = swz(ra1, ja1);
+  // copy q of a step fills slots q * 512 + tid: lane-contiguous per wave, as the LDS copy
+  // requires. Slot -> (row, chunk) inverts the swizzle; rows past the end re-read the last
+  // row (their products land in rows/columns that are never stored).
+  const uint8_t* src[kLoads];
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q) {
+    const int slot = q * kThreads + tid;
+    const bool is_a = slot < kSlotsA;
+    const int r = (is_a ? slot : slot - kSlotsA) >> 2;
+    const int j = (slot & 3) ^ swz_key(r);
+    const int row = is_a ? min(m0 + r, g.M - 1) : min(n0 + r, g.N - 1);
+    src[q] = (is_a ? g.qa : g.qw) + (int64_t)row * rowbytes + j * 16;
+  }
+  const int steps = rowbytes / kStepBytes;
+  // copies for `step` go to its stage; past the last step they repeat the last step's data
+  // into a stage nobody reads again, which keeps the loop free of branches
+  auto issue_copies = [&](int step) {
+    u32x4_g* dst = lds + (step % kStages) * kSlots + wave * 64;
+    const int off = min(step, steps - 1) * kStepBytes;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + off), (void*)(dst + q * kThreads), 16, 0, 0);
+  };
 
   v16i_t acc[4][2];
 #pragma unroll
@@ -102,90 +141,145 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16i_t{};
 
-  // fragment rows of this lane: lanes 0..31 and 32..63 read the two halves (g) of a row
+  // fragment rows of this lane: lanes 0..31 and 32..63 read the two halves (fg) of a row
   const int fr = lane & 31, fg = lane >> 5;
+  int fa_slot[4], fw_slot[2];  // slot of chunk 2 fg of each fragment row (chunk c: ^ c)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa_slot[i] = swz(wm0 + i * 32 + fr, 2 * fg);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fw_slot[j] = kSlotsA + swz(wn0 + j * 32 + fr, 2 * fg);
 
-  const int steps = rowbytes / kStepBytes;
-  u32x4_g ga0 = *(const u32x4_g*)pa0, ga1 = *(const u32x4_g*)pa1;
-  u32x4_g gw0 = *(const u32x4_g*)pw0, gw1 = *(const u32x4_g*)pw1;
-  lds[0][0][sa0] = ga0; lds[0][0][sa1] = ga1;
-  lds[0][1][sa0] = gw0; lds[0][1][sa1] = gw1;
-  __syncthreads();
-
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < steps;
-    if (more) {
-      const int off = (s + 1) * kStepBytes;
-      ga0 = *(const u32x4_g*)(pa0 + off); ga1 = *(const u32x4_g*)(pa1 + off);
-      gw0 = *(const u32x4_g*)(pw0 + off); gw1 = *(const u32x4_g*)(pw1 + off);
-    }
-    // packed fragments: 32 bytes (two chunks) per row and lane
-    u32x4_g fa[4][2], fw[2][2];
+  auto mma_chunk = [&](const u32x4_g (&fa)[4], const u32x4_g (&fw)[2]) {
+    // 16 packed bytes per fragment row = two sub-steps of 32 codes
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm0 + i * 32 + fr;
-      fa[i][0] = lds[cur][0][swz(r, 2 * fg)];
-      fa[i][1] = lds[cur][0][swz(r, 2 * fg + 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wn0 + j * 32 + fr;
-      fw[j][0] = lds[cur][1][swz(r, 2 * fg)];
-      fw[j][1] = lds[cur][1][swz(r, 2 * fg + 1)];
-    }
-    // four sub-steps of 32 codes: bytes 8u..8u+7 of the lane's 32 bytes
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int h = 0; h < 2; ++h) {
       v4i_t xa[4], xw[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4_g& q = fa[i][u >> 1];
-        xa[i] = widen(q[(u & 1) * 2], q[(u & 1) * 2 + 1]);
-      }
+      for (int i = 0; i < 4; ++i) xa[i] = widen(fa[i][2 * h], fa[i][2 * h + 1]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4_g& q = fw[j][u >> 1];
-        xw[j] = widen(q[(u & 1) * 2], q[(u & 1) * 2 + 1]);
-      }
+      for (int j = 0; j < 2; ++j) xw[j] = widen(fw[j][2 * h], fw[j][2 * h + 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xw[j], xa[i], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      lds[cur ^ 1][0][sa0] = ga0; lds[cur ^ 1][0][sa1] = ga1;
-      lds[cur ^ 1][1][sa0] = gw0; lds[cur ^ 1][1][sa1] = gw1;
-    }
-    __syncthreads();
+  };
+  auto read_chunk = [&](int step, int c, u32x4_g (&fa)[4], u32x4_g (&fw)[2]) {
+    const u32x4_g* sb = lds + (step % kStages) * kSlots;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = sb[fa_slot[i] ^ c];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fw[j] = sb[fw_slot[j] ^ c];
+  };
+
+  // four-stage ring. Invariant at the top of iteration s: steps s and s + 1 are published,
+  // chunk 0 of step s is in registers and its first sub-step already widened, the copies
+  // for step s + 2 may be in flight. Every sub-step's MFMAs overlap the widening of the
+  // next sub-step's operands.
+  issue_copies(0);
+  issue_copies(1);
+  issue_copies(2);
+  wait_copies_and_sync<kLoads>();  // steps 0 and 1 published
+  u32x4_g fa0[4], fw0[2], fa1[4], fw1[2];
+  v4i_t xa[2][4], xw[2][2];
+  auto widen_sub = [&](const u32x4_g (&fa)[4], const u32x4_g (&fw)[2], int h, v4i_t (&ya)[4], v4i_t (&yw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ya[i] = widen(fa[i][2 * h], fa[i][2 * h + 1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) yw[j] = widen(fw[j][2 * h], fw[j][2 * h + 1]);
+  };
+  auto mma_sub = [&](const v4i_t (&ya)[4], const v4i_t (&yw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], acc[i][j], 0, 0, 0);
+  };
+  read_chunk(0, 0, fa0, fw0);
+  widen_sub(fa0, fw0, 0, xa[0], xw[0]);
+  for (int s = 0; s < steps; ++s) {
+    // stage (s + 3) % 4 last held step s - 1, which every wave finished before the
+    // barrier that ended the previous iteration
+    issue_copies(s + 3);
+    read_chunk(s, 1, fa1, fw1);
+    mma_sub(xa[0], xw[0]);
+    widen_sub(fa0, fw0, 1, xa[1], xw[1]);
+    mma_sub(xa[1], xw[1]);
+    widen_sub(fa1, fw1, 0, xa[0], xw[0]);
+    read_chunk(s + 1, 0, fa0, fw0);  // (after the last step: a stale stage, never used)
+    mma_sub(xa[0], xw[0]);
+    widen_sub(fa1, fw1, 1, xa[1], xw[1]);
+    mma_sub(xa[1], xw[1]);
+    widen_sub(fa0, fw0, 0, xa[0], xw[0]);
+    // publish step s + 2: this wave's copies for it are done when at most those of step
+    // s + 3 are in flight
+    wait_copies_and_sync<kLoads>();
   }
 
-  // epilogue: lane holds m = column (lane & 31) of each MFMA tile and, per group q of four
-  // accumulators, n = 8 q + 4 (lane >> 5) + {0, 1, 2, 3}
+  // epilogue. Lane holds m = column (lane & 31) of each MFMA tile and, per group q of four
+  // accumulators, n = 8 q + 4 (lane >> 5) + {0, 1, 2, 3}.
+  if (g.acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm0 + i * 32 + fr;
-    if (m >= g.M) continue;
-    const float sam = load_scale(g.sa, m, g.scale_f16);
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm0 + i * 32 + fr;
+      if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + j * 32 + 8 * q + 4 * fg;
-        if (n >= g.N) continue;
-        int32_t iv[4];
-        uint32_t bits[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          iv[e] = acc[i][j][4 * q + e] >> 8;  // exact: every product carried a factor 256
-          const float y = ((float)iv[e] * sam) * load_scale(g.sw, n + e, g.scale_f16);
-          bits[e] = f32_to_bf16(y);
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + j * 32 + 8 * q + 4 * fg;
+          if (n >= g.N) continue;
+          // exact: every product carried a factor 256
+          *(u32x4*)(g.acc + (int64_t)m * g.N + n) =
+              u32x4{(uint32_t)(acc[i][j][4 * q] >> 8), (uint32_t)(acc[i][j][4 * q + 1] >> 8),
+                    (uint32_t)(acc[i][j][4 * q + 2] >> 8), (uint32_t)(acc[i][j][4 * q + 3] >> 8)};
         }
-        *(u32x2*)(g.out + (int64_t)m * g.N + n) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
-        if (g.acc) *(u32x4*)(g.acc + (int64_t)m * g.N + n) = u32x4{(uint32_t)iv[0], (uint32_t)iv[1], (uint32_t)iv[2], (uint32_t)iv[3]};
-      }
     }
+  }
+  float swv[2][4][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        swv[j][q][e] = load_scale(g.sw, min(n0 + wn0 + j * 32 + 8 * q + 4 * fg + e, g.N - 1), g.scale_f16);
+
+  // bf16 results go through this wave's private LDS rows (64 m x 64 n per half), then out
+  // as 16-byte pieces, eight lanes per 128-byte row segment
+  wait_copies_and_sync<0>();  // every wave is done with the ring
+  char* stage = (char*)lds + wave * 64 * kEpiStride;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * hh + ii;
+      const float sam = load_scale(g.sa, min(m0 + wm0 + i * 32 + fr, g.M - 1), g.scale_f16);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t bits[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bits[e] = f32_to_bf16(((float)(acc[i][j][4 * q + e] >> 8) * sam) * swv[j][q][e]);
+          *(u32x2*)(stage + (ii * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
+              u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rloc = it * 8 + (lane >> 3);
+      const u32x4 v = *(const u32x4*)(stage + rloc * kEpiStride + (lane & 7) * 16);
+      const int m = m0 + wm0 + hh * 64 + rloc;
+      const int n = n0 + wn0 + (lane & 7) * 8;
+      if (m < g.M && n < g.N) *(u32x4*)(g.out + (int64_t)m * g.N + n) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
