@@ -104,12 +104,105 @@ def cpu_baseline():
     }
 
 
+def time_calls(torch, fn, reps):
+    """Average device time per call (events on the current stream) and host time per call
+    (wall clock from the first launch to the end of the last, synchronised)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    host = (time.perf_counter() - t0) / reps
+    return e0.elapsed_time(e1) * 1e3 / reps, host * 1e6
+
+
+def time_graph(torch, fn, calls=20, replays=10):
+    """Device time per call with the launches captured in a HIP graph (no host overhead
+    between kernels); returns (us per call, graph output equals an eager call's)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
+def report_small_workloads(torch, rbq, workloads, dev):
+    """The latency-bound workloads: the 64 x 4096 fp32 worked example (int8 codes, fp32
+    scales; MSE of the dequantized values with and without rotation, computed from the
+    GPU outputs) and the decode sweep (per call: device and host microseconds of eager
+    launches through the binding, and device microseconds with the launches replayed from
+    a HIP graph; next to the same figures for a one-element torch kernel)."""
+    out = {}
+    x = workloads.gen_worked_example(seed=0)
+    xd = torch.from_numpy(x).to(dev)
+    codes = torch.empty((64, 4096), dtype=torch.int8, device=dev)
+    scales = torch.empty((64,), dtype=torch.float32, device=dev)
+    dev_us, host_us = time_calls(
+        torch, lambda: rbq.hadamard_quant_int4(xd, scale_dtype=torch.float32, packed=False, codes=codes, scales=scales), 200)
+    c, sc, rot = rbq.hadamard_quant_int4(xd, scale_dtype=torch.float32, packed=False, return_rotated=True)
+    dc, ds = rbq.hadamard_quant_int4(xd, scale_dtype=torch.float32, packed=False, rotate=False)
+    y = rot.cpu().numpy().astype(np.float64)
+    q = c.cpu().numpy().astype(np.float64) * sc.cpu().numpy().astype(np.float64)[:, None]
+    qd = dc.cpu().numpy().astype(np.float64) * ds.cpu().numpy().astype(np.float64)[:, None]
+    # rotation is orthogonal, so the error measured in the rotated basis equals the error of
+    # rotate -> quantize -> rotate back in the original basis
+    mse_rot = float(np.mean((y - q) ** 2))
+    mse_direct = float(np.mean((x.astype(np.float64) - qd) ** 2))
+    out["worked_example"] = {
+        "workload": "fp32 [64, 4096], channel 142 = 60; int8 codes, fp32 scales",
+        "device_us": round(dev_us, 3), "host_us": round(host_us, 3),
+        "mse_rotated": mse_rot, "mse_direct": mse_direct, "mse_ratio": mse_rot / mse_direct,
+    }
+    one = torch.zeros((1,), dtype=torch.float32, device=dev)
+    floor_dev, floor_host = time_calls(torch, lambda: one.add_(0.0), 500)
+    floor_graph = time_graph(torch, lambda: one.add_(0.0))
+    pts = []
+    for n in workloads.DECODE_N:
+        for t in workloads.DECODE_TOKENS:
+            xb, _ = workloads.gen_decode(seed=0, tokens=t, n=n)
+            xd16 = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
+            cb = torch.empty((t, n // 2), dtype=torch.uint8, device=dev)
+            sb = torch.empty((t,), dtype=torch.float16, device=dev)
+            call = lambda: rbq.hadamard_quant_int4(xd16, codes=cb, scales=sb)  # noqa: E731
+            d_us, h_us = time_calls(torch, call, 200)
+            ref_codes = cb.clone()
+            g_us = time_graph(torch, call)
+            same = bool(torch.equal(cb, ref_codes))
+            nbytes = t * n * 2 + t * n // 2 + 2 * t
+            pts.append({"tokens": t, "n": n, "device_us": round(d_us, 3), "host_us": round(h_us, 3),
+                        "graph_us": round(g_us, 3), "graph_matches_eager": same,
+                        "GB_s_graph": round(nbytes / (g_us * 1e-6) / 1e9, 2)})
+    out["decode_sweep"] = {"floor_device_us": round(floor_dev, 3), "floor_host_us": round(floor_host, 3),
+                           "floor_graph_us": round(floor_graph, 3),
+                           "floor_kernel": "one-element torch add", "points": pts}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the worked-example and decode-sweep reports")
     ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "copy"], default="all",
                     help="restrict the step (for profiling one kernel); 'copy' runs a plain 1 GiB "
                          "device copy used to calibrate the HBM byte counters")
@@ -286,6 +379,10 @@ def main():
             "frac": k["frac_int8_mfma_peak"],
             "traffic": load_traffic("w4a4_gemm", kernel_source_hash(GEMM_SOURCES))}
 
+    extras = {}
+    if args.only == "all" and not args.no_extras:
+        extras = report_small_workloads(torch, rbq, workloads, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -315,6 +412,7 @@ def main():
         "roofline_other": extra_roofline,
         "cpu_baseline": cpu,
     }
+    line.update(extras)
     print(json.dumps(line), flush=True)
 
 

@@ -137,6 +137,16 @@ def _require_cuda(*ts):
             raise ValueError("rbq kernels take GPU tensors only")
 
 
+def _require_buffer(name, t, shape, dtypes, device):
+    """A caller-provided output must be a contiguous tensor of exactly this shape and one
+    of these dtypes on the input's device: the kernels write it without bounds checks."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {'/'.join(str(d) for d in dtypes)} tensor of shape "
+                         f"{tuple(shape)} on {device}; got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=None, scales=None,
                         rotated=None, return_rotated=False, stream=None):
     """Rotate every row of ``x`` [tokens, n] (last dim contiguous) by H_n / sqrt(n) and
@@ -160,6 +170,10 @@ def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=
     if rotated is None and return_rotated:
         rotated = torch.empty((tokens, n), dtype=torch.float32, device=dev)
     _require_cuda(codes, scales, rotated)
+    _require_buffer("codes", codes, (tokens, n // 2) if packed else (tokens, n),
+                    (torch.uint8,) if packed else (torch.int8, torch.uint8), dev)
+    _require_buffer("scales", scales, (tokens,), (torch.float16, torch.float32), dev)
+    _require_buffer("rotated", rotated, (tokens, n), (torch.float32,), dev)
     flags = (RBQ_PACKED if packed else 0) | (0 if rotate else RBQ_NO_ROTATE)
     st = lib().hadamard_quant_int4(
         _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
@@ -202,6 +216,12 @@ def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None
     if k_scales is None:
         k_scales = torch.empty((B, H, S), dtype=scale_dtype, device=dev)
     out["k_codes"], out["k_scales"] = k_codes, k_scales
+    _require_cuda(q_codes, q_scales, k_codes, k_scales, q_rotated)
+    _require_buffer("q_codes", q_codes, (B, H, S, D // 2), (torch.uint8,), dev)
+    _require_buffer("k_codes", k_codes, (B, H, S, D // 2), (torch.uint8,), dev)
+    _require_buffer("q_scales", q_scales, (B, H, S), (k_scales.dtype,), dev)
+    _require_buffer("k_scales", k_scales, (B, H, S), (torch.float16, torch.float32), dev)
+    _require_buffer("q_rotated", q_rotated, (B, H, S, D), (q.dtype,), dev)
     qs = (ctypes.c_int64 * 4)(*q.stride())
     ks = (ctypes.c_int64 * 4)(*k.stride())
     sdt = _dtype_code(k_scales.dtype)
@@ -234,6 +254,13 @@ def w4a4_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=No
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if acc is None and return_acc:
         acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _require_cuda(out, acc)
+    if qa.dtype != torch.uint8 or qw.dtype != torch.uint8:
+        raise ValueError("qa and qw must be uint8 packed codes")
+    if tuple(sa.shape) != (M,) or tuple(sw.shape) != (N,):
+        raise ValueError("sa must be [M] and sw [N]")
+    _require_buffer("out", out, (M, N), (torch.bfloat16,), dev)
+    _require_buffer("acc", acc, (M, N), (torch.int32,), dev)
     st = lib().w4a4_gemm(
         _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _dtype_code(sa.dtype), M, N, K, _ptr(out), _ptr(acc),
         _stream(stream, dev),

@@ -235,3 +235,26 @@ def test_kv_config_full_size(rbq):
         check_quant(oracle.unpack_nibbles(c[sample]), s[sample], ref, "float16", x64)
         q_all = oracle.unpack_nibbles(c[::97])
         assert np.all(np.max(np.abs(q_all), axis=1) == 7) and not np.any(q_all == -8)
+
+
+def test_binding_rejects_bad_output_buffers(rbq):
+    """Caller-provided outputs of the wrong shape, dtype or layout are refused before any
+    launch (the kernels write them without bounds checks)."""
+    x = torch.zeros((8, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        rbq.hadamard_quant_int4(x, codes=torch.empty((8, 64), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):
+        rbq.hadamard_quant_int4(x, codes=torch.empty((8, 128), dtype=torch.int8, device="cuda"))
+    with pytest.raises(ValueError):
+        rbq.hadamard_quant_int4(x, scales=torch.empty((7,), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        rbq.hadamard_quant_int4(x, codes=torch.empty((128, 8), dtype=torch.uint8, device="cuda").t())
+    q = torch.zeros((1, 2, 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        rbq.kv_rotate_quant(q, q.clone(), k_codes=torch.empty((1, 2, 4, 32), dtype=torch.uint8, device="cuda"))
+    qa = torch.zeros((4, 64), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((4,), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        rbq.w4a4_gemm(qa, sa, qa, sa, out=torch.empty((4, 3), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        rbq.w4a4_gemm(qa, sa, qa, sa[:3])
