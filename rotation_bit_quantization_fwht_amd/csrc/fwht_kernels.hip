@@ -22,9 +22,10 @@ using KPlan = PlanOf<K, use_matrix_plan(K, IN, ROT)>;
 
 // at least RBQ_WAVES_PER_EU waves per SIMD: enough resident workgroups to overlap one
 // block's loads with another's arithmetic. The variants that also write rotated values
-// keep more live registers; they get one wave less rather than spilling.
+// keep more live registers; they get one wave less rather than spilling. Plans with 32
+// values per lane aim at 8 waves (64 registers).
 template <int K, int IN, bool ROT, bool FOURD, bool FAST>
-__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(FAST ? RBQ_WAVES_PER_EU : RBQ_WAVES_PER_EU - 1)))
+__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(KPlan<K, IN, ROT>::value.e == 5 ? 8 : (FAST ? RBQ_WAVES_PER_EU : RBQ_WAVES_PER_EU - 1))))
 void fwht_quant_kernel(KArgs a) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   __shared__ float lds[lds_words(P) + (1 << P.w) + 1];

@@ -159,13 +159,15 @@ constexpr Plan make_matrix_plan(int k) {
   p.pre_done = 0x1Fu;  // element bits 0..4 are transformed by the 32-point factor
   auto R = [k](int j) { return (int8_t)(k + j); };
   if (k == 7) {
-    // 4 rows per 512-element load block; 32 rows per wave; 128 rows per workgroup
-    p.e = 6; p.w = 2; p.r = 7; p.nph = 2;
-    const int8_t r0[6] = {0, 1, 2, R(2), R(3), R(4)}, l0[6] = {5, 6, R(0), R(1), 3, 4};
-    const int8_t r1[6] = {0, 1, 2, 5, 6, R(2)}, l1[6] = {3, 4, R(0), R(3), R(4), R(1)};
-    set8(p.reg[0], r0, 6); set8(p.lane[0], l0, 6); set8(p.reg[1], r1, 6); set8(p.lane[1], l1, 6);
-    for (int a = 0; a < 2; ++a) { p.wave[a][0] = R(5); p.wave[a][1] = R(6); }
-    p.sr[0] = 2; p.pad[0][0] = 3; p.pad[0][1] = 5;
+    // 4 rows per 512-element load block; 16 rows per wave; 64 rows per workgroup. Half the
+    // registers of the larger plans (32 values per lane), so twice the waves fit per SIMD:
+    // at 128 points a row is too short for one workgroup's arithmetic to hide its loads.
+    p.e = 5; p.w = 2; p.r = 6; p.nph = 2;
+    const int8_t r0[5] = {0, 1, 2, R(2), R(3)}, l0[6] = {5, 6, R(0), R(1), 3, 4};
+    const int8_t r1[5] = {0, 1, 2, 5, 6}, l1[6] = {3, 4, R(0), R(1), R(2), R(3)};
+    set8(p.reg[0], r0, 5); set8(p.lane[0], l0, 6); set8(p.reg[1], r1, 5); set8(p.lane[1], l1, 6);
+    for (int a = 0; a < 2; ++a) { p.wave[a][0] = R(4); p.wave[a][1] = R(5); }
+    p.sr[0] = 2; p.pad[0][0] = 2; p.pad[0][1] = 3;
   } else if (k == 8) {
     p.e = 6; p.w = 2; p.r = 6; p.nph = 2;
     const int8_t r0[6] = {0, 1, 2, R(1), R(2), R(3)}, l0[6] = {5, 6, 7, R(0), 3, 4};
