@@ -23,7 +23,7 @@ the mathematics fix (worked examples, closed forms, invariants, brute force); a
 function without such a pin says "parity unpinned" in its docstring.
 """
 
-from .hadamard import sylvester, hadamard_popcount, hadamard_column_block, rotate
+from .hadamard import sylvester, hadamard_popcount, hadamard_column_block, rotate, rotate_signed
 from .quant import (
     SCALE_FLOOR,
     QMIN,

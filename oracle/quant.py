@@ -29,7 +29,7 @@ Readings fixed here where the pages are silent:
 
 import numpy as np
 
-from .hadamard import rotate
+from .hadamard import rotate, rotate_signed
 
 SCALE_FLOOR = 1e-8
 QMIN = -8
@@ -128,12 +128,14 @@ def round_to_bf16(v):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True):
+def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True, signs=None):
     """Rotate each row of x by H_n / sqrt(n), then quantize it to INT4 per row.
 
     x: [rows, n] (any real dtype; upcast exactly to float64).
     rotate_input=False quantizes x itself (the "without rotation" arm, and the quantizer
     for activations that already live in a rotated basis).
+    signs: optional [n] vector of +-1; the rotation is then the randomized Hadamard
+    H_n diag(signs) / sqrt(n) (see ``hadamard.rotate_signed``).
 
     Returns a dict with
       y        float64 [rows, n]  values that were quantized (rotated, or x itself),
@@ -144,7 +146,12 @@ def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True
       codes    uint8 [rows, n/2] packed (packed=True) or int8 [rows, n] codes.
     """
     x = np.asarray(x, dtype=np.float64)
-    y = rotate(x) if rotate_input else x.copy()
+    if not rotate_input:
+        y = x.copy()
+    elif signs is not None:
+        y = rotate_signed(x, signs)
+    else:
+        y = rotate(x)
     s = absmax_scale(y)
     s_stored, scales = round_scale(s, scale_dtype)
     q = quantize_codes(y, s_stored)

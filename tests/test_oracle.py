@@ -407,3 +407,63 @@ def test_kv_rotate_quant_per_head_spike():
     assert out["k"]["codes"].shape == (1, 2, 3, d // 2)
     rot_only = oracle.kv_rotate_quant(q, k, q_rotate_only=True)
     assert np.allclose(np.abs(rot_only["q_rot"][0, 1, 2]), 0.70703125)  # bf16(8/sqrt(128))
+
+
+# ------------------------------------------------------------------ randomized Hadamard
+# "Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices": the
+# randomized transform H_n diag(+-1) / sqrt(n).
+
+
+@pytest.mark.parametrize("n", [2, 16, 128, 1024])
+def test_signed_rotation_equals_explicit_matrix(n):
+    s = workloads.gen_signs(1, n).astype(np.float64)
+    x = np.random.default_rng(n).integers(-5, 6, size=(3, n)).astype(np.float64)
+    # row form: y = x (H diag(s))^T / sqrt(n) = x diag(s) H / sqrt(n), H symmetric
+    m = np.diag(s) @ oracle.hadamard_popcount(n)
+    # integer inputs: x @ m is exact, so only the one division by sqrt(n) rounds
+    np.testing.assert_allclose(oracle.rotate_signed(x, s), (x @ m) / math.sqrt(n), rtol=1e-15, atol=1e-13)
+
+
+def test_signed_rotation_all_plus_is_plain_and_is_orthogonal():
+    n = 4096
+    x = np.random.default_rng(5).standard_normal((4, n))
+    np.testing.assert_array_equal(oracle.rotate_signed(x, np.ones(n)), oracle.rotate(x))
+    s = workloads.gen_signs(2, n)
+    y = oracle.rotate_signed(x, s)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    # inverse: x = diag(s) H y / sqrt(n)
+    np.testing.assert_allclose(oracle.rotate(y) * s, x, rtol=0, atol=1e-12)
+
+
+def test_signed_rotation_spreads_a_spike_exactly():
+    n, j, a = 4096, 142, 60.0
+    s = workloads.gen_signs(3, n).astype(np.float64)
+    x = np.zeros((1, n)); x[0, j] = a
+    y = oracle.rotate_signed(x, s)[0]
+    i = np.arange(n)
+    expect = s[j] * a / 64.0 * (1.0 - 2.0 * (np.array([bin(v & j).count("1") for v in i]) & 1))
+    np.testing.assert_array_equal(y, expect)
+
+
+def test_signed_rotation_makes_a_hadamard_row_incoherent():
+    """A row of H is the worst case for the plain transform (all its energy lands on one
+    output); random signs spread it so the largest entry is within a small factor of the
+    RMS, as the page states for the randomized transform."""
+    n, j = 4096, 777
+    x = oracle.sylvester(n)[j:j + 1].astype(np.float64)
+    plain = oracle.rotate(x)[0]
+    assert np.count_nonzero(plain) == 1 and abs(plain[j]) == math.sqrt(n)
+    rms = np.sqrt(np.mean(x ** 2))
+    for seed in range(5):
+        y = oracle.rotate_signed(x, workloads.gen_signs(seed, n))[0]
+        assert np.max(np.abs(y)) < 6.0 * rms
+
+
+def test_signed_quantizer_uses_the_signed_rotation():
+    n = 256
+    x = workloads.gen_rows(4, 5, n, "float32").astype(np.float64)
+    s = workloads.gen_signs(4, n)
+    r = oracle.hadamard_quant_int4(x, "float16", packed=False, signs=s)
+    np.testing.assert_array_equal(r["y"], oracle.rotate_signed(x, s))
+    plain = oracle.hadamard_quant_int4(x * s, "float16", packed=False)
+    np.testing.assert_array_equal(r["q"], plain["q"])

@@ -175,3 +175,8 @@ def gen_scales(seed, n, dtype="float16", lo=1e-3, hi=0.1):
     """Positive per-row scales, log-uniform in [lo, hi], in the storage dtype."""
     v = np.exp(_rng(seed, 8, n).uniform(np.log(lo), np.log(hi), size=n))
     return v.astype(np.float16 if dtype == "float16" else np.float32)
+
+
+def gen_signs(seed, n):
+    """A seeded random +-1 diagonal of length n (float32), for the randomized Hadamard."""
+    return np.where(_rng(seed, 9, n).integers(0, 2, size=n) == 1, 1.0, -1.0).astype(np.float32)
