@@ -391,6 +391,26 @@ def main():
     extras = {}
     if args.only == "all" and not args.no_extras:
         extras = report_small_workloads(torch, rbq, workloads, dev)
+    if run_r4 and not args.no_extras:
+        # the randomized transform H diag(s) / sqrt(n) on the same workload and buffers
+        sg = torch.from_numpy(workloads.gen_signs(0, R4_N)).to(dev).to(torch.bfloat16)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NSETS + 1)]
+        for i in range(NSETS):
+            rbq.hadamard_quant_int4(sets["r4_x"][i], codes=sets["r4_codes"][i], scales=sets["r4_scales"][i], signs=sg)
+        ts = []
+        for rep in range(5):
+            for i in range(NSETS):
+                ev[2 * i].record()
+                rbq.hadamard_quant_int4(sets["r4_x"][i], codes=sets["r4_codes"][i], scales=sets["r4_scales"][i],
+                                        signs=sg)
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            ts += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(NSETS)]
+        t = float(np.mean(ts)) * 1e-3
+        extras["randomized_r4"] = {
+            "workload": "R4 bf16 [8192, 16384] with a seeded +-1 diagonal (H diag(s) / sqrt(n))",
+            "avg_us": round(t * 1e6, 3), "GB_s": round(R4_BYTES / t / 1e9, 2),
+            "frac_hbm_peak": round(R4_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

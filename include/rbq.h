@@ -82,6 +82,24 @@ rbq_status hadamard_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n, int6
                                hipStream_t stream);
 
 /*
+ * hadamard_quant_int4_signed -- as hadamard_quant_int4 with the randomized transform
+ * H_n diag(signs) / sqrt(n) ("Rotations: QuaRot, SpinQuant and incoherence", section
+ * "Hadamard matrices": a random +-1 diagonal before the normalised Hadamard makes the
+ * largest entry close to the row's RMS with high probability).
+ *
+ *  signs        device vector [n] of +1 / -1 in x_dtype (any value's sign bit is used),
+ *               aligned like a row of x; owned by the caller, read only. The same
+ *               diagonal applies to every row; rotated (if given) holds H diag(s) x / sqrt(n).
+ *  all other arguments as for hadamard_quant_int4.
+ * Errors: as hadamard_quant_int4, plus RBQ_EINVAL for a NULL or misaligned `signs` (when
+ * tokens > 0) or for RBQ_NO_ROTATE (the diagonal only makes sense with the rotation).
+ */
+rbq_status hadamard_quant_int4_signed(const void *x, rbq_dtype x_dtype, int64_t n,
+                                      int64_t tokens, int64_t x_row_stride, const void *signs,
+                                      void *codes, void *scales, rbq_dtype scale_dtype,
+                                      float *rotated, unsigned flags, hipStream_t stream);
+
+/*
  * kv_rotate_quant -- R3: rotate every head_dim vector of post-RoPE Q and K by
  * H_d / sqrt(d) and quantize it to INT4 with one scale per (batch, head, token).
  * Q and K are processed in one launch.

@@ -25,6 +25,7 @@ __all__ = [
     "lib",
     "library_path",
     "hadamard_quant_int4",
+    "hadamard_quant_int4_signed",
     "kv_rotate_quant",
     "w4a4_gemm",
     "RBQ_OK",
@@ -46,6 +47,7 @@ RBQ_PACKED, RBQ_NO_ROTATE, RBQ_Q_ROTATE_ONLY = 1, 2, 4
 
 EXPORTED_SYMBOLS = (
     "hadamard_quant_int4",
+    "hadamard_quant_int4_signed",
     "kv_rotate_quant",
     "w4a4_gemm",
     "rbq_status_string",
@@ -88,6 +90,8 @@ def lib():
     p64 = ctypes.POINTER(ctypes.c_int64)
     L.hadamard_quant_int4.argtypes = [vp, ci, i64, i64, i64, vp, vp, ci, vp, cu, vp]
     L.hadamard_quant_int4.restype = ci
+    L.hadamard_quant_int4_signed.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp, ci, vp, cu, vp]
+    L.hadamard_quant_int4_signed.restype = ci
     L.kv_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, vp, vp, ci, vp, cu, vp]
     L.kv_rotate_quant.restype = ci
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
@@ -148,13 +152,15 @@ def _require_buffer(name, t, shape, dtypes, device):
 
 
 def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=None, scales=None,
-                        rotated=None, return_rotated=False, stream=None):
+                        rotated=None, return_rotated=False, signs=None, stream=None):
     """Rotate every row of ``x`` [tokens, n] (last dim contiguous) by H_n / sqrt(n) and
     quantize it to INT4 with one absmax scale per row.
 
     Returns ``(codes, scales)`` -- codes uint8 [tokens, n/2] (packed) or int8
     [tokens, n]; scales [tokens] in ``scale_dtype`` (default float16) -- plus the float
     rotated rows when ``return_rotated`` (or a ``rotated`` buffer) is given.
+    ``signs`` ([n] of +-1 in x's dtype) selects the randomized transform
+    H_n diag(signs) / sqrt(n) (entry point hadamard_quant_int4_signed).
     """
     torch = _torch()
     _require_cuda(x)
@@ -175,11 +181,20 @@ def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=
     _require_buffer("scales", scales, (tokens,), (torch.float16, torch.float32), dev)
     _require_buffer("rotated", rotated, (tokens, n), (torch.float32,), dev)
     flags = (RBQ_PACKED if packed else 0) | (0 if rotate else RBQ_NO_ROTATE)
-    st = lib().hadamard_quant_int4(
-        _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
-        _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), flags, _stream(stream, dev),
-    )
-    _check("hadamard_quant_int4", st)
+    if signs is not None:
+        _require_cuda(signs)
+        _require_buffer("signs", signs, (n,), (x.dtype,), dev)
+        st = lib().hadamard_quant_int4_signed(
+            _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n, _ptr(signs),
+            _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), flags, _stream(stream, dev),
+        )
+        _check("hadamard_quant_int4_signed", st)
+    else:
+        st = lib().hadamard_quant_int4(
+            _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
+            _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), flags, _stream(stream, dev),
+        )
+        _check("hadamard_quant_int4", st)
     if rotated is not None:
         return codes, scales, rotated
     return codes, scales

@@ -45,6 +45,8 @@ struct TensorArgs {
   void* scales;            // [rows] fp16 or fp32
   float* rot32;            // [rows, n] float
   uint16_t* rot16;         // [rows, n] bf16/fp16 bits
+  const void* signs;       // optional [n] +-1 in the input dtype: rows are multiplied by
+                           // this diagonal before the transform (randomized Hadamard)
   uint32_t mode;
 };
 
@@ -201,6 +203,25 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
         w[0] = c.template load<uint32_t>(src);
       }
     }
+    if (t.signs) {
+      // multiply by the +-1 diagonal: flip each value's sign bit where the sign is negative
+      constexpr uint32_t SIGN = (IN == IN_F32) ? 0x80000000u : 0x80008000u;
+      const char* sp = (const char*)t.signs + el * (uint32_t)ESZ;
+      uint32_t sw[BYTES / 4];
+      if constexpr (BYTES >= 16) {
+        static_for<0, BYTES / 16>([&](auto Q) {
+          const u32x4 q4 = c.template load<u32x4>(sp + 16 * Q.value);
+          sw[4 * Q.value + 0] = q4.x; sw[4 * Q.value + 1] = q4.y;
+          sw[4 * Q.value + 2] = q4.z; sw[4 * Q.value + 3] = q4.w;
+        });
+      } else if constexpr (BYTES == 8) {
+        const u32x2 q2 = c.template load<u32x2>(sp);
+        sw[0] = q2.x; sw[1] = q2.y;
+      } else {
+        sw[0] = c.template load<uint32_t>(sp);
+      }
+      static_for<0, BYTES / 4>([&](auto I) { w[I.value] ^= sw[I.value] & SIGN; });
+    }
     if constexpr (IN == IN_F32) {
       static_for<0, L>([&](auto I) { v[rb + I.value] = bits_f32(w[I.value]); });
     } else {
@@ -232,7 +253,12 @@ RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0
     // rows past the end re-read the last row (their results are never stored)
     const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : min_u32(idx >> K, last);
     const uint32_t el = idx & ((1u << K) - 1u);
-    const u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
+    u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
+    if (t.signs) {  // randomized Hadamard: flip the 16-bit sign bits where the diagonal is -1
+      const u32x4 s4 = c.template load<u32x4>((const char*)t.signs + el * 2u);
+      q4.x ^= s4.x & 0x80008000u; q4.y ^= s4.y & 0x80008000u;
+      q4.z ^= s4.z & 0x80008000u; q4.w ^= s4.w & 0x80008000u;
+    }
     raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
   });
 }

@@ -48,10 +48,10 @@ static int in_kind(rbq_dtype d) { return d == RBQ_F32 ? IN_F32 : (d == RBQ_BF16 
 
 using namespace rbq;
 
-extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int64_t n,
-                                          int64_t tokens, int64_t x_row_stride, void* codes,
-                                          void* scales, rbq_dtype scale_dtype, float* rotated,
-                                          unsigned flags, hipStream_t stream) {
+static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
+                            int64_t x_row_stride, const void* signs, void* codes, void* scales,
+                            rbq_dtype scale_dtype, float* rotated, unsigned flags,
+                            hipStream_t stream) {
   const HqCheck chk = check_hadamard_quant(x, x_dtype, n, tokens, x_row_stride, codes, scales,
                                            scale_dtype, rotated, flags);
   if (chk.status != RBQ_OK || tokens == 0) return chk.status;
@@ -68,6 +68,7 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   t.codes = codes;
   t.scales = scales;
   t.rot32 = rotated;
+  t.signs = signs;
   t.mode = MODE_QUANT | (rotated ? MODE_ROT32 : 0u);
   a.t[1] = t;
   a.rows = tokens;
@@ -78,6 +79,25 @@ extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int6
   if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, stream) != hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
+}
+
+extern "C" rbq_status hadamard_quant_int4(const void* x, rbq_dtype x_dtype, int64_t n,
+                                          int64_t tokens, int64_t x_row_stride, void* codes,
+                                          void* scales, rbq_dtype scale_dtype, float* rotated,
+                                          unsigned flags, hipStream_t stream) {
+  return hq_launch(x, x_dtype, n, tokens, x_row_stride, nullptr, codes, scales, scale_dtype,
+                   rotated, flags, stream);
+}
+
+extern "C" rbq_status hadamard_quant_int4_signed(const void* x, rbq_dtype x_dtype, int64_t n,
+                                                 int64_t tokens, int64_t x_row_stride,
+                                                 const void* signs, void* codes, void* scales,
+                                                 rbq_dtype scale_dtype, float* rotated,
+                                                 unsigned flags, hipStream_t stream) {
+  const rbq_status st = check_signs(x_dtype, n, tokens, signs, flags);
+  if (st != RBQ_OK) return st;
+  return hq_launch(x, x_dtype, n, tokens, x_row_stride, signs, codes, scales, scale_dtype,
+                   rotated, flags, stream);
 }
 
 extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dtype, int64_t batch,

@@ -57,6 +57,19 @@ inline HqCheck check_hadamard_quant(const void* x, int x_dtype, int64_t n, int64
   return r;
 }
 
+// the +-1 diagonal of the randomized transform: one value per element in the input dtype,
+// aligned like a row; it only makes sense with the rotation
+inline rbq_status check_signs(int x_dtype, int64_t n, int64_t tokens, const void* signs,
+                              unsigned flags) {
+  if (flags & RBQ_NO_ROTATE) return RBQ_EINVAL;
+  if (tokens == 0) return RBQ_OK;
+  if (!signs || !valid_in_dtype(x_dtype) || !is_pow2(n)) return RBQ_EINVAL;
+  const int64_t esz = dtype_size((rbq_dtype)x_dtype);
+  const int64_t align = (n * esz < 16) ? n * esz : 16;
+  if (!aligned(signs, (uint64_t)align)) return RBQ_EINVAL;
+  return RBQ_OK;
+}
+
 struct KvCheck {
   rbq_status status;
   int k;

@@ -195,6 +195,13 @@ int main(int argc, char** argv) {
   t.rot32 = (mode0 & MODE_ROT32) ? (float*)rotb : nullptr;
   t.rot16 = (mode0 & MODE_ROT16) ? (uint16_t*)rotb : nullptr;
   t.mode = mode0;
+  // RBQ_EMU_SIGNS names a file with the +-1 diagonal of the randomized transform
+  static std::vector<char> signs;
+  if (const char* sp = getenv("RBQ_EMU_SIGNS")) {
+    signs = read_file(sp);
+    g_bufs.push_back({signs.data(), signs.data() + signs.size(), "signs"});
+    t.signs = signs.data();
+  }
   if (argc >= 19) {
     const long long B = atoll(argv[13]), H = atoll(argv[14]), S = atoll(argv[15]);
     t.sb = atoll(argv[16]); t.sh = atoll(argv[17]); t.ss = atoll(argv[18]);

@@ -84,6 +84,20 @@ def test_hadamard_quant_validation(L):
     assert hq(L, n=2, stride=2, x=ctypes.c_void_p(0x10004), tokens=0) == rbq.RBQ_OK
 
 
+def test_signed_validation(L):
+    E = rbq.RBQ_EINVAL
+
+    def hs(signs=A16c, flags=rbq.RBQ_PACKED, tokens=8, n=4096, dt=rbq.RBQ_BF16):
+        return L.hadamard_quant_int4_signed(A16, dt, n, tokens, n, signs, A16b, A16c, rbq.RBQ_F16, NULL, flags, NULL)
+
+    assert hs(tokens=0) == rbq.RBQ_OK
+    assert hs(signs=NULL) == E
+    assert hs(signs=ctypes.c_void_p(0x30008)) == E     # not aligned like a row
+    assert hs(flags=rbq.RBQ_PACKED | rbq.RBQ_NO_ROTATE) == E
+    assert hs(n=4095) == E
+    assert hs(dt=9) == E
+
+
 def kv(L, q=A16, k=A16b, dt=rbq.RBQ_BF16, B=2, H=4, S=16, D=128, qs=None, ks=None, qc=A16c, qsc=A16c,
        kc=A16c, ksc=A16c, sdt=rbq.RBQ_F16, qrot=NULL, flags=0):
     def st(v):

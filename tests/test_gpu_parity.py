@@ -258,3 +258,27 @@ def test_binding_rejects_bad_output_buffers(rbq):
         rbq.w4a4_gemm(qa, sa, qa, sa, out=torch.empty((4, 3), dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):
         rbq.w4a4_gemm(qa, sa, qa, sa[:3])
+
+
+@pytest.mark.parametrize("k,dtype", [(1, "float32"), (3, "bfloat16"), (7, "bfloat16"), (9, "float16"),
+                                     (12, "float32"), (14, "bfloat16"), (15, "float16")])
+def test_randomized_rotation(rbq, k, dtype):
+    """H diag(signs) / sqrt(n) through hadamard_quant_int4_signed: codes-only launches and
+    launches that also return the rotated rows, against the oracle's randomized transform."""
+    n = 1 << k
+    rows = max(3, min(300, (1 << 16) // n))
+    print(f"case randomized k={k} {dtype} rows={rows}", flush=True)
+    x = workloads.gen_rows(50 + k, rows, n, dtype, kind="swiglu", n_outliers=3, factor=120)
+    s32 = workloads.gen_signs(k, n)
+    sd = torch.from_numpy(s32).to("cuda").to({"float32": torch.float32, "bfloat16": torch.bfloat16,
+                                             "float16": torch.float16}[dtype])
+    xd = to_dev(x, dtype)
+    x64 = workloads.to_float64(x, dtype)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, signs=s32)
+    codes, scales = rbq.hadamard_quant_int4(xd, signs=sd)
+    check_quant(oracle.unpack_nibbles(codes.cpu().numpy()), scales.cpu().numpy(), ref, "float16", x64)
+    codes, scales, rot = rbq.hadamard_quant_int4(xd, signs=sd, return_rotated=True)
+    check_quant(oracle.unpack_nibbles(codes.cpu().numpy()), scales.cpu().numpy(), ref, "float16", x64,
+                y_gpu=rot.cpu().numpy())
+    with pytest.raises(rbq.RBQError):
+        rbq.hadamard_quant_int4(xd, signs=sd, rotate=False)

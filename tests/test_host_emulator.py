@@ -51,7 +51,7 @@ def emu():
 
 
 def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, mode=MODE_QUANT | MODE_ROT32,
-            row_stride=None, fourd=None, fast=False, grid=3):
+            row_stride=None, fourd=None, fast=False, grid=3, signs=None):
     n = 1 << k
     xb = np.ascontiguousarray(x)
     xpath = str(tmp_path / "x.bin")
@@ -66,6 +66,10 @@ def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, m
     env = dict(os.environ, RBQ_EMU_GRID=str(grid))
     if fast:
         env["RBQ_EMU_FAST"] = "1"
+    if signs is not None:
+        signs_path = str(tmp_path / "signs.bin")
+        np.ascontiguousarray(signs).tofile(signs_path)
+        env["RBQ_EMU_SIGNS"] = signs_path
     r = subprocess.run(args, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, r.stderr
     codes = np.fromfile(cpath, dtype=np.uint8).reshape(rows, -1)
@@ -197,3 +201,24 @@ def test_fast_variant_codes_only(emu, tmp_path, k, dtype):
     x64 = workloads.to_float64(x, dtype)
     ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
     check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", x64)
+
+
+@pytest.mark.parametrize("k,dtype", [(3, "float32"), (7, "bfloat16"), (10, "float16"), (12, "float32"),
+                                     (14, "bfloat16"), (15, "bfloat16")])
+def test_randomized_rotation(emu, tmp_path, k, dtype):
+    """H diag(signs) / sqrt(n): the signs are applied to the loaded values (vector and
+    matrix load paths) and everything downstream is the plain transform."""
+    n = 1 << k
+    rows = 5
+    x = workloads.gen_rows(31 + k, rows, n, dtype, n_outliers=2, factor=80.0)
+    s32 = workloads.gen_signs(k, n)
+    sgn = s32 if dtype == "float32" else (workloads.f32_to_bf16_bits(s32) if dtype == "bfloat16"
+                                          else s32.astype(np.float16).view(np.uint16))
+    for fast in ((False, True) if dtype != "float32" and k >= 7 else (False,)):
+        mode = MODE_QUANT if fast else MODE_QUANT | MODE_ROT32
+        codes, scales, rot = run_emu(emu, tmp_path, x, dtype, k, rows, mode=mode, fast=fast, signs=sgn)
+        x64 = workloads.to_float64(x, dtype)
+        ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, signs=s32)
+        check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", x64,
+                    y_gpu=None if fast else rot)
+
