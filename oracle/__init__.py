@@ -26,6 +26,7 @@ function without such a pin says "parity unpinned" in its docstring.
 from .hadamard import sylvester, hadamard_popcount, hadamard_column_block, rotate, rotate_signed
 from .quant import (
     SCALE_FLOOR,
+    qrange,
     QMIN,
     QMAX,
     absmax_scale,
@@ -40,13 +41,15 @@ from .quant import (
     hadamard_quant_int4,
     kv_rotate_quant,
 )
-from .gemm import int_gemm, w4a4_gemm
+from .gemm import int_gemm, w4a4_gemm, w4a8_gemm
 
 __all__ = [
     "sylvester",
     "hadamard_popcount",
     "hadamard_column_block",
     "rotate",
+    "rotate_signed",
+    "qrange",
     "SCALE_FLOOR",
     "QMIN",
     "QMAX",
@@ -63,4 +66,5 @@ __all__ = [
     "kv_rotate_quant",
     "int_gemm",
     "w4a4_gemm",
+    "w4a8_gemm",
 ]

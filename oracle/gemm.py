@@ -46,3 +46,11 @@ def w4a4_gemm(qa, sa, qw, sw):
     sw = np.asarray(sw, dtype=np.float64)
     out = acc.astype(np.float64) * sa[:, None] * sw[None, :]
     return acc, out
+
+
+def w4a8_gemm(qa, sa, qw, sw):
+    """Dequantized W4A8 product: INT8 activation codes qa [M, K] (scale max/127 per
+    token), INT4 weight codes qw [N, K]; the same exact integer sum and epilogue as
+    ``w4a4_gemm`` (|sum| <= K * 128 * 8, exact in float64)."""
+    return w4a4_gemm(qa, sa, qw, sw)
+

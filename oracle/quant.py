@@ -38,11 +38,21 @@ QMAX = 7
 _SCALE_DTYPES = {"float32": np.float32, "float16": np.float16}
 
 
-def absmax_scale(y):
-    """Unrounded per-row scale s = max(max_i |y_i| / 7, 1e-8), float64, shape [rows]."""
+def qrange(bits=4):
+    """Symmetric signed grid of a b-bit code: [-2^(b-1), 2^(b-1) - 1] ("SpinQuant Guide:
+    Learned Rotations for 4-Bit LLMs", step-size equation: step = max|X| / (2^(b-1) - 1));
+    b = 4 gives [-8, 7] and step max/7, b = 8 gives [-128, 127] and step max/127."""
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    return -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+
+
+def absmax_scale(y, bits=4):
+    """Unrounded per-row scale s = max(max_i |y_i| / qmax, 1e-8), float64, shape [rows];
+    qmax = 7 for INT4, 127 for INT8."""
     y = np.asarray(y, dtype=np.float64)
     m = np.max(np.abs(y), axis=-1) if y.shape[-1] > 0 else np.zeros(y.shape[:-1])
-    return np.maximum(m / QMAX, SCALE_FLOOR)
+    return np.maximum(m / qrange(bits)[1], SCALE_FLOOR)
 
 
 def round_scale(s, dtype):
@@ -55,8 +65,9 @@ def round_scale(s, dtype):
     return stored.astype(np.float64), stored
 
 
-def quantize_codes(y, s_stored):
-    """Codes q = round_half_even(clamp(y / s, -8, 7)) per row, as int8.
+def quantize_codes(y, s_stored, bits=4):
+    """Codes q = round_half_even(clamp(y / s, qmin, qmax)) per row, as int8 ([-8, 7] for
+    INT4, [-128, 127] for INT8).
 
     y: [..., n] float64; s_stored: [...] float64 (the stored scale). Rows whose stored
     scale is 0 get code 0 everywhere.
@@ -66,7 +77,8 @@ def quantize_codes(y, s_stored):
     zero = s == 0.0
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(zero, 0.0, y / np.where(zero, 1.0, s))
-    q = np.rint(np.clip(t, QMIN, QMAX))
+    lo, hi = qrange(bits)
+    q = np.rint(np.clip(t, lo, hi))
     return q.astype(np.int8)
 
 
@@ -128,7 +140,7 @@ def round_to_bf16(v):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True, signs=None):
+def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True, signs=None, bits=4):
     """Rotate each row of x by H_n / sqrt(n), then quantize it to INT4 per row.
 
     x: [rows, n] (any real dtype; upcast exactly to float64).
@@ -136,6 +148,8 @@ def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True
     for activations that already live in a rotated basis).
     signs: optional [n] vector of +-1; the rotation is then the randomized Hadamard
     H_n diag(signs) / sqrt(n) (see ``hadamard.rotate_signed``).
+    bits: 4 (default) or 8 -- INT8 codes (scale max/127, range [-128, 127]) are never
+    packed.
 
     Returns a dict with
       y        float64 [rows, n]  values that were quantized (rotated, or x itself),
@@ -152,9 +166,11 @@ def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True
         y = rotate_signed(x, signs)
     else:
         y = rotate(x)
-    s = absmax_scale(y)
+    if bits == 8 and packed:
+        raise ValueError("INT8 codes are stored one per byte")
+    s = absmax_scale(y, bits)
     s_stored, scales = round_scale(s, scale_dtype)
-    q = quantize_codes(y, s_stored)
+    q = quantize_codes(y, s_stored, bits)
     codes = pack_nibbles(q) if packed else q
     return {"y": y, "s": s, "scales": scales, "s_stored": s_stored, "q": q, "codes": codes}
 

@@ -467,3 +467,54 @@ def test_signed_quantizer_uses_the_signed_rotation():
     np.testing.assert_array_equal(r["y"], oracle.rotate_signed(x, s))
     plain = oracle.hadamard_quant_int4(x * s, "float16", packed=False)
     np.testing.assert_array_equal(r["q"], plain["q"])
+
+
+# ------------------------------------------------------------------ INT8 activation codes
+# "SpinQuant Guide: Learned Rotations for 4-Bit LLMs", step-size equation with b = 8:
+# step = max|X| / 127 on the grid [-128, 127] (the W4A8 configuration the pages' only
+# latency figure uses).
+
+
+def test_int8_grid_and_ties_without_rotation():
+    assert oracle.qrange(8) == (-128, 127) and oracle.qrange(4) == (-8, 7)
+    row = np.array([[127.0, 2.5, 3.5, -2.5, 126.5, -126.5, 0.5, -127.0]])
+    r = oracle.hadamard_quant_int4(row, "float32", packed=False, rotate_input=False, bits=8)
+    assert r["s_stored"][0] == 1.0
+    assert r["q"].tolist() == [[127, 2, 4, -2, 126, -126, 0, -127]]
+    with pytest.raises(ValueError):
+        oracle.hadamard_quant_int4(row, "float32", packed=True, rotate_input=False, bits=8)
+
+
+def test_int8_invariants_on_rotated_rows():
+    x = workloads.gen_rows(21, 64, 1024, "float32", kind="swiglu", n_outliers=3, factor=150).astype(np.float64)
+    r = oracle.hadamard_quant_int4(x, "float16", packed=False, bits=8)
+    q = r["q"].astype(np.int64)
+    assert np.all(np.max(np.abs(q), axis=1) == 127)
+    assert not np.any(q == -128)
+    # the absmax element of each row lands on +-127
+    idx = np.argmax(np.abs(r["y"]), axis=1)
+    assert np.all(np.abs(q[np.arange(len(idx)), idx]) == 127)
+
+
+def test_int8_error_matches_uniform_noise_model():
+    """With a step this small the rounding error of Gaussian data is uniform on
+    [-s/2, s/2], so the mean squared error is s^2 / 12 (the pages' noise analysis)."""
+    x = np.random.default_rng(8).standard_normal((256, 4096))
+    r = oracle.hadamard_quant_int4(x, "float32", packed=False, bits=8)
+    err = np.mean((r["y"] - r["q"] * r["s_stored"][:, None]) ** 2, axis=1)
+    ratio = err / (r["s_stored"] ** 2 / 12.0)
+    assert 0.97 < float(np.mean(ratio)) < 1.03
+
+
+def test_w4a8_gemm_brute_force_extremes():
+    rng = np.random.default_rng(12)
+    qa = rng.integers(-128, 128, size=(5, 96))
+    qa[0, :] = -128
+    qw = rng.integers(-8, 8, size=(7, 96))
+    qw[1, :] = -8
+    acc, out = oracle.w4a8_gemm(qa, np.full(5, 0.5), qw, np.full(7, 0.25))
+    for m in range(5):
+        for n in range(7):
+            assert acc[m, n] == sum(int(qa[m, k]) * int(qw[n, k]) for k in range(96))
+    assert acc[0, 1] == 96 * 1024
+    np.testing.assert_array_equal(out, acc * 0.125)
