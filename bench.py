@@ -284,6 +284,7 @@ def main():
         del ab, w
         qa, sa = rbq.hadamard_quant_int4(a0)                     # activations, online rotation
         qw, sw = rbq.hadamard_quant_int4(w0)                     # weights, offline rotation
+        qa8, sa8 = rbq.hadamard_quant_int8(a0)                   # W4A8: INT8 activation codes
         out = torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=dev)
         try:
             rbq.w4a4_gemm(qa, sa, qw, sw, out=out)
@@ -391,6 +392,22 @@ def main():
     extras = {}
     if args.only == "all" and not args.no_extras:
         extras = report_small_workloads(torch, rbq, workloads, dev)
+    if run_gemm and gemm_ok and not args.no_extras:
+        # the W4A8 variant on the same workload (INT8 activation codes, INT4 weights)
+        out8 = torch.empty_like(out)
+        rbq.w4a8_gemm(qa8, sa8, qw, sw, out=out8)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            rbq.w4a8_gemm(qa8, sa8, qw, sw, out=out8)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 20
+        extras["w4a8_gemm"] = {
+            "workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], bf16 out",
+            "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
+            "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
     if run_r4 and not args.no_extras:
         # the randomized transform H diag(s) / sqrt(n) on the same workload and buffers
         sg = torch.from_numpy(workloads.gen_signs(0, R4_N)).to(dev).to(torch.bfloat16)

@@ -100,6 +100,20 @@ rbq_status hadamard_quant_int4_signed(const void *x, rbq_dtype x_dtype, int64_t 
                                       float *rotated, unsigned flags, hipStream_t stream);
 
 /*
+ * hadamard_quant_int8 -- as hadamard_quant_int4 with 8-bit codes for W4A8 layers: the
+ * step-size equation of "SpinQuant Guide: Learned Rotations for 4-Bit LLMs" at b = 8,
+ * s = max(max|y| / 127, 1e-8) rounded to scale_dtype, q = RNE(clamp(y / s, -128, 127)).
+ *
+ *  codes        int8 [tokens, n] contiguous, 16-byte aligned (one code per byte).
+ *  flags        RBQ_NO_ROTATE only (RBQ_PACKED is rejected).
+ *  all other arguments and errors as for hadamard_quant_int4.
+ */
+rbq_status hadamard_quant_int8(const void *x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
+                               int64_t x_row_stride, int8_t *codes, void *scales,
+                               rbq_dtype scale_dtype, float *rotated, unsigned flags,
+                               hipStream_t stream);
+
+/*
  * kv_rotate_quant -- R3: rotate every head_dim vector of post-RoPE Q and K by
  * H_d / sqrt(d) and quantize it to INT4 with one scale per (batch, head, token).
  * Q and K are processed in one launch.
@@ -145,6 +159,22 @@ rbq_status kv_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_
  * scale dtype; RBQ_ENOTSUP as above; RBQ_EHIP if the launch fails.
  */
 rbq_status w4a4_gemm(const uint8_t *qA, const void *sA, const uint8_t *qW, const void *sW,
+                     rbq_dtype scale_dtype, int64_t M, int64_t N, int64_t K, void *out_bf16,
+                     int32_t *acc, hipStream_t stream);
+
+/*
+ * w4a8_gemm -- the W4A8 variant: INT8 activation codes (hadamard_quant_int8) times packed
+ * INT4 weight codes, out[m, n] = bf16( sA[m] * sW[n] * sum_k qA[m, k] * qW[n, k] ). The
+ * pages' only latency figure is for this configuration ("SpinQuant: LLM Quantization with
+ * Learned Rotations", measured effects); the step-size equation of "SpinQuant Guide:
+ * Learned Rotations for 4-Bit LLMs" at b = 8 gives the activation codes.
+ *
+ *  qA     int8 [M, K] row-major (K-contiguous), 16-byte aligned.
+ *  qW     uint8 [N, K/2] packed INT4 as for w4a4_gemm.
+ *  all other arguments, limits (K % 128 == 0, K <= 65536, N % 8 == 0) and errors as for
+ *  w4a4_gemm; the integer sums are exact.
+ */
+rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const void *sW,
                      rbq_dtype scale_dtype, int64_t M, int64_t N, int64_t K, void *out_bf16,
                      int32_t *acc, hipStream_t stream);
 

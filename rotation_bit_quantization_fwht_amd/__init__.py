@@ -25,9 +25,10 @@ __all__ = [
     "lib",
     "library_path",
     "hadamard_quant_int4",
-    "hadamard_quant_int4_signed",
+    "hadamard_quant_int8",
     "kv_rotate_quant",
     "w4a4_gemm",
+    "w4a8_gemm",
     "RBQ_OK",
     "RBQ_EINVAL",
     "RBQ_ENOTSUP",
@@ -48,8 +49,10 @@ RBQ_PACKED, RBQ_NO_ROTATE, RBQ_Q_ROTATE_ONLY = 1, 2, 4
 EXPORTED_SYMBOLS = (
     "hadamard_quant_int4",
     "hadamard_quant_int4_signed",
+    "hadamard_quant_int8",
     "kv_rotate_quant",
     "w4a4_gemm",
+    "w4a8_gemm",
     "rbq_status_string",
     "rbq_version",
 )
@@ -92,10 +95,14 @@ def lib():
     L.hadamard_quant_int4.restype = ci
     L.hadamard_quant_int4_signed.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp, ci, vp, cu, vp]
     L.hadamard_quant_int4_signed.restype = ci
+    L.hadamard_quant_int8.argtypes = [vp, ci, i64, i64, i64, vp, vp, ci, vp, cu, vp]
+    L.hadamard_quant_int8.restype = ci
     L.kv_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, vp, vp, ci, vp, cu, vp]
     L.kv_rotate_quant.restype = ci
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
     L.w4a4_gemm.restype = ci
+    L.w4a8_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
+    L.w4a8_gemm.restype = ci
     L.rbq_status_string.argtypes = [ci]
     L.rbq_status_string.restype = ctypes.c_char_p
     L.rbq_version.argtypes = []
@@ -200,6 +207,38 @@ def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=
     return codes, scales
 
 
+def hadamard_quant_int8(x, *, scale_dtype=None, rotate=True, codes=None, scales=None, rotated=None,
+                        return_rotated=False, stream=None):
+    """As ``hadamard_quant_int4`` with INT8 codes (scale max/127, int8 [tokens, n]) for
+    W4A8 layers. Returns ``(codes, scales)`` (+ the rotated rows when requested)."""
+    torch = _torch()
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with a contiguous last dimension")
+    tokens, n = x.shape
+    scale_dtype = torch.float16 if scale_dtype is None else scale_dtype
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((tokens, n), dtype=torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty((tokens,), dtype=scale_dtype, device=dev)
+    if rotated is None and return_rotated:
+        rotated = torch.empty((tokens, n), dtype=torch.float32, device=dev)
+    _require_cuda(codes, scales, rotated)
+    _require_buffer("codes", codes, (tokens, n), (torch.int8,), dev)
+    _require_buffer("scales", scales, (tokens,), (torch.float16, torch.float32), dev)
+    _require_buffer("rotated", rotated, (tokens, n), (torch.float32,), dev)
+    st = lib().hadamard_quant_int8(
+        _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
+        _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated),
+        0 if rotate else RBQ_NO_ROTATE, _stream(stream, dev),
+    )
+    _check("hadamard_quant_int8", st)
+    if rotated is not None:
+        return codes, scales, rotated
+    return codes, scales
+
+
 def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None, q_scales=None,
                     k_codes=None, k_scales=None, q_rotated=None, stream=None):
     """R3 on post-RoPE ``q`` and ``k`` [B, H, S, D] (bf16/fp16, D contiguous): rotate every
@@ -284,3 +323,39 @@ def w4a4_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=No
     if acc is not None:
         return out, acc
     return out
+
+
+def w4a8_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=None):
+    """out[m, n] = bf16(sa[m] * sw[n] * sum_k qa[m, k] qw[n, k]) with INT8 activation codes
+    qa int8 [M, K] and packed INT4 weight codes qw uint8 [N, K/2] (contiguous); sa [M],
+    sw [N] share an fp16/fp32 dtype. Returns ``out`` (+ the int32 sums when requested)."""
+    torch = _torch()
+    _require_cuda(qa, sa, qw, sw)
+    if qa.dim() != 2 or qw.dim() != 2 or qa.shape[1] != 2 * qw.shape[1]:
+        raise ValueError("qa must be [M, K] and qw [N, K/2]")
+    if not (qa.is_contiguous() and qw.is_contiguous() and sa.is_contiguous() and sw.is_contiguous()):
+        raise ValueError("operands must be contiguous")
+    if qa.dtype != torch.int8 or qw.dtype != torch.uint8:
+        raise ValueError("qa must be int8 codes and qw uint8 packed codes")
+    if sa.dtype != sw.dtype:
+        raise ValueError("sa and sw must share a dtype")
+    M, N, K = qa.shape[0], qw.shape[0], qa.shape[1]
+    if tuple(sa.shape) != (M,) or tuple(sw.shape) != (N,):
+        raise ValueError("sa must be [M] and sw [N]")
+    dev = qa.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if acc is None and return_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    _require_cuda(out, acc)
+    _require_buffer("out", out, (M, N), (torch.bfloat16,), dev)
+    _require_buffer("acc", acc, (M, N), (torch.int32,), dev)
+    st = lib().w4a8_gemm(
+        _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _dtype_code(sa.dtype), M, N, K, _ptr(out), _ptr(acc),
+        _stream(stream, dev),
+    )
+    _check("w4a8_gemm", st)
+    if acc is not None:
+        return out, acc
+    return out
+

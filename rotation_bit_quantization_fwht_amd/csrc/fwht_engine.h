@@ -13,7 +13,8 @@
 // ("Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices");
 // s = max(max|y| / 7, 1e-8) rounded to the scale dtype; q = RNE(clamp(y / s, -8, 7))
 // ("SpinQuant Guide: Learned Rotations for 4-Bit LLMs", step-size equation and
-// quantizer listing). The 1/sqrt(n) is folded into the per-row multiplier: the kernel
+// quantizer listing), or with OPT_INT8 the same equation at b = 8: s = max|y| / 127,
+// q in [-128, 127], one code per byte. The 1/sqrt(n) is folded into the per-row multiplier: the kernel
 // keeps u = H_n x and uses q = RNE(u * (1 / (s * sqrt(n)))).
 //
 // The body is written against a small context object (lane/wave ids, LDS, barriers,
@@ -33,7 +34,8 @@ enum : uint32_t {
   MODE_ROT32 = 2u,  // write the rotated row as float
   MODE_ROT16 = 4u   // write the rotated row in the input's 16-bit format
 };
-enum : uint32_t { OPT_PACKED = 1u, OPT_SCALE_F16 = 2u };
+// OPT_INT8: 8-bit codes (scale max/127, grid [-128, 127], one per byte) instead of INT4
+enum : uint32_t { OPT_PACKED = 1u, OPT_SCALE_F16 = 2u, OPT_INT8 = 4u };
 
 struct TensorArgs {
   const void* x;
@@ -369,7 +371,10 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   constexpr uint32_t WEM = wave_elem_mask(RBQ_PLAN, PH);
   constexpr int N = 1 << K;
   constexpr float SQRTN = ROT ? sqrt_pow2(K) : 1.0f;
-  constexpr float SEVEN_SQRTN = 7.0f * SQRTN;
+  // INT4: qmax 7, grid [-8, 7]; INT8: qmax 127, grid [-128, 127] (a uniform choice)
+  const bool int8 = (a.opts & OPT_INT8) != 0;
+  const float qmax = int8 ? 127.0f : 7.0f;
+  const float QMAX_SQRTN = qmax * SQRTN;
   constexpr float INV_SQRTN = ROT ? 1.0f / sqrt_pow2(K) : 1.0f;
   // exact rounding decisions where the quotient is exact often enough to tie
   constexpr bool EXACT = !ROT || (K <= 6 && (K % 2) == 0);
@@ -409,7 +414,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   bool any_clamp = false;
   static_for<0, NC>([&](auto C) {
     const float mu = m[C.value];
-    float s = mu / SEVEN_SQRTN;
+    float s = mu / QMAX_SQRTN;
     s = fmaxf(s, 1e-8f);
     float s_st;
     uint32_t h16 = 0;
@@ -418,8 +423,8 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     const float mk = (s_st == 0.0f) ? 0.0f : 1.0f / (s_st * SQRTN);
     mul[C.value] = mk;
     divv[C.value] = s_st * SQRTN;
-    // subnormal fp16 scales can sit far below max/7: then codes need the clamp
-    any_clamp = any_clamp || ((mu * mk) > 7.25f);
+    // subnormal fp16 scales can sit far below max/qmax: then codes need the clamp
+    any_clamp = any_clamp || ((mu * mk) > qmax + 0.25f);
     if (FAST || (mode & MODE_QUANT)) {
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
       const uint32_t rw = ONE_ROW ? 0u : ((lp | rp) >> K);
@@ -459,7 +464,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
           float q;
           if constexpr (EXACT) q = round_quotient_exact(u, mk, divv[ci]) + kMagic;
           else q = fmaf(u, mk, kMagic);
-          if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic - 8.0f), kMagic + 7.0f);
+          if constexpr (CLAMP) q = fminf(fmaxf(q, kMagic - qmax - 1.0f), kMagic + qmax);
           // insert the low FB bits of the field at the top, shifting earlier ones down
           acc = alignbit(f32_bits(q), acc, FB);
         });

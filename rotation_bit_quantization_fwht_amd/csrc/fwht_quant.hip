@@ -51,7 +51,7 @@ using namespace rbq;
 static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
                             int64_t x_row_stride, const void* signs, void* codes, void* scales,
                             rbq_dtype scale_dtype, float* rotated, unsigned flags,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool int8 = false) {
   const HqCheck chk = check_hadamard_quant(x, x_dtype, n, tokens, x_row_stride, codes, scales,
                                            scale_dtype, rotated, flags);
   if (chk.status != RBQ_OK || tokens == 0) return chk.status;
@@ -74,7 +74,8 @@ static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t
   a.rows = tokens;
   a.blocks0 = (uint32_t)blocks;
   a.nblocks = (uint32_t)blocks;
-  a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
+  a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u) |
+           (int8 ? OPT_INT8 : 0u);
   const bool fast = (flags & RBQ_PACKED) && rotated == nullptr;
   if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, stream) != hipSuccess)
     return RBQ_EHIP;
@@ -98,6 +99,15 @@ extern "C" rbq_status hadamard_quant_int4_signed(const void* x, rbq_dtype x_dtyp
   if (st != RBQ_OK) return st;
   return hq_launch(x, x_dtype, n, tokens, x_row_stride, signs, codes, scales, scale_dtype,
                    rotated, flags, stream);
+}
+
+extern "C" rbq_status hadamard_quant_int8(const void* x, rbq_dtype x_dtype, int64_t n,
+                                          int64_t tokens, int64_t x_row_stride, int8_t* codes,
+                                          void* scales, rbq_dtype scale_dtype, float* rotated,
+                                          unsigned flags, hipStream_t stream) {
+  if (flags & RBQ_PACKED) return RBQ_EINVAL;  // one code per byte
+  return hq_launch(x, x_dtype, n, tokens, x_row_stride, nullptr, codes, scales, scale_dtype,
+                   rotated, flags, stream, true);
 }
 
 extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dtype, int64_t batch,

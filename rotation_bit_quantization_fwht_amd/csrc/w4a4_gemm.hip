@@ -283,6 +283,204 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------------------------ W4A8
+// INT8 activation codes (one byte per code, scale max/127 per token) times packed INT4
+// weight codes. Same tiling as above; per K step (128 codes) an A row brings 128 bytes
+// (8 chunks) and a W row 64 bytes. Each 32-code sub-step takes one 16-byte A chunk per
+// lane; its bytes are permuted into the order the W widening produces (even codes of the
+// first 8, odd codes of the first 8, even of the next 8, odd of the next 8), so both MFMA
+// operands list the same k in the same positions. W carries the factor 16, so the sums
+// are 16 times the integer dot product (|sum| <= 16 * 128 * 8 * K < 2^31 for K <= 65536)
+// and are shifted back by 4.
+constexpr int kA8Chunks = 8;                                  // A chunks per row per step
+constexpr int kA8SlotsA = kBM * kA8Chunks;                    // 2048
+constexpr int kA8Slots = kA8SlotsA + kBN * kChunks;           // 3072 per stage (48 KB)
+constexpr int kA8Loads = kA8Slots / kThreads;                 // 6 copies per thread
+constexpr int kA8Stages = 3;
+constexpr int kA8Lds = (kA8Stages * kA8Slots * 16 > 8 * 64 * kEpiStride) ? kA8Stages * kA8Slots * 16 : 8 * 64 * kEpiStride;
+static_assert(kA8Slots % kThreads == 0, "whole copies per thread");
+static_assert(kA8Loads == 6, "the wait counts below assume six copies per thread and step");
+
+// chunk j of A row r: slot r * 8 + (j ^ key8(r)), key8(r) = ((r >> 1) ^ (r << 2)) & 7, so
+// 8 and 16 consecutive rows reading one chunk fall in distinct 16-byte bank groups
+__device__ __forceinline__ int swz_key8(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+__device__ __forceinline__ int swz8(int r, int j) { return r * kA8Chunks + (j ^ swz_key8(r)); }
+
+// bytes c0..c15 of one A chunk -> [c0 c2 c4 c6 | c1 c3 c5 c7 | c8 c10 c12 c14 | c9 c11 c13 c15]
+__device__ __forceinline__ v4i_t order_like_widen(const u32x4_g& q) {
+  v4i_t r;
+  r[0] = (int)__builtin_amdgcn_perm(q[1], q[0], 0x06040200u);
+  r[1] = (int)__builtin_amdgcn_perm(q[1], q[0], 0x07050301u);
+  r[2] = (int)__builtin_amdgcn_perm(q[3], q[2], 0x06040200u);
+  r[3] = (int)__builtin_amdgcn_perm(q[3], q[2], 0x07050301u);
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
+  __shared__ u32x4_g lds[kA8Lds / 16];
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int b = blockIdx.x;
+  const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
+  const int tn = t / g.tiles_m, tm = t % g.tiles_m;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave & 1) * 128, wn0 = (wave >> 1) * 64;
+  const int abytes = g.K, wbytes = g.K / 2;       // row bytes of A (int8) and W (packed)
+  const int steps = g.K / 128;
+
+  const uint8_t* src[kA8Loads];
+  int src_step[kA8Loads];                           // bytes per step of that source row
+#pragma unroll
+  for (int q = 0; q < kA8Loads; ++q) {
+    const int slot = q * kThreads + tid;
+    if (slot < kA8SlotsA) {
+      const int r = slot >> 3;
+      const int j = (slot & 7) ^ swz_key8(r);
+      src[q] = g.qa + (int64_t)min(m0 + r, g.M - 1) * abytes + j * 16;
+      src_step[q] = 128;
+    } else {
+      const int r = (slot - kA8SlotsA) >> 2;
+      const int j = (slot & 3) ^ swz_key(r);
+      src[q] = g.qw + (int64_t)min(n0 + r, g.N - 1) * wbytes + j * 16;
+      src_step[q] = 64;
+    }
+  }
+  auto issue_copies = [&](int step) {
+    u32x4_g* dst = lds + (step % kA8Stages) * kA8Slots + wave * 64;
+    const int st = min(step, steps - 1);
+#pragma unroll
+    for (int q = 0; q < kA8Loads; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + st * src_step[q]), (void*)(dst + q * kThreads), 16, 0, 0);
+  };
+
+  v16i_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16i_t{};
+
+  // lane (fr, fg) covers codes 64 fg .. 64 fg + 63 of each step: W chunks 2 fg, 2 fg + 1
+  // (two sub-steps each), A chunks 4 fg .. 4 fg + 3 (one per sub-step)
+  const int fr = lane & 31, fg = lane >> 5;
+  int fa_row[4], fw_slot[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa_row[i] = wm0 + i * 32 + fr;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fw_slot[j] = kA8SlotsA + swz(wn0 + j * 32 + fr, 2 * fg);
+  auto read_a = [&](int step, int u, u32x4_g (&fa)[4]) {
+    const u32x4_g* sb = lds + (step % kA8Stages) * kA8Slots;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = sb[swz8(fa_row[i], 4 * fg + u)];
+  };
+  auto read_w = [&](int step, int c, u32x4_g (&fw)[2]) {
+    const u32x4_g* sb = lds + (step % kA8Stages) * kA8Slots;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fw[j] = sb[fw_slot[j] ^ c];
+  };
+  auto prep = [&](const u32x4_g (&fa)[4], const u32x4_g (&fw)[2], int h, v4i_t (&ya)[4], v4i_t (&yw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ya[i] = order_like_widen(fa[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) yw[j] = widen(fw[j][2 * h], fw[j][2 * h + 1]);
+  };
+  auto mma_sub = [&](const v4i_t (&ya)[4], const v4i_t (&yw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], acc[i][j], 0, 0, 0);
+  };
+
+  // three-stage ring; at the top of iteration s steps s and s + 1 are published and the
+  // operands of sub-step 0 of step s are ready
+  issue_copies(0);
+  issue_copies(1);
+  wait_copies_and_sync<0>();
+  u32x4_g fa[4], fw0[2], fw1[2];
+  v4i_t xa[2][4], xw[2][2];
+  read_a(0, 0, fa);
+  read_w(0, 0, fw0);
+  prep(fa, fw0, 0, xa[0], xw[0]);
+  for (int s = 0; s < steps; ++s) {
+    issue_copies(s + 2);  // its stage last held step s - 1, finished before the last barrier
+    read_a(s, 1, fa);
+    read_w(s, 1, fw1);
+    mma_sub(xa[0], xw[0]);
+    prep(fa, fw0, 1, xa[1], xw[1]);
+    read_a(s, 2, fa);
+    mma_sub(xa[1], xw[1]);
+    prep(fa, fw1, 0, xa[0], xw[0]);
+    read_a(s, 3, fa);
+    mma_sub(xa[0], xw[0]);
+    prep(fa, fw1, 1, xa[1], xw[1]);
+    read_a(s + 1, 0, fa);   // (after the last step: a stale stage, never used)
+    read_w(s + 1, 0, fw0);
+    mma_sub(xa[1], xw[1]);
+    prep(fa, fw0, 0, xa[0], xw[0]);
+    wait_copies_and_sync<0>();  // publishes step s + 2
+  }
+
+  if (g.acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm0 + i * 32 + fr;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + j * 32 + 8 * q + 4 * fg;
+          if (n >= g.N) continue;
+          *(u32x4*)(g.acc + (int64_t)m * g.N + n) =
+              u32x4{(uint32_t)(acc[i][j][4 * q] >> 4), (uint32_t)(acc[i][j][4 * q + 1] >> 4),
+                    (uint32_t)(acc[i][j][4 * q + 2] >> 4), (uint32_t)(acc[i][j][4 * q + 3] >> 4)};
+        }
+    }
+  }
+  float swv[2][4][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        swv[j][q][e] = load_scale(g.sw, min(n0 + wn0 + j * 32 + 8 * q + 4 * fg + e, g.N - 1), g.scale_f16);
+  wait_copies_and_sync<0>();
+  char* stage = (char*)lds + wave * 64 * kEpiStride;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * hh + ii;
+      const float sam = load_scale(g.sa, min(m0 + wm0 + i * 32 + fr, g.M - 1), g.scale_f16);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t bits[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bits[e] = f32_to_bf16(((float)(acc[i][j][4 * q + e] >> 4) * sam) * swv[j][q][e]);
+          *(u32x2*)(stage + (ii * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
+              u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rloc = it * 8 + (lane >> 3);
+      const u32x4 v = *(const u32x4*)(stage + rloc * kEpiStride + (lane & 7) * 16);
+      const int m = m0 + wm0 + hh * 64 + rloc;
+      const int n = n0 + wn0 + (lane & 7) * 8;
+      if (m < g.M && n < g.N) *(u32x4*)(g.out + (int64_t)m * g.N + n) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 }  // namespace rbq
 
 using namespace rbq;
@@ -305,3 +503,23 @@ extern "C" rbq_status w4a4_gemm(const uint8_t* qA, const void* sA, const uint8_t
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
+
+extern "C" rbq_status w4a8_gemm(const int8_t* qA, const void* sA, const uint8_t* qW,
+                                const void* sW, rbq_dtype scale_dtype, int64_t M, int64_t N,
+                                int64_t K, void* out_bf16, int32_t* acc, hipStream_t stream) {
+  const rbq_status st = check_gemm(qA, sA, qW, sW, scale_dtype, M, N, K, out_bf16, acc);
+  if (st != RBQ_OK || M == 0 || N == 0) return st;
+  GemmArgs g{};
+  g.qa = (const uint8_t*)qA; g.qw = qW; g.sa = sA; g.sw = sW;
+  g.out = (uint16_t*)out_bf16;
+  g.acc = acc;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.scale_f16 = scale_dtype == RBQ_F16;
+  g.tiles_m = (int)((M + kBM - 1) / kBM);
+  g.tiles_n = (int)((N + kBN - 1) / kBN);
+  const int64_t ntiles = (int64_t)g.tiles_m * g.tiles_n;
+  if (ntiles > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  hipLaunchKernelGGL(w4a8_gemm_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, g);
+  return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+}
+

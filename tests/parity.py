@@ -54,10 +54,10 @@ def check_scales(s_gpu, ref, scale_dtype):
     return ok | alt, s_used
 
 
-def check_codes(q_gpu, y_ref, s_used):
+def check_codes(q_gpu, y_ref, s_used, bits=4):
     """q_gpu int codes [rows, n]; returns (n_flips, n_bad) where bad flips are > 1 step or
     not near a rounding boundary."""
-    q_exp = oracle.quantize_codes(y_ref, s_used)
+    q_exp = oracle.quantize_codes(y_ref, s_used, bits)
     q_gpu = np.asarray(q_gpu, dtype=np.int64)
     diff = q_gpu - q_exp.astype(np.int64)
     flips = diff != 0
@@ -72,8 +72,9 @@ def check_codes(q_gpu, y_ref, s_used):
     return n_flips, n_bad
 
 
-def check_quant(q_gpu, s_gpu, ref, scale_dtype, x64, rotate=True, y_gpu=None, n=None):
-    """Full check of one hadamard_quant_int4 result. Raises AssertionError with details."""
+def check_quant(q_gpu, s_gpu, ref, scale_dtype, x64, rotate=True, y_gpu=None, n=None, bits=4):
+    """Full check of one hadamard_quant_int4 (bits=4) or hadamard_quant_int8 (bits=8)
+    result. Raises AssertionError with details."""
     rows = q_gpu.shape[0]
     n = n or q_gpu.shape[1]
     stats = {"rows": rows, "n": n}
@@ -89,7 +90,7 @@ def check_quant(q_gpu, s_gpu, ref, scale_dtype, x64, rotate=True, y_gpu=None, n=
     ok, s_used = check_scales(s_gpu, ref, scale_dtype)
     stats["scale_mismatch_rows"] = int(np.sum(~ok))
     assert np.all(ok), f"{int(np.sum(~ok))} scales differ (first rows {np.nonzero(~ok)[0][:5].tolist()})"
-    n_flips, n_bad = check_codes(q_gpu, ref["y"], s_used)
+    n_flips, n_bad = check_codes(q_gpu, ref["y"], s_used, bits)
     stats["code_flips"] = n_flips
     stats["flip_rate"] = n_flips / max(1, q_gpu.size)
     assert n_bad == 0, f"{n_bad} code differences are not one-step near-tie flips"

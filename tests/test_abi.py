@@ -148,3 +148,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rbq, "_lib", None)
     with pytest.raises(rbq.LibraryMissing):
         rbq.lib()
+
+
+def test_int8_entry_points_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+    hq8 = lambda flags=0, tokens=8: L.hadamard_quant_int8(A16, rbq.RBQ_BF16, 4096, tokens, 4096, A16b, A16c,
+                                                          rbq.RBQ_F16, NULL, flags, NULL)
+    assert hq8(tokens=0) == rbq.RBQ_OK
+    assert hq8(flags=rbq.RBQ_PACKED) == E          # INT8 codes are never packed
+    assert hq8(flags=0x80) == E
+
+    def g8(K=4096, N=64, qa=A16):
+        return L.w4a8_gemm(qa, A16b, A16c, A16b, rbq.RBQ_F16, 64, N, K, A16, NULL, NULL)
+
+    assert g8(K=4000) == NS
+    assert g8(N=60) == NS
+    assert g8(K=131072) == NS
+    assert g8(qa=NULL) == E
+    assert L.w4a8_gemm(A16, A16b, A16c, A16b, rbq.RBQ_F16, 0, 64, 4096, A16, NULL, NULL) == rbq.RBQ_OK
+

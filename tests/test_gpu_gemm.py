@@ -95,3 +95,61 @@ def test_gemm_full_size_sampled(rbq):
     # sum over n of acc[m, n] = a[m] . (sum_n w[n]);  sum over m = (sum_m a[m]) . w[n]
     assert np.array_equal(acc.astype(np.int64).sum(axis=1), a_codes @ w_codes.sum(axis=0))
     assert np.array_equal(acc.astype(np.int64).sum(axis=0), w_codes @ a_codes.sum(axis=0))
+
+
+# ------------------------------------------------------------------------------ W4A8
+
+def gen_int8_codes(seed, rows, k):
+    """Uniform INT8 activation codes in [-127, 127] (what the quantizer can produce)."""
+    return np.random.default_rng([seed, 11, rows, k]).integers(-127, 128, size=(rows, k)).astype(np.int8)
+
+
+def run8(rbq, qa, sa, qw, sw):
+    out, acc = rbq.w4a8_gemm(dev(qa), dev(sa), dev(qw), dev(sw), return_acc=True)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (64, 256, 128), (300, 264, 1024), (256, 512, 4096),
+                                   (513, 1032, 2048)])
+def test_w4a8_random_codes(rbq, M, N, K):
+    print(f"case w4a8_gemm M={M} N={N} K={K}", flush=True)
+    qa = gen_int8_codes(1, M, K)
+    qw = workloads.gen_packed_codes(2, N, K)
+    sa = workloads.gen_scales(3, M, "float16")
+    sw = workloads.gen_scales(4, N, "float16")
+    acc, out = run8(rbq, qa, sa, qw, sw)
+    acc_ref, _ = oracle.w4a8_gemm(qa, sa, oracle.unpack_nibbles(qw), sw)
+    check_out(acc, out, acc_ref, sa, sw)
+
+
+def test_w4a8_extreme_codes(rbq):
+    """-128 x -8 everywhere at the largest supported K: the sums reach 1024 * 65536 = 2^26
+    (2^30 with the kernel's factor 16) and must stay exact."""
+    M, N, K = 32, 64, 65536
+    print("case w4a8_gemm extremes K=65536", flush=True)
+    qa = np.full((M, K), -128, dtype=np.int8)
+    qa[1::2, ::3] = 127
+    qw = np.full((N, K // 2), 0x88, dtype=np.uint8)  # every nibble -8
+    sa = np.ones(M, dtype=np.float32)
+    sw = np.ones(N, dtype=np.float32)
+    acc, out = run8(rbq, qa, sa, qw, sw)
+    acc_ref, _ = oracle.w4a8_gemm(qa, sa, oracle.unpack_nibbles(qw), sw)
+    check_out(acc, out, acc_ref, sa, sw)
+
+
+def test_w4a8_on_int8_quantized_workload(rbq):
+    """The W4A8 pipeline end to end on the GEMM workload's shapes (reduced M): A rotated and
+    quantized to INT8 by hadamard_quant_int8, W to INT4 by hadamard_quant_int4."""
+    M, N, K = 256, 1024, 4096
+    print("case w4a8 pipeline 256x1024x4096", flush=True)
+    ab, w, _ = workloads.gen_gemm_inputs(seed=3, m=M, n=N, k=K)
+    a_d = torch.from_numpy(np.ascontiguousarray(ab).view(np.int16)).view(torch.bfloat16).cuda()
+    qa, sa = rbq.hadamard_quant_int8(a_d)
+    qw, sw = rbq.hadamard_quant_int4(torch.from_numpy(w).cuda())
+    out, acc = rbq.w4a8_gemm(qa, sa, qw, sw, return_acc=True)
+    torch.cuda.synchronize()
+    qa_h, sa_h = qa.cpu().numpy(), sa.cpu().numpy()
+    qw_h, sw_h = oracle.unpack_nibbles(qw.cpu().numpy()), sw.cpu().numpy()
+    acc_ref, _ = oracle.w4a8_gemm(qa_h, sa_h, qw_h, sw_h)
+    check_out(acc.cpu().numpy(), out.float().cpu().numpy(), acc_ref, sa_h, sw_h)

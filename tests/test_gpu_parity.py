@@ -282,3 +282,24 @@ def test_randomized_rotation(rbq, k, dtype):
                 y_gpu=rot.cpu().numpy())
     with pytest.raises(rbq.RBQError):
         rbq.hadamard_quant_int4(xd, signs=sd, rotate=False)
+
+
+@pytest.mark.parametrize("k,dtype,rot", [(3, "float32", True), (7, "bfloat16", True), (10, "float16", True),
+                                         (12, "bfloat16", True), (14, "bfloat16", True), (15, "float32", True),
+                                         (12, "bfloat16", False)])
+def test_int8_codes(rbq, k, dtype, rot):
+    """hadamard_quant_int8: scale max/127, codes in [-128, 127] one per byte."""
+    n = 1 << k
+    rows = max(3, min(300, (1 << 16) // n))
+    print(f"case int8 k={k} {dtype} rot={rot} rows={rows}", flush=True)
+    x = workloads.gen_rows(90 + k, rows, n, dtype, kind="swiglu", n_outliers=3, factor=120)
+    xd = to_dev(x, dtype)
+    x64 = workloads.to_float64(x, dtype)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, rotate_input=rot, bits=8)
+    codes, scales, y = rbq.hadamard_quant_int8(xd, rotate=rot, return_rotated=True)
+    st = check_quant(codes.cpu().numpy(), scales.cpu().numpy(), ref, "float16", x64, rotate=rot,
+                     y_gpu=y.cpu().numpy(), bits=8)
+    if not rot:
+        assert st["code_flips"] == 0
+    codes2, scales2 = rbq.hadamard_quant_int8(xd, rotate=rot)
+    assert torch.equal(codes2, codes) and torch.equal(scales2, scales)

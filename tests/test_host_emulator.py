@@ -27,7 +27,7 @@ CSRC = os.path.join(ROOT, "rotation_bit_quantization_fwht_amd", "csrc")
 BUILD = os.path.join(HERE, "host", "_build")
 
 IN_CODE = {"float32": 0, "bfloat16": 1, "float16": 2}
-OPT_PACKED, OPT_F16 = 1, 2
+OPT_PACKED, OPT_F16, OPT_INT8 = 1, 2, 4
 MODE_QUANT, MODE_ROT32, MODE_ROT16 = 1, 2, 4
 
 
@@ -51,14 +51,14 @@ def emu():
 
 
 def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, mode=MODE_QUANT | MODE_ROT32,
-            row_stride=None, fourd=None, fast=False, grid=3, signs=None):
+            row_stride=None, fourd=None, fast=False, grid=3, signs=None, int8=False):
     n = 1 << k
     xb = np.ascontiguousarray(x)
     xpath = str(tmp_path / "x.bin")
     cpath = str(tmp_path / "codes.bin")
     spath = str(tmp_path / "scales.bin")
     xb.tofile(xpath)
-    opts = (OPT_PACKED if packed else 0) | (OPT_F16 if f16 else 0)
+    opts = (OPT_PACKED if packed else 0) | (OPT_F16 if f16 else 0) | (OPT_INT8 if int8 else 0)
     args = [exe, str(k), str(IN_CODE[dtype]), str(int(rot)), str(int(fourd is not None)), str(rows), str(opts),
             str(mode), xpath, str(xb.size), str(row_stride or n), cpath, spath]
     if fourd is not None:
@@ -221,4 +221,20 @@ def test_randomized_rotation(emu, tmp_path, k, dtype):
         ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, signs=s32)
         check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", x64,
                     y_gpu=None if fast else rot)
+
+
+@pytest.mark.parametrize("k,dtype,rot", [(2, "float32", True), (6, "bfloat16", True), (7, "bfloat16", True),
+                                         (9, "float16", True), (12, "float32", True), (14, "bfloat16", True),
+                                         (15, "bfloat16", True), (12, "bfloat16", False)])
+def test_int8_codes(emu, tmp_path, k, dtype, rot):
+    """8-bit codes (scale max/127, grid [-128, 127], one per byte) from the same kernels."""
+    n = 1 << k
+    rows = max(2, min(200, (1 << 15) // n))
+    x = workloads.gen_rows(70 + k, rows, n, dtype, kind="swiglu", n_outliers=2, factor=150)
+    codes, scales, yr = run_emu(emu, tmp_path, x, dtype, k, rows, rot=rot, packed=False, int8=True)
+    x64 = workloads.to_float64(x, dtype)
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, rotate_input=rot, bits=8)
+    st = check_quant(codes.view(np.int8), scales, ref, "float16", x64, rotate=rot, y_gpu=yr, bits=8)
+    if not rot:
+        assert st["code_flips"] == 0
 
