@@ -17,6 +17,7 @@ Everything is computed in float64 with NumPy, following the definitions on the p
   the outlier-curse figure, the step-size equation and the ``uniform_quantize_int4``
   listing), nibble packing, dequantization and MSE.
 * ``gemm``: exact integer product of the codes and the scale epilogue.
+* ``rope``: the rotary position embedding that the fused R3 operation applies first.
 
 Every function here is pinned by ``tests/test_oracle.py`` against facts the pages or
 the mathematics fix (worked examples, closed forms, invariants, brute force); a
@@ -42,6 +43,7 @@ from .quant import (
     kv_rotate_quant,
 )
 from .gemm import int_gemm, w4a4_gemm, w4a8_gemm
+from .rope import rope_exact, rope_16bit
 
 __all__ = [
     "sylvester",
@@ -67,4 +69,6 @@ __all__ = [
     "int_gemm",
     "w4a4_gemm",
     "w4a8_gemm",
+    "rope_exact",
+    "rope_16bit",
 ]

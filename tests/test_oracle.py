@@ -518,3 +518,62 @@ def test_w4a8_gemm_brute_force_extremes():
             assert acc[m, n] == sum(int(qa[m, k]) * int(qw[n, k]) for k in range(96))
     assert acc[0, 1] == 96 * 1024
     np.testing.assert_array_equal(out, acc * 0.125)
+
+
+# ------------------------------------------------------------------ RoPE before R3
+# "SpinQuant, when rotations are worth learning", section "Four rotation sites" (R3 after
+# RoPE); RoPE rotates coordinate pairs by position-dependent angles (half-split pairing).
+
+
+def _angles(positions, d, base=10000.0):
+    inv = base ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d)
+    return np.outer(np.asarray(positions, dtype=np.float64), inv)
+
+
+def test_rope_identity_at_position_zero_and_quarter_turn():
+    d = 128
+    x = workloads.bf16_bits_to_f32(workloads.gen_rows(1, 4, d, "bfloat16")).astype(np.float64)
+    one, zero = np.ones((4, d // 2), np.float32), np.zeros((4, d // 2), np.float32)
+    np.testing.assert_array_equal(oracle.rope_16bit(x, one, zero, "bfloat16"), x)
+    np.testing.assert_array_equal(oracle.rope_exact(x, one, zero), x)
+    q = oracle.rope_16bit(x, zero, one, "bfloat16")  # a quarter turn of every pair
+    np.testing.assert_array_equal(q[:, : d // 2], -x[:, d // 2:])
+    np.testing.assert_array_equal(q[:, d // 2:], x[:, : d // 2])
+
+
+def test_rope_is_complex_multiplication_and_preserves_pair_norms():
+    d = 64
+    x = np.random.default_rng(3).standard_normal((5, d))
+    th = _angles(np.arange(5) * 7 + 3, d)
+    y = oracle.rope_exact(x, np.cos(th), np.sin(th))
+    z = (x[:, : d // 2] + 1j * x[:, d // 2:]) * np.exp(1j * th)
+    np.testing.assert_allclose(y[:, : d // 2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[:, d // 2:], z.imag, rtol=0, atol=1e-13)
+    pair = lambda v: np.hypot(v[:, : d // 2], v[:, d // 2:])
+    np.testing.assert_allclose(pair(y), pair(x), rtol=1e-13)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    d = 128
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in [(5, 2), (100, 37), (9, 9)]:
+        tm, tn, tr = _angles([m], d), _angles([n], d), _angles([m - n], d)
+        a = oracle.rope_exact(q[None], np.cos(tm), np.sin(tm))[0] @ oracle.rope_exact(k[None], np.cos(tn), np.sin(tn))[0]
+        b = oracle.rope_exact(q[None], np.cos(tr), np.sin(tr))[0] @ k
+        assert abs(a - b) < 1e-10 * (1 + abs(b))
+
+
+def test_rope_16bit_is_the_exact_map_rounded_to_the_format():
+    """The float32 evaluation only moves a result across a bfloat16 rounding boundary when
+    the exact value sits within float32 error of it: rare, and then by one bf16 step."""
+    d = 128
+    x = workloads.bf16_bits_to_f32(workloads.gen_rows(5, 512, d, "bfloat16")).astype(np.float64)
+    th = _angles(np.arange(512), d)
+    c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    got = oracle.rope_16bit(x, c, s, "bfloat16")
+    ref = oracle.round_to_bf16(oracle.rope_exact(x, c.astype(np.float64), s.astype(np.float64)))
+    diff = got != ref
+    assert np.mean(diff) < 1e-3
+    ulp = np.abs(ref[diff]) * 2.0 ** -7
+    assert np.all(np.abs(got[diff] - ref[diff]) <= ulp * 1.0001)
