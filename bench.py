@@ -408,6 +408,39 @@ def main():
             "workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], bf16 out",
             "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
+    if run_kv and not args.no_extras:
+        # RoPE fused ahead of R3 on the same Q/K (read as pre-RoPE values), and the unfused
+        # sequence it replaces: the same RoPE in torch (fp32 arithmetic, bf16 result) writing
+        # Q and K back to HBM, then kv_rotate_quant
+        B, H, S, D = KV_SHAPE
+        inv = 10000.0 ** (-torch.arange(D // 2, dtype=torch.float64, device=dev) * 2.0 / D)
+        th = torch.outer(torch.arange(S, dtype=torch.float64, device=dev), inv)
+        cs, sn = torch.cos(th).float(), torch.sin(th).float()
+        o = sets["kv_out"][0]
+
+        def rope_torch(x):
+            xf = x.float()
+            a, b = xf[..., : D // 2], xf[..., D // 2:]
+            return torch.cat([a * cs - b * sn, b * cs + a * sn], dim=-1).to(x.dtype)
+
+        def fused(i):
+            rbq.kv_rotate_quant(sets["kv_q"][i], sets["kv_k"][i], rope_cos=cs, rope_sin=sn, **o)
+
+        def unfused(i):
+            rbq.kv_rotate_quant(rope_torch(sets["kv_q"][i]), rope_torch(sets["kv_k"][i]), **o)
+
+        for name, fn in (("rope_r3_fused", fused), ("rope_r3_unfused_torch", unfused)):
+            fn(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(8):
+                fn(r % NSETS)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 8
+            extras[name] = {"workload": "pre-RoPE bf16 Q and K [16, 32, 2048, 128] -> RoPE -> R3 -> packed INT4",
+                            "avg_us": round(t * 1e6, 3), "GB_s": round(KV_BYTES / t / 1e9, 2)}
     if run_r4 and not args.no_extras:
         # the randomized transform H diag(s) / sqrt(n) on the same workload and buffers
         sg = torch.from_numpy(workloads.gen_signs(0, R4_N)).to(dev).to(torch.bfloat16)

@@ -142,6 +142,38 @@ rbq_status kv_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_
                            hipStream_t stream);
 
 /*
+ * kv_rope_rotate_quant -- kv_rotate_quant with the rotary position embedding applied first,
+ * so pre-RoPE Q and K go straight to KV4 codes ("SpinQuant, when rotations are worth
+ * learning", section "Four rotation sites": R3 acts on queries and keys after RoPE;
+ * "SpinQuant Guide: Learned Rotations for 4-Bit LLMs": RoPE turns coordinate pairs by
+ * position-dependent angles). Element i pairs with i + D/2 (i < D/2); at position
+ * p = rope_pos0 + s (s = the token index of the vector):
+ *     x'[i] = x[i] cos[p][i] - x[i + D/2] sin[p][i],
+ *     x'[i + D/2] = x[i + D/2] cos[p][i] + x[i] sin[p][i],
+ * evaluated in fp32 (each product and the sum rounded, no fused multiply-add) and rounded
+ * to the input's 16-bit format (nearest even) -- the values an unfused RoPE would store --
+ * then rotated by H_D / sqrt(D) and quantized as by kv_rotate_quant.
+ *
+ *  rope_cos, rope_sin  device fp32 [rope_positions, head_dim / 2] row-major, 16-byte
+ *               aligned, owned by the caller, read only.
+ *  rope_positions  rows of the tables; rope_pos0 + seq must not exceed it.
+ *  rope_pos0    position of token 0 (>= 0), e.g. the cache length when appending.
+ *  head_dim     128 (other sizes return RBQ_ENOTSUP).
+ *  all other arguments as for kv_rotate_quant (RBQ_Q_ROTATE_ONLY writes RoPE'd and
+ *  rotated Q in bf16/fp16).
+ * Errors: as kv_rotate_quant, plus RBQ_EINVAL for NULL or misaligned tables, a negative
+ * rope_pos0 or tables that do not cover the positions; RBQ_ENOTSUP for head_dim != 128.
+ */
+rbq_status kv_rope_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_t batch,
+                                int64_t heads, int64_t seq, int64_t head_dim,
+                                const int64_t q_strides[4], const int64_t k_strides[4],
+                                const float *rope_cos, const float *rope_sin,
+                                int64_t rope_positions, int64_t rope_pos0, uint8_t *q_codes,
+                                void *q_scales, uint8_t *k_codes, void *k_scales,
+                                rbq_dtype scale_dtype, void *q_rotated, unsigned flags,
+                                hipStream_t stream);
+
+/*
  * w4a4_gemm -- out[m, n] = bf16( sA[m] * sW[n] * sum_k qA[m, k] * qW[n, k] ).
  * Codes are the packed INT4 produced above (two per byte, low nibble = even k).
  * The integer sum is exact (int32 accumulation on int8 matrix cores).

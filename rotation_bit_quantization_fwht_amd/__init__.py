@@ -51,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "hadamard_quant_int4_signed",
     "hadamard_quant_int8",
     "kv_rotate_quant",
+    "kv_rope_rotate_quant",
     "w4a4_gemm",
     "w4a8_gemm",
     "rbq_status_string",
@@ -99,6 +100,9 @@ def lib():
     L.hadamard_quant_int8.restype = ci
     L.kv_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, vp, vp, ci, vp, cu, vp]
     L.kv_rotate_quant.restype = ci
+    L.kv_rope_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, i64, i64,
+                                       vp, vp, vp, vp, ci, vp, cu, vp]
+    L.kv_rope_rotate_quant.restype = ci
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
     L.w4a4_gemm.restype = ci
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
@@ -240,12 +244,16 @@ def hadamard_quant_int8(x, *, scale_dtype=None, rotate=True, codes=None, scales=
 
 
 def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None, q_scales=None,
-                    k_codes=None, k_scales=None, q_rotated=None, stream=None):
+                    k_codes=None, k_scales=None, q_rotated=None, rope_cos=None, rope_sin=None,
+                    rope_pos0=0, stream=None):
     """R3 on post-RoPE ``q`` and ``k`` [B, H, S, D] (bf16/fp16, D contiguous): rotate every
     head vector by H_D / sqrt(D) and quantize it to packed INT4 with one scale per vector.
 
     Returns a dict with ``k_codes`` [B,H,S,D/2], ``k_scales`` [B,H,S] and either
     ``q_codes``/``q_scales`` or, with ``q_rotate_only``, ``q_rotated`` [B,H,S,D].
+    With ``rope_cos``/``rope_sin`` (float32 [positions, D/2]) q and k are pre-RoPE and the
+    half-split rotary embedding at positions rope_pos0 + s is applied first
+    (entry point kv_rope_rotate_quant).
     """
     torch = _torch()
     _require_cuda(q, k)
@@ -279,10 +287,25 @@ def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None
     qs = (ctypes.c_int64 * 4)(*q.stride())
     ks = (ctypes.c_int64 * 4)(*k.stride())
     sdt = _dtype_code(k_scales.dtype)
+    flags = RBQ_Q_ROTATE_ONLY if q_rotate_only else 0
+    if rope_cos is not None or rope_sin is not None:
+        if rope_cos is None or rope_sin is None:
+            raise ValueError("rope_cos and rope_sin go together")
+        _require_cuda(rope_cos, rope_sin)
+        P = rope_cos.shape[0] if rope_cos.dim() == 2 else -1
+        _require_buffer("rope_cos", rope_cos, (P, D // 2), (torch.float32,), dev)
+        _require_buffer("rope_sin", rope_sin, (P, D // 2), (torch.float32,), dev)
+        st = lib().kv_rope_rotate_quant(
+            _ptr(q), _ptr(k), _dtype_code(q.dtype), B, H, S, D, qs, ks, _ptr(rope_cos), _ptr(rope_sin),
+            P, int(rope_pos0), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), sdt,
+            _ptr(q_rotated), flags, _stream(stream, dev),
+        )
+        _check("kv_rope_rotate_quant", st)
+        return out
     st = lib().kv_rotate_quant(
         _ptr(q), _ptr(k), _dtype_code(q.dtype), B, H, S, D, qs, ks,
         _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), sdt, _ptr(q_rotated),
-        RBQ_Q_ROTATE_ONLY if q_rotate_only else 0, _stream(stream, dev),
+        flags, _stream(stream, dev),
     )
     _check("kv_rotate_quant", st)
     return out

@@ -49,6 +49,9 @@ struct TensorArgs {
   uint16_t* rot16;         // [rows, n] bf16/fp16 bits
   const void* signs;       // optional [n] +-1 in the input dtype: rows are multiplied by
                            // this diagonal before the transform (randomized Hadamard)
+  const float* rope_cos;   // optional fp32 [positions, n/2]: RoPE before the transform,
+  const float* rope_sin;   // pairing element i with i + n/2 at position rope_pos0 + s
+  uint32_t rope_pos0;
   uint32_t mode;
 };
 
@@ -244,7 +247,56 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
 template <int K, bool MF>
 constexpr int kMatrixLoads = (1 << PlanOf<K, MF>::value.e) / 8;
 
-template <int K, bool MF, bool FOURD, class Ctx>
+// lane bit of phase 0 that holds element bit K - 1 (the RoPE partner i +- n/2 sits in the
+// lane that differs in this bit); -1 if it is not a lane bit
+template <int K, bool MF>
+constexpr int rope_partner_lane_bit() {
+  for (int i = 0; i < 6; ++i)
+    if (RBQ_PLAN.lane[0][i] == K - 1) return i;
+  return -1;
+}
+
+// RoPE on the 8 16-bit values of one lane (elements el .. el + 7 of tensor row `row`):
+// x' = x cos - p sin below n/2 and x cos + p sin above, p the partner i +- n/2, computed in
+// fp32 (products and sum rounded separately) and rounded back to the 16-bit format.
+template <int K, bool MF, int IN, class Ctx>
+RBQ_HD void apply_rope(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t el, u32x4& q4) {
+  constexpr int PB = rope_partner_lane_bit<K, MF>();
+  static_assert(PB >= 0, "RoPE needs the half-split partner in another lane");
+  constexpr uint32_t H = 1u << (K - 1);
+  uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
+  uint32_t p[4];
+  static_for<0, 4>([&](auto D) {
+    p[D.value] = f32_bits(c.shfl_xor(bits_f32(w[D.value]), 1 << PB));
+  });
+  const uint32_t srow = row - fastdiv(row, t.div_s) * t.seq;
+  const float* cp = t.rope_cos + (int64_t)(t.rope_pos0 + srow) * H + (el & (H - 1));
+  const float* sp = t.rope_sin + (int64_t)(t.rope_pos0 + srow) * H + (el & (H - 1));
+  const f32x4 c0 = c.template load<f32x4>(cp), c1 = c.template load<f32x4>(cp + 4);
+  const f32x4 s0 = c.template load<f32x4>(sp), s1 = c.template load<f32x4>(sp + 4);
+  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const bool upper = (el & H) != 0;
+  static_for<0, 4>([&](auto D) {
+    uint32_t out = 0u;
+    static_for<0, 2>([&](auto HALF) {
+      constexpr int j = 2 * D.value + HALF.value;
+      const uint32_t xb = (w[D.value] >> (16 * HALF.value)) & 0xFFFFu;
+      const uint32_t pb = (p[D.value] >> (16 * HALF.value)) & 0xFFFFu;
+      const float x = (IN == IN_F16) ? f16_to_f32(xb) : bits_f32(xb << 16);
+      const float pv = (IN == IN_F16) ? f16_to_f32(pb) : bits_f32(pb << 16);
+      const float t1 = x * cs[j];
+      const float t2 = pv * sn[j];
+      const float r = upper ? t1 + t2 : t1 - t2;
+      const uint32_t rb = (IN == IN_F16) ? f32_to_f16(r) : f32_to_bf16(r);
+      out |= rb << (16 * HALF.value);
+    });
+    w[D.value] = out;
+  });
+  q4 = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int K, bool MF, bool FOURD, int IN, bool ROPE, class Ctx>
 RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                          uint32_t (&raw)[kMatrixLoads<K, MF>][4]) {
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
@@ -261,6 +313,7 @@ RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0
       q4.x ^= s4.x & 0x80008000u; q4.y ^= s4.y & 0x80008000u;
       q4.z ^= s4.z & 0x80008000u; q4.w ^= s4.w & 0x80008000u;
     }
+    if constexpr (ROPE) apply_rope<K, MF, IN>(c, t, (uint32_t)(row0 + rw), el, q4);
     raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
   });
 }
@@ -587,7 +640,7 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
 // RBQ_PREFETCH and matrix plans the next block's loads are issued as soon as the MFMAs
 // have consumed the current block's, so they are in flight while the current block is
 // transformed.
-template <int K, int IN, bool ROT, bool FOURD, bool FAST, class Ctx>
+template <int K, int IN, bool ROT, bool FOURD, bool FAST, bool ROPE, class Ctx>
 RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32_t step) {
   constexpr bool MF = use_matrix_plan(K, IN, ROT);
   const uint32_t nb = a.nblocks;
@@ -596,7 +649,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       c.refresh_ids();
       const Block b = block_of<K, MF>(a, blk);
       uint32_t raw[kMatrixLoads<K, MF>][4];
-      matrix_issue<K, MF, FOURD>(c, *b.t, a.rows, b.row0, raw);
+      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, a.rows, b.row0, raw);
       Regs<K, MF> v;
       matrix_apply<K, MF, IN>(c, raw, v);
       stages<K, MF, 0, false>(v);
@@ -606,7 +659,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
     uint32_t raw[kMatrixLoads<K, MF>][4];
     if (first < nb) {
       const Block b = block_of<K, MF>(a, first);
-      matrix_issue<K, MF, FOURD>(c, *b.t, a.rows, b.row0, raw);
+      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, a.rows, b.row0, raw);
     }
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
@@ -616,7 +669,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       const uint32_t nxt = blk + step;
       if (nxt < nb) {
         const Block bn = block_of<K, MF>(a, nxt);
-        matrix_issue<K, MF, FOURD>(c, *bn.t, a.rows, bn.row0, raw);
+        matrix_issue<K, MF, FOURD, IN, ROPE>(c, *bn.t, a.rows, bn.row0, raw);
       }
       stages<K, MF, 0, false>(v);
       rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);

@@ -23,9 +23,10 @@ using KPlan = PlanOf<K, use_matrix_plan(K, IN, ROT)>;
 // at least RBQ_WAVES_PER_EU waves per SIMD: enough resident workgroups to overlap one
 // block's loads with another's arithmetic. The variants that also write rotated values
 // keep more live registers; they get one wave less rather than spilling. Plans with 32
-// values per lane aim at 8 waves (64 registers).
-template <int K, int IN, bool ROT, bool FOURD, bool FAST>
-__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(KPlan<K, IN, ROT>::value.e == 5 ? 8 : (FAST ? RBQ_WAVES_PER_EU : RBQ_WAVES_PER_EU - 1))))
+// values per lane aim at 8 waves (64 registers), 6 when they also write rotated values.
+// The RoPE variants hold each load's cos/sin values as well and get 4 waves.
+template <int K, int IN, bool ROT, bool FOURD, bool FAST, bool ROPE>
+__global__ __launch_bounds__((64 << KPlan<K, IN, ROT>::value.w)) __attribute__((amdgpu_waves_per_eu(ROPE ? 4 : (KPlan<K, IN, ROT>::value.e == 5 ? (FAST ? 8 : 6) : (FAST ? RBQ_WAVES_PER_EU : RBQ_WAVES_PER_EU - 1)))))
 void fwht_quant_kernel(KArgs a) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   __shared__ float lds[lds_words(P) + (1 << P.w) + 1];
@@ -34,18 +35,18 @@ void fwht_quant_kernel(KArgs a) {
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
   c.lds = lds;
   if constexpr (P.mfma) c.template load_hadamard_a<IN>();
-  fwht_quant_persistent<K, IN, ROT, FOURD, FAST>(c, a, blockIdx.x, gridDim.x);
+  fwht_quant_persistent<K, IN, ROT, FOURD, FAST, ROPE>(c, a, blockIdx.x, gridDim.x);
 }
 
 // Workgroups loop over the row blocks (see fwht_quant_persistent); the grid holds as many
 // workgroups as fit on the device at once, or fewer when there are fewer blocks.
-template <int K, int IN, bool ROT, bool FOURD, bool FAST = false>
+template <int K, int IN, bool ROT, bool FOURD, bool FAST = false, bool ROPE = false>
 static hipError_t launch_one(const KArgs& a, hipStream_t stream) {
   constexpr const Plan& P = KPlan<K, IN, ROT>::value;
   constexpr int threads = 64 << P.w;
   static const int per_cu = [] {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fwht_quant_kernel<K, IN, ROT, FOURD, FAST>, threads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, fwht_quant_kernel<K, IN, ROT, FOURD, FAST, ROPE>, threads, 0) !=
             hipSuccess || o < 1)
       o = 1;
     return o;
@@ -57,13 +58,29 @@ static hipError_t launch_one(const KArgs& a, hipStream_t stream) {
   // one workgroup per block, or (RBQ_RESIDENT_GRID) only as many as are resident at once
   const uint64_t cap = RBQ_RESIDENT_GRID ? (uint64_t)per_cu * (uint64_t)cus : 0xFFFFFFFFull;
   const uint32_t grid = (uint32_t)(a.nblocks < cap ? a.nblocks : cap);
-  hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD, FAST>), dim3(grid), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL((fwht_quant_kernel<K, IN, ROT, FOURD, FAST, ROPE>), dim3(grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
 // fast: packed codes and scales are the only outputs (no rotated rows, no int8 codes)
+// rope: RoPE before the transform (16-bit Q/K of head_dim 128 only)
 template <int K>
-hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, hipStream_t s) {
+hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope, hipStream_t s) {
+  if (rope) {
+    if constexpr (K == 7) {
+      if (!rot || in == IN_F32) return hipErrorNotSupported;
+      if (fourd) {
+        if (in == IN_BF16)
+          return fast ? launch_one<K, IN_BF16, true, true, true, true>(a, s) : launch_one<K, IN_BF16, true, true, false, true>(a, s);
+        return fast ? launch_one<K, IN_F16, true, true, true, true>(a, s) : launch_one<K, IN_F16, true, true, false, true>(a, s);
+      }
+      if (in == IN_BF16)
+        return fast ? launch_one<K, IN_BF16, true, false, true, true>(a, s) : launch_one<K, IN_BF16, true, false, false, true>(a, s);
+      return fast ? launch_one<K, IN_F16, true, false, true, true>(a, s) : launch_one<K, IN_F16, true, false, false, true>(a, s);
+    } else {
+      return hipErrorNotSupported;
+    }
+  }
   if (fourd) {
     // strided [B, H, S, D] addressing is instantiated for head_dim 64, 128 and 256
     if constexpr (K >= 6 && K <= 8) {
@@ -86,6 +103,6 @@ hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, 
   }
 }
 
-template hipError_t fwht_launch<RBQ_K>(const KArgs&, int, bool, bool, bool, hipStream_t);
+template hipError_t fwht_launch<RBQ_K>(const KArgs&, int, bool, bool, bool, bool, hipStream_t);
 
 }  // namespace rbq

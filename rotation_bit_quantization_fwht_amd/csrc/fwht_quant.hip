@@ -15,26 +15,26 @@
 namespace rbq {
 
 template <int K>
-hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, hipStream_t s);
+hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope, hipStream_t s);
 
-static hipError_t dispatch(int k, const KArgs& a, int in, bool rot, bool fourd, bool fast,
+static hipError_t dispatch(int k, const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope,
                            hipStream_t s) {
   switch (k) {
-    case 1: return fwht_launch<1>(a, in, rot, fourd, fast, s);
-    case 2: return fwht_launch<2>(a, in, rot, fourd, fast, s);
-    case 3: return fwht_launch<3>(a, in, rot, fourd, fast, s);
-    case 4: return fwht_launch<4>(a, in, rot, fourd, fast, s);
-    case 5: return fwht_launch<5>(a, in, rot, fourd, fast, s);
-    case 6: return fwht_launch<6>(a, in, rot, fourd, fast, s);
-    case 7: return fwht_launch<7>(a, in, rot, fourd, fast, s);
-    case 8: return fwht_launch<8>(a, in, rot, fourd, fast, s);
-    case 9: return fwht_launch<9>(a, in, rot, fourd, fast, s);
-    case 10: return fwht_launch<10>(a, in, rot, fourd, fast, s);
-    case 11: return fwht_launch<11>(a, in, rot, fourd, fast, s);
-    case 12: return fwht_launch<12>(a, in, rot, fourd, fast, s);
-    case 13: return fwht_launch<13>(a, in, rot, fourd, fast, s);
-    case 14: return fwht_launch<14>(a, in, rot, fourd, fast, s);
-    case 15: return fwht_launch<15>(a, in, rot, fourd, fast, s);
+    case 1: return fwht_launch<1>(a, in, rot, fourd, fast, rope, s);
+    case 2: return fwht_launch<2>(a, in, rot, fourd, fast, rope, s);
+    case 3: return fwht_launch<3>(a, in, rot, fourd, fast, rope, s);
+    case 4: return fwht_launch<4>(a, in, rot, fourd, fast, rope, s);
+    case 5: return fwht_launch<5>(a, in, rot, fourd, fast, rope, s);
+    case 6: return fwht_launch<6>(a, in, rot, fourd, fast, rope, s);
+    case 7: return fwht_launch<7>(a, in, rot, fourd, fast, rope, s);
+    case 8: return fwht_launch<8>(a, in, rot, fourd, fast, rope, s);
+    case 9: return fwht_launch<9>(a, in, rot, fourd, fast, rope, s);
+    case 10: return fwht_launch<10>(a, in, rot, fourd, fast, rope, s);
+    case 11: return fwht_launch<11>(a, in, rot, fourd, fast, rope, s);
+    case 12: return fwht_launch<12>(a, in, rot, fourd, fast, rope, s);
+    case 13: return fwht_launch<13>(a, in, rot, fourd, fast, rope, s);
+    case 14: return fwht_launch<14>(a, in, rot, fourd, fast, rope, s);
+    case 15: return fwht_launch<15>(a, in, rot, fourd, fast, rope, s);
   }
   return hipErrorInvalidValue;
 }
@@ -77,7 +77,7 @@ static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t
   a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u) |
            (int8 ? OPT_INT8 : 0u);
   const bool fast = (flags & RBQ_PACKED) && rotated == nullptr;
-  if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, stream) != hipSuccess)
+  if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, false, stream) != hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
 }
@@ -110,12 +110,13 @@ extern "C" rbq_status hadamard_quant_int8(const void* x, rbq_dtype x_dtype, int6
                    rotated, flags, stream, true);
 }
 
-extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dtype, int64_t batch,
-                                      int64_t heads, int64_t seq, int64_t head_dim,
-                                      const int64_t q_strides[4], const int64_t k_strides[4],
-                                      uint8_t* q_codes, void* q_scales, uint8_t* k_codes,
-                                      void* k_scales, rbq_dtype scale_dtype, void* q_rotated,
-                                      unsigned flags, hipStream_t stream) {
+static rbq_status kv_launch(const void* q, const void* k, rbq_dtype dtype, int64_t batch,
+                            int64_t heads, int64_t seq, int64_t head_dim,
+                            const int64_t q_strides[4], const int64_t k_strides[4],
+                            const float* rope_cos, const float* rope_sin, int64_t rope_pos0,
+                            uint8_t* q_codes, void* q_scales, uint8_t* k_codes, void* k_scales,
+                            rbq_dtype scale_dtype, void* q_rotated, unsigned flags,
+                            hipStream_t stream) {
   const KvCheck chk = check_kv(q, k, dtype, batch, heads, seq, head_dim, q_strides, k_strides,
                                q_codes, q_scales, k_codes, k_scales, scale_dtype, q_rotated, flags);
   if (chk.status != RBQ_OK) return chk.status;
@@ -142,6 +143,9 @@ extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dt
     t.heads = (uint32_t)heads;
     t.div_s = make_fastdiv((uint32_t)seq);
     t.div_h = make_fastdiv((uint32_t)heads);
+    t.rope_cos = rope_cos;
+    t.rope_sin = rope_sin;
+    t.rope_pos0 = (uint32_t)rope_pos0;
   }
   a.t[0].codes = q_codes;
   a.t[0].scales = q_scales;
@@ -154,8 +158,37 @@ extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dt
   a.blocks0 = (uint32_t)blocks;
   a.nblocks = (uint32_t)(2 * blocks);
   a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
-  if (dispatch(chk.k, a, in_kind(dtype), true, !chk.flat, !rot_only, stream) !=
+  if (dispatch(chk.k, a, in_kind(dtype), true, !chk.flat, !rot_only, rope_cos != nullptr, stream) !=
       hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
 }
+
+extern "C" rbq_status kv_rotate_quant(const void* q, const void* k, rbq_dtype dtype, int64_t batch,
+                                      int64_t heads, int64_t seq, int64_t head_dim,
+                                      const int64_t q_strides[4], const int64_t k_strides[4],
+                                      uint8_t* q_codes, void* q_scales, uint8_t* k_codes,
+                                      void* k_scales, rbq_dtype scale_dtype, void* q_rotated,
+                                      unsigned flags, hipStream_t stream) {
+  return kv_launch(q, k, dtype, batch, heads, seq, head_dim, q_strides, k_strides, nullptr,
+                   nullptr, 0, q_codes, q_scales, k_codes, k_scales, scale_dtype, q_rotated,
+                   flags, stream);
+}
+
+extern "C" rbq_status kv_rope_rotate_quant(const void* q, const void* k, rbq_dtype dtype,
+                                           int64_t batch, int64_t heads, int64_t seq,
+                                           int64_t head_dim, const int64_t q_strides[4],
+                                           const int64_t k_strides[4], const float* rope_cos,
+                                           const float* rope_sin, int64_t rope_positions,
+                                           int64_t rope_pos0, uint8_t* q_codes, void* q_scales,
+                                           uint8_t* k_codes, void* k_scales,
+                                           rbq_dtype scale_dtype, void* q_rotated,
+                                           unsigned flags, hipStream_t stream) {
+  const rbq_status st = check_rope(dtype, batch, heads, seq, head_dim, rope_cos, rope_sin,
+                                   rope_positions, rope_pos0);
+  if (st != RBQ_OK) return st;
+  return kv_launch(q, k, dtype, batch, heads, seq, head_dim, q_strides, k_strides, rope_cos,
+                   rope_sin, rope_pos0, q_codes, q_scales, k_codes, k_scales, scale_dtype,
+                   q_rotated, flags, stream);
+}
+

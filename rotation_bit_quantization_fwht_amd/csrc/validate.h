@@ -125,6 +125,21 @@ inline KvCheck check_kv(const void* q, const void* k, int dtype, int64_t B, int6
   return r;
 }
 
+// RoPE tables: fp32 [rope_positions, head_dim / 2], 16-byte aligned, covering positions
+// rope_pos0 .. rope_pos0 + seq - 1; head_dim 128 (the layout whose load registers leave
+// room for each element's cos and sin)
+inline rbq_status check_rope(int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                             const float* cos, const float* sin, int64_t positions,
+                             int64_t pos0) {
+  if (B < 0 || H < 0 || S < 0 || pos0 < 0 || positions < 0) return RBQ_EINVAL;
+  if (B == 0 || H == 0 || S == 0) return RBQ_OK;
+  if (!cos || !sin || !aligned(cos, 16) || !aligned(sin, 16)) return RBQ_EINVAL;
+  if (pos0 + S > positions || positions > (int64_t{1} << 30)) return RBQ_EINVAL;
+  if (dtype != RBQ_BF16 && dtype != RBQ_F16) return RBQ_EINVAL;
+  if (D != 128) return RBQ_ENOTSUP;
+  return RBQ_OK;
+}
+
 inline rbq_status check_gemm(const void* qA, const void* sA, const void* qW, const void* sW,
                              int scale_dtype, int64_t M, int64_t N, int64_t K, const void* out,
                              const void* acc) {

@@ -127,8 +127,16 @@ static void run(const KArgs& a, uint32_t grid) {
     for (int t = 0; t < nthreads; ++t)
       th.emplace_back([&, t] {
         HostCtx c{(uint32_t)(t & 63), (uint32_t)(t >> 6), &sh};
-        if (getenv("RBQ_EMU_FAST")) fwht_quant_persistent<K, IN, ROT, FOURD, true>(c, a, wg, grid);
-        else fwht_quant_persistent<K, IN, ROT, FOURD, false>(c, a, wg, grid);
+        const bool fast = getenv("RBQ_EMU_FAST") != nullptr;
+        if constexpr (K == 7 && IN != IN_F32 && ROT) {
+          if (a.t[0].rope_cos) {
+            if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, true>(c, a, wg, grid);
+            else fwht_quant_persistent<K, IN, ROT, FOURD, false, true>(c, a, wg, grid);
+            return;
+          }
+        }
+        if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, false>(c, a, wg, grid);
+        else fwht_quant_persistent<K, IN, ROT, FOURD, false, false>(c, a, wg, grid);
       });
     for (auto& x : th) x.join();
   }
@@ -201,6 +209,20 @@ int main(int argc, char** argv) {
     signs = read_file(sp);
     g_bufs.push_back({signs.data(), signs.data() + signs.size(), "signs"});
     t.signs = signs.data();
+  }
+  // RBQ_EMU_ROPE="cos.bin sin.bin pos0": RoPE tables (fp32 [positions, n/2])
+  static std::vector<char> rope_c, rope_s;
+  if (const char* rp = getenv("RBQ_EMU_ROPE")) {
+    char cpath[512], spath[512];
+    unsigned pos0 = 0;
+    if (sscanf(rp, "%511s %511s %u", cpath, spath, &pos0) != 3) { fprintf(stderr, "bad RBQ_EMU_ROPE\n"); return 2; }
+    rope_c = read_file(cpath);
+    rope_s = read_file(spath);
+    g_bufs.push_back({rope_c.data(), rope_c.data() + rope_c.size(), "rope_cos"});
+    g_bufs.push_back({rope_s.data(), rope_s.data() + rope_s.size(), "rope_sin"});
+    t.rope_cos = (const float*)rope_c.data();
+    t.rope_sin = (const float*)rope_s.data();
+    t.rope_pos0 = pos0;
   }
   if (argc >= 19) {
     const long long B = atoll(argv[13]), H = atoll(argv[14]), S = atoll(argv[15]);

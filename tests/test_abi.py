@@ -167,3 +167,20 @@ def test_int8_entry_points_validation(L):
     assert g8(qa=NULL) == E
     assert L.w4a8_gemm(A16, A16b, A16c, A16b, rbq.RBQ_F16, 0, 64, 4096, A16, NULL, NULL) == rbq.RBQ_OK
 
+
+
+def test_rope_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+
+    def kr(D=128, cos=A16c, sin=A16c, P=64, pos0=0, S=16, dt=rbq.RBQ_BF16):
+        st = (ctypes.c_int64 * 4)(4 * S * D, S * D, D, 1)
+        return L.kv_rope_rotate_quant(A16, A16b, dt, 2, 4, S, D, st, st, cos, sin, P, pos0,
+                                      A16c, A16c, A16c, A16c, rbq.RBQ_F16, NULL, 0, NULL)
+
+    assert kr(S=0) == rbq.RBQ_OK
+    assert kr(cos=NULL) == E
+    assert kr(sin=ctypes.c_void_p(0x30004)) == E   # tables must be 16-byte aligned
+    assert kr(P=16, pos0=1) == E                     # positions 1..16 exceed 16 table rows
+    assert kr(pos0=-1) == E
+    assert kr(dt=rbq.RBQ_F32) == E
+    assert kr(D=256) == NS

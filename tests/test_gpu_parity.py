@@ -303,3 +303,66 @@ def test_int8_codes(rbq, k, dtype, rot):
         assert st["code_flips"] == 0
     codes2, scales2 = rbq.hadamard_quant_int8(xd, rotate=rot)
     assert torch.equal(codes2, codes) and torch.equal(scales2, scales)
+
+
+def rope_tables(positions, d, base=10000.0):
+    inv = base ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d)
+    th = np.outer(np.arange(positions, dtype=np.float64), inv)
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,layout,pos0", [("bfloat16", "contiguous", 0), ("bfloat16", "bshd_view", 7),
+                                               ("float16", "contiguous", 100), ("float16", "bshd_view", 0)])
+def test_kv_rope_small(rbq, dtype, layout, pos0):
+    """kv_rope_rotate_quant: RoPE (half-split, fp32 arithmetic rounded to the 16-bit
+    format) then R3 and INT4, on Q and K, against the oracle's RoPE + rotation + quantizer."""
+    B, H, S, D = 2, 3, 45, 128
+    print(f"case kv rope {dtype} {layout} pos0={pos0}", flush=True)
+    q_bits, k_bits, _ = workloads.gen_kv(seed=17, batch=B, heads=H, seq=S, head_dim=D)
+    if dtype == "float16":
+        q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
+        k_bits = workloads.bf16_bits_to_f32(k_bits).astype(np.float16).view(np.uint16)
+    if layout == "contiguous":
+        qd, kd = to_dev(q_bits, dtype), to_dev(k_bits, dtype)
+    else:
+        qd = to_dev(np.ascontiguousarray(q_bits.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+        kd = to_dev(np.ascontiguousarray(k_bits.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+    cos, sin = rope_tables(pos0 + S, D)
+    out = rbq.kv_rotate_quant(qd, kd, rope_cos=torch.from_numpy(cos).cuda(), rope_sin=torch.from_numpy(sin).cuda(),
+                              rope_pos0=pos0)
+    pos = pos0 + np.arange(S)
+    rows = B * H * S
+    for name, bits in (("q", q_bits), ("k", k_bits)):
+        xr = oracle.rope_16bit(workloads.to_float64(bits, dtype), cos[pos][None, None], sin[pos][None, None], dtype)
+        xr = xr.reshape(rows, D)
+        ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
+        got_q = oracle.unpack_nibbles(out[f"{name}_codes"].cpu().numpy().reshape(rows, D // 2))
+        check_quant(got_q, out[f"{name}_scales"].cpu().numpy().reshape(rows), ref, "float16", xr)
+
+
+def test_kv_rope_full_size_and_errors(rbq):
+    """The fused RoPE + R3 at the full R3 workload (sampled rows against the oracle, all
+    rows against the invariants), and the argument checks."""
+    print("case kv rope full size", flush=True)
+    B, H, S, D = 16, 32, 2048, 128
+    q_bits, k_bits, _ = workloads.gen_kv(seed=2)
+    cos, sin = rope_tables(S + 64, D)
+    cd, sd = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    qd, kd = to_dev(q_bits, "bfloat16"), to_dev(k_bits, "bfloat16")
+    out = rbq.kv_rotate_quant(qd, kd, rope_cos=cd, rope_sin=sd, rope_pos0=64)
+    rng = np.random.default_rng(5)
+    flat = rng.integers(0, B * H * S, 40)
+    b, h, s = flat // (H * S), (flat // S) % H, flat % S
+    xr = oracle.rope_16bit(workloads.to_float64(k_bits[b, h, s], "bfloat16"), cos[64 + s], sin[64 + s], "bfloat16")
+    ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
+    kc = out["k_codes"].cpu().numpy().reshape(B * H * S, D // 2)[flat]
+    ks = out["k_scales"].cpu().numpy().reshape(B * H * S)[flat]
+    check_quant(oracle.unpack_nibbles(kc), ks, ref, "float16", xr)
+    qa = oracle.unpack_nibbles(out["q_codes"].cpu().numpy().reshape(B * H * S, D // 2))
+    assert np.all(np.max(np.abs(qa), axis=1) == 7) and not np.any(qa == -8)
+    with pytest.raises(rbq.RBQError):   # tables too short for rope_pos0 + seq
+        rbq.kv_rotate_quant(qd, kd, rope_cos=cd, rope_sin=sd, rope_pos0=65)
+    q256 = torch.zeros((1, 1, 4, 256), dtype=torch.bfloat16, device="cuda")
+    c256 = torch.zeros((8, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(rbq.RBQError):   # head_dim 256 is not fused
+        rbq.kv_rotate_quant(q256, q256.clone(), rope_cos=c256, rope_sin=c256)

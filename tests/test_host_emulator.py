@@ -51,7 +51,7 @@ def emu():
 
 
 def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, mode=MODE_QUANT | MODE_ROT32,
-            row_stride=None, fourd=None, fast=False, grid=3, signs=None, int8=False):
+            row_stride=None, fourd=None, fast=False, grid=3, signs=None, int8=False, rope=None, bhs=None):
     n = 1 << k
     xb = np.ascontiguousarray(x)
     xpath = str(tmp_path / "x.bin")
@@ -63,7 +63,16 @@ def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, m
             str(mode), xpath, str(xb.size), str(row_stride or n), cpath, spath]
     if fourd is not None:
         args += [str(v) for v in fourd]
+    elif bhs is not None:  # flat rows, but the (batch, head, token) shape is known (RoPE positions)
+        B, H, S = bhs
+        args += [str(B), str(H), str(S), str(H * S * n), str(S * n), str(n)]
     env = dict(os.environ, RBQ_EMU_GRID=str(grid))
+    if rope is not None:
+        cos, sin, pos0 = rope
+        cpath_r, spath_r = str(tmp_path / "rope_cos.bin"), str(tmp_path / "rope_sin.bin")
+        np.ascontiguousarray(cos, dtype=np.float32).tofile(cpath_r)
+        np.ascontiguousarray(sin, dtype=np.float32).tofile(spath_r)
+        env["RBQ_EMU_ROPE"] = f"{cpath_r} {spath_r} {int(pos0)}"
     if fast:
         env["RBQ_EMU_FAST"] = "1"
     if signs is not None:
@@ -237,4 +246,36 @@ def test_int8_codes(emu, tmp_path, k, dtype, rot):
     st = check_quant(codes.view(np.int8), scales, ref, "float16", x64, rotate=rot, y_gpu=yr, bits=8)
     if not rot:
         assert st["code_flips"] == 0
+
+
+def rope_tables(positions, d, base=10000.0):
+    inv = base ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d)
+    th = np.outer(np.arange(positions, dtype=np.float64), inv)
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype,layout,pos0,fast", [("bfloat16", "flat", 0, True), ("bfloat16", "bshd", 5, False),
+                                                    ("float16", "flat", 3, False), ("float16", "bshd", 0, True)])
+def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast):
+    """RoPE (half-split pairs, fp32 arithmetic, rounded to the 16-bit format) ahead of R3,
+    on flat and strided [B, H, S, D] addressing, against the oracle's RoPE + rotation."""
+    B, H, S, D = 2, 3, 37, 128
+    q_bits, _, _ = workloads.gen_kv(seed=9, batch=B, heads=H, seq=S, head_dim=D)
+    if dtype == "float16":
+        q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
+    cos, sin = rope_tables(pos0 + S + 4, D)
+    rows = B * H * S
+    mode = MODE_QUANT if fast else MODE_QUANT | MODE_ROT32
+    if layout == "bshd":
+        mem = np.ascontiguousarray(q_bits.transpose(0, 2, 1, 3))
+        codes, scales, yr = run_emu(emu, tmp_path, mem, dtype, 7, rows, mode=mode, fast=fast,
+                                    fourd=(B, H, S, S * H * D, D, H * D), rope=(cos, sin, pos0))
+    else:
+        codes, scales, yr = run_emu(emu, tmp_path, q_bits.reshape(rows, D), dtype, 7, rows, mode=mode,
+                                    fast=fast, bhs=(B, H, S), rope=(cos, sin, pos0))
+    x = workloads.to_float64(q_bits, dtype)
+    pos = pos0 + np.arange(S)
+    xr = oracle.rope_16bit(x, cos[pos][None, None], sin[pos][None, None], dtype).reshape(rows, D)
+    ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
+    check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", xr, y_gpu=None if fast else yr)
 
