@@ -27,6 +27,13 @@
  *    nothing is launched and no output is written.
  *  - Inputs must be finite; NaN/Inf inputs are outside the contract.
  *  - Sizes are element counts unless stated otherwise.
+ *
+ * Diagnostics, read once per process from the environment:
+ *  - RBQ_LOG=1: every call that passes validation prints one line to stderr with its
+ *    sizes and the kernel variant and grid it launches.
+ *  - RBQ_FAULT_INJECT=launch: every call that passes validation returns RBQ_EHIP
+ *    without launching anything, so callers can test their error handling (also on a
+ *    machine without a GPU).
  */
 #ifndef RBQ_H
 #define RBQ_H

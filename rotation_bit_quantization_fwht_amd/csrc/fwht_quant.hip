@@ -11,6 +11,7 @@
 #include "../../include/rbq.h"
 #include "fwht_engine.h"
 #include "validate.h"
+#include "diag.h"
 
 namespace rbq {
 
@@ -77,6 +78,11 @@ static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t
   a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u) |
            (int8 ? OPT_INT8 : 0u);
   const bool fast = (flags & RBQ_PACKED) && rotated == nullptr;
+  if (diag_log())
+    fprintf(stderr, "rbq: hadamard_quant n=%lld tokens=%lld dtype=%d rotate=%d signs=%d int8=%d packed=%d "
+            "fast=%d blocks=%lld\n", (long long)n, (long long)tokens, (int)x_dtype, (int)rot, signs != nullptr,
+            (int)int8, (flags & RBQ_PACKED) != 0, (int)fast, (long long)blocks);
+  if (diag_fail_launch()) return RBQ_EHIP;
   if (dispatch(chk.k, a, in_kind(x_dtype), rot, false, fast, false, stream) != hipSuccess)
     return RBQ_EHIP;
   return RBQ_OK;
@@ -158,6 +164,11 @@ static rbq_status kv_launch(const void* q, const void* k, rbq_dtype dtype, int64
   a.blocks0 = (uint32_t)blocks;
   a.nblocks = (uint32_t)(2 * blocks);
   a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
+  if (diag_log())
+    fprintf(stderr, "rbq: kv_rotate_quant B=%lld H=%lld S=%lld D=%lld dtype=%d flat=%d rope=%d q_rotate_only=%d "
+            "blocks=%lld\n", (long long)batch, (long long)heads, (long long)seq, (long long)head_dim, (int)dtype,
+            (int)chk.flat, rope_cos != nullptr, (int)rot_only, (long long)(2 * blocks));
+  if (diag_fail_launch()) return RBQ_EHIP;
   if (dispatch(chk.k, a, in_kind(dtype), true, !chk.flat, !rot_only, rope_cos != nullptr, stream) !=
       hipSuccess)
     return RBQ_EHIP;

@@ -34,6 +34,7 @@
 #include "../../include/rbq.h"
 #include "common.h"
 #include "validate.h"
+#include "diag.h"
 
 namespace rbq {
 
@@ -149,22 +150,6 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) fw_slot[j] = kSlotsA + swz(wn0 + j * 32 + fr, 2 * fg);
 
-  auto mma_chunk = [&](const u32x4_g (&fa)[4], const u32x4_g (&fw)[2]) {
-    // 16 packed bytes per fragment row = two sub-steps of 32 codes
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i_t xa[4], xw[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = widen(fa[i][2 * h], fa[i][2 * h + 1]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) xw[j] = widen(fw[j][2 * h], fw[j][2 * h + 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xw[j], xa[i], acc[i][j], 0, 0, 0);
-    }
-  };
   auto read_chunk = [&](int step, int c, u32x4_g (&fa)[4], u32x4_g (&fw)[2]) {
     const u32x4_g* sb = lds + (step % kStages) * kSlots;
 #pragma unroll
@@ -500,6 +485,10 @@ extern "C" rbq_status w4a4_gemm(const uint8_t* qA, const void* sA, const uint8_t
   g.tiles_n = (int)((N + kBN - 1) / kBN);
   const int64_t ntiles = (int64_t)g.tiles_m * g.tiles_n;
   if (ntiles > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (diag_log())
+    fprintf(stderr, "rbq: w4a4_gemm M=%lld N=%lld K=%lld tiles=%lld acc=%d\n", (long long)M, (long long)N,
+            (long long)K, (long long)ntiles, acc != nullptr);
+  if (diag_fail_launch()) return RBQ_EHIP;
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
@@ -519,6 +508,10 @@ extern "C" rbq_status w4a8_gemm(const int8_t* qA, const void* sA, const uint8_t*
   g.tiles_n = (int)((N + kBN - 1) / kBN);
   const int64_t ntiles = (int64_t)g.tiles_m * g.tiles_n;
   if (ntiles > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (diag_log())
+    fprintf(stderr, "rbq: w4a8_gemm M=%lld N=%lld K=%lld tiles=%lld acc=%d\n", (long long)M, (long long)N,
+            (long long)K, (long long)ntiles, acc != nullptr);
+  if (diag_fail_launch()) return RBQ_EHIP;
   hipLaunchKernelGGL(w4a8_gemm_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }

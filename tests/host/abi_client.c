@@ -1,0 +1,79 @@
+/* A plain C client of include/rbq.h: compiled by gcc, linked against librbq.so, no
+ * Python and no device memory. It checks what the boundary promises without a GPU:
+ * status strings, the version string, rejection of invalid arguments before any HIP
+ * call, and (run with RBQ_FAULT_INJECT=launch) that every valid call reports RBQ_EHIP
+ * without launching.
+ *
+ * Usage: abi_client validate | abi_client inject. Exit status 0 = all checks passed;
+ * each failed check prints one line. */
+#include <stdio.h>
+#include <string.h>
+
+#include "rbq.h"
+
+static int failures = 0;
+
+#define EXPECT(call, want)                                                              \
+  do {                                                                                  \
+    rbq_status got_ = (call);                                                           \
+    if (got_ != (want)) {                                                               \
+      printf("FAIL %s:%d %s -> %s, want %s\n", __FILE__, __LINE__, #call,               \
+             rbq_status_string(got_), rbq_status_string(want));                         \
+      ++failures;                                                                       \
+    }                                                                                   \
+  } while (0)
+
+/* 16-byte aligned addresses that are never dereferenced: every call below either fails
+ * validation or is stopped by the fault-injection switch before it reaches the GPU. */
+#define PX ((void *)0x10000)
+#define PC ((void *)0x20000)
+#define PS ((void *)0x30000)
+
+int main(int argc, char **argv) {
+  const int inject = argc > 1 && strcmp(argv[1], "inject") == 0;
+  const rbq_status launched = inject ? RBQ_EHIP : RBQ_OK;
+  const int64_t B = 2, H = 4, S = 16, D = 128;
+  const int64_t st[4] = {H * S * D, S * D, D, 1};
+  const int64_t bad_st[4] = {H * S * D, S * D, D, 2};
+
+  if (strcmp(rbq_status_string(RBQ_OK), "RBQ_OK") != 0) { puts("FAIL status string"); ++failures; }
+  if (strcmp(rbq_status_string((rbq_status)42), "RBQ_UNKNOWN") != 0) { puts("FAIL unknown status"); ++failures; }
+  if (!strstr(rbq_version(), "gfx950")) { puts("FAIL version"); ++failures; }
+
+  /* empty problems succeed without launching, in both modes */
+  EXPECT(hadamard_quant_int4(PX, RBQ_BF16, 4096, 0, 4096, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL), RBQ_OK);
+  EXPECT(kv_rotate_quant(PX, PX, RBQ_BF16, B, H, 0, D, st, st, PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL), RBQ_OK);
+  EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 0, 64, 4096, PX, NULL, NULL), RBQ_OK);
+
+  /* invalid arguments are rejected on the host in both modes */
+  EXPECT(hadamard_quant_int4(PX, RBQ_BF16, 4095, 8, 4096, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL), RBQ_EINVAL);
+  EXPECT(hadamard_quant_int4(NULL, RBQ_BF16, 4096, 8, 4096, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL), RBQ_EINVAL);
+  EXPECT(hadamard_quant_int4_signed(PX, RBQ_BF16, 4096, 8, 4096, NULL, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
+         RBQ_EINVAL);
+  EXPECT(hadamard_quant_int8(PX, RBQ_BF16, 4096, 8, 4096, (int8_t *)PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
+         RBQ_EINVAL);
+  EXPECT(kv_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, bad_st, st, PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
+         RBQ_EINVAL);
+  EXPECT(kv_rope_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, (const float *)PS, (const float *)PS, S, 1,
+                              PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
+         RBQ_EINVAL);
+  EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4000, PX, NULL, NULL), RBQ_ENOTSUP);
+  EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 60, 4096, PX, NULL, NULL), RBQ_ENOTSUP);
+
+  /* valid calls: only reached in inject mode, where nothing is launched */
+  if (inject) {
+    EXPECT(hadamard_quant_int4(PX, RBQ_BF16, 4096, 8, 4096, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL), launched);
+    EXPECT(hadamard_quant_int4_signed(PX, RBQ_F16, 4096, 8, 4096, PS, PC, PS, RBQ_F32, NULL, RBQ_PACKED, NULL),
+           launched);
+    EXPECT(hadamard_quant_int8(PX, RBQ_F32, 1024, 3, 1024, (int8_t *)PC, PS, RBQ_F16, NULL, 0, NULL), launched);
+    EXPECT(kv_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL), launched);
+    EXPECT(kv_rope_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, (const float *)PS, (const float *)PS, S, 0,
+                                PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
+           launched);
+    EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
+    EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
+  }
+
+  printf("%s: %d failure(s)\n", inject ? "inject" : "validate", failures);
+  return failures ? 1 : 0;
+}

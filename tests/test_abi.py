@@ -184,3 +184,52 @@ def test_rope_validation(L):
     assert kr(pos0=-1) == E
     assert kr(dt=rbq.RBQ_F32) == E
     assert kr(D=256) == NS
+
+
+@pytest.fixture(scope="session")
+def abi_client(L, tmp_path_factory):
+    """tests/host/abi_client.c built with gcc against include/rbq.h and librbq.so."""
+    exe = str(tmp_path_factory.mktemp("abi") / "abi_client")
+    libdir = os.path.dirname(rbq.library_path())
+    libname = os.path.basename(rbq.library_path())
+    assert libname.startswith("lib") and libname.endswith(".so")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "host", "abi_client.c"), "-o", exe,
+           "-L", libdir, "-l" + libname[3:-3], "-Wl,-rpath," + libdir]
+    subprocess.run(cmd, check=True)
+    return exe
+
+
+def _run_client(exe, mode, **env):
+    e = {k: v for k, v in os.environ.items() if not k.startswith("RBQ_")}
+    e.update(env)
+    return subprocess.run([exe, mode], capture_output=True, text=True, env=e, timeout=120)
+
+
+def test_plain_c_client_validation(abi_client):
+    p = _run_client(abi_client, "validate")
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "validate: 0 failure(s)" in p.stdout
+    assert "rbq:" not in p.stderr  # no diagnostics unless asked for
+
+
+def test_fault_injection_reports_launch_failure(abi_client):
+    p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch")
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "inject: 0 failure(s)" in p.stdout
+    # invalid arguments still fail validation first, under injection too
+    p = _run_client(abi_client, "validate", RBQ_FAULT_INJECT="launch")
+    assert p.returncode == 0, p.stdout + p.stderr
+
+
+def test_dispatch_log(abi_client):
+    p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
+    assert p.returncode == 0, p.stdout + p.stderr
+    lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
+    assert len(lines) == 7, p.stderr  # one line per valid call, none for rejected ones
+    assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
+    assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
+    assert "rope=0" in lines[3] and "rope=1" in lines[4]
+    assert lines[5].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
+    assert lines[6].startswith("rbq: w4a8_gemm")

@@ -153,3 +153,25 @@ def test_w4a8_on_int8_quantized_workload(rbq):
     qw_h, sw_h = oracle.unpack_nibbles(qw.cpu().numpy()), sw.cpu().numpy()
     acc_ref, _ = oracle.w4a8_gemm(qa_h, sa_h, qw_h, sw_h)
     check_out(acc.cpu().numpy(), out.float().cpu().numpy(), acc_ref, sa_h, sw_h)
+
+
+@pytest.mark.parametrize("which", ["w4a4", "w4a8"])
+def test_gemm_bitwise_deterministic(rbq, which):
+    """Integer sums and a fixed epilogue order: repeated calls on the same operands give
+    bit-identical accumulators and outputs (full 4096 x 11008 x 4096 shape)."""
+    M, N, K = 4096, 11008, 4096
+    print(f"case {which}_gemm determinism M={M} N={N} K={K}", flush=True)
+    if which == "w4a4":
+        qa = dev(workloads.gen_packed_codes(41, M, K))
+        call = rbq.w4a4_gemm
+    else:
+        qa = dev(gen_int8_codes(41, M, K))
+        call = rbq.w4a8_gemm
+    qw = dev(workloads.gen_packed_codes(42, N, K))
+    sa = dev(workloads.gen_scales(43, M, "float16"))
+    sw = dev(workloads.gen_scales(44, N, "float16"))
+    runs = [call(qa, sa, qw, sw, return_acc=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for out, acc in runs[1:]:
+        assert torch.equal(acc, runs[0][1])
+        assert torch.equal(out.view(torch.int16), runs[0][0].view(torch.int16))
