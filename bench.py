@@ -408,6 +408,28 @@ def main():
             "workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], bf16 out",
             "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
+    if run_gemm and gemm_ok and not args.no_extras:
+        # context only: the vendor library's int8 GEMM (torch._int_mm, hipBLASLt) on the same
+        # shape with the codes already unpacked to int8 and a plain int32 result (no scales)
+        try:
+            a8 = torch.randint(-8, 8, (GEMM_M, GEMM_K), dtype=torch.int8, device=dev)
+            w8 = torch.randint(-8, 8, (GEMM_N, GEMM_K), dtype=torch.int8, device=dev)
+            c32 = torch._int_mm(a8, w8.t())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                c32 = torch._int_mm(a8, w8.t())
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 20
+            extras["library_int8_gemm"] = {
+                "workload": "torch._int_mm int8 [4096, 4096] x int8 [4096, 11008]^T -> int32 (unpacked codes, no epilogue)",
+                "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
+                "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
+            del a8, w8, c32
+        except Exception as e:  # the library call is context, not part of the step
+            extras["library_int8_gemm"] = {"error": f"{type(e).__name__}: {e}"[:200]}
     if run_kv and not args.no_extras:
         # RoPE fused ahead of R3 on the same Q/K (read as pre-RoPE values), and the unfused
         # sequence it replaces: the same RoPE in torch (fp32 arithmetic, bf16 result) writing

@@ -18,6 +18,8 @@ Everything is computed in float64 with NumPy, following the definitions on the p
   listing), nibble packing, dequantization and MSE.
 * ``gemm``: exact integer product of the codes and the scale epilogue.
 * ``rope``: the rotary position embedding that the fused R3 operation applies first.
+* ``kron``: rotations of rows whose length is not a power of two, by the Kronecker
+  product of a Paley matrix with a Sylvester matrix.
 
 Every function here is pinned by ``tests/test_oracle.py`` against facts the pages or
 the mathematics fix (worked examples, closed forms, invariants, brute force); a
@@ -44,6 +46,7 @@ from .quant import (
 )
 from .gemm import int_gemm, w4a4_gemm, w4a8_gemm
 from .rope import rope_exact, rope_16bit
+from .kron import legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron
 
 __all__ = [
     "sylvester",
@@ -71,4 +74,10 @@ __all__ = [
     "w4a8_gemm",
     "rope_exact",
     "rope_16bit",
+    "legendre",
+    "paley_kind",
+    "paley_hadamard",
+    "kron_factor",
+    "kron_hadamard",
+    "rotate_kron",
 ]

@@ -1,0 +1,134 @@
+"""Hadamard rotations of rows whose length is not a power of two, in float64.
+
+Test infrastructure (see the package docstring): not part of the product path.
+
+Source: "Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices":
+lengths that are not powers of two are rotated by the Kronecker product of a
+power-of-two Hadamard matrix with a small known Hadamard matrix. The page names neither
+the small matrix nor the order of the factors; the readings fixed here are:
+
+* n = m * p with p a power of two; the rotation is y = (H_m (x) H_p) x / sqrt(n), where
+  element a * p + b of a row is index (a, b) of the product (a in [0, m), b in [0, p)),
+  H_p is the Sylvester matrix and H_m is a Paley matrix.
+* m is the smallest of 4 o, 8 o, 16 o, ... (o the odd part of n, m <= 256, m dividing n)
+  for which a Paley construction over a prime field exists: Paley I when m - 1 is a prime
+  q = 3 (mod 4), else Paley II when m / 2 - 1 is a prime q = 1 (mod 4). A power of two has
+  m = 1 (the Sylvester matrix alone).
+* Paley I: H = I + [[0, j^T], [-j, Q]], with j the all-ones column and Q the Jacobsthal
+  matrix Q[a][b] = chi(a - b), chi the quadratic character of GF(q).
+* Paley II: C = [[0, j^T], [j, Q]] (symmetric for q = 1 mod 4); every 0 of C becomes the
+  2 x 2 block [[1, -1], [-1, -1]] and every +-1 becomes +-[[1, 1], [1, -1]], block (R, C)
+  of H covering rows 2R, 2R + 1 and columns 2C, 2C + 1.
+
+The Paley matrices are the textbook constructions (R. E. A. C. Paley, "On orthogonal
+matrices", 1933), written here from their definitions.
+"""
+
+import math
+
+import numpy as np
+
+from .hadamard import sylvester
+
+
+def is_prime(v):
+    """Trial division."""
+    if v < 2:
+        return False
+    d = 2
+    while d * d <= v:
+        if v % d == 0:
+            return False
+        d += 1
+    return True
+
+
+def legendre(a, q):
+    """Quadratic character chi(a) of GF(q), q an odd prime, by Euler's criterion:
+    a^((q-1)/2) mod q is 1 for a nonzero square, q - 1 for a non-square, 0 for a = 0."""
+    r = pow(int(a) % q, (q - 1) // 2, q)
+    return 0 if r == 0 else (1 if r == 1 else -1)
+
+
+def paley_kind(m):
+    """(q, 1) for Paley I, (q, 2) for Paley II, or None when neither applies to order m."""
+    if m >= 4 and is_prime(m - 1) and (m - 1) % 4 == 3:
+        return m - 1, 1
+    if m >= 4 and m % 2 == 0 and is_prime(m // 2 - 1) and (m // 2 - 1) % 4 == 1:
+        return m // 2 - 1, 2
+    return None
+
+
+def jacobsthal(q):
+    """Q[a][b] = chi(a - b), a, b in GF(q)."""
+    chi = [legendre(d, q) for d in range(q)]
+    return np.array([[chi[(a - b) % q] for b in range(q)] for a in range(q)], dtype=np.float64)
+
+
+def paley_hadamard(m):
+    """The Paley Hadamard matrix of order m (entries +-1, float64)."""
+    kind = paley_kind(m)
+    if kind is None:
+        raise ValueError(f"no Paley construction of order {m}")
+    q, k = kind
+    Q = jacobsthal(q)
+    if k == 1:
+        S = np.zeros((m, m))
+        S[0, 1:] = 1.0
+        S[1:, 0] = -1.0
+        S[1:, 1:] = Q
+        return np.eye(m) + S
+    C = np.zeros((q + 1, q + 1))
+    C[0, 1:] = 1.0
+    C[1:, 0] = 1.0
+    C[1:, 1:] = Q
+    zero_block = np.array([[1.0, -1.0], [-1.0, -1.0]])
+    one_block = np.array([[1.0, 1.0], [1.0, -1.0]])
+    H = np.empty((m, m))
+    for R in range(q + 1):
+        for Cc in range(q + 1):
+            v = C[R, Cc]
+            H[2 * R:2 * R + 2, 2 * Cc:2 * Cc + 2] = zero_block if v == 0 else v * one_block
+    return H
+
+
+def kron_factor(n):
+    """m for a row length n (1 for a power of two), or None when the rule finds none."""
+    if n < 1:
+        return None
+    if n & (n - 1) == 0:
+        return 1
+    o = n
+    while o % 2 == 0:
+        o //= 2
+    m = 4 * o
+    while m <= 256 and n % m == 0:
+        if paley_kind(m) is not None:
+            return m
+        m *= 2
+    return None
+
+
+def kron_hadamard(n):
+    """The full n x n matrix H_m (x) H_p (explicit; small n only)."""
+    m = kron_factor(n)
+    if m is None:
+        raise ValueError(f"no supported factorization of {n}")
+    hm = np.ones((1, 1)) if m == 1 else paley_hadamard(m)
+    return np.kron(hm, sylvester(n // m))
+
+
+def rotate_kron(x):
+    """y = (H_m (x) H_p) x / sqrt(n) for every row of x [..., n], by the mixed-product
+    property: H_p applied to each of the m blocks of p elements, then H_m across the
+    blocks (two matrix products, no fast transform)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    m = kron_factor(n)
+    if m is None:
+        raise ValueError(f"no supported factorization of {n}")
+    p = n // m
+    hm = np.ones((1, 1)) if m == 1 else paley_hadamard(m)
+    blocks = x.reshape(-1, m, p) @ sylvester(p)          # H_p is symmetric
+    y = np.einsum("ac,rcb->rab", hm, blocks)              # (H_m Y)[a, b] = sum_c H_m[a, c] Y[c, b]
+    return (y / math.sqrt(n)).reshape(x.shape)

@@ -30,6 +30,7 @@ Readings fixed here where the pages are silent:
 import numpy as np
 
 from .hadamard import rotate, rotate_signed
+from .kron import rotate_kron
 
 SCALE_FLOOR = 1e-8
 QMIN = -8
@@ -140,7 +141,8 @@ def round_to_bf16(v):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True, signs=None, bits=4):
+def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True, signs=None, bits=4,
+                        kron=False):
     """Rotate each row of x by H_n / sqrt(n), then quantize it to INT4 per row.
 
     x: [rows, n] (any real dtype; upcast exactly to float64).
@@ -150,6 +152,8 @@ def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True
     H_n diag(signs) / sqrt(n) (see ``hadamard.rotate_signed``).
     bits: 4 (default) or 8 -- INT8 codes (scale max/127, range [-128, 127]) are never
     packed.
+    kron: rotate by (H_m (x) H_p) / sqrt(n) (``kron.rotate_kron``), which also accepts
+    row lengths that are not powers of two.
 
     Returns a dict with
       y        float64 [rows, n]  values that were quantized (rotated, or x itself),
@@ -162,6 +166,8 @@ def hadamard_quant_int4(x, scale_dtype="float16", packed=True, rotate_input=True
     x = np.asarray(x, dtype=np.float64)
     if not rotate_input:
         y = x.copy()
+    elif kron:
+        y = rotate_kron(x)
     elif signs is not None:
         y = rotate_signed(x, signs)
     else:
