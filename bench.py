@@ -36,6 +36,8 @@ NSETS = 4
 R4_TOKENS, R4_N = 8192, 16384
 KV_SHAPE = (16, 32, 2048, 128)
 GEMM_M, GEMM_N, GEMM_K = 4096, 11008, 4096
+KRON_N = 14336
+KRON_BYTES = 8192 * KRON_N * 2 + 8192 * KRON_N // 2 + 8192 * 2
 
 R4_BYTES = R4_TOKENS * R4_N * 2 + R4_TOKENS * R4_N // 2 + R4_TOKENS * 2
 KV_ROWS = KV_SHAPE[0] * KV_SHAPE[1] * KV_SHAPE[2]
@@ -203,7 +205,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the worked-example and decode-sweep reports")
-    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "kron", "copy"], default="all",
                     help="restrict the step (for profiling one kernel); 'copy' runs a plain 1 GiB "
                          "device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
@@ -483,6 +485,33 @@ def main():
             "workload": "R4 bf16 [8192, 16384] with a seeded +-1 diagonal (H diag(s) / sqrt(n))",
             "avg_us": round(t * 1e6, 3), "GB_s": round(R4_BYTES / t / 1e9, 2),
             "frac_hbm_peak": round(R4_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if args.only == "kron" or (args.only == "all" and not args.no_extras):
+        # a row length that is not a power of two: the down-projection input of width
+        # 14336 = 28 * 512 (Paley factor of the second kind, q = 13), R4's recipe
+        kb, _ = workloads.gen_ffn(seed=0, n=KRON_N)
+        k0 = to_dev16(kb)
+        del kb
+        kx = [k0] + [torch.roll(k0, shifts=97 * i, dims=0).contiguous() for i in range(1, NSETS)]
+        kc = [torch.empty((R4_TOKENS, KRON_N // 2), dtype=torch.uint8, device=dev) for _ in range(NSETS)]
+        ks = [torch.empty((R4_TOKENS,), dtype=torch.float16, device=dev) for _ in range(NSETS)]
+        for i in range(NSETS):
+            rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i])
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NSETS)]
+        ts = []
+        for rep in range(max(1, args.steps // NSETS)):
+            for i in range(NSETS):
+                ev[2 * i].record()
+                rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i])
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            ts += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(NSETS)]
+        t = float(np.mean(ts)) * 1e-3
+        extras["kron_r4_14336"] = {
+            "workload": "R4 bf16 [8192, 14336] = (H_28 (x) H_512) / sqrt(n), packed INT4 + fp16 scales",
+            "avg_us": round(t * 1e6, 3), "GB_s": round(KRON_BYTES / t / 1e9, 2),
+            "frac_hbm_peak": round(KRON_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del kx, kc, ks, k0
 
     cpu = None
     if not args.no_cpu_baseline:

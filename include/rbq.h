@@ -217,6 +217,41 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
                      rbq_dtype scale_dtype, int64_t M, int64_t N, int64_t K, void *out_bf16,
                      int32_t *acc, hipStream_t stream);
 
+/*
+ * hadamard_kron_quant_int4 -- hadamard_quant_int4 for row lengths that are not powers of
+ * two ("Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices": such
+ * lengths use the Kronecker product of a power-of-two Hadamard matrix with a small known
+ * one). n = m * p with p a power of two, and each row is rotated by
+ * (H_m (x) H_p) / sqrt(n), element a * p + b of the row being index (a, b) of the
+ * product; H_p is the Sylvester matrix and H_m the Paley matrix of order m:
+ *   Paley I (q = m - 1 prime, q = 3 mod 4): I + [[0, 1...], [-1..., Q]],
+ *     Q[a][b] = chi(a - b) with chi the quadratic character of GF(q);
+ *   Paley II (q = m/2 - 1 prime, q = 1 mod 4): the conference matrix [[0, 1...], [1..., Q]]
+ *     with each 0 replaced by [[1, -1], [-1, -1]] and each +-1 by +-[[1, 1], [1, -1]].
+ * m is the smallest of 4o, 8o, 16o, ... (o the odd part of n, m <= 256, m dividing n) with
+ * such a construction (rbq_kron_factor reports it). The quantizer, the codes and the
+ * scales are those of hadamard_quant_int4.
+ *
+ *  x, x_dtype, tokens, x_row_stride, codes, scales, scale_dtype, rotated: as for
+ *               hadamard_quant_int4; x rows 16-byte aligned.
+ *  n            2 <= n <= 32768. A power of two is passed to hadamard_quant_int4.
+ *  flags        RBQ_PACKED only.
+ * Errors: RBQ_EINVAL for the argument errors of hadamard_quant_int4 and for flags other
+ * than RBQ_PACKED; RBQ_ENOTSUP when n has no factor by the rule above or the kernel does
+ * not take it (m > 160, p < 16, p > 2048); RBQ_EHIP if the launch fails.
+ */
+rbq_status hadamard_kron_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
+                                    int64_t x_row_stride, void *codes, void *scales,
+                                    rbq_dtype scale_dtype, float *rotated, unsigned flags,
+                                    hipStream_t stream);
+
+/*
+ * rbq_kron_factor -- the order m of the Paley factor hadamard_kron_quant_int4 uses for a
+ * row length n (1 for a power of two). Host only, no HIP call.
+ * Errors: RBQ_EINVAL for n < 1 or m == NULL; RBQ_ENOTSUP when the rule finds no factor.
+ */
+rbq_status rbq_kron_factor(int64_t n, int64_t *m);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *rbq_status_string(rbq_status s);
 

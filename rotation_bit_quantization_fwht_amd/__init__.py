@@ -1,13 +1,19 @@
 """Thin Python binding of librbq.so, the C-ABI HIP library for MI355X (gfx950).
 
-The three calls have the same names and meaning as the C functions declared in
+The calls have the same names and meaning as the C functions declared in
 ``include/rbq.h``:
 
 * ``hadamard_quant_int4`` -- Sylvester-Hadamard rotation per row fused with per-row
-  symmetric INT4 absmax quantization (round half to even), codes packed two per byte;
-* ``kv_rotate_quant`` -- the same per (batch, head, token) vector of post-RoPE Q and K;
-* ``w4a4_gemm`` -- the W4A4 GEMM on packed codes with int32 accumulation and a bf16
-  dequantization epilogue.
+  symmetric INT4 absmax quantization (round half to even), codes packed two per byte
+  (optionally the randomized transform with a +-1 diagonal);
+* ``hadamard_kron_quant_int4`` -- the same for row lengths that are not powers of two,
+  rotated by the Kronecker product of a Paley matrix with a Sylvester matrix
+  (``kron_factor`` reports the Paley order);
+* ``hadamard_quant_int8`` -- the same with INT8 codes;
+* ``kv_rotate_quant`` -- the same per (batch, head, token) vector of post-RoPE Q and K
+  (optionally with RoPE applied first);
+* ``w4a4_gemm`` / ``w4a8_gemm`` -- the GEMMs on packed INT4 weight codes with int32
+  accumulation and a bf16 dequantization epilogue.
 
 This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
 memory, allocates outputs with torch when the caller does not pass them, and hands raw
@@ -26,6 +32,8 @@ __all__ = [
     "library_path",
     "hadamard_quant_int4",
     "hadamard_quant_int8",
+    "hadamard_kron_quant_int4",
+    "kron_factor",
     "kv_rotate_quant",
     "w4a4_gemm",
     "w4a8_gemm",
@@ -50,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "hadamard_quant_int4",
     "hadamard_quant_int4_signed",
     "hadamard_quant_int8",
+    "hadamard_kron_quant_int4",
+    "rbq_kron_factor",
     "kv_rotate_quant",
     "kv_rope_rotate_quant",
     "w4a4_gemm",
@@ -98,6 +108,10 @@ def lib():
     L.hadamard_quant_int4_signed.restype = ci
     L.hadamard_quant_int8.argtypes = [vp, ci, i64, i64, i64, vp, vp, ci, vp, cu, vp]
     L.hadamard_quant_int8.restype = ci
+    L.hadamard_kron_quant_int4.argtypes = [vp, ci, i64, i64, i64, vp, vp, ci, vp, cu, vp]
+    L.hadamard_kron_quant_int4.restype = ci
+    L.rbq_kron_factor.argtypes = [i64, p64]
+    L.rbq_kron_factor.restype = ci
     L.kv_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, vp, vp, ci, vp, cu, vp]
     L.kv_rotate_quant.restype = ci
     L.kv_rope_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, i64, i64,
@@ -206,6 +220,52 @@ def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=
             _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), flags, _stream(stream, dev),
         )
         _check("hadamard_quant_int4", st)
+    if rotated is not None:
+        return codes, scales, rotated
+    return codes, scales
+
+
+def kron_factor(n):
+    """Order m of the Paley factor used for row length n (1 for a power of two), or None
+    when the library has no factorization for n."""
+    m = ctypes.c_int64(0)
+    st = lib().rbq_kron_factor(int(n), ctypes.byref(m))
+    if st == RBQ_ENOTSUP:
+        return None
+    _check("rbq_kron_factor", st)
+    return m.value
+
+
+def hadamard_kron_quant_int4(x, *, scale_dtype=None, packed=True, codes=None, scales=None, rotated=None,
+                             return_rotated=False, stream=None):
+    """As ``hadamard_quant_int4`` for any supported row length n = m * p: every row of
+    ``x`` [tokens, n] is rotated by (H_m (x) H_p) / sqrt(n) and quantized to INT4 with
+    one absmax scale per row. Returns ``(codes, scales)`` (+ the rotated rows when
+    requested)."""
+    torch = _torch()
+    _require_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with a contiguous last dimension")
+    tokens, n = x.shape
+    scale_dtype = torch.float16 if scale_dtype is None else scale_dtype
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((tokens, n // 2 if packed else n), dtype=torch.uint8 if packed else torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty((tokens,), dtype=scale_dtype, device=dev)
+    if rotated is None and return_rotated:
+        rotated = torch.empty((tokens, n), dtype=torch.float32, device=dev)
+    _require_cuda(codes, scales, rotated)
+    _require_buffer("codes", codes, (tokens, n // 2) if packed else (tokens, n),
+                    (torch.uint8,) if packed else (torch.int8, torch.uint8), dev)
+    _require_buffer("scales", scales, (tokens,), (torch.float16, torch.float32), dev)
+    _require_buffer("rotated", rotated, (tokens, n), (torch.float32,), dev)
+    st = lib().hadamard_kron_quant_int4(
+        _ptr(x), _dtype_code(x.dtype), n, tokens, x.stride(0) if tokens > 0 else n,
+        _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), _ptr(rotated), RBQ_PACKED if packed else 0,
+        _stream(stream, dev),
+    )
+    _check("hadamard_kron_quant_int4", st)
     if rotated is not None:
         return codes, scales, rotated
     return codes, scales

@@ -48,12 +48,41 @@ struct DevCtx {
     d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
   }
 
+  // d += A B for one 16x16x32 MFMA with both operands in registers (eight 16-bit values
+  // per lane each, operand layouts as in hadamard32); bf16 unless IN is IN_F16
+  template <int IN>
+  __device__ __forceinline__ void mfma16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4],
+                                               float (&d)[4]) const {
+    const u32x4_t av = {a[0], a[1], a[2], a[3]};
+    const u32x4_t bv = {b[0], b[1], b[2], b[3]};
+    f32x4_t cv = {d[0], d[1], d[2], d[3]};
+    if constexpr (IN == IN_F16)
+      cv = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av),
+                                                  __builtin_bit_cast(f16x8_t, bv), cv, 0, 0, 0);
+    else
+      cv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                   __builtin_bit_cast(bf16x8_t, bv), cv, 0, 0, 0);
+    d[0] = cv[0]; d[1] = cv[1]; d[2] = cv[2]; d[3] = cv[3];
+  }
+
+  // hides a value's origin from the optimizer (keeps a 32-bit address offset from being
+  // widened and hoisted)
+  __device__ __forceinline__ uint32_t opaque(uint32_t v) const {
+    asm volatile("" : "+v"(v));
+    return v;
+  }
+
   // Called at the top of every block iteration: makes the lane id opaque to the compiler
   // so that per-lane address arithmetic is recomputed in each iteration instead of being
   // hoisted out of the block loop (hoisting keeps dozens of registers live across it).
   __device__ __forceinline__ void refresh_ids() { asm volatile("" : "+v"(lane)); }
 
   __device__ __forceinline__ void barrier() const { __syncthreads(); }
+  // workgroup barrier that waits for this wave's LDS accesses only: global loads issued
+  // before it (prefetches) stay in flight across it
+  __device__ __forceinline__ void barrier_lds() const {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   // LDS operations of one wave execute in program order; this only keeps the
   // compiler from moving LDS accesses across the point.
   __device__ __forceinline__ void wave_sync() const { __builtin_amdgcn_wave_barrier(); }
@@ -69,6 +98,9 @@ struct DevCtx {
   }
   __device__ __forceinline__ void lds_store(uint32_t i, float v) const { lds[i] = v; }
   __device__ __forceinline__ float lds_load(uint32_t i) const { return lds[i]; }
+  // four consecutive words at a 16-byte aligned word index i (one 128-bit LDS access)
+  __device__ __forceinline__ f32x4 lds_load4(uint32_t i) const { return *(const f32x4*)(lds + i); }
+  __device__ __forceinline__ void lds_store4(uint32_t i, f32x4 v) const { *(f32x4*)(lds + i) = v; }
 
   // 16-bit pair (element 2j in the low half) -> two floats
   template <int IN>

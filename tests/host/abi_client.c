@@ -57,6 +57,17 @@ int main(int argc, char **argv) {
   EXPECT(kv_rope_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, (const float *)PS, (const float *)PS, S, 1,
                               PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
          RBQ_EINVAL);
+  EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 11008, 8, 11008, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
+         RBQ_ENOTSUP);
+  EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 5120, 8, 5120, PC, PS, RBQ_F16, NULL, RBQ_NO_ROTATE, NULL),
+         RBQ_EINVAL);
+  {
+    int64_t m = 0;
+    EXPECT(rbq_kron_factor(14336, &m), RBQ_OK);
+    if (m != 28) { printf("FAIL kron factor of 14336: %lld\n", (long long)m); ++failures; }
+    EXPECT(rbq_kron_factor(11008, &m), RBQ_ENOTSUP);
+    EXPECT(rbq_kron_factor(0, &m), RBQ_EINVAL);
+  }
   EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4000, PX, NULL, NULL), RBQ_ENOTSUP);
   EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 60, 4096, PX, NULL, NULL), RBQ_ENOTSUP);
 
@@ -69,6 +80,8 @@ int main(int argc, char **argv) {
     EXPECT(kv_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL), launched);
     EXPECT(kv_rope_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, (const float *)PS, (const float *)PS, S, 0,
                                 PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
+           launched);
+    EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 5120, 8, 5120, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
            launched);
     EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
     EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);

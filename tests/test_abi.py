@@ -9,6 +9,7 @@ import subprocess
 
 import pytest
 
+import oracle
 import rotation_bit_quantization_fwht_amd as rbq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -227,9 +228,37 @@ def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 7, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 8, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
-    assert lines[5].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
-    assert lines[6].startswith("rbq: w4a8_gemm")
+    assert lines[5].startswith("rbq: hadamard_kron_quant n=5120 m=20 p=256 paley=1 q=19 tokens=8")
+    assert lines[6].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
+    assert lines[7].startswith("rbq: w4a8_gemm")
+
+
+def test_kron_validation_and_factor(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+
+    def hk(n=5120, tokens=8, stride=None, x=A16, flags=rbq.RBQ_PACKED, dt=rbq.RBQ_BF16, sdt=rbq.RBQ_F16):
+        return L.hadamard_kron_quant_int4(x, dt, n, tokens, stride or n, A16b, A16c, sdt, NULL, flags, NULL)
+
+    assert hk(tokens=0) == rbq.RBQ_OK
+    assert hk(n=11008) == NS          # 172 and 344 have no Paley construction over a prime
+    assert hk(n=252 * 16) == NS       # Paley order 252 is above what the kernel takes
+    assert hk(n=12 * 8) == NS         # p = 8 < 16
+    assert hk(n=6) == NS              # no factor
+    assert hk(n=40000) == E
+    assert hk(tokens=-1) == E
+    assert hk(x=NULL) == E
+    assert hk(stride=5119) == E
+    assert hk(stride=5124) == E       # 10248-byte rows are not 16-byte aligned
+    assert hk(x=ctypes.c_void_p(0x10008)) == E
+    assert hk(flags=rbq.RBQ_NO_ROTATE) == E
+    assert hk(dt=9) == E
+    assert hk(sdt=rbq.RBQ_BF16) == E
+    # the library's factor rule agrees with the oracle's on every length up to 40000
+    for n in range(1, 40001):
+        want = oracle.kron_factor(n)
+        got = rbq.kron_factor(n)
+        assert got == want, n
