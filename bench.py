@@ -55,6 +55,7 @@ def kernel_source_hash(files):
 
 FWHT_SOURCES = ("common.h", "plan.h", "fwht_engine.h", "devctx.h", "fwht_kernels.hip")
 GEMM_SOURCES = ("common.h", "w4a4_gemm.hip")
+KRON_SOURCES = ("common.h", "fwht_engine.h", "devctx.h", "kron_engine.h", "kron_factor.h", "kron_quant.hip")
 
 
 def load_traffic(name, src_hash):
@@ -510,7 +511,8 @@ def main():
         extras["kron_r4_14336"] = {
             "workload": "R4 bf16 [8192, 14336] = (H_28 (x) H_512) / sqrt(n), packed INT4 + fp16 scales",
             "avg_us": round(t * 1e6, 3), "GB_s": round(KRON_BYTES / t / 1e9, 2),
-            "frac_hbm_peak": round(KRON_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(KRON_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("hadamard_kron_quant_int4", kernel_source_hash(KRON_SOURCES))}
         del kx, kc, ks, k0
 
     cpu = None
