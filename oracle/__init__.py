@@ -43,8 +43,9 @@ from .quant import (
     round_to_bf16,
     hadamard_quant_int4,
     kv_rotate_quant,
+    quantize_groups,
 )
-from .gemm import int_gemm, w4a4_gemm, w4a8_gemm
+from .gemm import int_gemm, w4a4_gemm, w4a8_gemm, w4a8_gemm_grouped
 from .rope import rope_exact, rope_16bit
 from .kron import legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron
 
@@ -72,6 +73,8 @@ __all__ = [
     "int_gemm",
     "w4a4_gemm",
     "w4a8_gemm",
+    "w4a8_gemm_grouped",
+    "quantize_groups",
     "rope_exact",
     "rope_16bit",
     "legendre",

@@ -54,3 +54,32 @@ def w4a8_gemm(qa, sa, qw, sw):
     ``w4a4_gemm`` (|sum| <= K * 128 * 8, exact in float64)."""
     return w4a4_gemm(qa, sa, qw, sw)
 
+
+
+def w4a8_gemm_grouped(qa, sa, qw, sw_groups, group):
+    """W4A8 product with group-wise weight scales ("SpinQuant, when rotations are worth
+    learning": its ExecuTorch export quantizes weights to 4 bits in groups of 256 or 32
+    input channels, with 8-bit dynamic activations):
+        out[m, n] = sa[m] * sum_g sw_groups[n, g] * sum_{k in group g} qa[m, k] * qw[n, k]
+    with group g covering k in [g * group, (g + 1) * group).
+
+    qa int codes [M, K], qw int codes [N, K], sa [M], sw_groups [N, K / group].
+    Returns (partial int64 [K / group, M, N], out float64 [M, N]); every partial sum is
+    exact (float64 products of integers), the group sums are combined in float64.
+    """
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    k = qa.shape[1]
+    if group < 1 or k % group:
+        raise ValueError("the group size must divide K")
+    ng = k // group
+    sa = np.asarray(sa, dtype=np.float64)
+    sw = np.asarray(sw_groups, dtype=np.float64)
+    if sw.shape != (qw.shape[0], ng):
+        raise ValueError("sw_groups must be [N, K / group]")
+    partial = np.stack([int_gemm(qa[:, g * group:(g + 1) * group], qw[:, g * group:(g + 1) * group])
+                        for g in range(ng)])
+    out = np.zeros(partial.shape[1:], dtype=np.float64)
+    for g in range(ng):
+        out += partial[g].astype(np.float64) * sw[None, :, g]
+    return partial, out * sa[:, None]

@@ -208,3 +208,27 @@ def kv_rotate_quant(q_in, k_in, scale_dtype="float16", q_rotate_only=False):
             "y": r["y"].reshape(shape),
         }
     return out
+
+
+def quantize_groups(y, group, scale_dtype="float16", packed=True, bits=4):
+    """Group-wise symmetric absmax quantization of rows y [rows, K]: each run of ``group``
+    consecutive elements gets its own scale s = max(max|y_g| / qmax, 1e-8), stored in
+    ``scale_dtype``, and codes round_half_even(clamp(y / s*, qmin, qmax)) against the
+    stored scale -- the per-row quantizer of this module applied to every group
+    ("SpinQuant, when rotations are worth learning": group-size 256/32 4-bit weights in
+    its ExecuTorch export path; the step-size equation of "SpinQuant Guide: Learned
+    Rotations for 4-Bit LLMs" per group).
+
+    Returns a dict with s (unrounded) and s_stored (float64) [rows, K / group], scales
+    (stored dtype), q int8 [rows, K] and codes (packed uint8 [rows, K/2] or int8).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    rows, k = y.shape
+    if group < 1 or k % group:
+        raise ValueError("the group size must divide the row length")
+    g = y.reshape(rows, k // group, group)
+    s = absmax_scale(g, bits)
+    s_stored, scales = round_scale(s, scale_dtype)
+    q = quantize_codes(g, s_stored, bits).reshape(rows, k)
+    codes = pack_nibbles(q) if packed else q
+    return {"s": s, "s_stored": s_stored, "scales": scales, "q": q, "codes": codes}

@@ -698,3 +698,57 @@ def test_kron_quantizer_invariants():
     # the rotation spreads the outlier channel: the step shrinks by an order of magnitude
     plain = oracle.hadamard_quant_int4(x, "float16", packed=True, rotate_input=False)
     assert np.all(r["s_stored"] * 5 < plain["s_stored"])
+
+
+# ------------------------------------------------------------ group-wise scales
+# "SpinQuant, when rotations are worth learning": the ExecuTorch export uses 4-bit weights
+# with group sizes 256 or 32 and 8-bit dynamic activations.
+
+def test_groups_of_the_whole_row_equal_the_row_quantizer():
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal((5, 256)) * 3
+    g = oracle.quantize_groups(y, 256, "float16", packed=True)
+    r = oracle.hadamard_quant_int4(y, "float16", packed=True, rotate_input=False)
+    assert np.array_equal(g["codes"], r["codes"])
+    assert np.array_equal(g["s_stored"][:, 0], r["s_stored"])
+
+
+def test_group_quantizer_brute_force():
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((3, 64)) * np.array([1.0, 10.0, 0.01])[:, None]
+    y[1, 40] = 0.0
+    r = oracle.quantize_groups(y, 16, "float32", packed=False)
+    for i in range(3):
+        for gi in range(4):
+            seg = y[i, 16 * gi:16 * gi + 16]
+            s = max(max(abs(v) for v in seg) / 7.0, 1e-8)
+            s32 = float(np.float32(s))
+            assert r["s_stored"][i, gi] == s32
+            for j, v in enumerate(seg):
+                t = min(max(v / s32, -8.0), 7.0)
+                assert r["q"][i, 16 * gi + j] == round_half_even(t)
+    # every group's absmax element lands on +-7
+    assert np.all(np.abs(r["q"].reshape(3, 4, 16)).max(axis=2) == 7)
+
+
+def test_grouped_gemm_brute_force_and_reduction_to_per_channel():
+    rng = np.random.default_rng(10)
+    M, N, K, G = 3, 4, 96, 32
+    qa = rng.integers(-128, 128, size=(M, K))
+    qw = rng.integers(-8, 8, size=(N, K))
+    sa = rng.uniform(0.01, 0.1, M)
+    sw = rng.uniform(0.01, 0.1, (N, K // G))
+    partial, out = oracle.w4a8_gemm_grouped(qa, sa, qw, sw, G)
+    for m in range(M):
+        for n in range(N):
+            tot = 0.0
+            for g in range(K // G):
+                p = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(g * G, g * G + G))
+                assert partial[g, m, n] == p
+                tot += p * sw[n, g]
+            assert abs(out[m, n] - sa[m] * tot) <= 1e-12 * abs(sa[m] * tot) + 1e-15
+    # equal group scales reduce to the per-output-channel product
+    swc = np.repeat(sw[:, :1], K // G, axis=1)
+    _, out_c = oracle.w4a8_gemm_grouped(qa, sa, qw, swc, G)
+    _, ref = oracle.w4a8_gemm(qa, sa, qw, sw[:, 0])
+    np.testing.assert_allclose(out_c, ref, rtol=1e-14)
