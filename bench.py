@@ -412,6 +412,35 @@ def main():
             "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
     if run_gemm and gemm_ok and not args.no_extras:
+        # group-wise weight scales (groups of 256 codes along K) on the same shape: the
+        # rotated weights quantized per group, the INT8 activation codes as above
+        wr = torch.empty((GEMM_N, GEMM_K), dtype=torch.float32, device=dev)
+        wgt = torch.from_numpy(workloads.gen_gemm_inputs(seed=0)[1]).to(dev)
+        rbq.hadamard_quant_int4(wgt, rotated=wr)
+        del wgt
+        qwg, swg = rbq.quantize_groups_int4(wr, 256)
+        outg = torch.empty_like(out)
+        for name, fn in (("quantize_groups_int4", lambda: rbq.quantize_groups_int4(wr, 256, codes=qwg, scales=swg)),
+                         ("w4a8_gemm_grouped", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg, swg, 256, out=outg))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 20
+            if name == "w4a8_gemm_grouped":
+                extras[name] = {"workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], weight scales per "
+                                            "256 codes, bf16 out",
+                                "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
+                                "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
+            else:
+                nbytes = GEMM_N * GEMM_K * 4 + GEMM_N * GEMM_K // 2 + GEMM_N * (GEMM_K // 256) * 2
+                extras[name] = {"workload": "rotated fp32 weights [11008, 4096] -> packed INT4, fp16 scales per 256",
+                                "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2)}
+        del wr, qwg, swg, outg
         # context only: the vendor library's int8 GEMM (torch._int_mm, hipBLASLt) on the same
         # shape with the codes already unpacked to int8 and a plain int32 result (no scales)
         try:

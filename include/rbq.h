@@ -218,6 +218,47 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
                      int32_t *acc, hipStream_t stream);
 
 /*
+ * w4a8_gemm_grouped -- W4A8 with group-wise weight scales: one scale per run of `group`
+ * consecutive K elements of each weight row ("SpinQuant, when rotations are worth
+ * learning": its ExecuTorch export uses 4-bit weights in groups of 256 or 32 input
+ * channels with 8-bit dynamic activations):
+ *   out[m, n] = bf16( sA[m] * sum_g sW[n, g] * sum_{k in group g} qA[m, k] * qW[n, k] ),
+ * each group's integer sum exact, the scaled group sums added in fp32.
+ *
+ *  qA     int8 [M, K] (hadamard_quant_int8 codes), 16-byte aligned.
+ *  qW     uint8 [N, K/2] packed INT4 (quantize_groups_int4 codes), 16-byte aligned.
+ *  sA     [M]; sW [N, K/group] row-major; both scale_dtype (F16 or F32).
+ *  group  power of two, 32 <= group <= K, dividing K.
+ *  out_bf16 bf16 [M, N] row-major, 16-byte aligned.
+ * Errors: as w4a4_gemm, plus RBQ_EINVAL for a bad group size and RBQ_ENOTSUP for groups of
+ * 32 or 64 (the per-group fold is instantiated for groups of 128 codes or more).
+ */
+rbq_status w4a8_gemm_grouped(const int8_t *qA, const void *sA, const uint8_t *qW, const void *sW,
+                             rbq_dtype scale_dtype, int64_t group, int64_t M, int64_t N,
+                             int64_t K, void *out_bf16, hipStream_t stream);
+
+/*
+ * quantize_groups_int4 -- group-wise symmetric INT4 quantization of rows that are already
+ * in the rotated basis (the offline weight path: rows rotated by hadamard_quant_int4's
+ * `rotated` output, then quantized per group): each run of `group` consecutive elements
+ * gets s = max(max|y_g| / 7, 1e-8), stored in scale_dtype, and codes
+ * round_half_even(clamp(y / s_stored, -8, 7)) ("SpinQuant Guide: Learned Rotations for
+ * 4-Bit LLMs", step-size equation, per group).
+ *
+ *  y        [rows, K], dtype F32, BF16 or F16, row stride `y_row_stride` elements; rows
+ *           16-byte aligned.
+ *  group    power of two, 32 <= group <= min(K, 4096), dividing K.
+ *  codes    RBQ_PACKED: uint8 [rows, K/2]; else int8 [rows, K]; 16-byte aligned.
+ *  scales   [rows, K/group] row-major in scale_dtype (F32 or F16).
+ *  flags    RBQ_PACKED only.
+ * Errors: RBQ_EINVAL for NULL pointers (rows > 0), misalignment, a bad dtype, group size or
+ * flag; RBQ_EHIP if the launch fails.
+ */
+rbq_status quantize_groups_int4(const void *y, rbq_dtype dtype, int64_t K, int64_t rows,
+                                int64_t y_row_stride, int64_t group, void *codes, void *scales,
+                                rbq_dtype scale_dtype, unsigned flags, hipStream_t stream);
+
+/*
  * hadamard_kron_quant_int4 -- hadamard_quant_int4 for row lengths that are not powers of
  * two ("Rotations: QuaRot, SpinQuant and incoherence", section "Hadamard matrices": such
  * lengths use the Kronecker product of a power-of-two Hadamard matrix with a small known

@@ -13,7 +13,9 @@ The calls have the same names and meaning as the C functions declared in
 * ``kv_rotate_quant`` -- the same per (batch, head, token) vector of post-RoPE Q and K
   (optionally with RoPE applied first);
 * ``w4a4_gemm`` / ``w4a8_gemm`` -- the GEMMs on packed INT4 weight codes with int32
-  accumulation and a bf16 dequantization epilogue.
+  accumulation and a bf16 dequantization epilogue;
+* ``quantize_groups_int4`` / ``w4a8_gemm_grouped`` -- group-wise weight scales: the
+  quantizer (one scale per run of ``group`` elements) and the W4A8 GEMM that consumes it.
 
 This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
 memory, allocates outputs with torch when the caller does not pass them, and hands raw
@@ -37,6 +39,8 @@ __all__ = [
     "kv_rotate_quant",
     "w4a4_gemm",
     "w4a8_gemm",
+    "w4a8_gemm_grouped",
+    "quantize_groups_int4",
     "RBQ_OK",
     "RBQ_EINVAL",
     "RBQ_ENOTSUP",
@@ -64,6 +68,8 @@ EXPORTED_SYMBOLS = (
     "kv_rope_rotate_quant",
     "w4a4_gemm",
     "w4a8_gemm",
+    "w4a8_gemm_grouped",
+    "quantize_groups_int4",
     "rbq_status_string",
     "rbq_version",
 )
@@ -121,6 +127,10 @@ def lib():
     L.w4a4_gemm.restype = ci
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
     L.w4a8_gemm.restype = ci
+    L.w4a8_gemm_grouped.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, vp, vp]
+    L.w4a8_gemm_grouped.restype = ci
+    L.quantize_groups_int4.argtypes = [vp, ci, i64, i64, i64, i64, vp, vp, ci, cu, vp]
+    L.quantize_groups_int4.restype = ci
     L.rbq_status_string.argtypes = [ci]
     L.rbq_status_string.restype = ctypes.c_char_p
     L.rbq_version.argtypes = []
@@ -442,3 +452,55 @@ def w4a8_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=No
         return out, acc
     return out
 
+
+
+def quantize_groups_int4(y, group, *, scale_dtype=None, packed=True, codes=None, scales=None, stream=None):
+    """Group-wise INT4 quantization of rows ``y`` [rows, K] (already in the rotated basis):
+    one absmax scale per run of ``group`` consecutive elements. Returns ``(codes, scales)``
+    -- codes uint8 [rows, K/2] (packed) or int8 [rows, K], scales [rows, K/group]."""
+    torch = _torch()
+    _require_cuda(y)
+    if y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be a 2-D tensor with a contiguous last dimension")
+    rows, K = y.shape
+    if group <= 0 or K % group:
+        raise ValueError("group must divide the row length")
+    scale_dtype = torch.float16 if scale_dtype is None else scale_dtype
+    dev = y.device
+    if codes is None:
+        codes = torch.empty((rows, K // 2 if packed else K), dtype=torch.uint8 if packed else torch.int8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, K // group), dtype=scale_dtype, device=dev)
+    _require_cuda(codes, scales)
+    _require_buffer("codes", codes, (rows, K // 2) if packed else (rows, K),
+                    (torch.uint8,) if packed else (torch.int8, torch.uint8), dev)
+    _require_buffer("scales", scales, (rows, K // group), (torch.float16, torch.float32), dev)
+    st = lib().quantize_groups_int4(
+        _ptr(y), _dtype_code(y.dtype), K, rows, y.stride(0) if rows > 0 else K, int(group),
+        _ptr(codes), _ptr(scales), _dtype_code(scales.dtype), RBQ_PACKED if packed else 0, _stream(stream, dev))
+    _check("quantize_groups_int4", st)
+    return codes, scales
+
+
+def w4a8_gemm_grouped(qa, sa, qw, sw, group, *, out=None, stream=None):
+    """out[m, n] = bf16(sa[m] * sum_g sw[n, g] * sum_{k in group g} qa[m, k] qw[n, k]) with
+    INT8 activation codes qa int8 [M, K], packed INT4 weight codes qw uint8 [N, K/2] and
+    group-wise weight scales sw [N, K/group] (same dtype as sa [M])."""
+    torch = _torch()
+    _require_cuda(qa, sa, qw, sw)
+    M, K = qa.shape
+    N = qw.shape[0]
+    if qw.shape != (N, K // 2) or group <= 0 or K % group:
+        raise ValueError("qa must be [M, K], qw [N, K/2] and group must divide K")
+    dev = qa.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _require_buffer("qa", qa, (M, K), (torch.int8,), dev)
+    _require_buffer("qw", qw, (N, K // 2), (torch.uint8,), dev)
+    _require_buffer("sa", sa, (M,), (sw.dtype,), dev)
+    _require_buffer("sw", sw, (N, K // group), (torch.float16, torch.float32), dev)
+    _require_buffer("out", out, (M, N), (torch.bfloat16,), dev)
+    st = lib().w4a8_gemm_grouped(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _dtype_code(sw.dtype), int(group),
+                                 M, N, K, _ptr(out), _stream(stream, dev))
+    _check("w4a8_gemm_grouped", st)
+    return out

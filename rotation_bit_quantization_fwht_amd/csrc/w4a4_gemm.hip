@@ -52,6 +52,7 @@ struct GemmArgs {
   int M, N, K;
   int scale_f16;
   int tiles_m, tiles_n;
+  int group;           // group-wise weight scales: codes per group (sw is [N, K / group])
 };
 
 constexpr int kBM = 256, kBN = 256;                 // output tile (m x n)
@@ -466,6 +467,162 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
   }
 }
 
+
+// ------------------------------------------------------------- W4A8, group-wise W scales
+// out[m, n] = bf16( sA[m] * sum_g sW[n, g] * sum_{k in group g} qA[m, k] * qW[n, k] ):
+// the int32 sums of each group of G codes (G a power of two dividing K; the kernel is
+// written for any G >= 32 and instantiated for G >= 128) are exact, and are scaled and
+// added in fp32 when the group ends. A 512-thread workgroup computes a 128 x 128 tile; its
+// eight waves hold 64 (m) x 32 (n) wave tiles of 2 x 1 MFMA tiles, with int32 accumulators
+// for the current group and fp32 ones for the finished groups (small enough for two
+// workgroups per CU). Each 32-code sub-step covers 32 consecutive codes (32u .. 32u + 31
+// of a 128-code step), so every group boundary falls between sub-steps: lane half fg
+// takes codes 16 fg .. 16 fg + 15 of the sub-step, one 16-byte A chunk and one 8-byte half
+// of the W chunk. Copies go through a three-stage LDS ring as in the kernels above (A
+// chunks swizzled by key8, W by key); the operand reads of the next sub-step overlap the
+// MFMAs of the current one.
+constexpr int kGBM = 128, kGBN = 128, kGThreads = 512;
+constexpr int kGSlotsA = kGBM * kA8Chunks;                // 1024
+constexpr int kGSlots = kGSlotsA + kGBN * kChunks;        // 1536 per stage (24 KB)
+constexpr int kGLoads = kGSlots / kGThreads;              // 3 copies per thread
+constexpr int kGStages = 3;
+static_assert(kGSlots % kGThreads == 0 && kGLoads == 3, "the wait counts below assume three copies");
+
+// FS: sub-steps per group, up to 4 (groups of 128 codes or more end at step boundaries)
+template <int FS>
+__global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g) {
+  __shared__ u32x4_g lds[kGStages * kGSlots];
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int b = blockIdx.x;
+  const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
+  const int tn = t / g.tiles_m, tm = t % g.tiles_m;
+  const int m0 = tm * kGBM, n0 = tn * kGBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 32;
+  const int abytes = g.K, wbytes = g.K / 2;
+  const int steps = g.K / 128;
+  const int ngroups = g.K / g.group;
+  const int steps_per_group = g.group >= 128 ? g.group / 128 : 1;
+
+  const uint8_t* src[kGLoads];
+  int src_step[kGLoads];
+#pragma unroll
+  for (int q = 0; q < kGLoads; ++q) {
+    const int slot = q * kGThreads + tid;
+    if (slot < kGSlotsA) {
+      const int r = slot >> 3;
+      const int j = (slot & 7) ^ swz_key8(r);
+      src[q] = g.qa + (int64_t)min(m0 + r, g.M - 1) * abytes + j * 16;
+      src_step[q] = 128;
+    } else {
+      const int r = (slot - kGSlotsA) >> 2;
+      const int j = (slot & 3) ^ swz_key(r);
+      src[q] = g.qw + (int64_t)min(n0 + r, g.N - 1) * wbytes + j * 16;
+      src_step[q] = 64;
+    }
+  }
+  auto issue_copies = [&](int step) {
+    u32x4_g* dst = lds + (step % kGStages) * kGSlots + wave * 64;
+    const int st = min(step, steps - 1);
+#pragma unroll
+    for (int q = 0; q < kGLoads; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(src[q] + st * src_step[q]), (void*)(dst + q * kGThreads), 16, 0, 0);
+  };
+
+  v16i_t acc[2];
+  float facc[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    acc[i] = v16i_t{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) facc[i][e] = 0.0f;
+  }
+
+  const int fr = lane & 31, fg = lane >> 5;
+  int fa_row[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fa_row[i] = wm0 + i * 32 + fr;
+  const int fw_row = wn0 + fr;
+  // lane's output columns n (MFMA rows): n0 + wn0 + 8 q + 4 fg + e; the scales of a group
+  // are loaded when the previous group is folded, so the fold does not wait for loads
+  // issued after the copies in flight
+  float swg[4][4];
+  auto load_group_scales = [&](int grp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = min(n0 + wn0 + 8 * q + 4 * fg + e, g.N - 1);
+        swg[q][e] = load_scale(g.sw, n * ngroups + min(grp, ngroups - 1), g.scale_f16);
+      }
+  };
+  auto fold = [&](int grp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          facc[i][4 * q + e] += (float)(acc[i][4 * q + e] >> 4) * swg[q][e];
+          acc[i][4 * q + e] = 0;
+        }
+    load_group_scales(grp + 1);
+  };
+  load_group_scales(0);
+
+  // the operands of one sub-step: two A chunks (m blocks i) and one W chunk
+  auto read_sub = [&](const u32x4_g* sb, int u, u32x4_g (&ca)[2], u32x4_g& cw) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ca[i] = sb[swz8(fa_row[i], 2 * u + fg)];
+    cw = sb[kGSlotsA + swz(fw_row, u)];
+  };
+
+  issue_copies(0);
+  issue_copies(1);
+  for (int s = 0; s < steps; ++s) {
+    wait_copies_and_sync<kGLoads>();  // publishes step s (step s + 1 may stay in flight)
+    const u32x4_g* sb = lds + (s % kGStages) * kGSlots;
+    u32x4_g ca[2], cw;
+    read_sub(sb, 0, ca, cw);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v4i_t ya[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ya[i] = order_like_widen(ca[i]);
+      const v4i_t yw = fg ? widen(cw[2], cw[3]) : widen(cw[0], cw[1]);
+      if (u < 3) read_sub(sb, u + 1, ca, cw);  // the next sub-step's reads overlap these MFMAs
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw, ya[i], acc[i], 0, 0, 0);
+      if constexpr (FS < 4) {
+        if ((u + 1) % FS == 0) fold((4 * s + u) / FS);
+      }
+    }
+    if constexpr (FS == 4) {
+      if ((s + 1) % steps_per_group == 0) fold(s / steps_per_group);
+    }
+    // every wave is done with step s - 1's stage (it passed the barrier above after
+    // reading it), which step s + 2 now reuses
+    issue_copies(s + 2);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm0 + i * 32 + fr;
+    if (m >= g.M) continue;
+    const float sam = load_scale(g.sa, m, g.scale_f16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + wn0 + 8 * q + 4 * fg;
+      if (n >= g.N) continue;
+      uint32_t bits[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bits[e] = f32_to_bf16(facc[i][4 * q + e] * sam);
+      *(u32x2*)(g.out + (int64_t)m * g.N + n) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+    }
+  }
+}
+
 }  // namespace rbq
 
 using namespace rbq;
@@ -516,3 +673,31 @@ extern "C" rbq_status w4a8_gemm(const int8_t* qA, const void* sA, const uint8_t*
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
 
+extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const uint8_t* qW,
+                                        const void* sW, rbq_dtype scale_dtype, int64_t group,
+                                        int64_t M, int64_t N, int64_t K, void* out_bf16,
+                                        hipStream_t stream) {
+  const rbq_status st = check_gemm(qA, sA, qW, sW, scale_dtype, M, N, K, out_bf16, nullptr);
+  if (st != RBQ_OK) return st;
+  if (group < 32 || group > K || !is_pow2(group) || K % group != 0) return RBQ_EINVAL;
+  // groups of 32 or 64 codes would end inside a K step: their per-group fold (an fp32
+  // multiply-add per accumulator every one or two MFMAs) is not instantiated
+  if (group < 128) return RBQ_ENOTSUP;
+  if (M == 0 || N == 0) return RBQ_OK;
+  GemmArgs g{};
+  g.qa = (const uint8_t*)qA; g.qw = qW; g.sa = sA; g.sw = sW;
+  g.out = (uint16_t*)out_bf16;
+  g.M = (int)M; g.N = (int)N; g.K = (int)K;
+  g.group = (int)group;
+  g.scale_f16 = scale_dtype == RBQ_F16;
+  g.tiles_m = (int)((M + kGBM - 1) / kGBM);
+  g.tiles_n = (int)((N + kGBN - 1) / kGBN);
+  const int64_t ntiles = (int64_t)g.tiles_m * g.tiles_n;
+  if (ntiles > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (diag_log())
+    fprintf(stderr, "rbq: w4a8_gemm_grouped M=%lld N=%lld K=%lld group=%lld tiles=%lld\n", (long long)M,
+            (long long)N, (long long)K, (long long)group, (long long)ntiles);
+  if (diag_fail_launch()) return RBQ_EHIP;
+  hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<4>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
+  return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+}

@@ -262,3 +262,32 @@ def test_kron_validation_and_factor(L):
         want = oracle.kron_factor(n)
         got = rbq.kron_factor(n)
         assert got == want, n
+
+
+def test_group_entry_points_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+
+    def qg(K=4096, rows=8, stride=None, group=256, y=A16, dt=rbq.RBQ_F32, flags=rbq.RBQ_PACKED, sdt=rbq.RBQ_F16):
+        return L.quantize_groups_int4(y, dt, K, rows, stride or K, group, A16b, A16c, sdt, flags, NULL)
+
+    assert qg(rows=0) == rbq.RBQ_OK
+    for g in (16, 48, 8192, 4096 * 2):
+        assert qg(group=g, K=8192) == E, g
+    assert qg(group=512, K=768) == E        # must divide K
+    assert qg(y=NULL) == E
+    assert qg(stride=4095) == E
+    assert qg(y=ctypes.c_void_p(0x10004)) == E
+    assert qg(flags=rbq.RBQ_NO_ROTATE) == E
+    assert qg(sdt=rbq.RBQ_BF16) == E
+
+    def gg(group=256, K=4096, N=64, qa=A16):
+        return L.w4a8_gemm_grouped(qa, A16b, A16c, A16b, rbq.RBQ_F16, group, 64, N, K, A16, NULL)
+
+    assert L.w4a8_gemm_grouped(A16, A16b, A16c, A16b, rbq.RBQ_F16, 256, 0, 64, 4096, A16, NULL) == rbq.RBQ_OK
+    assert gg(group=48) == E
+    assert gg(group=8192) == E
+    assert gg(group=32) == NS               # groups below 128 codes are not instantiated
+    assert gg(group=64) == NS
+    assert gg(K=4000) == NS
+    assert gg(N=60) == NS
+    assert gg(qa=NULL) == E

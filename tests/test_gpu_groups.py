@@ -1,0 +1,141 @@
+"""GPU parity of the group-wise scale variants against the fp64 oracle, through the C ABI:
+quantize_groups_int4 (one absmax scale per run of G elements of rows already in the
+rotated basis) and w4a8_gemm_grouped (INT8 activations x packed INT4 weights with
+group-wise weight scales): scales exact in the stored dtype, codes bit-exact (the
+quantizer's rounding decision is exact), GEMM outputs within 1e-2 relative of the exact
+product plus the fp32 accumulation bound of the scaled group sums (``check_grouped``)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def rbq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotation_bit_quantization_fwht_amd as m
+
+    m.lib()
+    return m
+
+
+def to_dev(x, dtype):
+    if dtype == "float32":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+        t = t.view(torch.bfloat16 if dtype == "bfloat16" else torch.float16)
+    return t.cuda()
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "float16"])
+def test_quantize_groups(rbq, group, dtype):
+    K, rows = 8192, 37
+    print(f"case quantize_groups_int4 group={group} dtype={dtype}", flush=True)
+    y = workloads.gen_rows(group, rows, K, dtype, n_outliers=3, factor=30)
+    codes, scales = rbq.quantize_groups_int4(to_dev(y, dtype), group)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_groups(workloads.to_float64(y, dtype), group, "float16", packed=True)
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref["s_stored"])
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+
+
+def test_quantize_groups_unpacked_fp32_scales_strided_and_ragged(rbq):
+    K, rows, group = 4096, 1001, 256
+    print("case quantize_groups_int4 unpacked fp32 scales strided", flush=True)
+    y = workloads.gen_rows(5, rows, K + 32, "float32", n_outliers=1, factor=50)
+    y[7, :] = 0.0                                                     # an all-zero row
+    yd = to_dev(y, "float32")[:, :K]
+    codes, scales = rbq.quantize_groups_int4(yd, group, packed=False, scale_dtype=torch.float32)
+    ref = oracle.quantize_groups(y[:, :K].astype(np.float64), group, "float32", packed=False)
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref["s_stored"])
+    assert np.array_equal(codes.cpu().numpy().view(np.int8), ref["q"])
+
+
+def check_grouped(out_dev, partial, out_ref, sa, sw):
+    """bf16 outputs against the exact product: |got - ref| <= 1e-2 |ref| + (G + 2) 2^-24 T,
+    where G = K / group and T = |sa| sum_g |sw[n, g] partial_g|: the group sums are exact
+    integers, and the fp32 steps (G products with the group scale, G additions, the product
+    with sa) each round by at most 2^-24 relative to a value bounded by T; the final bf16
+    rounding is within the relative term. Outputs whose every group sum is 0 must be 0."""
+    got = out_dev.float().cpu().numpy().astype(np.float64)
+    sa = np.asarray(sa, dtype=np.float64)
+    sw = np.asarray(sw, dtype=np.float64)
+    terms = np.zeros_like(out_ref)
+    for g in range(partial.shape[0]):
+        terms += np.abs(partial[g].astype(np.float64) * sw[None, :, g])
+    terms *= np.abs(sa)[:, None]
+    zero = terms == 0
+    assert np.all(got[zero] == 0)
+    err = np.abs(got - out_ref)
+    bound = 1e-2 * np.abs(out_ref) + (partial.shape[0] + 2) * 2.0 ** -24 * terms
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert np.all(err <= bound), f"worst error {worst:.3g}x the bound"
+
+
+def _weights_and_activations(seed, M, N, K, group):
+    """A: bf16 rows -> INT8 codes (the library's own per-token quantizer); W: fp32 rows,
+    rotated and quantized per group by the oracle (operands identical on both sides)."""
+    a = workloads.gen_rows(seed, M, K, "bfloat16", n_outliers=1, factor=40)
+    w = workloads.gen_rows(seed + 1, N, K, "float32", n_outliers=0) * np.float32(0.02)
+    rw = oracle.quantize_groups(oracle.rotate(w.astype(np.float64)), group, "float16", packed=True)
+    ra = oracle.hadamard_quant_int4(workloads.to_float64(a, "bfloat16"), "float16", packed=False, bits=8)
+    return ra, rw
+
+
+@pytest.mark.parametrize("M,N,K,group", [(1, 8, 128, 128), (64, 256, 1024, 128), (300, 264, 2048, 256),
+                                         (513, 1032, 4096, 256), (130, 136, 4096, 1024), (64, 64, 4096, 4096)])
+def test_w4a8_gemm_grouped(rbq, M, N, K, group):
+    print(f"case w4a8_gemm_grouped M={M} N={N} K={K} group={group}", flush=True)
+    ra, rw = _weights_and_activations(M + N, M, N, K, group)
+    out = rbq.w4a8_gemm_grouped(torch.from_numpy(ra["q"].astype(np.int8)).cuda(),
+                                torch.from_numpy(ra["scales"]).cuda(),
+                                torch.from_numpy(rw["codes"]).cuda(),
+                                torch.from_numpy(rw["scales"]).cuda(), group)
+    torch.cuda.synchronize()
+    partial, ref = oracle.w4a8_gemm_grouped(ra["q"], ra["s_stored"], rw["q"], rw["s_stored"], group)
+    check_grouped(out, partial, ref, ra["s_stored"], rw["s_stored"])
+
+
+def test_w4a8_gemm_grouped_random_codes_extremes(rbq):
+    # uniform random codes over the full grids and log-uniform scales, including -128 / -8
+    M, N, K, group = 256, 512, 4096, 256
+    print("case w4a8_gemm_grouped random codes", flush=True)
+    rng = np.random.default_rng(12)
+    qa = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    qw = workloads.gen_packed_codes(13, N, K)
+    sa = workloads.gen_scales(14, M, "float32")
+    sw = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(N, K // group))).astype(np.float32)
+    out = rbq.w4a8_gemm_grouped(torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(),
+                                torch.from_numpy(qw).cuda(), torch.from_numpy(sw).cuda(), group)
+    partial, ref = oracle.w4a8_gemm_grouped(qa, sa, oracle.unpack_nibbles(qw), sw, group)
+    check_grouped(out, partial, ref, sa, sw)
+
+
+def test_w4a8_gemm_grouped_full_size_sampled(rbq):
+    """4096 x 11008 x 4096 with groups of 256: rows sampled against the oracle, and two
+    calls bit-identical."""
+    M, N, K, group = 4096, 11008, 4096, 256
+    print("case w4a8_gemm_grouped full size", flush=True)
+    rng = np.random.default_rng(21)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = workloads.gen_packed_codes(22, N, K)
+    sa = workloads.gen_scales(23, M, "float16")
+    sw = workloads.gen_scales(24, N * (K // group), "float16").reshape(N, K // group)
+    args = (torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(), torch.from_numpy(qw).cuda(),
+            torch.from_numpy(sw).cuda(), group)
+    out = rbq.w4a8_gemm_grouped(*args)
+    out2 = rbq.w4a8_gemm_grouped(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    rows = np.unique(np.concatenate([[0, 1, 4095], rng.integers(0, M, 13)]))
+    partial, ref = oracle.w4a8_gemm_grouped(qa[rows], sa[rows], oracle.unpack_nibbles(qw), sw, group)
+    check_grouped(out[torch.from_numpy(rows).cuda()], partial, ref, sa[rows], sw)
