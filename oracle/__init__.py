@@ -20,6 +20,7 @@ Everything is computed in float64 with NumPy, following the definitions on the p
 * ``rope``: the rotary position embedding that the fused R3 operation applies first.
 * ``kron``: rotations of rows whose length is not a power of two, by the Kronecker
   product of a Paley matrix with a Sylvester matrix.
+* ``attention``: decode attention over the INT4 key/value cache.
 
 Every function here is pinned by ``tests/test_oracle.py`` against facts the pages or
 the mathematics fix (worked examples, closed forms, invariants, brute force); a
@@ -47,6 +48,7 @@ from .quant import (
 )
 from .gemm import int_gemm, w4a4_gemm, w4a8_gemm, w4a8_gemm_grouped
 from .rope import rope_exact, rope_16bit
+from .attention import attention_decode
 from .kron import legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron
 
 __all__ = [
@@ -83,4 +85,5 @@ __all__ = [
     "kron_factor",
     "kron_hadamard",
     "rotate_kron",
+    "attention_decode",
 ]

@@ -752,3 +752,47 @@ def test_grouped_gemm_brute_force_and_reduction_to_per_channel():
     _, out_c = oracle.w4a8_gemm_grouped(qa, sa, qw, swc, G)
     _, ref = oracle.w4a8_gemm(qa, sa, qw, sw[:, 0])
     np.testing.assert_allclose(out_c, ref, rtol=1e-14)
+
+
+# ------------------------------------------------------------ attention over the INT4 KV cache
+# "SpinQuant, when rotations are worth learning", "Four rotation sites": R3 rotates queries
+# and keys by the same orthogonal Hadamard so that scores are unchanged and K can be cached
+# in INT4.
+
+def test_attention_scores_are_invariant_under_the_shared_rotation():
+    rng = np.random.default_rng(31)
+    B, H, S, D = 2, 3, 7, 128
+    q = rng.standard_normal((B, H, D))
+    k = rng.standard_normal((B, H, S, D))
+    v = rng.standard_normal((B, H, S, D))
+    ones = np.ones((B, H, S))
+    out_plain, p_plain = oracle.attention_decode(q, k, ones, v, ones, 0.1)
+    out_rot, p_rot = oracle.attention_decode(oracle.rotate(q), oracle.rotate(k), ones, v, ones, 0.1)
+    np.testing.assert_allclose(p_rot, p_plain, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(out_rot, out_plain, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(32)
+    B, H, Hkv, S, D = 1, 4, 2, 5, 8
+    q = rng.standard_normal((B, H, D))
+    kc = rng.integers(-8, 8, (B, Hkv, S, D))
+    vc = rng.integers(-8, 8, (B, Hkv, S, D))
+    ks = rng.uniform(0.1, 1.0, (B, Hkv, S))
+    vs = rng.uniform(0.1, 1.0, (B, Hkv, S))
+    out, p = oracle.attention_decode(q, kc, ks, vc, vs, 0.3)
+    np.testing.assert_allclose(p.sum(axis=-1), 1.0, rtol=1e-14)
+    # brute force for one head (query heads 2, 3 read key/value head 1)
+    b, h, kvh = 0, 3, 1
+    sc = [0.3 * sum(q[b, h, d] * ks[b, kvh, s] * kc[b, kvh, s, d] for d in range(D)) for s in range(S)]
+    mx = max(sc)
+    w = [np.exp(x - mx) for x in sc]
+    ref = [sum(w[s] / sum(w) * vs[b, kvh, s] * vc[b, kvh, s, d] for s in range(S)) for d in range(D)]
+    np.testing.assert_allclose(out[b, h], ref, rtol=1e-12)
+    # a single cached token: the output is that token's dequantized value row
+    o1, _ = oracle.attention_decode(q, kc[:, :, :1], ks[:, :, :1], vc[:, :, :1], vs[:, :, :1], 0.3)
+    np.testing.assert_allclose(o1[0, 1], vc[0, 0, 0] * vs[0, 0, 0], rtol=1e-14)
+    # equal scores (all keys zero): the output is the mean of the values
+    o2, p2 = oracle.attention_decode(q, np.zeros_like(kc), ks, vc, vs, 0.3)
+    np.testing.assert_allclose(p2, 1.0 / S, rtol=1e-14)
+    np.testing.assert_allclose(o2[0, 0], (vc[0, 0] * vs[0, 0][:, None]).mean(axis=0), rtol=1e-13)
