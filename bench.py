@@ -516,6 +516,32 @@ def main():
             "avg_us": round(t * 1e6, 3), "GB_s": round(R4_BYTES / t / 1e9, 2),
             "frac_hbm_peak": round(R4_BYTES / t / 1e9 / HBM_PEAK_GBS, 4)}
 
+    if run_kv and not args.no_extras:
+        # decode attention of one query per (batch, head) over the R3 workload's INT4 key
+        # cache (the codes kv_rotate_quant just wrote) and an INT4 value cache of the same shape
+        B, H, S, D = KV_SHAPE
+        o = sets["kv_out"][0]
+        kc, ks = o["k_codes"], o["k_scales"]
+        vcodes = torch.from_numpy(workloads.gen_packed_codes(31, B * H * S, D)).to(dev).reshape(B, H, S, D // 2)
+        vscales = torch.from_numpy(workloads.gen_scales(32, B * H * S, "float16")).to(dev).reshape(B, H, S)
+        qdec = sets["kv_q"][0][:, :, -1, :].contiguous()
+        aout = torch.empty_like(qdec)
+        fn = lambda: rbq.attention_decode_int4kv(qdec, kc, ks, vcodes, vscales, 1.0 / math.sqrt(D), out=aout)
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 20
+        nbytes = 2 * B * H * S * (D // 2 + 2) + 2 * B * H * D * 2
+        extras["attention_decode_int4kv"] = {
+            "workload": "one query per (batch, head) over INT4 K and V caches [16, 32, 2048, 128], fp16 scales",
+            "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2),
+            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del vcodes, vscales, aout
     if args.only == "kron" or (args.only == "all" and not args.no_extras):
         # a row length that is not a power of two: the down-projection input of width
         # 14336 = 28 * 512 (Paley factor of the second kind, q = 13), R4's recipe

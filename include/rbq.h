@@ -218,6 +218,35 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
                      int32_t *acc, hipStream_t stream);
 
 /*
+ * attention_decode_int4kv -- decode attention of one query position per (batch, head) over
+ * the INT4 key/value cache: keys as kv_rotate_quant writes them (R3-rotated, packed INT4,
+ * one scale per token and head), values as hadamard_quant_int4 writes them with
+ * RBQ_NO_ROTATE per (token, head) row. Because the query is rotated by the same
+ * orthogonal H / sqrt(head_dim) as the keys, the scores equal those of the unrotated pair
+ * ("SpinQuant, when rotations are worth learning", section "Four rotation sites"):
+ *   score[s] = softmax_scale * sum_d q[d] * k_scale[s] * k_code[s, d]
+ *   out[d]   = sum_s softmax(score)[s] * v_scale[s] * v_code[s, d]
+ * with key/value head kvh = h / (heads / kv_heads). Arithmetic in fp32; the output is
+ * rounded to the query's format.
+ *
+ *  q         [batch, heads, head_dim] contiguous, BF16 or F16 (kv_rotate_quant's rotated Q
+ *            with RBQ_Q_ROTATE_ONLY), 16-byte aligned.
+ *  k_codes, v_codes  uint8 [batch, kv_heads, seq_cap, head_dim/2], 16-byte aligned; tokens
+ *            0 .. seq-1 of each head are used (seq_cap is the cache capacity).
+ *  k_scales, v_scales  [batch, kv_heads, seq_cap] in scale_dtype (F16 or F32).
+ *  head_dim  128 (others: RBQ_ENOTSUP).
+ *  out       [batch, heads, head_dim] in q_dtype, 16-byte aligned.
+ * Errors: RBQ_EINVAL for NULL or misaligned pointers, bad dtypes, seq < 1, seq_cap < seq,
+ * heads not a multiple of kv_heads or a NaN scale; RBQ_ENOTSUP for head_dim != 128.
+ */
+rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
+                                   const void *k_scales, const uint8_t *v_codes,
+                                   const void *v_scales, rbq_dtype scale_dtype, int64_t batch,
+                                   int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap,
+                                   int64_t head_dim, float softmax_scale, void *out,
+                                   hipStream_t stream);
+
+/*
  * w4a8_gemm_grouped -- W4A8 with group-wise weight scales: one scale per run of `group`
  * consecutive K elements of each weight row ("SpinQuant, when rotations are worth
  * learning": its ExecuTorch export uses 4-bit weights in groups of 256 or 32 input

@@ -15,7 +15,8 @@ The calls have the same names and meaning as the C functions declared in
 * ``w4a4_gemm`` / ``w4a8_gemm`` -- the GEMMs on packed INT4 weight codes with int32
   accumulation and a bf16 dequantization epilogue;
 * ``quantize_groups_int4`` / ``w4a8_gemm_grouped`` -- group-wise weight scales: the
-  quantizer (one scale per run of ``group`` elements) and the W4A8 GEMM that consumes it.
+  quantizer (one scale per run of ``group`` elements) and the W4A8 GEMM that consumes it;
+* ``attention_decode_int4kv`` -- decode attention over the INT4 key/value cache.
 
 This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
 memory, allocates outputs with torch when the caller does not pass them, and hands raw
@@ -41,6 +42,7 @@ __all__ = [
     "w4a8_gemm",
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
+    "attention_decode_int4kv",
     "RBQ_OK",
     "RBQ_EINVAL",
     "RBQ_ENOTSUP",
@@ -70,6 +72,7 @@ EXPORTED_SYMBOLS = (
     "w4a8_gemm",
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
+    "attention_decode_int4kv",
     "rbq_status_string",
     "rbq_version",
 )
@@ -131,6 +134,9 @@ def lib():
     L.w4a8_gemm_grouped.restype = ci
     L.quantize_groups_int4.argtypes = [vp, ci, i64, i64, i64, i64, vp, vp, ci, cu, vp]
     L.quantize_groups_int4.restype = ci
+    L.attention_decode_int4kv.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
+                                          ctypes.c_float, vp, vp]
+    L.attention_decode_int4kv.restype = ci
     L.rbq_status_string.argtypes = [ci]
     L.rbq_status_string.restype = ctypes.c_char_p
     L.rbq_version.argtypes = []
@@ -503,4 +509,33 @@ def w4a8_gemm_grouped(qa, sa, qw, sw, group, *, out=None, stream=None):
     st = lib().w4a8_gemm_grouped(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _dtype_code(sw.dtype), int(group),
                                  M, N, K, _ptr(out), _stream(stream, dev))
     _check("w4a8_gemm_grouped", st)
+    return out
+
+
+def attention_decode_int4kv(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, *, seq=None, out=None,
+                            stream=None):
+    """Decode attention of q [B, H, 128] (the R3-rotated query) over the INT4 cache:
+    k_codes / v_codes uint8 [B, Hkv, S_cap, 64], k_scales / v_scales [B, Hkv, S_cap];
+    the first ``seq`` tokens (default S_cap) are attended. Returns out [B, H, 128] in q's
+    dtype."""
+    torch = _torch()
+    _require_cuda(q, k_codes, k_scales, v_codes, v_scales)
+    B, H, D = q.shape
+    _, Hkv, S_cap, half = k_codes.shape
+    seq = S_cap if seq is None else int(seq)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    _require_buffer("q", q, (B, H, D), (torch.bfloat16, torch.float16), dev)
+    for name, t, shape in (("k_codes", k_codes, (B, Hkv, S_cap, D // 2)), ("v_codes", v_codes, (B, Hkv, S_cap, D // 2))):
+        _require_buffer(name, t, shape, (torch.uint8,), dev)
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _require_buffer(name, t, (B, Hkv, S_cap), (torch.float16, torch.float32), dev)
+    if v_scales.dtype != k_scales.dtype:
+        raise ValueError("k_scales and v_scales must share a dtype")
+    _require_buffer("out", out, (B, H, D), (q.dtype,), dev)
+    st = lib().attention_decode_int4kv(_ptr(q), _dtype_code(q.dtype), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                       _ptr(v_scales), _dtype_code(k_scales.dtype), B, H, Hkv, seq, S_cap, D,
+                                       float(softmax_scale), _ptr(out), _stream(stream, dev))
+    _check("attention_decode_int4kv", st)
     return out

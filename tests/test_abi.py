@@ -291,3 +291,21 @@ def test_group_entry_points_validation(L):
     assert gg(K=4000) == NS
     assert gg(N=60) == NS
     assert gg(qa=NULL) == E
+
+
+def test_attention_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+
+    def at(q=A16, qdt=rbq.RBQ_BF16, sdt=rbq.RBQ_F16, B=2, H=8, Hkv=2, S=16, cap=16, D=128, scale=0.1):
+        return L.attention_decode_int4kv(q, qdt, A16b, A16c, A16b, A16c, sdt, B, H, Hkv, S, cap, D, scale, A16, NULL)
+
+    assert at(B=0) == rbq.RBQ_OK
+    assert at(S=0) == E
+    assert at(cap=8) == E                    # capacity below the sequence
+    assert at(H=6, Hkv=4) == E               # heads not a multiple of kv heads
+    assert at(qdt=rbq.RBQ_F32) == E
+    assert at(sdt=rbq.RBQ_BF16) == E
+    assert at(q=NULL) == E
+    assert at(q=ctypes.c_void_p(0x10008)) == E
+    assert at(scale=float("nan")) == E
+    assert at(D=64) == NS
