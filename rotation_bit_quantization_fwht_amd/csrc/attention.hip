@@ -9,12 +9,13 @@
 // scores equal those of the unrotated pair ("SpinQuant, when rotations are worth
 // learning", section "Four rotation sites": R3 is there so that K can be cached in INT4).
 //
-// One 256-thread workgroup per (batch, head). Sixteen lanes share one cached token: lane c
+// One 512-thread workgroup per (batch, head). Sixteen lanes share one cached token: lane c
 // takes dims 8c .. 8c + 7, i.e. one dword of codes of the token's 64-byte row, so a wave
-// reads four consecutive rows (256 contiguous bytes) per load. The sequence is processed
-// in tiles of 1024 tokens with an online softmax: the tile's scores go to LDS, the running
+// reads four consecutive rows (256 contiguous bytes) per load, and each group loads 16 of
+// its tokens before using any of them. The sequence is processed
+// in tiles of 2048 tokens with an online softmax: the tile's scores go to LDS, the running
 // maximum and sum are updated, and the value rows are accumulated with the tile's
-// probabilities. At the end the sixteen token groups' partial outputs are summed in LDS.
+// probabilities. At the end the 32 token groups' partial outputs are summed in LDS.
 #include <hip/hip_runtime.h>
 
 #include "../../include/rbq.h"
@@ -36,9 +37,10 @@ struct AttnArgs {
   int q_f16, scale_f16;
 };
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnTile = 1024;   // tokens per tile
+constexpr int kAttnThreads = 512;
+constexpr int kAttnTile = 2048;   // tokens per tile
 constexpr int kAttnD = 128;
+constexpr int kAttnU = 16;        // tokens per token group loaded ahead of use
 
 __device__ __forceinline__ float attn_load16(const void* p, int64_t i, int f16) {
   const uint32_t h = ((const uint16_t*)p)[i];
@@ -98,21 +100,32 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 
   for (int s0 = 0; s0 < a.S; s0 += kAttnTile) {
     const int n = min(kAttnTile, a.S - s0);
-    // ---- scores of the tile: sixteen lanes per token, eight dims each
+    // ---- scores of the tile: sixteen lanes per token, eight dims each; kAttnU tokens per
+    // token group are loaded before any is used, so their latencies overlap
     float tmax = -INFINITY;
-    for (int t = tg; t < ((n + 15) & ~15); t += kAttnThreads / 16) {
-      float dot = 0.0f;
-      if (t < n) {
-        const uint32_t w = krow[(int64_t)(s0 + t) * 16 + c];
+    for (int t0 = tg; t0 < ((n + 15) & ~15); t0 += kAttnU * (kAttnThreads / 16)) {
+      uint32_t w[kAttnU];
+      float ksv[kAttnU];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], attn_code(w, i), dot);
+      for (int u = 0; u < kAttnU; ++u) {
+        const int t = t0 + u * (kAttnThreads / 16);
+        const bool ok = t < n;
+        w[u] = ok ? krow[(int64_t)(s0 + t) * 16 + c] : 0u;
+        ksv[u] = ok ? attn_scale(a.ks, srow + s0 + t, a.scale_f16) : 0.0f;
       }
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-      if (t < n) {
-        const float sv = dot * attn_scale(a.ks, srow + s0 + t, a.scale_f16);
-        if (c == 0) sc[t] = sv;
-        tmax = fmaxf(tmax, sv);
+      for (int u = 0; u < kAttnU; ++u) {
+        const int t = t0 + u * (kAttnThreads / 16);
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], attn_code(w[u], i), dot);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+        if (t < n) {
+          const float sv = dot * ksv[u];
+          if (c == 0) sc[t] = sv;
+          tmax = fmaxf(tmax, sv);
+        }
       }
     }
     const float m_new = fmaxf(m_run, attn_reduce<true>(tmax, red));  // (its barrier publishes sc)
@@ -129,16 +142,25 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
     // ---- value rows weighted by the probabilities
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= corr;
-    for (int t = tg; t < n; t += kAttnThreads / 16) {
-      const float pv = sc[t] * attn_scale(a.vs, srow + s0 + t, a.scale_f16);
-      const uint32_t w = vrow[(int64_t)(s0 + t) * 16 + c];
+    for (int t0 = tg; t0 < n; t0 += kAttnU * (kAttnThreads / 16)) {
+      uint32_t w[kAttnU];
+      float pv[kAttnU];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pv, attn_code(w, i), acc[i]);
+      for (int u = 0; u < kAttnU; ++u) {
+        const int t = t0 + u * (kAttnThreads / 16);
+        const bool ok = t < n;
+        w[u] = ok ? vrow[(int64_t)(s0 + t) * 16 + c] : 0u;
+        pv[u] = ok ? sc[t] * attn_scale(a.vs, srow + s0 + t, a.scale_f16) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kAttnU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(pv[u], attn_code(w[u], i), acc[i]);
     }
     __syncthreads();  // the next tile overwrites sc
   }
 
-  // ---- sum the sixteen token groups' partial outputs
+  // ---- sum the token groups' partial outputs
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[tg][8 * c + i] = acc[i];
   __syncthreads();
