@@ -540,7 +540,8 @@ def main():
         extras["attention_decode_int4kv"] = {
             "workload": "one query per (batch, head) over INT4 K and V caches [16, 32, 2048, 128], fp16 scales",
             "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2),
-            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("attention_decode_int4kv", kernel_source_hash(("common.h", "attention.hip")))}
         del vcodes, vscales, aout
     if args.only == "kron" or (args.only == "all" and not args.no_extras):
         # a row length that is not a power of two: the down-projection input of width
