@@ -228,13 +228,16 @@ def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 8, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 11, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
     assert lines[5].startswith("rbq: hadamard_kron_quant n=5120 m=20 p=256 paley=1 q=19 tokens=8")
-    assert lines[6].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
-    assert lines[7].startswith("rbq: w4a8_gemm")
+    assert lines[6].startswith("rbq: quantize_groups_int4 K=4096 rows=8 group=256")
+    assert lines[7].startswith("rbq: w4a8_gemm_grouped M=64 N=64 K=4096 group=256")
+    assert lines[8].startswith("rbq: attention_decode_int4kv B=2 H=8 Hkv=2 S=16")
+    assert lines[9].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
+    assert lines[10].startswith("rbq: w4a8_gemm M=64")
 
 
 def test_kron_validation_and_factor(L):
