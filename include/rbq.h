@@ -237,7 +237,9 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
  *  head_dim  128 (others: RBQ_ENOTSUP).
  *  out       [batch, heads, head_dim] in q_dtype, 16-byte aligned.
  * Errors: RBQ_EINVAL for NULL or misaligned pointers, bad dtypes, seq < 1, seq_cap < seq,
- * heads not a multiple of kv_heads or a NaN scale; RBQ_ENOTSUP for head_dim != 128.
+ * heads not a multiple of kv_heads or a NaN scale; RBQ_ENOTSUP for head_dim != 128,
+ * seq >= 2^26 (one head's codes are addressed with 32-bit byte offsets), seq_cap > 2^30
+ * or batch * heads > 2^31 - 1.
  */
 rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
                                    const void *k_scales, const uint8_t *v_codes,

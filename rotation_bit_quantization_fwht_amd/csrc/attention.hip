@@ -9,13 +9,13 @@
 // scores equal those of the unrotated pair ("SpinQuant, when rotations are worth
 // learning", section "Four rotation sites": R3 is there so that K can be cached in INT4).
 //
-// One 512-thread workgroup per (batch, head). Sixteen lanes share one cached token: lane c
-// takes dims 8c .. 8c + 7, i.e. one dword of codes of the token's 64-byte row, so a wave
-// reads four consecutive rows (256 contiguous bytes) per load, and each group loads 16 of
-// its tokens before using any of them. The sequence is processed
-// in tiles of 2048 tokens with an online softmax: the tile's scores go to LDS, the running
-// maximum and sum are updated, and the value rows are accumulated with the tile's
-// probabilities. At the end the 32 token groups' partial outputs are summed in LDS.
+// One 512-thread workgroup per (batch, head), one pass over the cache. Sixteen lanes share
+// one cached token: lane c takes dims 8c .. 8c + 7, i.e. one dword of codes of the token's
+// 64-byte row, so a wave reads four consecutive rows (256 contiguous bytes) per load. Each
+// 16-lane group runs its own online softmax over its tokens (every 32nd token): per batch
+// of kAttnU tokens it takes the scores, raises its running maximum, rescales its sum and
+// output, and accumulates the value rows with the probabilities. At the end the 32
+// groups' (maximum, sum, output) triples are merged in LDS.
 #include <hip/hip_runtime.h>
 
 #include "../../include/rbq.h"
@@ -38,17 +38,13 @@ struct AttnArgs {
 };
 
 constexpr int kAttnThreads = 512;
-constexpr int kAttnTile = 2048;   // tokens per tile
+constexpr int kAttnGroups = kAttnThreads / 16;  // token groups of sixteen lanes
 constexpr int kAttnD = 128;
-constexpr int kAttnU = 16;        // tokens per token group loaded ahead of use
+constexpr int kAttnU = 8;  // tokens per group and batch
 
 __device__ __forceinline__ float attn_load16(const void* p, int64_t i, int f16) {
   const uint32_t h = ((const uint16_t*)p)[i];
   return f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h) : bits_f32(h << 16);
-}
-
-__device__ __forceinline__ float attn_scale(const void* p, int64_t i, int f16) {
-  return f16 ? attn_load16(p, i, 1) : ((const float*)p)[i];
 }
 
 // code i of a dword of packed codes (low nibble first), sign-extended: the builtin's
@@ -57,28 +53,46 @@ __device__ __forceinline__ float attn_code(uint32_t w, int i) {
   return (float)(int)__builtin_amdgcn_sbfe(w, 4 * i, 4);
 }
 
-// workgroup reduction of one float per thread (max or sum) through LDS
-template <bool MAX>
-__device__ __forceinline__ float attn_reduce(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float w = __shfl_xor(v, o);
-    v = MAX ? fmaxf(v, w) : v + w;
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kAttnThreads / 64; ++w) r = MAX ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();  // red is reused by the next reduction
-  return r;
+// one batch of a group's tokens: the lane's dword of each key and value row and the
+// tokens' scales. The loads are buffer loads range-checked against the head's first S
+// tokens: a token past the sequence reads zeros (its score is then set to -inf, so it
+// weighs 0), and no load is predicated.
+struct AttnBatch {
+  uint32_t kw[kAttnU], vw[kAttnU];
+  float ks[kAttnU], vs[kAttnU];
+};
+
+struct AttnRsrc {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
+};
+
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data, no swizzle, range-checked
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+template <int SF16>
+__device__ __forceinline__ void attn_fetch(AttnBatch& r, const AttnRsrc& rs, int t0, int c) {
+#pragma unroll
+  for (int u = 0; u < kAttnU; ++u) {
+    const uint32_t t = (uint32_t)(t0 + u * kAttnGroups);
+    r.kw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, t * 64u + 4u * c, 0, 0);
+    r.vw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs.vc, t * 64u + 4u * c, 0, 0);
+    if constexpr (SF16) {
+      r.ks[u] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.ks, t * 2u, 0, 0));
+      r.vs[u] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.vs, t * 2u, 0, 0));
+    } else {
+      r.ks[u] = bits_f32(__builtin_amdgcn_raw_buffer_load_b32(rs.ks, t * 4u, 0, 0));
+      r.vs[u] = bits_f32(__builtin_amdgcn_raw_buffer_load_b32(rs.vs, t * 4u, 0, 0));
+    }
+  }
+}
+
+template <int SF16>
 __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs a) {
-  __shared__ float sc[kAttnTile];
-  __shared__ float part[kAttnThreads / 16][kAttnD];
-  __shared__ float red[kAttnThreads / 64];
+  __shared__ float part[kAttnGroups][kAttnD];
+  __shared__ float gmax[kAttnGroups], gsum[kAttnGroups];
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh - b * a.H;
   const int kvh = h / (a.H / a.Hkv);
@@ -89,86 +103,76 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
   for (int i = 0; i < 8; ++i) qd[i] = attn_load16(a.q, (int64_t)bh * kAttnD + 8 * c + i, a.q_f16) * a.scale;
 
   const int64_t head = (int64_t)b * a.Hkv + kvh;
-  const uint32_t* krow = (const uint32_t*)(a.kc + head * a.S_cap * 64);
-  const uint32_t* vrow = (const uint32_t*)(a.vc + head * a.S_cap * 64);
-  const int64_t srow = head * a.S_cap;
+  const uint32_t ssz = SF16 ? 2u : 4u;
+  AttnRsrc rs;
+  rs.kc = attn_rsrc(a.kc + head * a.S_cap * 64, (uint32_t)a.S * 64u);
+  rs.vc = attn_rsrc(a.vc + head * a.S_cap * 64, (uint32_t)a.S * 64u);
+  rs.ks = attn_rsrc((const char*)a.ks + head * a.S_cap * ssz, (uint32_t)a.S * ssz);
+  rs.vs = attn_rsrc((const char*)a.vs + head * a.S_cap * ssz, (uint32_t)a.S * ssz);
 
+  // the group's running maximum and sum (equal on its sixteen lanes) and its output dims
   float m_run = -INFINITY, l_run = 0.0f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
-  for (int s0 = 0; s0 < a.S; s0 += kAttnTile) {
-    const int n = min(kAttnTile, a.S - s0);
-    // ---- scores of the tile: sixteen lanes per token, eight dims each; kAttnU tokens per
-    // token group are loaded before any is used, so their latencies overlap
-    float tmax = -INFINITY;
-    for (int t0 = tg; t0 < ((n + 15) & ~15); t0 += kAttnU * (kAttnThreads / 16)) {
-      uint32_t w[kAttnU];
-      float ksv[kAttnU];
+  // per batch: scores (eight products per lane, summed over the sixteen lanes; the xor
+  // butterfly leaves the same bits on every lane), the raised maximum, the rescaled sum
+  // and output, then the value rows weighted by the probabilities. The batch's loads are
+  // all issued before any is used; the other waves of the CU hide their latency. The
+  // batch's first token is always in range.
+  for (int t0 = tg; t0 < a.S; t0 += kAttnU * kAttnGroups) {
+    AttnBatch r;
+    attn_fetch<SF16>(r, rs, t0, c);
+    float sc[kAttnU];
+    float bmax = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kAttnU; ++u) {
-        const int t = t0 + u * (kAttnThreads / 16);
-        const bool ok = t < n;
-        w[u] = ok ? krow[(int64_t)(s0 + t) * 16 + c] : 0u;
-        ksv[u] = ok ? attn_scale(a.ks, srow + s0 + t, a.scale_f16) : 0.0f;
-      }
+    for (int u = 0; u < kAttnU; ++u) {
+      float dot = 0.0f;
 #pragma unroll
-      for (int u = 0; u < kAttnU; ++u) {
-        const int t = t0 + u * (kAttnThreads / 16);
-        float dot = 0.0f;
+      for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], attn_code(r.kw[u], i), dot);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], attn_code(w[u], i), dot);
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-        if (t < n) {
-          const float sv = dot * ksv[u];
-          if (c == 0) sc[t] = sv;
-          tmax = fmaxf(tmax, sv);
-        }
-      }
+      for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      sc[u] = (t0 + u * kAttnGroups < a.S) ? dot * r.ks[u] : -INFINITY;
+      bmax = fmaxf(bmax, sc[u]);
     }
-    const float m_new = fmaxf(m_run, attn_reduce<true>(tmax, red));  // (its barrier publishes sc)
-    // ---- probabilities and the running sum
-    float tsum = 0.0f;
-    for (int t = tid; t < n; t += kAttnThreads) {
-      const float p = __expf(sc[t] - m_new);
-      sc[t] = p;
-      tsum += p;
-    }
-    const float corr = __expf(m_run - m_new);  // 0 on the first tile
-    l_run = l_run * corr + attn_reduce<false>(tsum, red);
-    m_run = m_new;
-    // ---- value rows weighted by the probabilities
+    const float m_new = fmaxf(m_run, bmax);
+    const float corr = __expf(m_run - m_new);  // 0 on the group's first batch
+    l_run *= corr;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= corr;
-    for (int t0 = tg; t0 < n; t0 += kAttnU * (kAttnThreads / 16)) {
-      uint32_t w[kAttnU];
-      float pv[kAttnU];
 #pragma unroll
-      for (int u = 0; u < kAttnU; ++u) {
-        const int t = t0 + u * (kAttnThreads / 16);
-        const bool ok = t < n;
-        w[u] = ok ? vrow[(int64_t)(s0 + t) * 16 + c] : 0u;
-        pv[u] = ok ? sc[t] * attn_scale(a.vs, srow + s0 + t, a.scale_f16) : 0.0f;
-      }
+    for (int u = 0; u < kAttnU; ++u) {
+      const float p = __expf(sc[u] - m_new);  // 0 past the sequence
+      l_run += p;
+      const float pv = p * r.vs[u];
 #pragma unroll
-      for (int u = 0; u < kAttnU; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(pv[u], attn_code(w[u], i), acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pv, attn_code(r.vw[u], i), acc[i]);
     }
-    __syncthreads();  // the next tile overwrites sc
+    m_run = m_new;
   }
 
-  // ---- sum the token groups' partial outputs
+  // ---- merge the groups: out = sum_g e^(m_g - M) acc_g / sum_g e^(m_g - M) l_g; groups
+  // without tokens hold (-inf, 0, 0) and weigh 0 (group 0 always has token 0)
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[tg][8 * c + i] = acc[i];
+  if (c == 0) {
+    gmax[tg] = m_run;
+    gsum[tg] = l_run;
+  }
   __syncthreads();
   if (tid < kAttnD) {
-    float o = 0.0f;
+    float mx = gmax[0];
 #pragma unroll
-    for (int g = 0; g < kAttnThreads / 16; ++g) o += part[g][tid];
-    o /= l_run;
+    for (int g = 1; g < kAttnGroups; ++g) mx = fmaxf(mx, gmax[g]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kAttnGroups; ++g) {
+      const float w = __expf(gmax[g] - mx);
+      o = fmaf(part[g][tid], w, o);
+      l = fmaf(gsum[g], w, l);
+    }
+    o /= l;
     uint16_t bits;
     if (a.q_f16) bits = __builtin_bit_cast(uint16_t, (_Float16)o);
     else bits = (uint16_t)f32_to_bf16(o);
@@ -196,7 +200,9 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16)) return RBQ_EINVAL;
   const uint64_t ssz = (uint64_t)dtype_size(scale_dtype);
   if (!aligned(k_scales, ssz) || !aligned(v_scales, ssz)) return RBQ_EINVAL;
-  if (batch * heads > 0x7FFFFFFF || heads > 0x7FFFFFFF || seq_cap > (int64_t{1} << 30)) return RBQ_ENOTSUP;
+  // buffer offsets within one head's cache are 32-bit: seq * 64 bytes must fit
+  if (batch * heads > 0x7FFFFFFF || heads > 0x7FFFFFFF || seq_cap > (int64_t{1} << 30) || seq >= (int64_t{1} << 26))
+    return RBQ_ENOTSUP;
   AttnArgs a{};
   a.q = q; a.kc = k_codes; a.ks = k_scales; a.vc = v_codes; a.vs = v_scales; a.out = out;
   a.H = (int)heads; a.Hkv = (int)kv_heads; a.S = (int)seq; a.S_cap = (int)seq_cap;
@@ -207,6 +213,9 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
     fprintf(stderr, "rbq: attention_decode_int4kv B=%lld H=%lld Hkv=%lld S=%lld cap=%lld\n", (long long)batch,
             (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap);
   if (diag_fail_launch()) return RBQ_EHIP;
-  hipLaunchKernelGGL(attention_decode_kernel, dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0, stream, a);
+  if (a.scale_f16)
+    hipLaunchKernelGGL(attention_decode_kernel<1>, dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attention_decode_kernel<0>, dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }

@@ -312,3 +312,5 @@ def test_attention_validation(L):
     assert at(q=ctypes.c_void_p(0x10008)) == E
     assert at(scale=float("nan")) == E
     assert at(D=64) == NS
+    assert at(S=1 << 26, cap=1 << 26) == NS  # one head's codes past 32-bit byte offsets
+    assert at(S=16, cap=(1 << 30) + 1) == NS

@@ -4,7 +4,9 @@ kernel and the oracle read the same INT4 key/value codes and scales.
 Tolerance, derived from the kernel's fp32 arithmetic: a score takes 8 fused multiply-adds,
 4 shuffle additions and one product with the key scale, so its error is at most
 d_s = 14 * 2^-24 * |scale| * k_scale[s] * sum_d |q_d code_sd|; the probabilities then err by
-at most 2 max(d_s) + 2^-20 (the exponential) relative, the sums over S tokens by S * 2^-23,
+at most 2 max(d_s) + 2^-20 relative (each is a product of at most S/256 + 3 exponentials:
+the token's own, its group's rescalings and the merge weight, whose arguments add up to the
+score's distance from the maximum), the sums over S tokens by S * 2^-23,
 the output is rounded to bf16 (2^-8 relative covers it), and probabilities below the
 fp32 normal range (2^-126) are flushed to zero:
     |out - ref| <= 2^-8 |ref| + (2 max_s d_s + 2^-20 + S 2^-23) * sum_s p_s |v_sd|
