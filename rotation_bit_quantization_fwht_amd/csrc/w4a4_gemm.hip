@@ -470,28 +470,34 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------- W4A8, group-wise W scales
 // out[m, n] = bf16( sA[m] * sum_g sW[n, g] * sum_{k in group g} qA[m, k] * qW[n, k] ):
-// the int32 sums of each group of G codes (G a power of two dividing K; the kernel is
-// written for any G >= 32 and instantiated for G >= 128) are exact, and are scaled and
-// added in fp32 when the group ends. A 512-thread workgroup computes a 128 x 128 tile; its
-// eight waves hold 64 (m) x 32 (n) wave tiles of 2 x 1 MFMA tiles, with int32 accumulators
-// for the current group and fp32 ones for the finished groups (small enough for two
-// workgroups per CU). Each 32-code sub-step covers 32 consecutive codes (32u .. 32u + 31
-// of a 128-code step), so every group boundary falls between sub-steps: lane half fg
-// takes codes 16 fg .. 16 fg + 15 of the sub-step, one 16-byte A chunk and one 8-byte half
-// of the W chunk. Copies go through a three-stage LDS ring as in the kernels above (A
-// chunks swizzled by key8, W by key); the operand reads of the next sub-step overlap the
-// MFMAs of the current one.
-constexpr int kGBM = 128, kGBN = 128, kGThreads = 512;
+// the int32 sums of each group of G codes (G a power of two dividing K, G >= 128, so every
+// group ends at a 128-code step boundary) are exact, and are scaled and added in fp32 when
+// the group ends. A 512-thread workgroup computes a 128 (m) x 256 (n) tile; its eight
+// waves form a 2 x 4 grid of 64 x 64 wave tiles of 2 x 2 MFMA tiles, with int32
+// accumulators for the current group and fp32 ones for the finished groups. Each 32-code
+// sub-step covers 32 consecutive codes (32u .. 32u + 31 of a step): lane half fg takes
+// codes 16 fg .. 16 fg + 15 of it, one 16-byte A chunk and one 8-byte half of the W chunk.
+// Copies go through a three-stage LDS ring as in the kernels above (A chunks swizzled by
+// key8, W by key), and the operand reads of the next sub-step (and of the next step's
+// first one) overlap the MFMAs of the current one.
+//
+// Fold at a group's end: acc holds 16 x the group sum (W is widened to 16 x code), so the
+// fp32 accumulator collects 16 x sum_g sW * sum_g; the epilogue multiplies by 1/16 (exact)
+// and sA. The next group's first MFMAs take a zero accumulator instead of clearing acc.
+// The group's scales of the wave's 64 output columns are loaded one per lane a group
+// ahead and handed to the lanes that use them through a 64-float LDS area per wave.
+constexpr int kGBM = 128, kGBN = 256, kGThreads = 512;
 constexpr int kGSlotsA = kGBM * kA8Chunks;                // 1024
-constexpr int kGSlots = kGSlotsA + kGBN * kChunks;        // 1536 per stage (24 KB)
-constexpr int kGLoads = kGSlots / kGThreads;              // 3 copies per thread
+constexpr int kGSlots = kGSlotsA + kGBN * kChunks;        // 2048 per stage (32 KB)
+constexpr int kGLoads = kGSlots / kGThreads;              // 4 copies per thread
 constexpr int kGStages = 3;
-static_assert(kGSlots % kGThreads == 0 && kGLoads == 3, "the wait counts below assume three copies");
+constexpr int kGRing = kGStages * kGSlots * 16;           // 96 KB
+static_assert(kGSlots % kGThreads == 0, "whole copies per thread");
+static_assert(8 * 64 * kEpiStride <= kGRing, "the epilogue staging must fit the ring");
 
-// FS: sub-steps per group, up to 4 (groups of 128 codes or more end at step boundaries)
-template <int FS>
 __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g) {
-  __shared__ u32x4_g lds[kGStages * kGSlots];
+  __shared__ u32x4_g lds[kGRing / 16];
+  __shared__ __align__(16) float sw_lds[kGThreads];  // 64 group scales per wave
   const int ntiles = g.tiles_m * g.tiles_n;
   const int b = blockIdx.x;
   const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
@@ -499,11 +505,11 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   const int m0 = tm * kGBM, n0 = tn * kGBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 32;
+  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
   const int abytes = g.K, wbytes = g.K / 2;
   const int steps = g.K / 128;
   const int ngroups = g.K / g.group;
-  const int steps_per_group = g.group >= 128 ? g.group / 128 : 1;
+  const int spg = g.group / 128;  // steps per group
 
   const uint8_t* src[kGLoads];
   int src_step[kGLoads];
@@ -530,96 +536,141 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
       __builtin_amdgcn_global_load_lds((const void*)(src[q] + st * src_step[q]), (void*)(dst + q * kGThreads), 16, 0, 0);
   };
 
-  v16i_t acc[2];
-  float facc[2][16];
+  v16i_t acc[2][2];
+  float facc[2][2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    acc[i] = v16i_t{};
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) facc[i][e] = 0.0f;
-  }
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = v16i_t{};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) facc[i][j][e] = 0.0f;
+    }
 
   const int fr = lane & 31, fg = lane >> 5;
-  int fa_row[2];
+  int fa_row[2], fw_row[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) fa_row[i] = wm0 + i * 32 + fr;
-  const int fw_row = wn0 + fr;
-  // lane's output columns n (MFMA rows): n0 + wn0 + 8 q + 4 fg + e; the scales of a group
-  // are loaded when the previous group is folded, so the fold does not wait for loads
-  // issued after the copies in flight
-  float swg[4][4];
-  auto load_group_scales = [&](int grp) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = min(n0 + wn0 + 8 * q + 4 * fg + e, g.N - 1);
-        swg[q][e] = load_scale(g.sw, n * ngroups + min(grp, ngroups - 1), g.scale_f16);
-      }
-  };
-  auto fold = [&](int grp) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          facc[i][4 * q + e] += (float)(acc[i][4 * q + e] >> 4) * swg[q][e];
-          acc[i][4 * q + e] = 0;
-        }
-    load_group_scales(grp + 1);
-  };
-  load_group_scales(0);
+  for (int j = 0; j < 2; ++j) fw_row[j] = wn0 + j * 32 + fr;
 
-  // the operands of one sub-step: two A chunks (m blocks i) and one W chunk
-  auto read_sub = [&](const u32x4_g* sb, int u, u32x4_g (&ca)[2], u32x4_g& cw) {
+  // lane l loads the scale of output column n0 + wn0 + l for group grp
+  const int64_t sw_row = (int64_t)min(n0 + wn0 + lane, g.N - 1) * ngroups;
+  auto load_sw = [&](int grp) {
+    const int64_t i = sw_row + min(grp, ngroups - 1);
+    return g.scale_f16 ? (float)((const _Float16*)g.sw)[i] : ((const float*)g.sw)[i];
+  };
+  float sw_cur = load_sw(0);
+  float* swl = sw_lds + wave * 64;
+
+  // acc[i][j] element 4q + e is output (m = wm0 + 32 i + fr, n = wn0 + 32 j + 8 q + 4 fg + e)
+  auto fold = [&]() {
+    swl[lane] = sw_cur;  // the wave's own 64 floats; LDS operations of a wave stay in order
+    float swv[2][4][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *(const f32x4*)(swl + 32 * j + 8 * q + 4 * fg);
+        swv[j][q][0] = v.x;
+        swv[j][q][1] = v.y;
+        swv[j][q][2] = v.z;
+        swv[j][q][3] = v.w;
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            facc[i][j][4 * q + e] = fmaf((float)acc[i][j][4 * q + e], swv[j][q][e], facc[i][j][4 * q + e]);
+  };
+
+  auto read_sub = [&](int step, int u, u32x4_g (&ca)[2], u32x4_g (&cw)[2]) {
+    const u32x4_g* sb = lds + (step % kGStages) * kGSlots;
 #pragma unroll
     for (int i = 0; i < 2; ++i) ca[i] = sb[swz8(fa_row[i], 2 * u + fg)];
-    cw = sb[kGSlotsA + swz(fw_row, u)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) cw[j] = sb[kGSlotsA + swz(fw_row[j], u)];
+  };
+  auto prep = [&](const u32x4_g (&ca)[2], const u32x4_g (&cw)[2], v4i_t (&ya)[2], v4i_t (&yw)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ya[i] = order_like_widen(ca[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) yw[j] = fg ? widen(cw[j][2], cw[j][3]) : widen(cw[j][0], cw[j][1]);
+  };
+  auto mma_sub = [&](const v4i_t (&ya)[2], const v4i_t (&yw)[2], bool fresh) {
+    if (fresh) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], v16i_t{}, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], acc[i][j], 0, 0, 0);
+    }
   };
 
+  // at the top of iteration s steps s and s + 1 are published and the operands of
+  // sub-step 0 of step s are read
   issue_copies(0);
   issue_copies(1);
+  wait_copies_and_sync<0>();
+  u32x4_g ca[2], cw[2];
+  v4i_t ya[2], yw[2];
+  read_sub(0, 0, ca, cw);
   for (int s = 0; s < steps; ++s) {
-    wait_copies_and_sync<kGLoads>();  // publishes step s (step s + 1 may stay in flight)
-    const u32x4_g* sb = lds + (s % kGStages) * kGSlots;
-    u32x4_g ca[2], cw;
-    read_sub(sb, 0, ca, cw);
+    issue_copies(s + 2);  // its stage last held step s - 1, finished before the last barrier
+    const bool fresh = s % spg == 0;       // a group starts with this step
+    const bool ends = (s + 1) % spg == 0;  // and one ends with it
+    // the next group's scale, loaded a whole step before the barrier waits for it
+    const float sw_nx = ends ? load_sw((s + 1) / spg) : 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      v4i_t ya[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) ya[i] = order_like_widen(ca[i]);
-      const v4i_t yw = fg ? widen(cw[2], cw[3]) : widen(cw[0], cw[1]);
-      if (u < 3) read_sub(sb, u + 1, ca, cw);  // the next sub-step's reads overlap these MFMAs
-#pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw, ya[i], acc[i], 0, 0, 0);
-      if constexpr (FS < 4) {
-        if ((u + 1) % FS == 0) fold((4 * s + u) / FS);
-      }
+      prep(ca, cw, ya, yw);
+      if (u < 3) read_sub(s, u + 1, ca, cw);
+      else read_sub(s + 1, 0, ca, cw);  // (after the last step: a stale stage, never used)
+      mma_sub(ya, yw, fresh && u == 0);
     }
-    if constexpr (FS == 4) {
-      if ((s + 1) % steps_per_group == 0) fold(s / steps_per_group);
+    if (ends) {
+      fold();
+      sw_cur = sw_nx;
     }
-    // every wave is done with step s - 1's stage (it passed the barrier above after
-    // reading it), which step s + 2 now reuses
-    issue_copies(s + 2);
+    wait_copies_and_sync<0>();  // publishes step s + 2
   }
 
+  // epilogue: scale, round, stage each wave's 64 x 64 bf16 tile in LDS (the ring is free
+  // after the last barrier) and write whole 128-byte row segments
+  char* stage = (char*)lds + wave * 64 * kEpiStride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm0 + i * 32 + fr;
-    if (m >= g.M) continue;
-    const float sam = load_scale(g.sa, m, g.scale_f16);
+    const float sam = load_scale(g.sa, min(m0 + wm0 + i * 32 + fr, g.M - 1), g.scale_f16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + wn0 + 8 * q + 4 * fg;
-      if (n >= g.N) continue;
-      uint32_t bits[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bits[e] = f32_to_bf16(facc[i][4 * q + e] * sam);
-      *(u32x2*)(g.out + (int64_t)m * g.N + n) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
-    }
+      for (int q = 0; q < 4; ++q) {
+        uint32_t bits[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits[e] = f32_to_bf16((facc[i][j][4 * q + e] * 0.0625f) * sam);
+        *(u32x2*)(stage + (i * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
+            u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+      }
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int rloc = it * 8 + (lane >> 3);
+    const u32x4 v = *(const u32x4*)(stage + rloc * kEpiStride + (lane & 7) * 16);
+    const int m = m0 + wm0 + rloc;
+    const int n = n0 + wn0 + (lane & 7) * 8;
+    if (m < g.M && n < g.N) *(u32x4*)(g.out + (int64_t)m * g.N + n) = v;
   }
 }
 
@@ -681,7 +732,7 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
   if (st != RBQ_OK) return st;
   if (group < 32 || group > K || !is_pow2(group) || K % group != 0) return RBQ_EINVAL;
   // groups of 32 or 64 codes would end inside a K step: their per-group fold (an fp32
-  // multiply-add per accumulator every one or two MFMAs) is not instantiated
+  // multiply-add per accumulator every one or two MFMAs) is not built
   if (group < 128) return RBQ_ENOTSUP;
   if (M == 0 || N == 0) return RBQ_OK;
   GemmArgs g{};
@@ -698,6 +749,6 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
     fprintf(stderr, "rbq: w4a8_gemm_grouped M=%lld N=%lld K=%lld group=%lld tiles=%lld\n", (long long)M,
             (long long)N, (long long)K, (long long)group, (long long)ntiles);
   if (diag_fail_launch()) return RBQ_EHIP;
-  hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<4>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
+  hipLaunchKernelGGL(w4a8_gemm_grouped_kernel, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
