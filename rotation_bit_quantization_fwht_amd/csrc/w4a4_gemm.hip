@@ -41,6 +41,7 @@ namespace rbq {
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef int v16i_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_g __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_g __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
   const uint8_t* qa;   // [M, K/2]
@@ -495,9 +496,16 @@ constexpr int kGRing = kGStages * kGSlots * 16;           // 96 KB
 static_assert(kGSlots % kGThreads == 0, "whole copies per thread");
 static_assert(8 * 64 * kEpiStride <= kGRing, "the epilogue staging must fit the ring");
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data, no swizzle, range-checked
+
+template <int SF16>
 __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g) {
-  __shared__ u32x4_g lds[kGRing / 16];
-  __shared__ __align__(16) float sw_lds[kGThreads];  // 64 group scales per wave
+  // one LDS object (the ring, then 64 group scales per wave): with a second object the
+  // compiler tags accesses with alias scopes and then waits for the copies in flight
+  // before every read of the ring
+  __shared__ u32x4_g lds[kGRing / 16 + kGThreads / 4];
+  float* const sw_lds = (float*)(lds + kGRing / 16);
   const int ntiles = g.tiles_m * g.tiles_n;
   const int b = blockIdx.x;
   const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
@@ -509,31 +517,38 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   const int abytes = g.K, wbytes = g.K / 2;
   const int steps = g.K / 128;
   const int ngroups = g.K / g.group;
-  const int spg = g.group / 128;  // steps per group
+  const int spg_mask = g.group / 128 - 1;  // steps per group, a power of two, minus one
+  const int spg_log = __builtin_ctz(g.group / 128);
 
-  const uint8_t* src[kGLoads];
-  int src_step[kGLoads];
+  // copies q = 0, 1 fill A slots and q = 2, 3 W slots, as buffer loads into LDS: each
+  // lane keeps a 32-bit offset from the tile's first row (rows clamped to the matrix) and
+  // the step offset is a uniform register, so the copies hold no address registers
+  static_assert(kGSlotsA == 2 * kGThreads, "copies 0 and 1 are the A rows");
+  uint32_t coff[kGLoads];
 #pragma unroll
   for (int q = 0; q < kGLoads; ++q) {
     const int slot = q * kGThreads + tid;
-    if (slot < kGSlotsA) {
+    if (q < 2) {
       const int r = slot >> 3;
       const int j = (slot & 7) ^ swz_key8(r);
-      src[q] = g.qa + (int64_t)min(m0 + r, g.M - 1) * abytes + j * 16;
-      src_step[q] = 128;
+      coff[q] = (uint32_t)((min(m0 + r, g.M - 1) - m0) * abytes + j * 16);
     } else {
       const int r = (slot - kGSlotsA) >> 2;
       const int j = (slot & 3) ^ swz_key(r);
-      src[q] = g.qw + (int64_t)min(n0 + r, g.N - 1) * wbytes + j * 16;
-      src_step[q] = 64;
+      coff[q] = (uint32_t)((min(n0 + r, g.N - 1) - n0) * wbytes + j * 16);
     }
   }
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.qa + (int64_t)m0 * abytes), (short)0, min(kGBM, g.M - m0) * abytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.qw + (int64_t)n0 * wbytes), (short)0, min(kGBN, g.N - n0) * wbytes, kBufferWord3);
   auto issue_copies = [&](int step) {
     u32x4_g* dst = lds + (step % kGStages) * kGSlots + wave * 64;
     const int st = min(step, steps - 1);
 #pragma unroll
     for (int q = 0; q < kGLoads; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(src[q] + st * src_step[q]), (void*)(dst + q * kGThreads), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? arsrc : wrsrc, (lds_ptr_t)(dst + q * kGThreads), 16,
+                                               coff[q], q < 2 ? st * 128 : st * 64, 0, 0);
   };
 
   v16i_t acc[2][2];
@@ -554,18 +569,27 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
 #pragma unroll
   for (int j = 0; j < 2; ++j) fw_row[j] = wn0 + j * 32 + fr;
 
-  // lane l loads the scale of output column n0 + wn0 + l for group grp
-  const int64_t sw_row = (int64_t)min(n0 + wn0 + lane, g.N - 1) * ngroups;
-  auto load_sw = [&](int grp) {
-    const int64_t i = sw_row + min(grp, ngroups - 1);
-    return g.scale_f16 ? (float)((const _Float16*)g.sw)[i] : ((const float*)g.sw)[i];
+  // lane l loads the scale of output column n0 + wn0 + l for group grp, kept as its bits
+  // until the fold (a conversion at the load would wait for the load at once)
+  // (a buffer load: a persistent lane offset and a uniform group offset, no address
+  // registers that later instructions would have to wait for)
+  constexpr int ssz = SF16 ? 2 : 4;
+  const int nw = min(n0 + wn0, g.N - 1);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)g.sw + (int64_t)nw * ngroups * ssz), (short)0, 64 * ngroups * ssz, kBufferWord3);
+  const uint32_t soff = (uint32_t)((min(n0 + wn0 + lane, g.N - 1) - nw) * ngroups * ssz);
+  auto load_sw = [&](int grp) -> uint32_t {
+    const int go = min(grp, ngroups - 1) * ssz;
+    if constexpr (SF16) return __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff, go, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff, go, 0);
   };
-  float sw_cur = load_sw(0);
+  uint32_t sw_cur = load_sw(0);
   float* swl = sw_lds + wave * 64;
 
   // acc[i][j] element 4q + e is output (m = wm0 + 32 i + fr, n = wn0 + 32 j + 8 q + 4 fg + e)
   auto fold = [&]() {
-    swl[lane] = sw_cur;  // the wave's own 64 floats; LDS operations of a wave stay in order
+    // the wave's own 64 floats; LDS operations of a wave stay in order
+    swl[lane] = SF16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sw_cur) : bits_f32(sw_cur);
     float swv[2][4][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -588,18 +612,25 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
             facc[i][j][4 * q + e] = fmaf((float)acc[i][j][4 * q + e], swv[j][q][e], facc[i][j][4 * q + e]);
   };
 
-  auto read_sub = [&](int step, int u, u32x4_g (&ca)[2], u32x4_g (&cw)[2]) {
+  // lane half fg reads the 8 bytes (16 codes) of the W chunk it uses. The second read's
+  // address is made opaque so the two are not merged into one ds_read2, which the
+  // compiler would make wait for the copies in flight.
+  auto read_sub = [&](int step, int u, u32x4_g (&ca)[2], u32x2_g (&cw)[2]) {
     const u32x4_g* sb = lds + (step % kGStages) * kGSlots;
 #pragma unroll
     for (int i = 0; i < 2; ++i) ca[i] = sb[swz8(fa_row[i], 2 * u + fg)];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) cw[j] = sb[kGSlotsA + swz(fw_row[j], u)];
+    for (int j = 0; j < 2; ++j) {
+      uint32_t slot = (uint32_t)(kGSlotsA + swz(fw_row[j], u));
+      if (j) asm volatile("" : "+v"(slot));
+      cw[j] = ((const u32x2_g*)(sb + slot))[fg];
+    }
   };
-  auto prep = [&](const u32x4_g (&ca)[2], const u32x4_g (&cw)[2], v4i_t (&ya)[2], v4i_t (&yw)[2]) {
+  auto prep = [&](const u32x4_g (&ca)[2], const u32x2_g (&cw)[2], v4i_t (&ya)[2], v4i_t (&yw)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) ya[i] = order_like_widen(ca[i]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) yw[j] = fg ? widen(cw[j][2], cw[j][3]) : widen(cw[j][0], cw[j][1]);
+    for (int j = 0; j < 2; ++j) yw[j] = widen(cw[j][0], cw[j][1]);
   };
   auto mma_sub = [&](const v4i_t (&ya)[2], const v4i_t (&yw)[2], bool fresh) {
     if (fresh) {
@@ -622,15 +653,16 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   issue_copies(0);
   issue_copies(1);
   wait_copies_and_sync<0>();
-  u32x4_g ca[2], cw[2];
+  u32x4_g ca[2];
+  u32x2_g cw[2];
   v4i_t ya[2], yw[2];
   read_sub(0, 0, ca, cw);
   for (int s = 0; s < steps; ++s) {
     issue_copies(s + 2);  // its stage last held step s - 1, finished before the last barrier
-    const bool fresh = s % spg == 0;       // a group starts with this step
-    const bool ends = (s + 1) % spg == 0;  // and one ends with it
+    const bool fresh = (s & spg_mask) == 0;       // a group starts with this step
+    const bool ends = ((s + 1) & spg_mask) == 0;  // and one ends with it
     // the next group's scale, loaded a whole step before the barrier waits for it
-    const float sw_nx = ends ? load_sw((s + 1) / spg) : 0.0f;
+    const uint32_t sw_nx = ends ? load_sw((s + 1) >> spg_log) : 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       prep(ca, cw, ya, yw);
@@ -749,6 +781,9 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
     fprintf(stderr, "rbq: w4a8_gemm_grouped M=%lld N=%lld K=%lld group=%lld tiles=%lld\n", (long long)M,
             (long long)N, (long long)K, (long long)group, (long long)ntiles);
   if (diag_fail_launch()) return RBQ_EHIP;
-  hipLaunchKernelGGL(w4a8_gemm_grouped_kernel, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
+  if (g.scale_f16)
+    hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<1>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<0>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
