@@ -97,6 +97,22 @@ def test_attention_fp32_scales_and_peaked_scores(rbq):
     check(out, q, kc, ks, vc, vs, 4.0)
 
 
+def test_attention_fp16_query_and_output(rbq):
+    # the query (and so the output) in fp16; the bound's 2^-8 output term covers fp16 rounding
+    B, H, Hkv, S, cap = 2, 8, 4, 700, 768
+    print("case attention fp16 query", flush=True)
+    _, kc, ks, vc, vs = make(41, B, H, Hkv, S, cap)
+    q = np.random.default_rng(42).standard_normal((B, H, 128)).astype(np.float16).astype(np.float64)
+    pk = lambda c: torch.from_numpy(oracle.pack_nibbles(c.reshape(-1, 128)).reshape(c.shape[:-1] + (64,))).cuda()
+    qd = torch.from_numpy(q.astype(np.float16)).cuda()
+    scale = 1.0 / math.sqrt(128)
+    out = rbq.attention_decode_int4kv(qd, pk(kc), torch.from_numpy(ks).cuda(), pk(vc), torch.from_numpy(vs).cuda(),
+                                      scale, seq=S)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16
+    check(out, q, kc[:, :, :S], ks[:, :, :S], vc[:, :, :S], vs[:, :, :S], scale)
+
+
 def test_attention_end_to_end_with_the_kv_cache_writers(rbq):
     """Q and K through kv_rotate_quant (Q rotated only, K rotated and quantized), V through
     hadamard_quant_int4 without rotation: the kernel reads exactly what the writers wrote,
