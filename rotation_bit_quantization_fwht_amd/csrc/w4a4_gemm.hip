@@ -478,9 +478,9 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
 // accumulators for the current group and fp32 ones for the finished groups. Each 32-code
 // sub-step covers 32 consecutive codes (32u .. 32u + 31 of a step): lane half fg takes
 // codes 16 fg .. 16 fg + 15 of it, one 16-byte A chunk and one 8-byte half of the W chunk.
-// Copies go through a three-stage LDS ring as in the kernels above (A chunks swizzled by
-// key8, W by key), and the operand reads of the next sub-step (and of the next step's
-// first one) overlap the MFMAs of the current one.
+// Copies go through a four-stage LDS ring as in the W4A4 kernel (A chunks swizzled by key8,
+// W by key; the copies of a step are issued two steps ahead), and the operand reads of the
+// next sub-step (and of the next step's first one) overlap the MFMAs of the current one.
 //
 // Fold at a group's end: acc holds 16 x the group sum (W is widened to 16 x code), so the
 // fp32 accumulator collects 16 x sum_g sW * sum_g; the epilogue multiplies by 1/16 (exact)
@@ -491,8 +491,8 @@ constexpr int kGBM = 128, kGBN = 256, kGThreads = 512;
 constexpr int kGSlotsA = kGBM * kA8Chunks;                // 1024
 constexpr int kGSlots = kGSlotsA + kGBN * kChunks;        // 2048 per stage (32 KB)
 constexpr int kGLoads = kGSlots / kGThreads;              // 4 copies per thread
-constexpr int kGStages = 3;
-constexpr int kGRing = kGStages * kGSlots * 16;           // 96 KB
+constexpr int kGStages = 4;
+constexpr int kGRing = kGStages * kGSlots * 16;           // 128 KB
 static_assert(kGSlots % kGThreads == 0, "whole copies per thread");
 static_assert(8 * 64 * kEpiStride <= kGRing, "the epilogue staging must fit the ring");
 
@@ -648,21 +648,23 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
     }
   };
 
-  // at the top of iteration s steps s and s + 1 are published and the operands of
-  // sub-step 0 of step s are read
+  // four-stage ring: at the top of iteration s steps s and s + 1 are published, the
+  // operands of sub-step 0 of step s are read and the copies for step s + 2 may be in
+  // flight
   issue_copies(0);
   issue_copies(1);
-  wait_copies_and_sync<0>();
+  issue_copies(2);
+  wait_copies_and_sync<kGLoads>();  // steps 0 and 1 published
   u32x4_g ca[2];
   u32x2_g cw[2];
   v4i_t ya[2], yw[2];
   read_sub(0, 0, ca, cw);
   for (int s = 0; s < steps; ++s) {
-    issue_copies(s + 2);  // its stage last held step s - 1, finished before the last barrier
     const bool fresh = (s & spg_mask) == 0;       // a group starts with this step
     const bool ends = ((s + 1) & spg_mask) == 0;  // and one ends with it
     // the next group's scale, loaded a whole step before the barrier waits for it
     const uint32_t sw_nx = ends ? load_sw((s + 1) >> spg_log) : 0u;
+    issue_copies(s + 3);  // its stage last held step s - 1, finished before the last barrier
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       prep(ca, cw, ya, yw);
@@ -674,11 +676,14 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
       fold();
       sw_cur = sw_nx;
     }
-    wait_copies_and_sync<0>();  // publishes step s + 2
+    // publish step s + 2: this wave's copies for it (and everything issued before them)
+    // are done when at most those of step s + 3 are in flight
+    wait_copies_and_sync<kGLoads>();
   }
+  wait_copies_and_sync<0>();  // no copy is in flight when the ring becomes the staging area
 
   // epilogue: scale, round, stage each wave's 64 x 64 bf16 tile in LDS (the ring is free
-  // after the last barrier) and write whole 128-byte row segments
+  // after the barrier above) and write whole 128-byte row segments
   char* stage = (char*)lds + wave * 64 * kEpiStride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
