@@ -190,11 +190,15 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
     // barrier that ended the previous iteration
     issue_copies(s + 3);
     read_chunk(s, 1, fa1, fw1);
+    // the scheduler would otherwise sink the fragment reads next to their first use and
+    // wait for them at once; here they are issued before the MFMAs they overlap
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[0], xw[0]);
     widen_sub(fa0, fw0, 1, xa[1], xw[1]);
     mma_sub(xa[1], xw[1]);
     widen_sub(fa1, fw1, 0, xa[0], xw[0]);
     read_chunk(s + 1, 0, fa0, fw0);  // (after the last step: a stale stage, never used)
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[0], xw[0]);
     widen_sub(fa1, fw1, 1, xa[1], xw[1]);
     mma_sub(xa[1], xw[1]);
@@ -391,18 +395,23 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
   prep(fa, fw0, 0, xa[0], xw[0]);
   for (int s = 0; s < steps; ++s) {
     issue_copies(s + 2);  // its stage last held step s - 1, finished before the last barrier
+    // (each sched_barrier keeps the fragment reads ahead of the MFMAs they overlap)
     read_a(s, 1, fa);
     read_w(s, 1, fw1);
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[0], xw[0]);
     prep(fa, fw0, 1, xa[1], xw[1]);
     read_a(s, 2, fa);
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[1], xw[1]);
     prep(fa, fw1, 0, xa[0], xw[0]);
     read_a(s, 3, fa);
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[0], xw[0]);
     prep(fa, fw1, 1, xa[1], xw[1]);
     read_a(s + 1, 0, fa);   // (after the last step: a stale stage, never used)
     read_w(s + 1, 0, fw0);
+    __builtin_amdgcn_sched_barrier(0);
     mma_sub(xa[1], xw[1]);
     prep(fa, fw0, 0, xa[0], xw[0]);
     wait_copies_and_sync<0>();  // publishes step s + 2
