@@ -419,9 +419,11 @@ def main():
         rbq.hadamard_quant_int4(wgt, rotated=wr)
         del wgt
         qwg, swg = rbq.quantize_groups_int4(wr, 256)
+        qwg32, swg32 = rbq.quantize_groups_int4(wr, 32)  # the other group size of the ExecuTorch export
         outg = torch.empty_like(out)
         for name, fn in (("quantize_groups_int4", lambda: rbq.quantize_groups_int4(wr, 256, codes=qwg, scales=swg)),
-                         ("w4a8_gemm_grouped", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg, swg, 256, out=outg))):
+                         ("w4a8_gemm_grouped", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg, swg, 256, out=outg)),
+                         ("w4a8_gemm_grouped_32", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg32, swg32, 32, out=outg))):
             fn()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -431,16 +433,17 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) * 1e-3 / 20
-            if name == "w4a8_gemm_grouped":
+            if name.startswith("w4a8_gemm_grouped"):
+                gsz = 32 if name.endswith("_32") else 256
                 extras[name] = {"workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], weight scales per "
-                                            "256 codes, bf16 out",
+                                            f"{gsz} codes, bf16 out",
                                 "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
                                 "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
             else:
                 nbytes = GEMM_N * GEMM_K * 4 + GEMM_N * GEMM_K // 2 + GEMM_N * (GEMM_K // 256) * 2
                 extras[name] = {"workload": "rotated fp32 weights [11008, 4096] -> packed INT4, fp16 scales per 256",
                                 "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2)}
-        del wr, qwg, swg, outg
+        del wr, qwg, swg, qwg32, swg32, outg
         # context only: the vendor library's int8 GEMM (torch._int_mm, hipBLASLt) on the same
         # shape with the codes already unpacked to int8 and a plain int32 result (no scales)
         try:

@@ -261,8 +261,7 @@ rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8
  *  sA     [M]; sW [N, K/group] row-major; both scale_dtype (F16 or F32).
  *  group  power of two, 32 <= group <= K, dividing K.
  *  out_bf16 bf16 [M, N] row-major, 16-byte aligned.
- * Errors: as w4a4_gemm, plus RBQ_EINVAL for a bad group size and RBQ_ENOTSUP for groups of
- * 32 or 64 (the per-group fold is instantiated for groups of 128 codes or more).
+ * Errors: as w4a4_gemm, plus RBQ_EINVAL for a bad group size.
  */
 rbq_status w4a8_gemm_grouped(const int8_t *qA, const void *sA, const uint8_t *qW, const void *sW,
                              rbq_dtype scale_dtype, int64_t group, int64_t M, int64_t N,

@@ -480,22 +480,25 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------- W4A8, group-wise W scales
 // out[m, n] = bf16( sA[m] * sum_g sW[n, g] * sum_{k in group g} qA[m, k] * qW[n, k] ):
-// the int32 sums of each group of G codes (G a power of two dividing K, G >= 128, so every
-// group ends at a 128-code step boundary) are exact, and are scaled and added in fp32 when
-// the group ends. A 512-thread workgroup computes a 128 (m) x 256 (n) tile; its eight
-// waves form a 2 x 4 grid of 64 x 64 wave tiles of 2 x 2 MFMA tiles, with int32
-// accumulators for the current group and fp32 ones for the finished groups. Each 32-code
-// sub-step covers 32 consecutive codes (32u .. 32u + 31 of a step): lane half fg takes
-// codes 16 fg .. 16 fg + 15 of it, one 16-byte A chunk and one 8-byte half of the W chunk.
-// Copies go through a four-stage LDS ring as in the W4A4 kernel (A chunks swizzled by key8,
-// W by key; the copies of a step are issued two steps ahead), and the operand reads of the
-// next sub-step (and of the next step's first one) overlap the MFMAs of the current one.
+// the int32 sums of each group of G codes (G a power of two dividing K, G >= 32) are
+// exact, and are scaled and added in fp32 when the group ends. A 512-thread workgroup
+// computes a 128 (m) x 256 (n) tile; its eight waves form a 2 x 4 grid of 64 x 64 wave
+// tiles of 2 x 2 MFMA tiles, with int32 accumulators for the current group and fp32 ones
+// for the finished groups. Each 32-code sub-step covers 32 consecutive codes (32u .. 32u +
+// 31 of a 128-code step), so every group boundary falls between sub-steps (FS sub-steps
+// per group: 1 for groups of 32, 2 for 64, and whole steps for 128 or more): lane half fg
+// takes codes 16 fg .. 16 fg + 15 of it, one 16-byte A chunk and one 8-byte half of the W
+// chunk. Copies go through a four-stage LDS ring as in the W4A4 kernel (A chunks swizzled
+// by key8, W by key; the copies of a step are issued two steps ahead), and the operand
+// reads of the next sub-step (and of the next step's first one) overlap the MFMAs of the
+// current one.
 //
-// Fold at a group's end: acc holds 16 x the group sum (W is widened to 16 x code), so the
-// fp32 accumulator collects 16 x sum_g sW * sum_g; the epilogue multiplies by 1/16 (exact)
-// and sA. The next group's first MFMAs take a zero accumulator instead of clearing acc.
-// The group's scales of the wave's 64 output columns are loaded one per lane a group
-// ahead and handed to the lanes that use them through a 64-float LDS area per wave.
+// A rows are MFMA operand A and W rows operand B, so each lane holds one output column n
+// per W block (and sixteen rows m): the fold at a group's end multiplies the lane's
+// accumulators by one of two group scales, which the lane loads itself a step ahead. acc
+// holds 16 x the group sum (W is widened to 16 x code), so the fp32 accumulator collects
+// 16 x sum_g sW * sum_g; the epilogue multiplies by 1/16 (exact) and sA. The next group's
+// first MFMAs take a zero accumulator instead of clearing acc.
 constexpr int kGBM = 128, kGBN = 256, kGThreads = 512;
 constexpr int kGSlotsA = kGBM * kA8Chunks;                // 1024
 constexpr int kGSlots = kGSlotsA + kGBN * kChunks;        // 2048 per stage (32 KB)
@@ -508,13 +511,10 @@ static_assert(8 * 64 * kEpiStride <= kGRing, "the epilogue staging must fit the 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data, no swizzle, range-checked
 
-template <int SF16>
+// FS: sub-steps per group (1, 2), or 4 for groups of 128 codes or more
+template <int SF16, int FS>
 __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g) {
-  // one LDS object (the ring, then 64 group scales per wave): with a second object the
-  // compiler tags accesses with alias scopes and then waits for the copies in flight
-  // before every read of the ring
-  __shared__ u32x4_g lds[kGRing / 16 + kGThreads / 4];
-  float* const sw_lds = (float*)(lds + kGRing / 16);
+  __shared__ u32x4_g lds[kGRing / 16];
   const int ntiles = g.tiles_m * g.tiles_n;
   const int b = blockIdx.x;
   const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
@@ -526,8 +526,9 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   const int abytes = g.K, wbytes = g.K / 2;
   const int steps = g.K / 128;
   const int ngroups = g.K / g.group;
-  const int spg_mask = g.group / 128 - 1;  // steps per group, a power of two, minus one
-  const int spg_log = __builtin_ctz(g.group / 128);
+  // groups of 128 codes or more: steps per group (a power of two), as a mask and a shift
+  const int spg_mask = FS == 4 ? g.group / 128 - 1 : 0;
+  const int spg_log = FS == 4 ? __builtin_ctz(g.group / 128) : 0;
 
   // copies q = 0, 1 fill A slots and q = 2, 3 W slots, as buffer loads into LDS: each
   // lane keeps a 32-bit offset from the tile's first row (rows clamped to the matrix) and
@@ -578,47 +579,35 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
 #pragma unroll
   for (int j = 0; j < 2; ++j) fw_row[j] = wn0 + j * 32 + fr;
 
-  // lane l loads the scale of output column n0 + wn0 + l for group grp, kept as its bits
-  // until the fold (a conversion at the load would wait for the load at once)
-  // (a buffer load: a persistent lane offset and a uniform group offset, no address
-  // registers that later instructions would have to wait for)
+  // the lane's two output columns n = n0 + wn0 + 32 j + fr: their group scales, loaded as
+  // bits (a buffer load: a persistent lane offset and a uniform group offset, so no address
+  // registers that later instructions would have to wait for) and converted at the fold
   constexpr int ssz = SF16 ? 2 : 4;
   const int nw = min(n0 + wn0, g.N - 1);
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const char*)g.sw + (int64_t)nw * ngroups * ssz), (short)0, 64 * ngroups * ssz, kBufferWord3);
-  const uint32_t soff = (uint32_t)((min(n0 + wn0 + lane, g.N - 1) - nw) * ngroups * ssz);
-  auto load_sw = [&](int grp) -> uint32_t {
+  uint32_t soff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) soff[j] = (uint32_t)((min(n0 + wn0 + 32 * j + fr, g.N - 1) - nw) * ngroups * ssz);
+  auto load_sw = [&](int j, int grp) -> uint32_t {
     const int go = min(grp, ngroups - 1) * ssz;
-    if constexpr (SF16) return __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff, go, 0);
-    else return __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff, go, 0);
+    if constexpr (SF16) return __builtin_amdgcn_raw_buffer_load_b16(srsrc, soff[j], go, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff[j], go, 0);
   };
-  uint32_t sw_cur = load_sw(0);
-  float* swl = sw_lds + wave * 64;
+  auto sw_value = [&](uint32_t bits) {
+    return SF16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)bits) : bits_f32(bits);
+  };
 
-  // acc[i][j] element 4q + e is output (m = wm0 + 32 i + fr, n = wn0 + 32 j + 8 q + 4 fg + e)
-  auto fold = [&]() {
-    // the wave's own 64 floats; LDS operations of a wave stay in order
-    swl[lane] = SF16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sw_cur) : bits_f32(sw_cur);
-    float swv[2][4][4];
+  // acc[i][j] element 4q + e is output (m = wm0 + 32 i + 8 q + 4 fg + e, n = wn0 + 32 j + fr)
+  auto fold = [&](const uint32_t (&bits)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const float sw = sw_value(bits[j]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *(const f32x4*)(swl + 32 * j + 8 * q + 4 * fg);
-        swv[j][q][0] = v.x;
-        swv[j][q][1] = v.y;
-        swv[j][q][2] = v.z;
-        swv[j][q][3] = v.w;
-      }
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            facc[i][j][4 * q + e] = fmaf((float)acc[i][j][4 * q + e], swv[j][q][e], facc[i][j][4 * q + e]);
+        for (int e = 0; e < 16; ++e) facc[i][j][e] = fmaf((float)acc[i][j][e], sw, facc[i][j][e]);
+    }
   };
 
   // lane half fg reads the 8 bytes (16 codes) of the W chunk it uses. The second read's
@@ -647,15 +636,24 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], v16i_t{}, 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ya[i], yw[j], v16i_t{}, 0, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw[j], ya[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ya[i], yw[j], acc[i][j], 0, 0, 0);
     }
   };
+
+  // scales of the groups the current step ends (FS < 4: 4 / FS groups; FS = 4: the one
+  // group that ends with some step), loaded a step ahead
+  constexpr int GPS = FS == 4 ? 1 : 4 / FS;
+  uint32_t swc[GPS][2];
+#pragma unroll
+  for (int gi = 0; gi < GPS; ++gi)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) swc[gi][j] = load_sw(j, gi);
 
   // four-stage ring: at the top of iteration s steps s and s + 1 are published, the
   // operands of sub-step 0 of step s are read and the copies for step s + 2 may be in
@@ -669,21 +667,38 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   v4i_t ya[2], yw[2];
   read_sub(0, 0, ca, cw);
   for (int s = 0; s < steps; ++s) {
-    const bool fresh = (s & spg_mask) == 0;       // a group starts with this step
-    const bool ends = ((s + 1) & spg_mask) == 0;  // and one ends with it
-    // the next group's scale, loaded a whole step before the barrier waits for it
-    const uint32_t sw_nx = ends ? load_sw((s + 1) >> spg_log) : 0u;
+    // the scales the next step needs, loaded a whole step before the barrier waits for them
+    const bool fresh = FS == 4 ? (s & spg_mask) == 0 : true;       // a group starts with this step
+    const bool ends = FS == 4 ? ((s + 1) & spg_mask) == 0 : true;  // and one ends with it
+    uint32_t swn[GPS][2];
+#pragma unroll
+    for (int gi = 0; gi < GPS; ++gi)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        swn[gi][j] = !ends ? 0u : load_sw(j, FS == 4 ? ((s + 1) >> spg_log) : (s + 1) * GPS + gi);
     issue_copies(s + 3);  // its stage last held step s - 1, finished before the last barrier
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       prep(ca, cw, ya, yw);
       if (u < 3) read_sub(s, u + 1, ca, cw);
       else read_sub(s + 1, 0, ca, cw);  // (after the last step: a stale stage, never used)
-      mma_sub(ya, yw, fresh && u == 0);
+      mma_sub(ya, yw, FS == 4 ? (fresh && u == 0) : (u % FS == 0));
+      if constexpr (FS < 4) {
+        if ((u + 1) % FS == 0) {
+          // (kept in place: spread among later MFMAs, the fold's temporaries would hold
+          // more registers than the workgroup has)
+          __builtin_amdgcn_sched_barrier(0);
+          fold(swc[u / FS]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
     if (ends) {
-      fold();
-      sw_cur = sw_nx;
+      if constexpr (FS == 4) fold(swc[0]);
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) swc[gi][j] = swn[gi][j];
     }
     // publish step s + 2: this wave's copies for it (and everything issued before them)
     // are done when at most those of step s + 3 are in flight
@@ -692,22 +707,22 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   wait_copies_and_sync<0>();  // no copy is in flight when the ring becomes the staging area
 
   // epilogue: scale, round, stage each wave's 64 x 64 bf16 tile in LDS (the ring is free
-  // after the barrier above) and write whole 128-byte row segments
+  // after the barrier above; a lane writes its column of each 32-row block, 16 bits at a
+  // time) and write whole 128-byte row segments
   char* stage = (char*)lds + wave * 64 * kEpiStride;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float sam = load_scale(g.sa, min(m0 + wm0 + i * 32 + fr, g.M - 1), g.scale_f16);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t bits[4];
+      for (int e = 0; e < 4; ++e) {
+        const int ml = i * 32 + 8 * q + 4 * fg + e;
+        const float sam = load_scale(g.sa, min(m0 + wm0 + ml, g.M - 1), g.scale_f16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bits[e] = f32_to_bf16((facc[i][j][4 * q + e] * 0.0625f) * sam);
-        *(u32x2*)(stage + (i * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
-            u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+        for (int j = 0; j < 2; ++j)
+          *(uint16_t*)(stage + ml * kEpiStride + (j * 32 + fr) * 2) =
+              (uint16_t)f32_to_bf16((facc[i][j][4 * q + e] * 0.0625f) * sam);
       }
-  }
   __builtin_amdgcn_wave_barrier();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -777,9 +792,6 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
   const rbq_status st = check_gemm(qA, sA, qW, sW, scale_dtype, M, N, K, out_bf16, nullptr);
   if (st != RBQ_OK) return st;
   if (group < 32 || group > K || !is_pow2(group) || K % group != 0) return RBQ_EINVAL;
-  // groups of 32 or 64 codes would end inside a K step: their per-group fold (an fp32
-  // multiply-add per accumulator every one or two MFMAs) is not built
-  if (group < 128) return RBQ_ENOTSUP;
   if (M == 0 || N == 0) return RBQ_OK;
   GemmArgs g{};
   g.qa = (const uint8_t*)qA; g.qw = qW; g.sa = sA; g.sw = sW;
@@ -795,9 +807,16 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
     fprintf(stderr, "rbq: w4a8_gemm_grouped M=%lld N=%lld K=%lld group=%lld tiles=%lld\n", (long long)M,
             (long long)N, (long long)K, (long long)group, (long long)ntiles);
   if (diag_fail_launch()) return RBQ_EHIP;
-  if (g.scale_f16)
-    hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<1>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(w4a8_gemm_grouped_kernel<0>, dim3((uint32_t)ntiles), dim3(kGThreads), 0, stream, g);
+  const dim3 grid((uint32_t)ntiles), block(kGThreads);
+  const int fs = group >= 128 ? 4 : (int)(group / 32);  // sub-steps per group
+  if (g.scale_f16) {
+    if (fs == 1) hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<1, 1>), grid, block, 0, stream, g);
+    else if (fs == 2) hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<1, 2>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<1, 4>), grid, block, 0, stream, g);
+  } else {
+    if (fs == 1) hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<0, 1>), grid, block, 0, stream, g);
+    else if (fs == 2) hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<0, 2>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((w4a8_gemm_grouped_kernel<0, 4>), grid, block, 0, stream, g);
+  }
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }

@@ -69,7 +69,7 @@ int main(int argc, char **argv) {
     EXPECT(rbq_kron_factor(0, &m), RBQ_EINVAL);
   }
   EXPECT(quantize_groups_int4(PX, RBQ_F32, 4096, 8, 4096, 48, PC, PS, RBQ_F16, RBQ_PACKED, NULL), RBQ_EINVAL);
-  EXPECT(w4a8_gemm_grouped((const int8_t *)PC, PS, PC, PS, RBQ_F16, 32, 64, 64, 4096, PX, NULL), RBQ_ENOTSUP);
+  EXPECT(w4a8_gemm_grouped((const int8_t *)PC, PS, PC, PS, RBQ_F16, 16, 64, 64, 4096, PX, NULL), RBQ_EINVAL);
   EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 64, 0.1f, PX, NULL),
          RBQ_ENOTSUP);
   EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 3, 16, 16, 128, 0.1f, PX, NULL),
@@ -91,6 +91,7 @@ int main(int argc, char **argv) {
            launched);
     EXPECT(quantize_groups_int4(PX, RBQ_F32, 4096, 8, 4096, 256, PC, PS, RBQ_F16, RBQ_PACKED, NULL), launched);
     EXPECT(w4a8_gemm_grouped((const int8_t *)PC, PS, PC, PS, RBQ_F16, 256, 64, 64, 4096, PX, NULL), launched);
+    EXPECT(w4a8_gemm_grouped((const int8_t *)PC, PS, PC, PS, RBQ_F32, 32, 64, 64, 4096, PX, NULL), launched);
     EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, PX, NULL),
            launched);
     EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);

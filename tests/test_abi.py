@@ -228,16 +228,17 @@ def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 11, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 12, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
     assert lines[5].startswith("rbq: hadamard_kron_quant n=5120 m=20 p=256 paley=1 q=19 tokens=8")
     assert lines[6].startswith("rbq: quantize_groups_int4 K=4096 rows=8 group=256")
     assert lines[7].startswith("rbq: w4a8_gemm_grouped M=64 N=64 K=4096 group=256")
-    assert lines[8].startswith("rbq: attention_decode_int4kv B=2 H=8 Hkv=2 S=16")
-    assert lines[9].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
-    assert lines[10].startswith("rbq: w4a8_gemm M=64")
+    assert lines[8].startswith("rbq: w4a8_gemm_grouped M=64 N=64 K=4096 group=32")
+    assert lines[9].startswith("rbq: attention_decode_int4kv B=2 H=8 Hkv=2 S=16")
+    assert lines[10].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
+    assert lines[11].startswith("rbq: w4a8_gemm M=64")
 
 
 def test_kron_validation_and_factor(L):
@@ -289,8 +290,9 @@ def test_group_entry_points_validation(L):
     assert L.w4a8_gemm_grouped(A16, A16b, A16c, A16b, rbq.RBQ_F16, 256, 0, 64, 4096, A16, NULL) == rbq.RBQ_OK
     assert gg(group=48) == E
     assert gg(group=8192) == E
-    assert gg(group=32) == NS               # groups below 128 codes are not instantiated
-    assert gg(group=64) == NS
+    assert gg(group=16) == E                # below the smallest group of 32 codes
+    assert gg(group=32, K=4000) == NS       # (valid groups are launched, so only failing shapes here)
+    assert gg(group=64, N=60) == NS
     assert gg(K=4000) == NS
     assert gg(N=60) == NS
     assert gg(qa=NULL) == E

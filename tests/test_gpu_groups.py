@@ -92,7 +92,9 @@ def _weights_and_activations(seed, M, N, K, group):
 
 
 @pytest.mark.parametrize("M,N,K,group", [(1, 8, 128, 128), (64, 256, 1024, 128), (300, 264, 2048, 256),
-                                         (513, 1032, 4096, 256), (130, 136, 4096, 1024), (64, 64, 4096, 4096)])
+                                         (513, 1032, 4096, 256), (130, 136, 4096, 1024), (64, 64, 4096, 4096),
+                                         (1, 8, 128, 32), (96, 520, 1024, 32), (257, 264, 2048, 64),
+                                         (200, 1024, 4096, 32)])
 def test_w4a8_gemm_grouped(rbq, M, N, K, group):
     print(f"case w4a8_gemm_grouped M={M} N={N} K={K} group={group}", flush=True)
     ra, rw = _weights_and_activations(M + N, M, N, K, group)
@@ -105,10 +107,11 @@ def test_w4a8_gemm_grouped(rbq, M, N, K, group):
     check_grouped(out, partial, ref, ra["s_stored"], rw["s_stored"])
 
 
-def test_w4a8_gemm_grouped_random_codes_extremes(rbq):
+@pytest.mark.parametrize("group", [256, 64, 32])
+def test_w4a8_gemm_grouped_random_codes_extremes(rbq, group):
     # uniform random codes over the full grids and log-uniform scales, including -128 / -8
-    M, N, K, group = 256, 512, 4096, 256
-    print("case w4a8_gemm_grouped random codes", flush=True)
+    M, N, K = 256, 512, 4096
+    print(f"case w4a8_gemm_grouped random codes group={group}", flush=True)
     rng = np.random.default_rng(12)
     qa = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
     qw = workloads.gen_packed_codes(13, N, K)
@@ -120,11 +123,12 @@ def test_w4a8_gemm_grouped_random_codes_extremes(rbq):
     check_grouped(out, partial, ref, sa, sw)
 
 
-def test_w4a8_gemm_grouped_full_size_sampled(rbq):
-    """4096 x 11008 x 4096 with groups of 256: rows sampled against the oracle, and two
-    calls bit-identical."""
-    M, N, K, group = 4096, 11008, 4096, 256
-    print("case w4a8_gemm_grouped full size", flush=True)
+@pytest.mark.parametrize("group", [256, 32])
+def test_w4a8_gemm_grouped_full_size_sampled(rbq, group):
+    """4096 x 11008 x 4096 with groups of 256 and of 32: rows sampled against the oracle,
+    and two calls bit-identical."""
+    M, N, K = 4096, 11008, 4096
+    print(f"case w4a8_gemm_grouped full size group={group}", flush=True)
     rng = np.random.default_rng(21)
     qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
     qw = workloads.gen_packed_codes(22, N, K)
