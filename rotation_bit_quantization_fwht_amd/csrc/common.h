@@ -42,14 +42,37 @@ RBQ_HD float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 // bfloat16 bits -> float (exact).
 RBQ_HD float bf16_to_f32(uint32_t h16) { return bits_f32(h16 << 16); }
 
+// The conversions below round to nearest even (finite inputs); device code uses the
+// gfx950 conversion instructions, which do the same, and host code (the emulator) the
+// integer forms written out here.
+
 // float -> bfloat16 bits, round to nearest even (finite inputs).
 RBQ_HD uint32_t f32_to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+#else
   uint32_t u = f32_bits(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+#endif
+}
+
+// two floats -> bfloat16 bits of lo (bits 0..15) and hi (bits 16..31), one
+// v_cvt_pk_bf16_f32 on the device
+RBQ_HD uint32_t f32x2_to_bf16x2(float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
+#else
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+#endif
 }
 
 // binary16 bits -> float (exact, handles subnormals).
 RBQ_HD float f16_to_f32(uint32_t h) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+#else
   uint32_t sign = (h & 0x8000u) << 16;
   uint32_t exp = (h >> 10) & 0x1Fu;
   uint32_t man = h & 0x3FFu;
@@ -60,12 +83,16 @@ RBQ_HD float f16_to_f32(uint32_t h) {
   }
   if (exp == 31) return bits_f32(sign | 0x7F800000u | (man << 13));
   return bits_f32(sign | ((exp + 112u) << 23) | (man << 13));
+#endif
 }
 
 // float -> binary16 bits, IEEE round to nearest even, including subnormal results and
 // overflow to infinity. Written from the binary16/binary32 formats: the result keeps
 // 11 significant bits (fewer for subnormals); the discarded bits decide the rounding.
 RBQ_HD uint32_t f32_to_f16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+#else
   uint32_t u = f32_bits(f);
   uint32_t sign = (u >> 16) & 0x8000u;
   uint32_t a = u & 0x7FFFFFFFu;
@@ -90,6 +117,7 @@ RBQ_HD uint32_t f32_to_f16(float f) {
   }
   // subnormal: keep is the 10-bit fraction; a carry into bit 10 yields the smallest normal
   return sign | keep;
+#endif
 }
 
 // Funnel shift: low 32 bits of ({hi, lo} >> s), 0 <= s < 32 (one v_alignbit_b32).

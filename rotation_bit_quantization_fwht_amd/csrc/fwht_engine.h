@@ -278,7 +278,7 @@ RBQ_HD void apply_rope(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t el, u
   const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   const bool upper = (el & H) != 0;
   static_for<0, 4>([&](auto D) {
-    uint32_t out = 0u;
+    float r[2];
     static_for<0, 2>([&](auto HALF) {
       constexpr int j = 2 * D.value + HALF.value;
       const uint32_t xb = (w[D.value] >> (16 * HALF.value)) & 0xFFFFu;
@@ -287,11 +287,9 @@ RBQ_HD void apply_rope(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t el, u
       const float pv = (IN == IN_F16) ? f16_to_f32(pb) : bits_f32(pb << 16);
       const float t1 = x * cs[j];
       const float t2 = pv * sn[j];
-      const float r = upper ? t1 + t2 : t1 - t2;
-      const uint32_t rb = (IN == IN_F16) ? f32_to_f16(r) : f32_to_bf16(r);
-      out |= rb << (16 * HALF.value);
+      r[HALF.value] = upper ? t1 + t2 : t1 - t2;
     });
-    w[D.value] = out;
+    w[D.value] = (IN == IN_F16) ? (f32_to_f16(r[0]) | (f32_to_f16(r[1]) << 16)) : f32x2_to_bf16x2(r[0], r[1]);
   });
   q4 = u32x4{w[0], w[1], w[2], w[3]};
 }
@@ -588,7 +586,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
         const float y0 = v[rb + 2 * D.value] * INV_SQRTN;
         const float y1 = v[rb + 2 * D.value + 1] * INV_SQRTN;
         if constexpr (IN == IN_F16) out[D.value] = f32_to_f16(y0) | (f32_to_f16(y1) << 16);
-        else out[D.value] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
+        else out[D.value] = f32x2_to_bf16x2(y0, y1);
       });
       if constexpr (L >= 8) {
         static_for<0, L / 8>([&](auto Q) {

@@ -251,12 +251,11 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t bits[4];
+          float y[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bits[e] = f32_to_bf16(((float)(acc[i][j][4 * q + e] >> 8) * sam) * swv[j][q][e]);
+          for (int e = 0; e < 4; ++e) y[e] = ((float)(acc[i][j][4 * q + e] >> 8) * sam) * swv[j][q][e];
           *(u32x2*)(stage + (ii * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
-              u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+              u32x2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -454,12 +453,11 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t bits[4];
+          float y[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bits[e] = f32_to_bf16(((float)(acc[i][j][4 * q + e] >> 4) * sam) * swv[j][q][e]);
+          for (int e = 0; e < 4; ++e) y[e] = ((float)(acc[i][j][4 * q + e] >> 4) * sam) * swv[j][q][e];
           *(u32x2*)(stage + (ii * 32 + fr) * kEpiStride + (j * 32 + 8 * q + 4 * fg) * 2) =
-              u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+              u32x2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
         }
     }
     __builtin_amdgcn_wave_barrier();
