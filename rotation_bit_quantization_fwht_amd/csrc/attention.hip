@@ -60,6 +60,22 @@ __device__ __forceinline__ void attn_codes16(uint32_t w, float (&c)[8]) {
   }
 }
 
+// sum over each row of sixteen lanes, the same bits on every lane of the row: four DPP
+// steps (pairs, quads, the two quads of each half, the two halves), each adding the values
+// of two lanes that then hold the same sum in swapped order
+template <int CTRL>
+__device__ __forceinline__ float attn_dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float attn_row16_sum(float v) {
+  v += attn_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += attn_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += attn_dpp<0x141>(v);  // row_half_mirror
+  v += attn_dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 // one batch of a group's tokens: the lane's dword of each key and value row and the
 // tokens' scales. The loads are buffer loads range-checked against the head's first S
 // tokens: a token past the sequence reads zeros (its score is then set to -inf, so it
@@ -124,8 +140,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 
-  // per batch: scores (eight products per lane, summed over the sixteen lanes; the xor
-  // butterfly leaves the same bits on every lane), the raised maximum, the rescaled sum
+  // per batch: scores (eight products per lane, summed over the sixteen lanes with the
+  // same bits on every lane), the raised maximum, the rescaled sum
   // and output, then the value rows weighted by the probabilities. The batch's loads are
   // all issued before any is used; the other waves of the CU hide their latency. The
   // batch's first token is always in range.
@@ -141,8 +157,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
       float dot = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], kc[i], dot);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+      dot = attn_row16_sum(dot);
       sc[u] = (t0 + u * kAttnGroups < a.S) ? dot * r.ks[u] : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
