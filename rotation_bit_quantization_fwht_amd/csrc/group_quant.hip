@@ -53,10 +53,22 @@ __global__ __launch_bounds__(256) void group_quant_kernel(GroupArgs a) {
     }
   });
 
-  // group maximum across the lanes of the group (groups never straddle waves)
+  // group maximum across the 2^lanes_log >= 4 lanes of the group (groups never straddle
+  // waves): within a row of sixteen lanes by DPP moves (quad swaps, then the quads of each
+  // half and the halves of the row by mirrors), across rows by lane permutes; every lane
+  // is active here
   float mx = 0.0f;
   static_for<0, E>([&](auto I) { mx = fmaxf(mx, fabsf(v[I.value])); });
-  for (uint32_t d = 1; d < (1u << a.lanes_log); d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, (int)d));
+  auto dpp = [](float x, auto CTRL) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(CTRL)::value,
+                                                                 0xF, 0xF, false));
+  };
+  mx = fmaxf(mx, dpp(mx, IC<0xB1>{}));                    // quad_perm [1, 0, 3, 2]
+  mx = fmaxf(mx, dpp(mx, IC<0x4E>{}));                    // quad_perm [2, 3, 0, 1]
+  if (a.lanes_log >= 3) mx = fmaxf(mx, dpp(mx, IC<0x141>{}));  // row_half_mirror
+  if (a.lanes_log >= 4) mx = fmaxf(mx, dpp(mx, IC<0x140>{}));  // row_mirror
+  if (a.lanes_log >= 5) mx = fmaxf(mx, __shfl_xor(mx, 16));
+  if (a.lanes_log >= 6) mx = fmaxf(mx, __shfl_xor(mx, 32));
 
   float s = fmaxf(mx / 7.0f, 1e-8f);
   uint32_t h16 = 0;
