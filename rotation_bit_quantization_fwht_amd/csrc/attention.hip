@@ -60,14 +60,17 @@ __device__ __forceinline__ void attn_codes16(uint32_t w, float (&c)[8]) {
   }
 }
 
-// sum over each row of sixteen lanes, the same bits on every lane of the row: four DPP
-// steps (pairs, quads, the two quads of each half, the two halves), each adding the values
-// of two lanes that then hold the same sum in swapped order
+// the value of another lane of the same 16-lane row, by a DPP move (CTRL: the DPP
+// control word)
 template <int CTRL>
 __device__ __forceinline__ float attn_dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// sum over each row of sixteen lanes, the same bits on every lane of the row: four DPP
+// steps (pairs, quads, the two quads of each half, the two halves), each adding the values
+// of two lanes that then hold the same sum in swapped order. A row is one token group, so
+// its lanes are active or inactive together.
 __device__ __forceinline__ float attn_row16_sum(float v) {
   v += attn_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v += attn_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
