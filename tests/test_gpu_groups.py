@@ -143,3 +143,21 @@ def test_w4a8_gemm_grouped_full_size_sampled(rbq, group):
     rows = np.unique(np.concatenate([[0, 1, 4095], rng.integers(0, M, 13)]))
     partial, ref = oracle.w4a8_gemm_grouped(qa[rows], sa[rows], oracle.unpack_nibbles(qw), sw, group)
     check_grouped(out[torch.from_numpy(rows).cuda()], partial, ref, sa[rows], sw)
+
+
+@pytest.mark.parametrize("group", [32, 4096])
+def test_w4a8_gemm_grouped_largest_k_extremes(rbq, group):
+    """K = 65536 with every code at its extreme (-128 x -8): each group sum is 1024 x group,
+    up to 2048 groups per output; random scales."""
+    M, N, K = 32, 64, 65536
+    print(f"case w4a8_gemm_grouped K=65536 extremes group={group}", flush=True)
+    rng = np.random.default_rng(77 + group)
+    qa = np.full((M, K), -128, dtype=np.int8)
+    qw = np.full((N, K // 2), 0x88, dtype=np.uint8)  # -8 in both nibbles
+    sa = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), M)).astype(np.float32)
+    sw = np.exp(rng.uniform(np.log(1e-4), np.log(1e-2), (N, K // group))).astype(np.float32)
+    out = rbq.w4a8_gemm_grouped(torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(),
+                                torch.from_numpy(qw).cuda(), torch.from_numpy(sw).cuda(), group)
+    partial, ref = oracle.w4a8_gemm_grouped(qa, sa, oracle.unpack_nibbles(qw), sw, group)
+    assert np.all(partial == 1024 * group)
+    check_grouped(out, partial, ref, sa, sw)
