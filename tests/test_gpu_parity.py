@@ -311,13 +311,18 @@ def rope_tables(positions, d, base=10000.0):
     return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
-@pytest.mark.parametrize("dtype,layout,pos0", [("bfloat16", "contiguous", 0), ("bfloat16", "bshd_view", 7),
-                                               ("float16", "contiguous", 100), ("float16", "bshd_view", 0)])
-def test_kv_rope_small(rbq, dtype, layout, pos0):
+@pytest.mark.parametrize("dtype,layout,pos0,bhs", [
+    ("bfloat16", "contiguous", 0, (2, 3, 45)), ("bfloat16", "bshd_view", 7, (2, 3, 45)),
+    ("float16", "contiguous", 100, (2, 3, 45)), ("float16", "bshd_view", 0, (2, 3, 45)),
+    # shapes whose rows fill whole 64-row blocks, several blocks per workgroup loop
+    ("bfloat16", "contiguous", 3, (2, 6, 80)), ("bfloat16", "bshd_view", 0, (4, 5, 48)),
+    ("float16", "contiguous", 0, (1, 4, 16)), ("float16", "bshd_view", 9, (8, 2, 272))])
+def test_kv_rope_small(rbq, dtype, layout, pos0, bhs):
     """kv_rope_rotate_quant: RoPE (half-split, fp32 arithmetic rounded to the 16-bit
     format) then R3 and INT4, on Q and K, against the oracle's RoPE + rotation + quantizer."""
-    B, H, S, D = 2, 3, 45, 128
-    print(f"case kv rope {dtype} {layout} pos0={pos0}", flush=True)
+    B, H, S = bhs
+    D = 128
+    print(f"case kv rope {dtype} {layout} pos0={pos0} B,H,S={bhs}", flush=True)
     q_bits, k_bits, _ = workloads.gen_kv(seed=17, batch=B, heads=H, seq=S, head_dim=D)
     if dtype == "float16":
         q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
@@ -338,6 +343,33 @@ def test_kv_rope_small(rbq, dtype, layout, pos0):
         ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
         got_q = oracle.unpack_nibbles(out[f"{name}_codes"].cpu().numpy().reshape(rows, D // 2))
         check_quant(got_q, out[f"{name}_scales"].cpu().numpy().reshape(rows), ref, "float16", xr)
+
+
+@pytest.mark.parametrize("bhs", [(1, 3, 37), (2, 2, 64)])
+def test_kv_rope_q_rotate_only(rbq, bhs):
+    """RoPE + R3 with Q written rotated in bf16 (no codes): each rotated row lands at its
+    own (batch, head, token) place, with a ragged last block and with whole blocks."""
+    B, H, S = bhs
+    D = 128
+    print(f"case kv rope q_rotate_only B,H,S={bhs}", flush=True)
+    q_bits, k_bits, _ = workloads.gen_kv(seed=23, batch=B, heads=H, seq=S, head_dim=D)
+    cos, sin = rope_tables(S + 2, D)
+    out = rbq.kv_rotate_quant(to_dev(q_bits, "bfloat16"), to_dev(k_bits, "bfloat16"), q_rotate_only=True,
+                              rope_cos=torch.from_numpy(cos).cuda(), rope_sin=torch.from_numpy(sin).cuda(),
+                              rope_pos0=2)
+    pos = 2 + np.arange(S)
+    rows = B * H * S
+    qr = oracle.rope_16bit(workloads.to_float64(q_bits, "bfloat16"), cos[pos][None, None], sin[pos][None, None],
+                           "bfloat16")
+    got = out["q_rotated"].float().cpu().numpy().astype(np.float64)
+    want = oracle.round_to_bf16(oracle.rotate(qr))
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7)
+    assert np.mean(got == want) > 0.999
+    kr = oracle.rope_16bit(workloads.to_float64(k_bits, "bfloat16"), cos[pos][None, None], sin[pos][None, None],
+                           "bfloat16").reshape(rows, D)
+    ref = oracle.hadamard_quant_int4(kr, "float16", packed=False)
+    check_quant(oracle.unpack_nibbles(out["k_codes"].cpu().numpy().reshape(rows, D // 2)),
+                out["k_scales"].cpu().numpy().reshape(rows), ref, "float16", kr)
 
 
 def test_kv_rope_full_size_and_errors(rbq):

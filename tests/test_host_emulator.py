@@ -254,12 +254,18 @@ def rope_tables(positions, d, base=10000.0):
     return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
-@pytest.mark.parametrize("dtype,layout,pos0,fast", [("bfloat16", "flat", 0, True), ("bfloat16", "bshd", 5, False),
-                                                    ("float16", "flat", 3, False), ("float16", "bshd", 0, True)])
-def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast):
+@pytest.mark.parametrize("dtype,layout,pos0,fast,bhs", [
+    ("bfloat16", "flat", 0, True, (2, 3, 37)), ("bfloat16", "bshd", 5, False, (2, 3, 37)),
+    ("float16", "flat", 3, False, (2, 3, 37)), ("float16", "bshd", 0, True, (2, 3, 37)),
+    # (batch, head) pair counts and lengths that fill every 64-row block, several blocks per
+    # workgroup loop
+    ("bfloat16", "flat", 7, False, (2, 2, 48)), ("bfloat16", "bshd", 0, True, (1, 8, 32)),
+    ("float16", "bshd", 2, False, (4, 3, 16)), ("float16", "flat", 0, True, (3, 4, 64))])
+def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
     """RoPE (half-split pairs, fp32 arithmetic, rounded to the 16-bit format) ahead of R3,
     on flat and strided [B, H, S, D] addressing, against the oracle's RoPE + rotation."""
-    B, H, S, D = 2, 3, 37, 128
+    B, H, S = bhs
+    D = 128
     q_bits, _, _ = workloads.gen_kv(seed=9, batch=B, heads=H, seq=S, head_dim=D)
     if dtype == "float16":
         q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
