@@ -36,8 +36,7 @@
 
 namespace rbq {
 
-constexpr uint32_t kKronThreads = 256;
-constexpr uint32_t kKronWaves = 4;
+constexpr uint32_t kKronMaxWaves = 8;              // LDS slots for the per-wave maxima
 constexpr uint32_t kKronMaxM = 160;                  // largest Paley order the kernel takes
 constexpr uint32_t kKronMaxKB = kKronMaxM / 32;      // 32-row K blocks of the MFMA
 constexpr uint32_t kKronMaxN = 32768;
@@ -60,7 +59,7 @@ struct KronArgs {
   uint32_t rs;           // LDS words per row a of the [m][p] buffer (p + 4)
   uint32_t hs;           // LDS words per row of the operand table (16 KB + 4)
   uint32_t tab0;         // LDS word offset of the table
-  uint32_t red0;         // LDS word offset of the four per-wave maxima
+  uint32_t red0;         // LDS word offset of the per-wave maxima (up to 8 waves)
 };
 
 // LDS words a launch needs (the row buffer, the table, the cross-wave maxima)
@@ -73,7 +72,20 @@ RBQ_HD uint32_t kron_lds_words(uint32_t m, uint32_t p_log, uint32_t* rs, uint32_
   *hs = kb * 16 + 4;
   *tab0 = m * *rs;
   *red0 = *tab0 + mb * 16 * *hs;
-  return *red0 + kKronWaves;
+  return *red0 + kKronMaxWaves;
+}
+
+// Waves per workgroup and operand blocks per gather chunk for KB K blocks of the MFMA.
+// Rows with m <= 32 in a 16-bit format take 8 waves with chunks of 4 blocks: their
+// registers then fit 4 waves per SIMD, so two workgroups of 8 waves share a CU and twice
+// as many gathers are in flight. Otherwise 4 waves with chunks of 8 / KB blocks.
+template <int IN, int KB>
+constexpr uint32_t kron_waves() { return (KB == 1 && IN != IN_F32) ? 8u : 4u; }
+
+template <int IN, int KB>
+constexpr int kron_chunk() {
+  if (IN == IN_F32 || KB > 8) return 1;
+  return kron_waves<IN, KB>() == 8u ? 4 : 8 / KB;
 }
 
 // quadratic character of GF(q) from the square mask: 0, +1 (nonzero square) or -1
@@ -116,14 +128,14 @@ RBQ_HD void kron_fwht_regs(float* v) {
 // wave: lanes 0..15 take sixteen consecutive b (bits 0..3), lane groups 1..3 the rows 4,
 // 8 and 12 below; the job index runs over the groups of sixteen rows, the first row of
 // the group, the bits of b above the pass and those between bit 4 and bit O.
-template <int O, int G, class Ctx>
+template <int O, int G, uint32_t W, class Ctx>
 RBQ_HD void kron_pass(Ctx& c, uint32_t m, uint32_t P, uint32_t rs) {
   const uint32_t hib = P - O - G;
   const uint32_t nlh = 1u << (O - 4);
   const uint32_t nhi = 1u << hib;
   const uint32_t njobs = ((m + 15) / 16) * 4 * nhi * nlh;
   const uint32_t lowlo = c.lane & 15u, t = c.lane >> 4;
-  for (uint32_t j = c.wave; j < njobs; j += kKronWaves) {
+  for (uint32_t j = c.wave; j < njobs; j += W) {
     const uint32_t lh = j & (nlh - 1u);
     const uint32_t r = j >> (O - 4);
     const uint32_t hi = r & (nhi - 1u);
@@ -148,13 +160,13 @@ RBQ_HD void kron_pass(Ctx& c, uint32_t m, uint32_t P, uint32_t rs) {
 // H_m on the matrix cores: Y[a][b] = sum_a' H_m[a][a'] X[a'][b] as D = A B, with A = H_m
 // (rows a, K = a') from the LDS table and B = X (K = a', columns b) gathered from HBM
 // straight into operand registers; rows a' >= m read row m - 1, which the zero columns of
-// the table cancel. Each wave takes the blocks of 16 columns nb = wave, wave + 4, ... in
+// the table cancel. Each wave takes the blocks of 16 columns nb = wave, wave + W, ... (W waves) in
 // chunks of NBC blocks: the operands of a chunk are gathered before its MFMAs, so one
 // memory latency covers the chunk, and the first chunk of the next row is gathered while
 // the current row is transformed and quantized. The fp32 results go to the row buffer.
 template <int IN, int KB>
 struct KronFrag {
-  static constexpr int NBC = (IN == IN_F32 || KB > 8) ? 1 : 8 / KB;  // blocks per chunk
+  static constexpr int NBC = kron_chunk<IN, KB>();  // blocks per chunk
   // the raw gathered values (one 16-bit or fp32 element per register): they are packed
   // or split into MFMA operands only where used, so the loads of a prefetch stay in
   // flight until then
@@ -191,7 +203,7 @@ RBQ_HD void kron_gather(Ctx& c, const KronArgs& a, const KronGatherOffsets<IN, K
   constexpr uint32_t ESZ = (IN == IN_F32) ? 4 : 2;
   const uint32_t NB = (1u << a.p_log) >> 4;
   static_for<0, F::NBC>([&](auto JJ) {
-    const uint32_t nb = nb0 + kKronWaves * JJ.value;
+    const uint32_t nb = nb0 + kron_waves<IN, KB>() * JJ.value;
     if (nb < NB) {
       const char* xb = xr + nb * 16 * ESZ;  // uniform: the block's first column
       static_for<0, KB>([&](auto KBI) {
@@ -215,7 +227,7 @@ RBQ_HD void kron_mma_store(Ctx& c, const KronArgs& a, uint32_t nb0, const KronFr
   const uint32_t MB = (m + 15) / 16;
   const uint32_t col = c.lane & 15u, grp = c.lane >> 4;
   static_for<0, F::NBC>([&](auto JJ) {
-    const uint32_t nb = nb0 + kKronWaves * JJ.value;
+    const uint32_t nb = nb0 + kron_waves<IN, KB>() * JJ.value;
     if (nb < NB) {
       // operand B of each K block: element i of the lane's eight in half i % 2 of word i / 2
       uint32_t bf[KB][NPART][4];
@@ -279,6 +291,7 @@ RBQ_HD void kron_load16(Ctx& c, uint32_t base, float (&v)[16]) {
 template <int IN, int KB, class Ctx>
 RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
   constexpr uint32_t ESZ = (IN == IN_F32) ? 4 : 2;
+  constexpr uint32_t W = kron_waves<IN, KB>(), NT = 64 * W;
   using F = KronFrag<IN, KB>;
   const uint32_t tid = c.wave * 64u + c.lane;
   const uint32_t m = a.m, P = a.p_log, p = 1u << P, n = m << P;
@@ -298,7 +311,7 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
 
     // ---- 1. H_m on the matrix cores
     kron_mma_store<IN, KB>(c, a, c.wave, pre);
-    for (uint32_t nb0 = c.wave + kKronWaves * F::NBC; nb0 < NB; nb0 += kKronWaves * F::NBC) {
+    for (uint32_t nb0 = c.wave + W * F::NBC; nb0 < NB; nb0 += W * F::NBC) {
       F f;
       kron_gather<IN, KB>(c, a, go, xr, nb0, f);
       kron_mma_store<IN, KB>(c, a, nb0, f);
@@ -308,21 +321,21 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
 
     // ---- 2. H_p over the bits of b above bit 3: bits 4..8, then bits 9..10
     switch (P) {
-      case 5: kron_pass<4, 1>(c, m, P, rs); break;
-      case 6: kron_pass<4, 2>(c, m, P, rs); break;
-      case 7: kron_pass<4, 3>(c, m, P, rs); break;
-      case 8: kron_pass<4, 4>(c, m, P, rs); break;
-      case 9: case 10: case 11: kron_pass<4, 5>(c, m, P, rs); break;
+      case 5: kron_pass<4, 1, W>(c, m, P, rs); break;
+      case 6: kron_pass<4, 2, W>(c, m, P, rs); break;
+      case 7: kron_pass<4, 3, W>(c, m, P, rs); break;
+      case 8: kron_pass<4, 4, W>(c, m, P, rs); break;
+      case 9: case 10: case 11: kron_pass<4, 5, W>(c, m, P, rs); break;
       default: break;
     }
     if (P > 4) c.barrier_lds();
-    if (P == 10) kron_pass<9, 1>(c, m, P, rs);
-    if (P == 11) kron_pass<9, 2>(c, m, P, rs);
+    if (P == 10) kron_pass<9, 1, W>(c, m, P, rs);
+    if (P == 11) kron_pass<9, 2, W>(c, m, P, rs);
     if (P > 9) c.barrier_lds();
 
     // ---- 2b. bits 0..3 on sixteen consecutive elements per run, and the row's absmax
     float mx = 0.0f;
-    for (uint32_t s = tid; s < nrun; s += kKronThreads) {
+    for (uint32_t s = tid; s < nrun; s += NT) {
       const uint32_t base = (s >> (P - 4)) * rs + (s & ((p >> 4) - 1u)) * 20u;
       float v[16];
       kron_load16(c, base, v);
@@ -339,7 +352,7 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
 
     // ---- 3. scale and codes, one run of sixteen consecutive elements at a time
     float mu = 0.0f;
-    static_for<0, (int)kKronWaves>([&](auto W) { mu = fmaxf(mu, c.lds_load(a.red0 + W.value)); });
+    static_for<0, (int)W>([&](auto WV) { mu = fmaxf(mu, c.lds_load(a.red0 + WV.value)); });
     const float qmax = 7.0f;
     float sc = mu / (qmax * a.sqrtn);
     sc = fmaxf(sc, 1e-8f);
@@ -356,7 +369,7 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
     const bool clamp = mu * mk > qmax + 0.25f;
     auto code_runs = [&](auto CL) {
       constexpr bool CLAMP = decltype(CL)::value != 0;
-      for (uint32_t s = tid; s < nrun; s += kKronThreads) {
+      for (uint32_t s = tid; s < nrun; s += NT) {
         const uint32_t base = (s >> (P - 4)) * rs + (s & ((p >> 4) - 1u)) * 20u;
         const uint32_t el = s << 4;  // the run's first element: a * p + b0
         float v[16];
@@ -391,8 +404,13 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
   }
 }
 
-template <int IN, class Ctx>
+// KS 1: the kernel for one K block (m <= 32); KS 0: the kernel for two or more
+template <int IN, int KS>
+constexpr uint32_t kron_body_waves() { return KS == 1 ? kron_waves<IN, 1>() : kron_waves<IN, 2>(); }
+
+template <int IN, int KS, class Ctx>
 RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
+  constexpr uint32_t NT = 64 * kron_body_waves<IN, KS>();
   const uint32_t tid = c.wave * 64u + c.lane;
   const uint32_t m = a.m;
   const uint32_t MB = (m + 15) / 16, KB = (m + 31) / 32;
@@ -402,7 +420,7 @@ RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t gri
   {
     const uint32_t one = (IN == IN_F16) ? 0x3C00u : 0x3F80u;
     const uint32_t wpr = KB * 16;
-    for (uint32_t w = tid; w < MB * 16 * wpr; w += kKronThreads) {
+    for (uint32_t w = tid; w < MB * 16 * wpr; w += NT) {
       const uint32_t r = w / wpr, cw = w - r * wpr;
       uint32_t bits = 0;
       for (uint32_t h = 0; h < 2; ++h) {
@@ -417,12 +435,15 @@ RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t gri
   }
   c.barrier();  // the table is read by every wave's MFMAs
 
-  switch (KB) {
-    case 1: kron_rows<IN, 1>(c, a, wg, grid); break;
-    case 2: kron_rows<IN, 2>(c, a, wg, grid); break;
-    case 3: kron_rows<IN, 3>(c, a, wg, grid); break;
-    case 4: kron_rows<IN, 4>(c, a, wg, grid); break;
-    default: kron_rows<IN, 5>(c, a, wg, grid); break;
+  if constexpr (KS == 1) {
+    kron_rows<IN, 1>(c, a, wg, grid);
+  } else {
+    switch (KB) {
+      case 2: kron_rows<IN, 2>(c, a, wg, grid); break;
+      case 3: kron_rows<IN, 3>(c, a, wg, grid); break;
+      case 4: kron_rows<IN, 4>(c, a, wg, grid); break;
+      default: kron_rows<IN, 5>(c, a, wg, grid); break;
+    }
   }
 }
 

@@ -14,26 +14,30 @@
 namespace rbq {
 
 // LW: LDS words of the variant (32 KiB, 80 KiB or 160 KiB), the smallest that holds the
-// row buffer and the operand table; smaller variants keep more workgroups per CU
-template <int IN, uint32_t LW>
-__global__ __launch_bounds__(kKronThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// row buffer and the operand table; smaller variants keep more workgroups per CU.
+// KS 1: rows with one K block of the MFMA (m <= 32), KS 0: the others; each has its own
+// wave count and register budget (8 waves at up to 128 VGPRs, or 4 at up to 256).
+template <int IN, uint32_t LW, int KS>
+__global__ __launch_bounds__((64 * kron_body_waves<IN, KS>()))
+__attribute__((amdgpu_waves_per_eu(kron_body_waves<IN, KS>() == 8u ? 4 : 2)))
 void kron_quant_kernel(KronArgs a) {
   __shared__ float lds[LW];
   DevCtx c;
   c.lane = threadIdx.x & 63u;
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.lds = lds;
-  kron_quant_body<IN>(c, a, blockIdx.x, gridDim.x);
+  kron_quant_body<IN, KS>(c, a, blockIdx.x, gridDim.x);
 }
 
 // Workgroups loop over rows: the grid holds as many as are resident at once (each one
 // prefetches its next row's first operands while it finishes the current row), or one
 // per row when there are fewer rows.
-template <int IN, uint32_t LW>
+template <int IN, uint32_t LW, int KS>
 static hipError_t kron_launch_lw(const KronArgs& a, hipStream_t s) {
+  constexpr int NT = 64 * (int)kron_body_waves<IN, KS>();
   static const int per_cu = [] {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kron_quant_kernel<IN, LW>, kKronThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kron_quant_kernel<IN, LW, KS>, NT, 0) != hipSuccess ||
         o < 1)
       o = 1;
     return o;
@@ -44,16 +48,21 @@ static hipError_t kron_launch_lw(const KronArgs& a, hipStream_t s) {
     return hipErrorInvalidDevice;
   const int64_t cap = (int64_t)per_cu * cus;
   const uint32_t grid = (uint32_t)(a.rows < cap ? a.rows : cap);
-  if (diag_log()) fprintf(stderr, "rbq: hadamard_kron_quant lds_words=%u grid=%u\n", LW, grid);
-  hipLaunchKernelGGL((kron_quant_kernel<IN, LW>), dim3(grid), dim3(kKronThreads), 0, s, a);
+  if (diag_log()) fprintf(stderr, "rbq: hadamard_kron_quant lds_words=%u grid=%u threads=%d\n", LW, grid, NT);
+  hipLaunchKernelGGL((kron_quant_kernel<IN, LW, KS>), dim3(grid), dim3(NT), 0, s, a);
   return hipGetLastError();
+}
+
+template <int IN, int KS>
+static hipError_t kron_launch_ks(const KronArgs& a, uint32_t words, hipStream_t s) {
+  if (words <= 8192u) return kron_launch_lw<IN, 8192u, KS>(a, s);
+  if (words <= 20480u) return kron_launch_lw<IN, 20480u, KS>(a, s);
+  return kron_launch_lw<IN, 40960u, KS>(a, s);
 }
 
 template <int IN>
 static hipError_t kron_launch_in(const KronArgs& a, uint32_t words, hipStream_t s) {
-  if (words <= 8192u) return kron_launch_lw<IN, 8192u>(a, s);
-  if (words <= 20480u) return kron_launch_lw<IN, 20480u>(a, s);
-  return kron_launch_lw<IN, 40960u>(a, s);
+  return a.m <= 32u ? kron_launch_ks<IN, 1>(a, words, s) : kron_launch_ks<IN, 0>(a, words, s);
 }
 
 }  // namespace rbq

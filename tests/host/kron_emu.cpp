@@ -17,18 +17,26 @@
 
 using namespace rbq;
 
-template <int IN>
-static void run(const KronArgs& a, uint32_t words, uint32_t grid) {
+// the kernel the library launches: one K block (m <= 32) or more, each with its waves
+template <int IN, int KS>
+static void run_ks(const KronArgs& a, uint32_t words, uint32_t grid) {
+  constexpr uint32_t W = kron_body_waves<IN, KS>();
   for (uint32_t wg = 0; wg < grid; ++wg) {
-    WgShared sh(words, (int)kKronThreads, (int)kKronWaves);
+    WgShared sh(words, (int)(64 * W), (int)W);
     std::vector<std::thread> th;
-    for (uint32_t t = 0; t < kKronThreads; ++t)
+    for (uint32_t t = 0; t < 64 * W; ++t)
       th.emplace_back([&, t] {
         HostCtx c{t & 63u, t >> 6, &sh};
-        kron_quant_body<IN>(c, a, wg, grid);
+        kron_quant_body<IN, KS>(c, a, wg, grid);
       });
     for (auto& x : th) x.join();
   }
+}
+
+template <int IN>
+static void run(const KronArgs& a, uint32_t words, uint32_t grid) {
+  if (a.m <= 32u) run_ks<IN, 1>(a, words, grid);
+  else run_ks<IN, 0>(a, words, grid);
 }
 
 static std::vector<char> read_file(const char* path) {
