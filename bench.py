@@ -4,16 +4,27 @@ One step is one pass over every hot-path call, each on its full workload:
   * kv_rotate_quant   -- R3 on post-RoPE Q and K, bf16 [16, 32, 2048, 128] each;
   * hadamard_quant_int4 -- R4 on the down-projection input, bf16 [8192, 16384], n = 16384;
   * w4a4_gemm         -- A [4096, 4096] x W [11008, 4096] packed INT4, bf16 output.
-Inputs are seeded synthetic tensors (workloads.py) already resident in HBM; four input
-sets (more than the 256 MB last-level cache per call) are rotated so the timed reads come
-from HBM. Each launch is bracketed by HIP events on the stream it runs on.
+Inputs are seeded synthetic tensors (workloads.py) already resident in HBM; four input and
+output sets per call (more than the 256 MB last-level cache between two uses of a set) are
+rotated so the timed reads come from HBM.
+
+Timing:
+  * pre-warm: steps run untimed until at least --prewarm-ms of wall time has passed (the
+    device runs slower for its first tens of milliseconds of sustained load), then the
+    --warmup steps;
+  * the timed region: exactly --steps steps, bracketed by synchronisation and one pair of
+    HIP events on the stream the library launches on (ms_per_step);
+  * per-kernel time: right after, each kernel alone, --steps launches back to back over
+    the rotated sets, bracketed by one event pair (no event between two launches, so no
+    marker packet separates them); this is the kernel's average launch duration that the
+    roofline figures use.
 
 The headline value is the fused Hadamard + INT4 quantizer's throughput at n = 16384 in
 algorithmic GB/s (bf16 input read once, packed codes and fp16 scales written once); the
 GEMM's TOPS and the per-call times are reported beside it, with the fp64 oracle timed on
 a bounded sample on the host cores as a baseline.
 
-usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--only r4|kv|gemm|kron|copy|stream]
 """
 
 import argparse
@@ -21,6 +32,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -58,9 +70,9 @@ GEMM_SOURCES = ("common.h", "w4a4_gemm.hip")
 KRON_SOURCES = ("common.h", "fwht_engine.h", "devctx.h", "kron_engine.h", "kron_factor.h", "kron_quant.hip")
 
 
-def load_traffic(name, src_hash):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
-    taken on the current kernel source (else None)."""
+def load_counters(name, src_hash):
+    """The committed rocprofv3 counter summary of one kernel (profiles/counters.json), if it
+    was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
@@ -71,7 +83,24 @@ def load_traffic(name, src_hash):
     e = d.get(name)
     if not e or e.get("source_hash") != src_hash:
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e
+
+
+def load_traffic(name, src_hash):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE passes (or None)."""
+    e = load_counters(name, src_hash)
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline():
@@ -97,6 +126,10 @@ def cpu_baseline():
             break
     dt = (time.perf_counter() - t0) / reps
     sample_bytes = rows * (R4_N * 2 + R4_N // 2 + 2)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     return {
         "value": round(sample_bytes / dt / 1e9, 6),
         "unit": "GB/s",
@@ -104,7 +137,25 @@ def cpu_baseline():
         "kind": "oracle",
         "sample": f"{rows} rows of the bf16 [8192, 16384] R4 workload, explicit fp64 Sylvester "
                   f"multiply + quantizer, {reps} repetitions, {dt:.2f} s each",
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "host_cpus_usable": affinity,
+        "blas_threads": int(cores),
     }
+
+
+def time_back_to_back(torch, fns, reps):
+    """Average device time per launch: ``reps`` launches cycling over ``fns`` (one callable
+    per rotated input set), issued back to back and bracketed by one event pair on the
+    current stream (the one the binding hands to the library)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def time_calls(torch, fn, reps):
@@ -125,7 +176,7 @@ def time_calls(torch, fn, reps):
 
 def time_graph(torch, fn, calls=20, replays=10):
     """Device time per call with the launches captured in a HIP graph (no host overhead
-    between kernels); returns (us per call, graph output equals an eager call's)."""
+    between kernels); returns us per call."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -144,6 +195,30 @@ def time_graph(torch, fn, calls=20, replays=10):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (calls * replays)
+
+
+def hbm_probe_rates(torch, rbq, dev, reps=20):
+    """The streaming probe (rbq_hbm_probe) on 2 GiB of reads and/or writes: reads alone,
+    writes alone, and R4's row shape (each workgroup reads 32 KiB then writes 8 KiB, the
+    bytes of one bf16 row of 16384 and its packed codes). GB/s of moved bytes."""
+    big = 1 << 31
+    src = torch.empty(big // 4, dtype=torch.int32, device=dev)
+    src.fill_(0x01234567)
+    dst = torch.empty(big // 4, dtype=torch.int32, device=dev)
+    out = {}
+    shapes = (("read_only", 65536, 0, big // 65536),
+              ("write_only", 0, 65536, big // 65536),
+              ("r4_row_mix", 32768, 8192, big // 32768))
+    for name, rd, wr, blocks in shapes:
+        fn = lambda rd=rd, wr=wr, blocks=blocks: rbq.hbm_probe(src, rd, dst, wr, blocks)  # noqa: E731
+        for _ in range(5):
+            fn()
+        us = time_back_to_back(torch, [fn], reps)
+        moved = blocks * (rd + wr)
+        out[name] = {"read_bytes": blocks * rd, "write_bytes": blocks * wr, "avg_us": round(us, 3),
+                     "GB_s": round(moved / (us * 1e-6) / 1e9, 1)}
+    del src, dst
+    return out
 
 
 def report_small_workloads(torch, rbq, workloads, dev):
@@ -198,42 +273,53 @@ def report_small_workloads(torch, rbq, workloads, dev):
     return out
 
 
+def copy_calibration(torch, args):
+    """Plain 1 GiB device copy: calibrates the HBM byte counters, and its rate is what a
+    simple read+write stream (torch's own copy kernel) reaches on this device."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    nbytes = src.numel() * 4
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                      "launches": args.warmup + args.steps,
+                      "copy_GB_s": round(2 * nbytes * args.steps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="untimed steps run for at least this much wall time before --warmup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the worked-example and decode-sweep reports")
-    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "kron", "copy"], default="all",
+                    help="skip the reports beside the step (worked example, decode sweep, variants)")
+    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "kron", "copy", "stream"], default="all",
                     help="restrict the step (for profiling one kernel); 'copy' runs a plain 1 GiB "
-                         "device copy used to calibrate the HBM byte counters")
+                         "device copy used to calibrate the HBM byte counters; 'stream' runs the "
+                         "HBM streaming probe")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1); "
+              "the design notes describe how the path would shard", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     if args.only == "copy":
-        # plain 1 GiB device copy: calibrates the HBM byte counters, and its rate is what a
-        # simple read+write stream (torch's own copy kernel) reaches on this device
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        src.fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(args.warmup):
-            dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        nbytes = src.numel() * 4
-        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
-                          "launches": args.warmup + args.steps,
-                          "copy_GB_s": round(2 * nbytes * args.steps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}))
+        copy_calibration(torch, args)
         return
 
     import rotation_bit_quantization_fwht_amd as rbq
@@ -246,6 +332,11 @@ def main():
     rbq.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "stream":
+        print(json.dumps({"hbm_probe": hbm_probe_rates(torch, rbq, dev, reps=args.steps),
+                          "peak_GB_s": HBM_PEAK_GBS}), flush=True)
+        return
 
     def to_dev16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -288,7 +379,14 @@ def main():
         qa, sa = rbq.hadamard_quant_int4(a0)                     # activations, online rotation
         qw, sw = rbq.hadamard_quant_int4(w0)                     # weights, offline rotation
         qa8, sa8 = rbq.hadamard_quant_int8(a0)                   # W4A8: INT8 activation codes
-        out = torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=dev)
+        # operand sets: row rotations of the codes and scales (a set's 121 MB of operands and
+        # output is not reused before three other sets have passed through the cache)
+        sets["gemm"] = [(qa, sa, qw, sw, torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=dev))]
+        for i in range(1, NSETS):
+            sets["gemm"].append((torch.roll(qa, 61 * i, 0).contiguous(), torch.roll(sa, 61 * i, 0).contiguous(),
+                                 torch.roll(qw, 173 * i, 0).contiguous(), torch.roll(sw, 173 * i, 0).contiguous(),
+                                 torch.empty((GEMM_M, GEMM_N), dtype=torch.bfloat16, device=dev)))
+        out = sets["gemm"][0][4]
         try:
             rbq.w4a4_gemm(qa, sa, qw, sw, out=out)
             gemm_ok = True
@@ -298,74 +396,84 @@ def main():
         del a0, w0
     torch.cuda.synchronize()
 
-    def step(i, ev):
-        s = i % NSETS
-        j = 0
-        if run_kv:
-            ev[j].record()
-            o = sets["kv_out"][s]
-            rbq.kv_rotate_quant(sets["kv_q"][s], sets["kv_k"][s], **o)
-            j += 1
-        if run_r4:
-            ev[j].record()
-            rbq.hadamard_quant_int4(sets["r4_x"][s], codes=sets["r4_codes"][s], scales=sets["r4_scales"][s])
-            j += 1
-        if run_gemm and gemm_ok:
-            ev[j].record()
-            rbq.w4a4_gemm(qa, sa, qw, sw, out=out)
-            j += 1
-        ev[j].record()
+    def call_kv(s):
+        rbq.kv_rotate_quant(sets["kv_q"][s], sets["kv_k"][s], **sets["kv_out"][s])
 
-    nk = int(run_kv) + int(run_r4) + int(run_gemm and gemm_ok)
-    for i in range(args.warmup):
-        step(i, [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)])
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    def call_r4(s):
+        rbq.hadamard_quant_int4(sets["r4_x"][s], codes=sets["r4_codes"][s], scales=sets["r4_scales"][s])
+
+    def call_gemm(s):
+        a, sa_, w_, sw_, o = sets["gemm"][s]
+        rbq.w4a4_gemm(a, sa_, w_, sw_, out=o)
+
+    kernels_in_step = []
+    if run_kv:
+        kernels_in_step.append(("kv_rotate_quant", call_kv))
+    if run_r4:
+        kernels_in_step.append(("hadamard_quant_int4", call_r4))
+    if run_gemm and gemm_ok:
+        kernels_in_step.append(("w4a4_gemm", call_gemm))
+
+    def step(i):
+        s = i % NSETS
+        for _, fn in kernels_in_step:
+            fn(s)
+
+    # ---- pre-warm (time-based, untimed), then the --warmup steps
     t0 = time.perf_counter()
+    pre = 0
+    while True:
+        step(pre)
+        pre += 1
+        if pre % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= args.prewarm_ms:
+                break
+    prewarm_ms = (time.perf_counter() - t0) * 1e3
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- the timed region: exactly --steps steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i)
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
 
-    names = []
-    if run_kv:
-        names.append("kv_rotate_quant")
-    if run_r4:
-        names.append("hadamard_quant_int4")
-    if run_gemm and gemm_ok:
-        names.append("w4a4_gemm")
-    per = {n: [] for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]))
-    step_ms = [ev[0].elapsed_time(ev[-1]) for ev in events]
-    avg = {n: float(np.mean(v)) for n, v in per.items()}
-    med = {n: float(np.median(v)) for n, v in per.items()}
+    # ---- per-kernel durations: each kernel alone, back to back over the rotated sets
+    avg = {}
+    for name, fn in kernels_in_step:
+        avg[name] = time_back_to_back(torch, [lambda s=s, fn=fn: fn(s) for s in range(NSETS)], args.steps)
 
     kernels = {}
     fwht_hash = kernel_source_hash(FWHT_SOURCES)
+    gemm_hash = kernel_source_hash(GEMM_SOURCES)
     if "hadamard_quant_int4" in avg:
-        t = avg["hadamard_quant_int4"] * 1e-3
+        t = avg["hadamard_quant_int4"] * 1e-6
         kernels["hadamard_quant_int4"] = {
             "workload": "R4 bf16 [8192, 16384], n=16384, packed INT4 + fp16 scales",
-            "avg_us": round(t * 1e6, 3), "median_us": round(med["hadamard_quant_int4"] * 1e3, 3),
-            "algorithmic_bytes": R4_BYTES, "GB_s": round(R4_BYTES / t / 1e9, 2),
+            "avg_us": round(t * 1e6, 3), "algorithmic_bytes": R4_BYTES, "GB_s": round(R4_BYTES / t / 1e9, 2),
             "frac_hbm_peak": round(R4_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
         }
     if "kv_rotate_quant" in avg:
-        t = avg["kv_rotate_quant"] * 1e-3
+        t = avg["kv_rotate_quant"] * 1e-6
         kernels["kv_rotate_quant"] = {
             "workload": "R3 bf16 Q and K [16, 32, 2048, 128], packed INT4 + fp16 scales",
-            "avg_us": round(t * 1e6, 3), "median_us": round(med["kv_rotate_quant"] * 1e3, 3),
-            "algorithmic_bytes": KV_BYTES, "GB_s": round(KV_BYTES / t / 1e9, 2),
+            "avg_us": round(t * 1e6, 3), "algorithmic_bytes": KV_BYTES, "GB_s": round(KV_BYTES / t / 1e9, 2),
             "frac_hbm_peak": round(KV_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
         }
     if "w4a4_gemm" in avg:
-        t = avg["w4a4_gemm"] * 1e-3
+        t = avg["w4a4_gemm"] * 1e-6
         kernels["w4a4_gemm"] = {
             "workload": "A [4096, 4096] x W [11008, 4096] packed INT4, bf16 out",
-            "avg_us": round(t * 1e6, 3), "median_us": round(med["w4a4_gemm"] * 1e3, 3),
-            "algorithmic_ops": GEMM_OPS, "TOPS": round(GEMM_OPS / t / 1e12, 2),
+            "avg_us": round(t * 1e6, 3), "algorithmic_ops": GEMM_OPS, "algorithmic_bytes": GEMM_BYTES,
+            "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4),
         }
 
@@ -387,31 +495,33 @@ def main():
             "frac": k["frac_hbm_peak"], "traffic": load_traffic("kv_rotate_quant", fwht_hash)}
     if "w4a4_gemm" in kernels:
         k = kernels["w4a4_gemm"]
-        extra_roofline["w4a4_gemm"] = {
-            "bound": "mfma", "achieved": k["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-            "frac": k["frac_int8_mfma_peak"],
-            "traffic": load_traffic("w4a4_gemm", kernel_source_hash(GEMM_SOURCES))}
+        entry = {"bound": "mfma", "achieved": k["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                 "frac": k["frac_int8_mfma_peak"], "traffic": load_traffic("w4a4_gemm", gemm_hash)}
+        c = load_counters("w4a4_gemm", gemm_hash)
+        if c and "mfma" in c:
+            # from the committed rocprofv3 pass: MFMA busy cycles over the GPU's active
+            # cycles, and int8 MFMA operations per dispatch against the algorithmic count
+            entry["mfma_counters"] = c["mfma"]
+        extra_roofline["w4a4_gemm"] = entry
 
     extras = {}
-    if args.only == "all" and not args.no_extras:
-        extras = report_small_workloads(torch, rbq, workloads, dev)
+    if not args.no_extras and args.only == "all":
+        extras["hbm_probe"] = hbm_probe_rates(torch, rbq, dev)
+        extras.update(report_small_workloads(torch, rbq, workloads, dev))
     if run_gemm and gemm_ok and not args.no_extras:
         # the W4A8 variant on the same workload (INT8 activation codes, INT4 weights)
         out8 = torch.empty_like(out)
-        rbq.w4a8_gemm(qa8, sa8, qw, sw, out=out8)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(20):
-            rbq.w4a8_gemm(qa8, sa8, qw, sw, out=out8)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 20
+        sets8 = [(torch.roll(qa8, 61 * i, 0).contiguous(), torch.roll(sa8, 61 * i, 0).contiguous()) for i in range(NSETS)]
+        fns = [lambda i=i: rbq.w4a8_gemm(sets8[i][0], sets8[i][1], sets["gemm"][i][2], sets["gemm"][i][3], out=out8)
+               for i in range(NSETS)]
+        for f in fns:
+            f()
+        t = time_back_to_back(torch, fns, 20) * 1e-6
         extras["w4a8_gemm"] = {
             "workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], bf16 out",
             "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
-    if run_gemm and gemm_ok and not args.no_extras:
+        del sets8
         # group-wise weight scales (groups of 256 codes along K) on the same shape: the
         # rotated weights quantized per group, the INT8 activation codes as above
         wr = torch.empty((GEMM_N, GEMM_K), dtype=torch.float32, device=dev)
@@ -425,18 +535,11 @@ def main():
                          ("w4a8_gemm_grouped", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg, swg, 256, out=outg)),
                          ("w4a8_gemm_grouped_32", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg32, swg32, 32, out=outg))):
             fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / 20
+            t = time_back_to_back(torch, [fn], 20) * 1e-6
             if name.startswith("w4a8_gemm_grouped"):
                 gsz = 32 if name.endswith("_32") else 256
                 extras[name] = {"workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], weight scales per "
-                                            f"{gsz} codes, bf16 out",
+                                            f"{gsz} codes, bf16 out (one operand set)",
                                 "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
                                 "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
             else:
@@ -450,16 +553,10 @@ def main():
             a8 = torch.randint(-8, 8, (GEMM_M, GEMM_K), dtype=torch.int8, device=dev)
             w8 = torch.randint(-8, 8, (GEMM_N, GEMM_K), dtype=torch.int8, device=dev)
             c32 = torch._int_mm(a8, w8.t())
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(20):
-                c32 = torch._int_mm(a8, w8.t())
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / 20
+            t = time_back_to_back(torch, [lambda: torch._int_mm(a8, w8.t())], 20) * 1e-6
             extras["library_int8_gemm"] = {
-                "workload": "torch._int_mm int8 [4096, 4096] x int8 [4096, 11008]^T -> int32 (unpacked codes, no epilogue)",
+                "workload": "torch._int_mm int8 [4096, 4096] x int8 [4096, 11008]^T -> int32 (unpacked codes, "
+                            "no epilogue, one operand set)",
                 "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
                 "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
             del a8, w8, c32
@@ -473,47 +570,29 @@ def main():
         inv = 10000.0 ** (-torch.arange(D // 2, dtype=torch.float64, device=dev) * 2.0 / D)
         th = torch.outer(torch.arange(S, dtype=torch.float64, device=dev), inv)
         cs, sn = torch.cos(th).float(), torch.sin(th).float()
-        o = sets["kv_out"][0]
 
         def rope_torch(x):
             xf = x.float()
             a, b = xf[..., : D // 2], xf[..., D // 2:]
             return torch.cat([a * cs - b * sn, b * cs + a * sn], dim=-1).to(x.dtype)
 
-        def fused(i):
-            rbq.kv_rotate_quant(sets["kv_q"][i], sets["kv_k"][i], rope_cos=cs, rope_sin=sn, **o)
-
-        def unfused(i):
-            rbq.kv_rotate_quant(rope_torch(sets["kv_q"][i]), rope_torch(sets["kv_k"][i]), **o)
-
-        for name, fn in (("rope_r3_fused", fused), ("rope_r3_unfused_torch", unfused)):
-            fn(0)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for r in range(8):
-                fn(r % NSETS)
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / 8
+        fused = [lambda i=i: rbq.kv_rotate_quant(sets["kv_q"][i], sets["kv_k"][i], rope_cos=cs, rope_sin=sn,
+                                                 **sets["kv_out"][i]) for i in range(NSETS)]
+        unfused = [lambda i=i: rbq.kv_rotate_quant(rope_torch(sets["kv_q"][i]), rope_torch(sets["kv_k"][i]),
+                                                   **sets["kv_out"][i]) for i in range(NSETS)]
+        for name, fns in (("rope_r3_fused", fused), ("rope_r3_unfused_torch", unfused)):
+            fns[0]()
+            t = time_back_to_back(torch, fns, 8) * 1e-6
             extras[name] = {"workload": "pre-RoPE bf16 Q and K [16, 32, 2048, 128] -> RoPE -> R3 -> packed INT4",
                             "avg_us": round(t * 1e6, 3), "GB_s": round(KV_BYTES / t / 1e9, 2)}
     if run_r4 and not args.no_extras:
         # the randomized transform H diag(s) / sqrt(n) on the same workload and buffers
         sg = torch.from_numpy(workloads.gen_signs(0, R4_N)).to(dev).to(torch.bfloat16)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NSETS + 1)]
-        for i in range(NSETS):
-            rbq.hadamard_quant_int4(sets["r4_x"][i], codes=sets["r4_codes"][i], scales=sets["r4_scales"][i], signs=sg)
-        ts = []
-        for rep in range(5):
-            for i in range(NSETS):
-                ev[2 * i].record()
-                rbq.hadamard_quant_int4(sets["r4_x"][i], codes=sets["r4_codes"][i], scales=sets["r4_scales"][i],
-                                        signs=sg)
-                ev[2 * i + 1].record()
-            torch.cuda.synchronize()
-            ts += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(NSETS)]
-        t = float(np.mean(ts)) * 1e-3
+        fns = [lambda i=i: rbq.hadamard_quant_int4(sets["r4_x"][i], codes=sets["r4_codes"][i],
+                                                   scales=sets["r4_scales"][i], signs=sg) for i in range(NSETS)]
+        for f in fns:
+            f()
+        t = time_back_to_back(torch, fns, 20) * 1e-6
         extras["randomized_r4"] = {
             "workload": "R4 bf16 [8192, 16384] with a seeded +-1 diagonal (H diag(s) / sqrt(n))",
             "avg_us": round(t * 1e6, 3), "GB_s": round(R4_BYTES / t / 1e9, 2),
@@ -529,16 +608,9 @@ def main():
         vscales = torch.from_numpy(workloads.gen_scales(32, B * H * S, "float16")).to(dev).reshape(B, H, S)
         qdec = sets["kv_q"][0][:, :, -1, :].contiguous()
         aout = torch.empty_like(qdec)
-        fn = lambda: rbq.attention_decode_int4kv(qdec, kc, ks, vcodes, vscales, 1.0 / math.sqrt(D), out=aout)
+        fn = lambda: rbq.attention_decode_int4kv(qdec, kc, ks, vcodes, vscales, 1.0 / math.sqrt(D), out=aout)  # noqa
         fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / 20
+        t = time_back_to_back(torch, [fn], 20) * 1e-6
         nbytes = 2 * B * H * S * (D // 2 + 2) + 2 * B * H * D * 2
         extras["attention_decode_int4kv"] = {
             "workload": "one query per (batch, head) over INT4 K and V caches [16, 32, 2048, 128], fp16 scales",
@@ -555,18 +627,10 @@ def main():
         kx = [k0] + [torch.roll(k0, shifts=97 * i, dims=0).contiguous() for i in range(1, NSETS)]
         kc = [torch.empty((R4_TOKENS, KRON_N // 2), dtype=torch.uint8, device=dev) for _ in range(NSETS)]
         ks = [torch.empty((R4_TOKENS,), dtype=torch.float16, device=dev) for _ in range(NSETS)]
-        for i in range(NSETS):
-            rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i])
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NSETS)]
-        ts = []
-        for rep in range(max(1, args.steps // NSETS)):
-            for i in range(NSETS):
-                ev[2 * i].record()
-                rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i])
-                ev[2 * i + 1].record()
-            torch.cuda.synchronize()
-            ts += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(NSETS)]
-        t = float(np.mean(ts)) * 1e-3
+        fns = [lambda i=i: rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i]) for i in range(NSETS)]
+        for f in fns:
+            f()
+        t = time_back_to_back(torch, fns, max(args.steps, 8)) * 1e-6
         extras["kron_r4_14336"] = {
             "workload": "R4 bf16 [8192, 14336] = (H_28 (x) H_512) / sqrt(n), packed INT4 + fp16 scales",
             "avg_us": round(t * 1e6, 3), "GB_s": round(KRON_BYTES / t / 1e9, 2),
@@ -585,7 +649,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(float(np.mean(step_ms)), 4),
+        "prewarm_ms": round(prewarm_ms, 1),
+        "prewarm_steps": pre,
+        "ms_per_step": round(step_ms, 4),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -597,6 +663,8 @@ def main():
                         "step also runs R3 Q/K [16,32,2048,128] and the W4A4 GEMM 4096x11008x4096",
             "tokens": R4_TOKENS, "n": R4_N, "input_sets_rotated": NSETS,
         },
+        "timing": "ms_per_step: events around the timed steps; kernels: events around --steps "
+                  "back-to-back launches of one kernel over the rotated sets",
         "gemm": kernels.get("w4a4_gemm"),
         "kernels": kernels,
         "roofline": roofline,

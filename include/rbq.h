@@ -323,6 +323,27 @@ rbq_status hadamard_kron_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n,
  */
 rbq_status rbq_kron_factor(int64_t n, int64_t *m);
 
+/*
+ * rbq_hbm_probe -- measurement only, not part of the method: a streaming kernel shaped
+ * like the row kernels above, whose rate is the ceiling this device reaches for a given
+ * mix of HBM reads and writes (the published 8 TB/s is the other reference). Workgroup b
+ * reads bytes [b * read_bytes_per_block, (b + 1) * read_bytes_per_block) of src with
+ * 16-byte loads, then writes bytes [b * write_bytes_per_block, ...) of dst with a value
+ * derived from what it read.
+ *
+ *  src      device buffer of blocks * read_bytes_per_block bytes (may be NULL when
+ *           read_bytes_per_block is 0), 16-byte aligned, read only.
+ *  dst      device buffer of blocks * write_bytes_per_block bytes, 16-byte aligned; with
+ *           write_bytes_per_block == 0 it must hold 16 * blocks bytes, of which a
+ *           workgroup writes one word only when its folded loads equal 0x9E3779B9.
+ *  read_bytes_per_block, write_bytes_per_block  multiples of 4096, not both 0.
+ *  blocks   number of workgroups (0 returns RBQ_OK).
+ * Errors: RBQ_EINVAL for NULL or misaligned buffers, negative sizes or sizes that are not
+ * multiples of 4096; RBQ_EHIP if the launch fails.
+ */
+rbq_status rbq_hbm_probe(const void *src, int64_t read_bytes_per_block, void *dst,
+                         int64_t write_bytes_per_block, int64_t blocks, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *rbq_status_string(rbq_status s);
 

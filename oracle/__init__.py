@@ -47,7 +47,7 @@ from .quant import (
     quantize_groups,
 )
 from .gemm import int_gemm, w4a4_gemm, w4a8_gemm, w4a8_gemm_grouped
-from .rope import rope_exact, rope_16bit
+from .rope import rope_exact, rope_16bit, rope_16bit_ambiguous, round_to_format
 from .attention import attention_decode
 from .kron import legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron
 
@@ -79,6 +79,8 @@ __all__ = [
     "quantize_groups",
     "rope_exact",
     "rope_16bit",
+    "rope_16bit_ambiguous",
+    "round_to_format",
     "legendre",
     "paley_kind",
     "paley_hadamard",

@@ -43,6 +43,7 @@ __all__ = [
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
     "attention_decode_int4kv",
+    "hbm_probe",
     "RBQ_OK",
     "RBQ_EINVAL",
     "RBQ_ENOTSUP",
@@ -73,6 +74,7 @@ EXPORTED_SYMBOLS = (
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
     "attention_decode_int4kv",
+    "rbq_hbm_probe",
     "rbq_status_string",
     "rbq_version",
 )
@@ -137,6 +139,8 @@ def lib():
     L.attention_decode_int4kv.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
                                           ctypes.c_float, vp, vp]
     L.attention_decode_int4kv.restype = ci
+    L.rbq_hbm_probe.argtypes = [vp, i64, vp, i64, i64, vp]
+    L.rbq_hbm_probe.restype = ci
     L.rbq_status_string.argtypes = [ci]
     L.rbq_status_string.restype = ctypes.c_char_p
     L.rbq_version.argtypes = []
@@ -539,3 +543,19 @@ def attention_decode_int4kv(q, k_codes, k_scales, v_codes, v_scales, softmax_sca
                                        float(softmax_scale), _ptr(out), _stream(stream, dev))
     _check("attention_decode_int4kv", st)
     return out
+
+
+def hbm_probe(src, read_bytes_per_block, dst, write_bytes_per_block, blocks, *, stream=None):
+    """Measurement only: the streaming probe of the C ABI (rbq_hbm_probe). ``src`` and
+    ``dst`` are GPU tensors of at least blocks * read / write bytes per block (``dst`` at
+    least 16 * blocks bytes when nothing is written per block)."""
+    _require_cuda(src, dst)
+    need_src = int(blocks) * int(read_bytes_per_block)
+    need_dst = int(blocks) * (int(write_bytes_per_block) if write_bytes_per_block else 16)
+    if src.numel() * src.element_size() < need_src or dst.numel() * dst.element_size() < need_dst:
+        raise ValueError("probe buffers are smaller than the blocks would touch")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("probe buffers must be contiguous")
+    st = lib().rbq_hbm_probe(_ptr(src), int(read_bytes_per_block), _ptr(dst), int(write_bytes_per_block),
+                             int(blocks), _stream(stream, dst.device))
+    _check("rbq_hbm_probe", st)

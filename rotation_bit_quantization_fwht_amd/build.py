@@ -50,6 +50,7 @@ def _units():
     units.append((os.path.join(CSRC, "w4a4_gemm.hip"), "w4a4_gemm.o", []))
     units.append((os.path.join(CSRC, "group_quant.hip"), "group_quant.o", []))
     units.append((os.path.join(CSRC, "attention.hip"), "attention.o", []))
+    units.append((os.path.join(CSRC, "probe.hip"), "probe.o", []))
     units.append((os.path.join(CSRC, "status.cpp"), "status.o", ["-x", "hip"]))
     return units
 

@@ -7,6 +7,7 @@
  * Usage: abi_client validate | abi_client inject. Exit status 0 = all checks passed;
  * each failed check prints one line. */
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "rbq.h"
@@ -31,6 +32,15 @@ static int failures = 0;
 
 int main(int argc, char **argv) {
   const int inject = argc > 1 && strcmp(argv[1], "inject") == 0;
+  if (inject) {
+    /* the valid calls below pass fake addresses: without the switch that stops every
+       launch they would reach the device, so refuse to run them at all */
+    const char *fi = getenv("RBQ_FAULT_INJECT");
+    if (!fi || strcmp(fi, "launch") != 0) {
+      puts("abi_client inject: RBQ_FAULT_INJECT=launch is required (refusing to make calls that would launch)");
+      return 2;
+    }
+  }
   const rbq_status launched = inject ? RBQ_EHIP : RBQ_OK;
   const int64_t B = 2, H = 4, S = 16, D = 128;
   const int64_t st[4] = {H * S * D, S * D, D, 1};
@@ -75,6 +85,10 @@ int main(int argc, char **argv) {
   EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 3, 16, 16, 128, 0.1f, PX, NULL),
          RBQ_EINVAL);
   EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4000, PX, NULL, NULL), RBQ_ENOTSUP);
+  EXPECT(rbq_hbm_probe(PX, 4000, PC, 4096, 8, NULL), RBQ_EINVAL);
+  EXPECT(rbq_hbm_probe(PX, 0, PC, 0, 8, NULL), RBQ_EINVAL);
+  EXPECT(rbq_hbm_probe(PX, 4096, NULL, 4096, 8, NULL), RBQ_EINVAL);
+  EXPECT(rbq_hbm_probe(PX, 4096, PC, 4096, 0, NULL), RBQ_OK);
   EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 60, 4096, PX, NULL, NULL), RBQ_ENOTSUP);
 
   /* valid calls: only reached in inject mode, where nothing is launched */
@@ -96,6 +110,7 @@ int main(int argc, char **argv) {
            launched);
     EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
     EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
+    EXPECT(rbq_hbm_probe(PX, 65536, PC, 16384, 8, NULL), launched);
   }
 
   printf("%s: %d failure(s)\n", inject ? "inject" : "validate", failures);

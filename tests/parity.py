@@ -96,3 +96,67 @@ def check_quant(q_gpu, s_gpu, ref, scale_dtype, x64, rotate=True, y_gpu=None, n=
     assert n_bad == 0, f"{n_bad} code differences are not one-step near-tie flips"
     assert n_flips <= FLIP_BUDGET * q_gpu.size, f"{n_flips} code flips exceed 1e-4 of {q_gpu.size}"
     return stats
+
+
+def rope_values_matching(x16, cos, sin, fmt, score, max_amb=8):
+    """The RoPE'd rows [rows, D] (float64) to compare a fused RoPE + R3 result with.
+
+    The oracle's RoPE is the exact map rounded once to ``fmt`` (oracle.rope_16bit). A device
+    evaluates the map in float32 first, which can round an element to the other neighbour
+    where the exact value lies within float32 error of a rounding midpoint (flagged by
+    oracle.rope_16bit_ambiguous). Rows without such an element use the oracle's values;
+    for a row with flagged elements every combination of the two neighbours is a correct
+    input, and the one with the lowest ``score(row_index, values)`` is taken.
+    Returns (values, number of rows with flagged elements)."""
+    val, other, amb = oracle.rope_16bit_ambiguous(x16, cos, sin, fmt)
+    xr = val.copy()
+    rows = np.nonzero(amb.any(axis=1))[0]
+    for r in rows:
+        idx = np.nonzero(amb[r])[0]
+        assert len(idx) <= max_amb, f"row {r}: {len(idx)} ambiguous RoPE elements"
+        best, best_v = None, None
+        for m in range(1 << len(idx)):
+            v = val[r].copy()
+            for j, i in enumerate(idx):
+                if (m >> j) & 1:
+                    v[i] = other[r, i]
+            sc = score(r, v)
+            if best is None or sc < best:
+                best, best_v = sc, v
+        xr[r] = best_v
+    return xr, len(rows)
+
+
+def check_rope_quant(q_gpu, s_gpu, x16, cos, sin, fmt, scale_dtype="float16", y_gpu=None):
+    """check_quant for a fused RoPE -> rotation -> INT4 result. x16 [rows, D] holds the 16-bit
+    inputs as float64, cos/sin the float32 tables broadcast to [rows, D/2]."""
+    q_gpu = np.asarray(q_gpu)
+    s_gpu = np.asarray(s_gpu, dtype=np.float64)
+
+    def score(r, v):
+        ref = oracle.hadamard_quant_int4(v[None], scale_dtype, packed=False)
+        return (int(ref["s_stored"][0] != s_gpu[r]), int(np.sum(ref["q"][0] != q_gpu[r])))
+
+    xr, n_amb = rope_values_matching(x16, cos, sin, fmt, score)
+    ref = oracle.hadamard_quant_int4(xr, scale_dtype, packed=False)
+    st = check_quant(q_gpu, s_gpu, ref, scale_dtype, xr, y_gpu=y_gpu)
+    st["rope_ambiguous_rows"] = n_amb
+    return st
+
+
+def check_rope_rotated(got, x16, cos, sin, fmt):
+    """A fused RoPE -> rotation result written in the 16-bit format (float64 values of the
+    bf16/fp16 output): equal to the oracle's rotation of the RoPE'd rows rounded to the
+    format, except for rare one-step differences at rounding midpoints (the transform runs
+    in float32)."""
+    got = np.asarray(got, dtype=np.float64)
+
+    def want_of(v):
+        return oracle.round_to_format(oracle.rotate(v[None])[0], fmt)
+
+    xr, n_amb = rope_values_matching(x16, cos, sin, fmt, lambda r, v: int(np.sum(want_of(v) != got[r])))
+    want = oracle.round_to_format(oracle.rotate(xr), fmt)
+    step = 2.0 ** -7 if fmt == "bfloat16" else 2.0 ** -10
+    assert np.all(np.abs(got - want) <= np.abs(want) * step + 2.0 ** -24)
+    assert np.mean(got == want) > 0.999
+    return {"rope_ambiguous_rows": n_amb, "equal_fraction": float(np.mean(got == want))}

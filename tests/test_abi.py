@@ -224,11 +224,21 @@ def test_fault_injection_reports_launch_failure(abi_client):
     assert p.returncode == 0, p.stdout + p.stderr
 
 
+def test_inject_mode_refuses_without_the_switch(abi_client):
+    """inject mode passes fake addresses to valid calls: without RBQ_FAULT_INJECT=launch it
+    must stop before any call instead of letting them launch."""
+    p = _run_client(abi_client, "inject")
+    assert p.returncode == 2, p.stdout + p.stderr
+    assert "RBQ_FAULT_INJECT=launch is required" in p.stdout
+    p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="other")
+    assert p.returncode == 2, p.stdout + p.stderr
+
+
 def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 12, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 13, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
@@ -239,6 +249,7 @@ def test_dispatch_log(abi_client):
     assert lines[9].startswith("rbq: attention_decode_int4kv B=2 H=8 Hkv=2 S=16")
     assert lines[10].startswith("rbq: w4a4_gemm M=64 N=64 K=4096 tiles=1")
     assert lines[11].startswith("rbq: w4a8_gemm M=64")
+    assert lines[12].startswith("rbq: hbm_probe read=65536 write=16384 blocks=8")
 
 
 def test_kron_validation_and_factor(L):

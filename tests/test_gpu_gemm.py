@@ -97,6 +97,29 @@ def test_gemm_full_size_sampled(rbq):
     assert np.array_equal(acc.astype(np.int64).sum(axis=0), w_codes @ a_codes.sum(axis=0))
 
 
+def test_gemm_full_size_rotated_workload(rbq):
+    """The GEMM workload end to end at its full shape, M=4096, N=11008, K=4096, on the
+    oracle's codes of the rotated workload (A: bf16 activations with an outlier channel x60,
+    W: fp32 N(0, 0.02^2) weights, both rotated by H_4096 / 64 and quantized per row):
+    sampled rows exactly, every accumulator through its row and column sums."""
+    M, N, K = 4096, 11008, 4096
+    print("case w4a4_gemm full size on rotated workload codes (oracle quantizes A and W)", flush=True)
+    ab, w, _ = workloads.gen_gemm_inputs(seed=0)
+    ra = oracle.hadamard_quant_int4(workloads.to_float64(ab, "bfloat16"), "float16", packed=True)
+    del ab
+    rw = oracle.hadamard_quant_int4(w.astype(np.float64), "float16", packed=True)
+    del w
+    print("case w4a4_gemm full size: oracle codes ready, launching", flush=True)
+    acc, out = run(rbq, ra["codes"], ra["scales"], rw["codes"], rw["scales"])
+    a_codes = ra["q"].astype(np.int64)
+    w_codes = rw["q"].astype(np.int64)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(6).integers(0, M, 28)]))
+    acc_ref = oracle.int_gemm(a_codes[rows], w_codes)
+    check_out(acc[rows], out[rows], acc_ref, ra["s_stored"][rows], rw["s_stored"])
+    assert np.array_equal(acc.astype(np.int64).sum(axis=1), a_codes @ w_codes.sum(axis=0))
+    assert np.array_equal(acc.astype(np.int64).sum(axis=0), w_codes @ a_codes.sum(axis=0))
+
+
 # ------------------------------------------------------------------------------ W4A8
 
 def gen_int8_codes(seed, rows, k):

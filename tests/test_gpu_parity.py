@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import check_quant
+from parity import check_quant, check_rope_quant, check_rope_rotated
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,32 @@ def test_rotate_quant_all_sizes(rbq, k, dtype):
     x64 = workloads.to_float64(x, dtype)
     ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
     check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64, y_gpu=rot.cpu().numpy())
+
+
+@pytest.mark.parametrize("signed", [False, True])
+@pytest.mark.parametrize("k", list(range(1, 16)))
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16", "float32"])
+def test_codes_only_all_sizes(rbq, k, dtype, signed):
+    """The default call: packed codes and fp16 scales with no rotated output. For 16-bit
+    inputs this is its own kernel build (codes-only, with its own register budget and
+    waves per SIMD), the one the benchmark times; every row length, with and without the
+    randomized diagonal, element by element against the oracle."""
+    n, rows = 1 << k, ROWS[k]
+    print(f"case codes-only k={k} dtype={dtype} signed={signed} rows={rows}", flush=True)
+    x = workloads.gen_rows(300 + k, rows, n, dtype, kind="swiglu", n_outliers=2, factor=150)
+    xd = to_dev(x, dtype)
+    x64 = workloads.to_float64(x, dtype)
+    if signed:
+        s32 = workloads.gen_signs(k + 40, n)
+        sd = torch.from_numpy(s32).to("cuda").to({"float32": torch.float32, "bfloat16": torch.bfloat16,
+                                                 "float16": torch.float16}[dtype])
+        ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, signs=s32)
+        codes, scales = rbq.hadamard_quant_int4(xd, signs=sd)
+    else:
+        ref = oracle.hadamard_quant_int4(x64, "float16", packed=False)
+        codes, scales = rbq.hadamard_quant_int4(xd)
+    torch.cuda.synchronize()
+    check_quant(unpack(codes), scales.cpu().numpy(), ref, "float16", x64)
 
 
 @pytest.mark.parametrize("k", [1, 4, 7, 12, 14, 15])
@@ -318,8 +344,9 @@ def rope_tables(positions, d, base=10000.0):
     ("bfloat16", "contiguous", 3, (2, 6, 80)), ("bfloat16", "bshd_view", 0, (4, 5, 48)),
     ("float16", "contiguous", 0, (1, 4, 16)), ("float16", "bshd_view", 9, (8, 2, 272))])
 def test_kv_rope_small(rbq, dtype, layout, pos0, bhs):
-    """kv_rope_rotate_quant: RoPE (half-split, fp32 arithmetic rounded to the 16-bit
-    format) then R3 and INT4, on Q and K, against the oracle's RoPE + rotation + quantizer."""
+    """kv_rope_rotate_quant: RoPE (half-split; the oracle evaluates it exactly and rounds it
+    once to the 16-bit format, accepting the other neighbour only where float32 evaluation
+    error reaches a rounding midpoint) then R3 and INT4, on Q and K."""
     B, H, S = bhs
     D = 128
     print(f"case kv rope {dtype} {layout} pos0={pos0} B,H,S={bhs}", flush=True)
@@ -337,12 +364,13 @@ def test_kv_rope_small(rbq, dtype, layout, pos0, bhs):
                               rope_pos0=pos0)
     pos = pos0 + np.arange(S)
     rows = B * H * S
+    cr = np.broadcast_to(cos[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+    sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
     for name, bits in (("q", q_bits), ("k", k_bits)):
-        xr = oracle.rope_16bit(workloads.to_float64(bits, dtype), cos[pos][None, None], sin[pos][None, None], dtype)
-        xr = xr.reshape(rows, D)
-        ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
+        x16 = workloads.to_float64(bits, dtype).reshape(rows, D)
         got_q = oracle.unpack_nibbles(out[f"{name}_codes"].cpu().numpy().reshape(rows, D // 2))
-        check_quant(got_q, out[f"{name}_scales"].cpu().numpy().reshape(rows), ref, "float16", xr)
+        st = check_rope_quant(got_q, out[f"{name}_scales"].cpu().numpy().reshape(rows), x16, cr, sr, dtype)
+        print(f"  {name}: {st}", flush=True)
 
 
 @pytest.mark.parametrize("bhs", [(1, 3, 37), (2, 2, 64)])
@@ -359,17 +387,13 @@ def test_kv_rope_q_rotate_only(rbq, bhs):
                               rope_pos0=2)
     pos = 2 + np.arange(S)
     rows = B * H * S
-    qr = oracle.rope_16bit(workloads.to_float64(q_bits, "bfloat16"), cos[pos][None, None], sin[pos][None, None],
-                           "bfloat16")
-    got = out["q_rotated"].float().cpu().numpy().astype(np.float64)
-    want = oracle.round_to_bf16(oracle.rotate(qr))
-    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7)
-    assert np.mean(got == want) > 0.999
-    kr = oracle.rope_16bit(workloads.to_float64(k_bits, "bfloat16"), cos[pos][None, None], sin[pos][None, None],
-                           "bfloat16").reshape(rows, D)
-    ref = oracle.hadamard_quant_int4(kr, "float16", packed=False)
-    check_quant(oracle.unpack_nibbles(out["k_codes"].cpu().numpy().reshape(rows, D // 2)),
-                out["k_scales"].cpu().numpy().reshape(rows), ref, "float16", kr)
+    cr = np.broadcast_to(cos[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+    sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+    got = out["q_rotated"].float().cpu().numpy().astype(np.float64).reshape(rows, D)
+    check_rope_rotated(got, workloads.to_float64(q_bits, "bfloat16").reshape(rows, D), cr, sr, "bfloat16")
+    check_rope_quant(oracle.unpack_nibbles(out["k_codes"].cpu().numpy().reshape(rows, D // 2)),
+                     out["k_scales"].cpu().numpy().reshape(rows),
+                     workloads.to_float64(k_bits, "bfloat16").reshape(rows, D), cr, sr, "bfloat16")
 
 
 def test_kv_rope_full_size_and_errors(rbq):
@@ -385,11 +409,10 @@ def test_kv_rope_full_size_and_errors(rbq):
     rng = np.random.default_rng(5)
     flat = rng.integers(0, B * H * S, 40)
     b, h, s = flat // (H * S), (flat // S) % H, flat % S
-    xr = oracle.rope_16bit(workloads.to_float64(k_bits[b, h, s], "bfloat16"), cos[64 + s], sin[64 + s], "bfloat16")
-    ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
     kc = out["k_codes"].cpu().numpy().reshape(B * H * S, D // 2)[flat]
     ks = out["k_scales"].cpu().numpy().reshape(B * H * S)[flat]
-    check_quant(oracle.unpack_nibbles(kc), ks, ref, "float16", xr)
+    check_rope_quant(oracle.unpack_nibbles(kc), ks, workloads.to_float64(k_bits[b, h, s], "bfloat16"),
+                     cos[64 + s], sin[64 + s], "bfloat16")
     qa = oracle.unpack_nibbles(out["q_codes"].cpu().numpy().reshape(B * H * S, D // 2))
     assert np.all(np.max(np.abs(qa), axis=1) == 7) and not np.any(qa == -8)
     with pytest.raises(rbq.RBQError):   # tables too short for rope_pos0 + seq

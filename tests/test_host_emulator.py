@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import check_quant
+from parity import check_quant, check_rope_quant
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -262,7 +262,8 @@ def rope_tables(positions, d, base=10000.0):
     ("bfloat16", "flat", 7, False, (2, 2, 48)), ("bfloat16", "bshd", 0, True, (1, 8, 32)),
     ("float16", "bshd", 2, False, (4, 3, 16)), ("float16", "flat", 0, True, (3, 4, 64))])
 def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
-    """RoPE (half-split pairs, fp32 arithmetic, rounded to the 16-bit format) ahead of R3,
+    """RoPE (half-split pairs, the oracle's exact map rounded once to the 16-bit format,
+    either neighbour accepted where float32 error reaches a rounding midpoint) ahead of R3,
     on flat and strided [B, H, S, D] addressing, against the oracle's RoPE + rotation."""
     B, H, S = bhs
     D = 128
@@ -279,9 +280,9 @@ def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
     else:
         codes, scales, yr = run_emu(emu, tmp_path, q_bits.reshape(rows, D), dtype, 7, rows, mode=mode,
                                     fast=fast, bhs=(B, H, S), rope=(cos, sin, pos0))
-    x = workloads.to_float64(q_bits, dtype)
+    x = workloads.to_float64(q_bits, dtype).reshape(rows, D)
     pos = pos0 + np.arange(S)
-    xr = oracle.rope_16bit(x, cos[pos][None, None], sin[pos][None, None], dtype).reshape(rows, D)
-    ref = oracle.hadamard_quant_int4(xr, "float16", packed=False)
-    check_quant(oracle.unpack_nibbles(codes), scales, ref, "float16", xr, y_gpu=None if fast else yr)
+    cr = np.broadcast_to(cos[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+    sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+    check_rope_quant(oracle.unpack_nibbles(codes), scales, x, cr, sr, dtype, y_gpu=None if fast else yr)
 

@@ -564,19 +564,97 @@ def test_rope_scores_depend_on_relative_position_only():
         assert abs(a - b) < 1e-10 * (1 + abs(b))
 
 
-def test_rope_16bit_is_the_exact_map_rounded_to_the_format():
-    """The float32 evaluation only moves a result across a bfloat16 rounding boundary when
-    the exact value sits within float32 error of it: rare, and then by one bf16 step."""
+def _all_16bit_values(fmt):
+    """Every finite value of the format with its bit pattern, decoded from the bit fields
+    (sign, exponent, significand) by hand: float64 values and the significand's low bit."""
+    pat = np.arange(1 << 16, dtype=np.int64)
+    if fmt == "bfloat16":
+        ebits, mbits, bias = 8, 7, 127
+    else:
+        ebits, mbits, bias = 5, 10, 15
+    sign = np.where(pat >> 15, -1.0, 1.0)
+    e = (pat >> mbits) & ((1 << ebits) - 1)
+    m = pat & ((1 << mbits) - 1)
+    finite = e != (1 << ebits) - 1
+    normal = np.ldexp(1.0 + m / float(1 << mbits), (e - bias).astype(np.int64))
+    sub = np.ldexp(m / float(1 << mbits), 1 - bias)
+    val = sign * np.where(e == 0, sub, normal)
+    return val[finite], (m[finite] & 1)
+
+
+@pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
+def test_round_to_format_is_nearest_even_by_brute_force(fmt):
+    vals, low_bit = _all_16bit_values(fmt)
+    order = np.argsort(vals, kind="stable")
+    vals, low_bit = vals[order], low_bit[order]
+    keep = np.concatenate([[True], np.diff(vals) > 0])  # +0 and -0 collapse
+    vals, low_bit = vals[keep], low_bit[keep]
+    rng = np.random.default_rng(11)
+    lim = 60000.0 if fmt == "float16" else 1e30
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 5, 4000),
+                        rng.uniform(-lim, lim, 1000)])
+    # exact midpoints between neighbours, where only the tie rule decides
+    i = rng.integers(len(vals) // 4, 3 * len(vals) // 4, 500)
+    v = np.concatenate([v, 0.5 * (vals[i] + vals[i + 1])])
+    if fmt == "float16":
+        v = v[np.abs(v) < 65504.0]
+    got = oracle.round_to_format(v, fmt)
+    j = np.clip(np.searchsorted(vals, v), 1, len(vals) - 1)
+    lo, hi = vals[j - 1], vals[j]
+    want = np.where(v - lo < hi - v, lo, np.where(v - lo > hi - v, hi, np.where(low_bit[j - 1] == 0, lo, hi)))
+    want = np.where(v == hi, hi, want)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_rope_16bit_rounds_the_exact_map_once():
+    """A value exactly halfway between two bfloat16 neighbours goes to the even one; the
+    float32 evaluation can land on either side, so the element is flagged with the other
+    neighbour."""
+    x = np.zeros((1, 4))
+    x[0, 0] = 1.0
+    c = np.array([[1.0 + 2.0 ** -8, 1.0]], dtype=np.float32)
+    s = np.zeros((1, 2), dtype=np.float32)
+    val, other, amb = oracle.rope_16bit_ambiguous(x, c, s, "bfloat16")
+    np.testing.assert_array_equal(val, oracle.rope_16bit(x, c, s, "bfloat16"))
+    assert val[0, 0] == 1.0 and other[0, 0] == 1.0 + 2.0 ** -7 and amb[0, 0]
+    assert val[0, 2] == 0.0 and not amb[0, 2]
+    # a value just off the midpoint, beyond the float32 error bound: unambiguous
+    c2 = np.array([[1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0]], dtype=np.float32)
+    val, other, amb = oracle.rope_16bit_ambiguous(x, c2, s, "bfloat16")
+    assert val[0, 0] == 1.0 + 2.0 ** -7 and not amb[0, 0]
+
+
+def _f32_eval_rope(x, c, s, fmt):
+    """The map evaluated in IEEE float32 (NumPy), each product and the sum rounded, then
+    rounded to the format (an implementation's arithmetic, used only to test the bound)."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    a, b = x[..., : d // 2], x[..., d // 2:]
+    lo = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+    hi = (b * c).astype(np.float32) + (a * s).astype(np.float32)
+    r = np.concatenate([lo, hi], axis=-1).astype(np.float32)
+    if fmt == "float16":
+        return r.astype(np.float16).astype(np.float64)
+    bits = r.view(np.uint32).astype(np.uint64)
+    rounded = ((bits + np.uint64(0x7FFF) + ((bits >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
+def test_rope_ambiguity_covers_every_float32_evaluation(fmt):
+    """Where an element is not flagged, a float32 evaluation gives exactly the oracle's
+    value; where it is flagged, it gives the value or the flagged neighbour."""
     d = 128
-    x = workloads.bf16_bits_to_f32(workloads.gen_rows(5, 512, d, "bfloat16")).astype(np.float64)
-    th = _angles(np.arange(512), d)
+    bits = workloads.gen_rows(5, 2048, d, fmt, n_outliers=2, factor=50)
+    x = workloads.to_float64(bits, fmt)
+    th = _angles(np.arange(2048), d)
     c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
-    got = oracle.rope_16bit(x, c, s, "bfloat16")
-    ref = oracle.round_to_bf16(oracle.rope_exact(x, c.astype(np.float64), s.astype(np.float64)))
-    diff = got != ref
-    assert np.mean(diff) < 1e-3
-    ulp = np.abs(ref[diff]) * 2.0 ** -7
-    assert np.all(np.abs(got[diff] - ref[diff]) <= ulp * 1.0001)
+    val, other, amb = oracle.rope_16bit_ambiguous(x, c, s, fmt)
+    f32 = _f32_eval_rope(x, c, s, fmt)
+    assert np.array_equal(f32[~amb], val[~amb])
+    assert np.all((f32[amb] == val[amb]) | (f32[amb] == other[amb]))
+    assert 0 < np.mean(amb) < 5e-3  # rare, and the float32 result does differ somewhere
+    assert np.any(f32 != val)
 
 
 # ------------------------------------------------------------ lengths that are not powers of two
