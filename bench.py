@@ -637,6 +637,24 @@ def main():
             "frac_hbm_peak": round(KRON_BYTES / t / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": load_traffic("hadamard_kron_quant_int4", kernel_source_hash(KRON_SOURCES))}
         del kx, kc, ks, k0
+        # the GEMM workload's FFN width 11008 = 172 * 64 (the Goethals-Seidel factor)
+        n2 = 11008
+        kb, _ = workloads.gen_ffn(seed=0, n=n2)
+        k0 = to_dev16(kb)
+        del kb
+        kx = [k0] + [torch.roll(k0, shifts=97 * i, dims=0).contiguous() for i in range(1, NSETS)]
+        kc = [torch.empty((R4_TOKENS, n2 // 2), dtype=torch.uint8, device=dev) for _ in range(NSETS)]
+        ks = [torch.empty((R4_TOKENS,), dtype=torch.float16, device=dev) for _ in range(NSETS)]
+        fns = [lambda i=i: rbq.hadamard_kron_quant_int4(kx[i], codes=kc[i], scales=ks[i]) for i in range(NSETS)]
+        for f in fns:
+            f()
+        t = time_back_to_back(torch, fns, max(args.steps, 8)) * 1e-6
+        nbytes = 8192 * n2 * 2 + 8192 * n2 // 2 + 8192 * 2
+        extras["kron_r4_11008"] = {
+            "workload": "bf16 [8192, 11008] = (H_172 (x) H_64) / sqrt(n), Goethals-Seidel H_172, packed INT4 + fp16 scales",
+            "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2),
+            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del kx, kc, ks, k0
 
     cpu = None
     if not args.no_cpu_baseline:

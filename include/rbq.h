@@ -294,14 +294,21 @@ rbq_status quantize_groups_int4(const void *y, rbq_dtype dtype, int64_t K, int64
  * lengths use the Kronecker product of a power-of-two Hadamard matrix with a small known
  * one). n = m * p with p a power of two, and each row is rotated by
  * (H_m (x) H_p) / sqrt(n), element a * p + b of the row being index (a, b) of the
- * product; H_p is the Sylvester matrix and H_m the Paley matrix of order m:
+ * product; H_p is the Sylvester matrix and H_m one of:
  *   Paley I (q = m - 1 prime, q = 3 mod 4): I + [[0, 1...], [-1..., Q]],
  *     Q[a][b] = chi(a - b) with chi the quadratic character of GF(q);
  *   Paley II (q = m/2 - 1 prime, q = 1 mod 4): the conference matrix [[0, 1...], [1..., Q]]
- *     with each 0 replaced by [[1, -1], [-1, -1]] and each +-1 by +-[[1, 1], [1, -1]].
+ *     with each 0 replaced by [[1, -1], [-1, -1]] and each +-1 by +-[[1, 1], [1, -1]];
+ *   m = 172: the Goethals-Seidel array [[A, BR, CR, DR], [-BR, A, D^T R, -C^T R],
+ *     [-CR, -D^T R, A, B^T R], [-DR, C^T R, -B^T R, A]] (R the back-diagonal permutation)
+ *     of circulant +-1 matrices A, B, C, D of order 43 whose periodic autocorrelations
+ *     add up to zero at every nonzero shift; their first rows are constant on the cosets
+ *     of the order-7 subgroup of (Z/43)^* and are the lexicographically first such
+ *     quadruple (+1 at 0 for bit 0 of a code, +1 on the j-th coset for bit j, cosets by
+ *     smallest element). This covers the FFN width 11008 = 172 * 64.
  * m is the smallest of 4o, 8o, 16o, ... (o the odd part of n, m <= 256, m dividing n) with
- * such a construction (rbq_kron_factor reports it). The quantizer, the codes and the
- * scales are those of hadamard_quant_int4.
+ * one of these constructions (rbq_kron_factor reports it). The quantizer, the codes and
+ * the scales are those of hadamard_quant_int4.
  *
  *  x, x_dtype, tokens, x_row_stride, codes, scales, scale_dtype, rotated: as for
  *               hadamard_quant_int4; x rows 16-byte aligned.
@@ -309,7 +316,8 @@ rbq_status quantize_groups_int4(const void *y, rbq_dtype dtype, int64_t K, int64
  *  flags        RBQ_PACKED only.
  * Errors: RBQ_EINVAL for the argument errors of hadamard_quant_int4 and for flags other
  * than RBQ_PACKED; RBQ_ENOTSUP when n has no factor by the rule above or the kernel does
- * not take it (m > 160, p < 16, p > 2048); RBQ_EHIP if the launch fails.
+ * not take it (p < 16, p > 2048, or the [m, p] row buffer and the m x m operand table
+ * exceed 160 KiB of LDS, e.g. 172 * 128); RBQ_EHIP if the launch fails.
  */
 rbq_status hadamard_kron_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n, int64_t tokens,
                                     int64_t x_row_stride, void *codes, void *scales,
@@ -317,7 +325,7 @@ rbq_status hadamard_kron_quant_int4(const void *x, rbq_dtype x_dtype, int64_t n,
                                     hipStream_t stream);
 
 /*
- * rbq_kron_factor -- the order m of the Paley factor hadamard_kron_quant_int4 uses for a
+ * rbq_kron_factor -- the order m of the small factor hadamard_kron_quant_int4 uses for a
  * row length n (1 for a power of two). Host only, no HIP call.
  * Errors: RBQ_EINVAL for n < 1 or m == NULL; RBQ_ENOTSUP when the rule finds no factor.
  */

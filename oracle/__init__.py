@@ -49,7 +49,8 @@ from .quant import (
 from .gemm import int_gemm, w4a4_gemm, w4a8_gemm, w4a8_gemm_grouped
 from .rope import rope_exact, rope_16bit, rope_16bit_ambiguous, round_to_format
 from .attention import attention_decode
-from .kron import legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron
+from .kron import (legendre, paley_kind, paley_hadamard, kron_factor, kron_hadamard, rotate_kron,
+                   gs_first_rows, goethals_seidel_hadamard, small_hadamard, periodic_autocorrelation)
 
 __all__ = [
     "sylvester",
@@ -87,5 +88,9 @@ __all__ = [
     "kron_factor",
     "kron_hadamard",
     "rotate_kron",
+    "gs_first_rows",
+    "goethals_seidel_hadamard",
+    "small_hadamard",
+    "periodic_autocorrelation",
     "attention_decode",
 ]

@@ -7,8 +7,8 @@ The calls have the same names and meaning as the C functions declared in
   symmetric INT4 absmax quantization (round half to even), codes packed two per byte
   (optionally the randomized transform with a +-1 diagonal);
 * ``hadamard_kron_quant_int4`` -- the same for row lengths that are not powers of two,
-  rotated by the Kronecker product of a Paley matrix with a Sylvester matrix
-  (``kron_factor`` reports the Paley order);
+  rotated by the Kronecker product of a Paley or Goethals-Seidel matrix with a Sylvester matrix
+  (``kron_factor`` reports the order of the small factor);
 * ``hadamard_quant_int8`` -- the same with INT8 codes;
 * ``kv_rotate_quant`` -- the same per (batch, head, token) vector of post-RoPE Q and K
   (optionally with RoPE applied first);
@@ -246,7 +246,7 @@ def hadamard_quant_int4(x, *, scale_dtype=None, packed=True, rotate=True, codes=
 
 
 def kron_factor(n):
-    """Order m of the Paley factor used for row length n (1 for a power of two), or None
+    """Order m of the small factor used for row length n (1 for a power of two), or None
     when the library has no factorization for n."""
     m = ctypes.c_int64(0)
     st = lib().rbq_kron_factor(int(n), ctypes.byref(m))

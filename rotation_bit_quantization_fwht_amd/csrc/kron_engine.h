@@ -37,7 +37,7 @@
 namespace rbq {
 
 constexpr uint32_t kKronMaxWaves = 8;              // LDS slots for the per-wave maxima
-constexpr uint32_t kKronMaxM = 160;                  // largest Paley order the kernel takes
+constexpr uint32_t kKronMaxM = 256;                  // largest factor order the kernel takes
 constexpr uint32_t kKronMaxKB = kKronMaxM / 32;      // 32-row K blocks of the MFMA
 constexpr uint32_t kKronMaxN = 32768;
 constexpr uint32_t kKronMinP = 16;
@@ -50,10 +50,11 @@ struct KronArgs {
   void* codes;         // uint8 [rows, n/2] (packed) or int8 [rows, n]
   void* scales;        // [rows] fp32 or fp16
   float* rot32;        // optional [rows, n]
-  uint32_t m, q, paley;  // paley 1: m = q + 1; paley 2: m = 2 (q + 1)
+  uint32_t m, q, paley;  // paley 1: m = q + 1; paley 2: m = 2 (q + 1); 3: Goethals-Seidel, m = 4 q
   uint32_t p_log;
   uint32_t opts;         // OPT_PACKED, OPT_SCALE_F16
-  uint32_t qr[8];        // bit d: d is a nonzero square modulo q (q < 256)
+  uint32_t qr[8];        // Paley: bit d is set iff d is a nonzero square modulo q (q < 256);
+                         // Goethals-Seidel: the first rows of A, B, C, D, two words each
   float sqrtn;           // sqrt(n) rounded to float
   float inv_sqrtn;       // 1 / sqrt(n) rounded to float
   uint32_t rs;           // LDS words per row a of the [m][p] buffer (p + 4)
@@ -94,10 +95,35 @@ RBQ_HD int kron_chi(const uint32_t* qr, uint32_t d) {
   return ((qr[d >> 5] >> (d & 31)) & 1u) ? 1 : -1;
 }
 
-// Entry (r, c) of the Paley matrix. Paley I: I + [[0, 1...], [-1..., Q]] with
+// Entry (i, j) of block (R, C) of the Goethals-Seidel array
+//   [[ A, BR, CR, DR], [-BR, A, D^T R, -C^T R], [-CR, -D^T R, A, B^T R], [-DR, C^T R, -B^T R, A]]
+// on circulants of order q with first rows in qr (two words per matrix). With
+// X[i][j] = x[(j - i) mod q]: X = x[(j - i)], X R = x[(q - 1 - i - j)], X^T R = x[(i + j + 1)].
+RBQ_HD int gs_entry(uint32_t q, const uint32_t* qr, uint32_t r, uint32_t c) {
+  // per block b = 4 R + C, two bits each: the matrix (0..3 = A..D) and the form
+  // (0: X, 1: X R, 2: X^T R); one bit each: a negative sign. Rows of the array:
+  //   mat  0 1 2 3 | 1 0 3 2 | 2 3 0 1 | 3 2 1 0
+  //   form 0 1 1 1 | 1 0 2 2 | 1 2 0 2 | 1 2 2 0
+  //   neg  0 0 0 0 | 1 0 0 1 | 1 1 0 0 | 1 0 1 0
+  constexpr uint32_t kMat = 0x1b4eb1e4u, kForm = 0x2989a154u, kNeg = 0x5390u;
+  const uint32_t R = r / q, C = c / q, i = r - R * q, j = c - C * q;
+  const uint32_t b = 4 * R + C;
+  const uint32_t mat = (kMat >> (2 * b)) & 3u, form = (kForm >> (2 * b)) & 3u;
+  uint32_t t;
+  if (form == 0) t = (j + q - i) % q;
+  else if (form == 1) t = (2 * q - 1 - i - j) % q;
+  else t = (i + j + 1) % q;
+  const uint32_t w = qr[2 * mat + (t >> 5)];
+  const int v = ((w >> (t & 31)) & 1u) ? 1 : -1;
+  return ((kNeg >> b) & 1u) ? -v : v;
+}
+
+// Entry (r, c) of the small factor. Paley I: I + [[0, 1...], [-1..., Q]] with
 // Q[a][b] = chi(a - b). Paley II: the conference matrix [[0, 1...], [1..., Q]] with each
-// 0 replaced by [[1, -1], [-1, -1]] and each +-1 by +-[[1, 1], [1, -1]].
+// 0 replaced by [[1, -1], [-1, -1]] and each +-1 by +-[[1, 1], [1, -1]]. Kind 3: the
+// Goethals-Seidel array above.
 RBQ_HD int paley_entry(uint32_t paley, uint32_t q, const uint32_t* qr, uint32_t r, uint32_t c) {
+  if (paley == 3) return gs_entry(q, qr, r, c);
   if (paley == 1) {
     if (r == c || r == 0) return 1;
     if (c == 0) return -1;
@@ -404,7 +430,9 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
   }
 }
 
-// KS 1: the kernel for one K block (m <= 32); KS 0: the kernel for two or more
+// KS 1: the kernel for one K block (m <= 32); KS 0: two to five (m <= 160); KS 2: six to
+// eight (m <= 256). Each range is its own kernel, so the register budget of the larger
+// orders does not weigh on the smaller ones.
 template <int IN, int KS>
 constexpr uint32_t kron_body_waves() { return KS == 1 ? kron_waves<IN, 1>() : kron_waves<IN, 2>(); }
 
@@ -437,12 +465,18 @@ RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t gri
 
   if constexpr (KS == 1) {
     kron_rows<IN, 1>(c, a, wg, grid);
-  } else {
+  } else if constexpr (KS == 0) {
     switch (KB) {
       case 2: kron_rows<IN, 2>(c, a, wg, grid); break;
       case 3: kron_rows<IN, 3>(c, a, wg, grid); break;
       case 4: kron_rows<IN, 4>(c, a, wg, grid); break;
       default: kron_rows<IN, 5>(c, a, wg, grid); break;
+    }
+  } else {
+    switch (KB) {
+      case 6: kron_rows<IN, 6>(c, a, wg, grid); break;
+      case 7: kron_rows<IN, 7>(c, a, wg, grid); break;
+      default: kron_rows<IN, 8>(c, a, wg, grid); break;
     }
   }
 }

@@ -1,5 +1,5 @@
 // HIP kernels and C-ABI entry points of the rotation + INT4 quantizer for row lengths
-// that are not powers of two (n = m * p, H_m (x) H_p with a Paley factor; the body is in
+// that are not powers of two (n = m * p, H_m (x) H_p with a Paley or Goethals-Seidel factor; the body is in
 // kron_engine.h, the choice of m in kron_factor.h). Powers of two go to the
 // power-of-two path of hadamard_quant_int4.
 #include <hip/hip_runtime.h>
@@ -15,8 +15,9 @@ namespace rbq {
 
 // LW: LDS words of the variant (32 KiB, 80 KiB or 160 KiB), the smallest that holds the
 // row buffer and the operand table; smaller variants keep more workgroups per CU.
-// KS 1: rows with one K block of the MFMA (m <= 32), KS 0: the others; each has its own
-// wave count and register budget (8 waves at up to 128 VGPRs, or 4 at up to 256).
+// KS 1: rows with one K block of the MFMA (m <= 32), KS 0: two to five (m <= 160), KS 2:
+// six to eight (m <= 256); each has its own wave count and register budget (8 waves at
+// up to 128 VGPRs, or 4 at up to 256).
 template <int IN, uint32_t LW, int KS>
 __global__ __launch_bounds__((64 * kron_body_waves<IN, KS>()))
 __attribute__((amdgpu_waves_per_eu(kron_body_waves<IN, KS>() == 8u ? 4 : 2)))
@@ -62,7 +63,10 @@ static hipError_t kron_launch_ks(const KronArgs& a, uint32_t words, hipStream_t 
 
 template <int IN>
 static hipError_t kron_launch_in(const KronArgs& a, uint32_t words, hipStream_t s) {
-  return a.m <= 32u ? kron_launch_ks<IN, 1>(a, words, s) : kron_launch_ks<IN, 0>(a, words, s);
+  if (a.m <= 32u) return kron_launch_ks<IN, 1>(a, words, s);
+  if (a.m <= 160u) return kron_launch_ks<IN, 0>(a, words, s);
+  // orders above 160: the operand table alone takes more than 80 KiB
+  return kron_launch_lw<IN, 40960u, 2>(a, s);
 }
 
 }  // namespace rbq

@@ -67,7 +67,7 @@ int main(int argc, char **argv) {
   EXPECT(kv_rope_rotate_quant(PX, PX, RBQ_BF16, B, H, S, D, st, st, (const float *)PS, (const float *)PS, S, 1,
                               PC, PS, PC, PS, RBQ_F16, NULL, 0, NULL),
          RBQ_EINVAL);
-  EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 11008, 8, 11008, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
+  EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 16640, 8, 16640, PC, PS, RBQ_F16, NULL, RBQ_PACKED, NULL),
          RBQ_ENOTSUP);
   EXPECT(hadamard_kron_quant_int4(PX, RBQ_BF16, 5120, 8, 5120, PC, PS, RBQ_F16, NULL, RBQ_NO_ROTATE, NULL),
          RBQ_EINVAL);
@@ -75,7 +75,9 @@ int main(int argc, char **argv) {
     int64_t m = 0;
     EXPECT(rbq_kron_factor(14336, &m), RBQ_OK);
     if (m != 28) { printf("FAIL kron factor of 14336: %lld\n", (long long)m); ++failures; }
-    EXPECT(rbq_kron_factor(11008, &m), RBQ_ENOTSUP);
+    EXPECT(rbq_kron_factor(11008, &m), RBQ_OK);
+    if (m != 172) { printf("FAIL kron factor of 11008: %lld\n", (long long)m); ++failures; }
+    EXPECT(rbq_kron_factor(16640, &m), RBQ_ENOTSUP);
     EXPECT(rbq_kron_factor(0, &m), RBQ_EINVAL);
   }
   EXPECT(quantize_groups_int4(PX, RBQ_F32, 4096, 8, 4096, 48, PC, PS, RBQ_F16, RBQ_PACKED, NULL), RBQ_EINVAL);

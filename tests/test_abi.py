@@ -259,8 +259,9 @@ def test_kron_validation_and_factor(L):
         return L.hadamard_kron_quant_int4(x, dt, n, tokens, stride or n, A16b, A16c, sdt, NULL, flags, NULL)
 
     assert hk(tokens=0) == rbq.RBQ_OK
-    assert hk(n=11008) == NS          # 172 and 344 have no Paley construction over a prime
-    assert hk(n=252 * 16) == NS       # Paley order 252 is above what the kernel takes
+    assert hk(n=16640) == NS          # 65 * 256: no construction of order 260 or below
+    assert hk(n=172 * 128) == NS      # the row buffer and the table exceed a workgroup's LDS
+    assert hk(n=252 * 32) == NS       # likewise for Paley order 252 with p = 32
     assert hk(n=12 * 8) == NS         # p = 8 < 16
     assert hk(n=6) == NS              # no factor
     assert hk(n=40000) == E

@@ -37,7 +37,10 @@ def to_dev(x, dtype):
 # (n, rows): Paley I and II factors of orders 12 .. 148, p from 16 to 2048; ragged row
 # counts; the 32 KiB, 80 KiB and 160 KiB LDS variants
 CASES = [(192, 37), (1536, 67), (2560, 41), (5120, 29), (3584, 33), (9216, 17), (6912, 19), (12288, 9),
-         (13824, 7), (14336, 9), (18944, 5), (24576, 5), (28672, 3)]
+         (13824, 7), (14336, 9), (18944, 5), (24576, 5), (28672, 3),
+         # the Goethals-Seidel order 172 (11008 = 172 * 64, the GEMM workload's FFN width), and
+         # Paley orders above 160 with up to eight K blocks of the MFMA
+         (11008, 13), (2752, 21), (5504, 11), (2624, 9), (3136, 9), (6784, 5), (4032, 9)]
 
 
 @pytest.mark.parametrize("n,rows", CASES)
@@ -103,10 +106,12 @@ def test_kron_edge_tokens_zero_rows_and_powers_of_two(rbq):
 
 
 def test_kron_unsupported_lengths_raise(rbq):
-    x = torch.zeros((2, 11008), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(rbq.RBQError) as e:
-        rbq.hadamard_kron_quant_int4(x)
-    assert e.value.status == rbq.RBQ_ENOTSUP
+    # 16640 = 65 * 256: no construction; 22016 = 172 * 128: more LDS than a workgroup has
+    for n in (16640, 22016):
+        x = torch.zeros((2, n), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(rbq.RBQError) as e:
+            rbq.hadamard_kron_quant_int4(x)
+        assert e.value.status == rbq.RBQ_ENOTSUP
 
 
 def test_kron_full_size_14336(rbq):
@@ -121,6 +126,28 @@ def test_kron_full_size_14336(rbq):
     torch.cuda.synchronize()
     assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
     rows = np.unique(np.concatenate([[0, 1, 8191], np.random.default_rng(4).integers(0, 8192, 21)]))
+    x64 = workloads.to_float64(xbits[rows], "bfloat16")
+    ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, kron=True)
+    c = codes.cpu().numpy()
+    check_quant(oracle.unpack_nibbles(c[rows]), scales.cpu().numpy()[rows], ref, "float16", x64)
+    q_all = oracle.unpack_nibbles(c)
+    assert np.all(np.max(np.abs(q_all), axis=1) == 7)
+    assert not np.any(q_all == -8)
+
+
+def test_kron_full_size_11008(rbq):
+    """FFN width 11008 = 172 * 64 (the Goethals-Seidel factor), bf16 [8192, 11008] with the
+    R4 workload's recipe: sampled rows against the oracle, every row against the
+    invariants, two calls bit-identical."""
+    print("case kron full size 8192x11008", flush=True)
+    assert rbq.kron_factor(11008) == 172
+    xbits, ch = workloads.gen_ffn(seed=0, n=11008)
+    xd = to_dev(xbits, "bfloat16")
+    codes, scales = rbq.hadamard_kron_quant_int4(xd)
+    codes2, scales2 = rbq.hadamard_kron_quant_int4(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes2) and torch.equal(scales, scales2)
+    rows = np.unique(np.concatenate([[0, 1, 8191], np.random.default_rng(7).integers(0, 8192, 29)]))
     x64 = workloads.to_float64(xbits[rows], "bfloat16")
     ref = oracle.hadamard_quant_int4(x64, "float16", packed=False, kron=True)
     c = codes.cpu().numpy()

@@ -723,10 +723,63 @@ def test_kron_factor_rule_by_hand():
     # n -> m by the rule: smallest 4o 2^j dividing n with a Paley construction over a prime
     cases = {4096: 1, 16384: 1, 24: 12, 1536: 12, 12288: 12, 2560: 20, 5120: 20, 3584: 28,
              14336: 28, 28672: 28, 9216: 36, 13824: 108, 27648: 108, 18944: 148,
-             11008: None,   # 172 = 4 * 43: 171 and 85 are not prime; 344: 343, 171 neither
+             11008: 172,    # 172 = 4 * 43: 171 and 85 are not prime; the Goethals-Seidel order
+             22016: 172, 2752: 172, 16640: None,   # 65 * 256: 260 is above 256
+             2624: 164, 3136: 196, 6784: 212, 4032: 252,
              6: None, 12: 12, 3: None, 7 * 4096: 28}
     for n, m in cases.items():
         assert oracle.kron_factor(n) == m, n
+
+
+def test_order_7_subgroup_and_cosets_mod_43_by_hand():
+    from oracle import kron as K
+    assert K.primitive_root(43) == 3
+    # 3^6 = 729 = 41 (mod 43) generates {1, 41, 4, 35, 16, 11, 21}
+    want = {1, 4, 11, 16, 21, 35, 41}
+    assert {pow(41, k, 43) for k in range(7)} == want
+    x = K.gs_coset_sequence(0b1000001)  # +1 at 0 and on the sixth coset (the one holding 9)
+    cosets, seen = [], set()
+    for t in range(1, 43):
+        if t not in seen:
+            c = {(t * u) % 43 for u in want}
+            seen |= c
+            cosets.append(sorted(c))
+    assert [c[0] for c in cosets] == [1, 2, 3, 6, 7, 9]
+    assert x[0] == 1 and all(x[c] == 1 for c in cosets[5]) and all(x[t] == -1 for c in cosets[:5] for t in c)
+
+
+def test_goethals_seidel_order_172_is_hadamard():
+    rows = oracle.gs_first_rows()
+    assert rows.shape == (4, 43) and set(np.unique(rows)) == {-1, 1}
+    # zero periodic autocorrelation sum at every nonzero shift, row sums squares add to 172
+    total = sum(oracle.periodic_autocorrelation(x) for x in rows)
+    assert np.all(total == 0)
+    assert int(np.sum(rows.sum(axis=1) ** 2)) == 172
+    H = oracle.goethals_seidel_hadamard()
+    assert set(np.unique(H)) == {-1.0, 1.0}
+    assert np.array_equal(H @ H.T, 172 * np.eye(172))
+    # a wrong sign or transposition anywhere in the array breaks orthogonality
+    from oracle import kron as K
+    a, b, c, d = [K.circulant(x) for x in rows]
+    r = np.fliplr(np.eye(43))
+    bad = np.block([[a, b @ r, c @ r, d @ r], [-b @ r, a, d @ r, -c.T @ r],
+                    [-c @ r, -d.T @ r, a, b.T @ r], [-d @ r, c.T @ r, -b.T @ r, a]])
+    assert not np.array_equal(bad @ bad.T, 172 * np.eye(172))
+
+
+def test_periodic_autocorrelation_brute_force():
+    x = np.array([1, -1, -1, 1, 1, 1, -1])
+    want = [sum(x[t] * x[(t + s) % 7] for t in range(7)) for s in range(1, 7)]
+    assert oracle.periodic_autocorrelation(x).tolist() == want
+
+
+@pytest.mark.parametrize("n", [2752])
+def test_rotate_kron_goethals_seidel_equals_explicit_kronecker_matrix(n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((2, n))
+    H = oracle.kron_hadamard(n)
+    assert np.array_equal(H @ H.T, n * np.eye(n))
+    np.testing.assert_allclose(oracle.rotate_kron(x), x @ H.T / np.sqrt(n), rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("n", [24, 40, 48, 56, 96, 144, 160, 224, 320])
