@@ -165,11 +165,12 @@ rbq_status kv_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_
  *               aligned, owned by the caller, read only.
  *  rope_positions  rows of the tables; rope_pos0 + seq must not exceed it.
  *  rope_pos0    position of token 0 (>= 0), e.g. the cache length when appending.
- *  head_dim     128 (other sizes return RBQ_ENOTSUP).
+ *  head_dim     64, 128 or 256 (other sizes return RBQ_ENOTSUP).
  *  all other arguments as for kv_rotate_quant (RBQ_Q_ROTATE_ONLY writes RoPE'd and
  *  rotated Q in bf16/fp16).
  * Errors: as kv_rotate_quant, plus RBQ_EINVAL for NULL or misaligned tables, a negative
- * rope_pos0 or tables that do not cover the positions; RBQ_ENOTSUP for head_dim != 128.
+ * rope_pos0 or tables that do not cover the positions; RBQ_ENOTSUP for head_dim other
+ * than 64, 128 and 256.
  */
 rbq_status kv_rope_rotate_quant(const void *q, const void *k, rbq_dtype dtype, int64_t batch,
                                 int64_t heads, int64_t seq, int64_t head_dim,
@@ -178,6 +179,51 @@ rbq_status kv_rope_rotate_quant(const void *q, const void *k, rbq_dtype dtype, i
                                 int64_t rope_positions, int64_t rope_pos0, uint8_t *q_codes,
                                 void *q_scales, uint8_t *k_codes, void *k_scales,
                                 rbq_dtype scale_dtype, void *q_rotated, unsigned flags,
+                                hipStream_t stream);
+
+/*
+ * kv_cache_append_int4 -- one attention step's writes to the KV4 cache: RoPE, then the R3
+ * rotation H_D / sqrt(D), then INT4 for the keys, written straight into the cache at
+ * positions pos0 .. pos0 + seq - 1 ("SpinQuant, when rotations are worth learning",
+ * section "Four rotation sites": R3 follows RoPE so that the KV cache can be quantized;
+ * "SpinQuant Guide: Learned Rotations for 4-Bit LLMs", the transformer-block figure: keys
+ * stored in the KV cache as INT4). Values are quantized to INT4 per (batch, head, token)
+ * without a rotation (their rotation R2 is folded offline into the weights) and appended
+ * the same way; queries get RoPE and R3 and are written in the input's 16-bit format, the
+ * operand attention_decode_int4kv takes. RoPE and the quantizer are those of
+ * kv_rope_rotate_quant and kv_rotate_quant (codes two per byte, low nibble first, one scale
+ * per (batch, head, token)); keys and values of tokens outside the written positions are
+ * left as they are. Two launches on `stream` (queries and keys, then values).
+ *
+ *  q            optional [batch, heads, seq, head_dim] (NULL: no query output), element
+ *               strides q_strides[4] in (b, h, s, d) order, d stride 1, vectors 16-byte
+ *               aligned; dtype BF16 or F16 (k and v the same).
+ *  k, v         [batch, kv_heads, seq, head_dim], strides k_strides[4] / v_strides[4] as for q.
+ *  heads        query heads, a multiple of kv_heads (grouped heads share a key/value head).
+ *  head_dim     64, 128 or 256 (other powers of two: RBQ_ENOTSUP).
+ *  rope_cos, rope_sin  optional fp32 [rope_positions, head_dim / 2] tables as for
+ *               kv_rope_rotate_quant (both NULL: queries and keys are taken as already
+ *               rotated by RoPE); token s of this call sits at position pos0 + s.
+ *  pos0         first cache position written (>= 0), the number of tokens already cached.
+ *  seq_cap      cache capacity per (batch, kv head); pos0 + seq <= seq_cap.
+ *  q_rotated    with q: [batch, heads, seq, head_dim] contiguous, 16-byte aligned, in q's dtype:
+ *               H RoPE(q) / sqrt(D) rounded to nearest even.
+ *  k_cache, v_cache  uint8 [batch, kv_heads, seq_cap, head_dim / 2] contiguous, 16-byte aligned.
+ *  k_cache_scales, v_cache_scales  [batch, kv_heads, seq_cap] contiguous in scale_dtype (F16 or F32).
+ * Errors: RBQ_EINVAL for NULL required pointers (q and q_rotated go together), bad dtypes,
+ * negative sizes, heads not a multiple of kv_heads, pos0 + seq > seq_cap, a d stride != 1,
+ * misalignment, one RoPE table without the other or tables that do not cover the positions;
+ * RBQ_ENOTSUP for head_dim other than 64, 128 and 256; an empty problem (batch, kv_heads or
+ * seq == 0) returns RBQ_OK; RBQ_EHIP if a launch fails.
+ */
+rbq_status kv_cache_append_int4(const void *q, const void *k, const void *v, rbq_dtype dtype,
+                                int64_t batch, int64_t heads, int64_t kv_heads, int64_t seq,
+                                int64_t head_dim, const int64_t q_strides[4],
+                                const int64_t k_strides[4], const int64_t v_strides[4],
+                                const float *rope_cos, const float *rope_sin,
+                                int64_t rope_positions, int64_t pos0, int64_t seq_cap,
+                                void *q_rotated, uint8_t *k_cache, void *k_cache_scales,
+                                uint8_t *v_cache, void *v_cache_scales, rbq_dtype scale_dtype,
                                 hipStream_t stream);
 
 /*

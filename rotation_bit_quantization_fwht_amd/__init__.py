@@ -38,6 +38,7 @@ __all__ = [
     "hadamard_kron_quant_int4",
     "kron_factor",
     "kv_rotate_quant",
+    "kv_cache_append_int4",
     "w4a4_gemm",
     "w4a8_gemm",
     "w4a8_gemm_grouped",
@@ -69,6 +70,7 @@ EXPORTED_SYMBOLS = (
     "rbq_kron_factor",
     "kv_rotate_quant",
     "kv_rope_rotate_quant",
+    "kv_cache_append_int4",
     "w4a4_gemm",
     "w4a8_gemm",
     "w4a8_gemm_grouped",
@@ -128,6 +130,9 @@ def lib():
     L.kv_rope_rotate_quant.argtypes = [vp, vp, ci, i64, i64, i64, i64, p64, p64, vp, vp, i64, i64,
                                        vp, vp, vp, vp, ci, vp, cu, vp]
     L.kv_rope_rotate_quant.restype = ci
+    L.kv_cache_append_int4.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, p64, p64, p64, vp, vp, i64, i64,
+                                       i64, vp, vp, vp, vp, vp, ci, vp]
+    L.kv_cache_append_int4.restype = ci
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
     L.w4a4_gemm.restype = ci
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, vp, vp, vp]
@@ -389,6 +394,57 @@ def kv_rotate_quant(q, k, *, scale_dtype=None, q_rotate_only=False, q_codes=None
     )
     _check("kv_rotate_quant", st)
     return out
+
+
+def kv_cache_append_int4(k, v, k_cache, k_cache_scales, v_cache, v_cache_scales, pos0, *, q=None, q_rotated=None,
+                         rope_cos=None, rope_sin=None, stream=None):
+    """Append one step's keys and values to the INT4 cache: ``k``, ``v`` [B, Hkv, S, D]
+    (bf16/fp16, D contiguous, any other strides) go through RoPE at positions pos0 + s
+    (when the float32 tables ``rope_cos``/``rope_sin`` [positions, D/2] are given) and, for
+    the keys, the rotation H_D / sqrt(D), are quantized to INT4 and written to rows
+    pos0 .. pos0 + S - 1 of ``k_cache``/``v_cache`` uint8 [B, Hkv, cap, D/2] and
+    ``k_cache_scales``/``v_cache_scales`` [B, Hkv, cap]. With ``q`` [B, H, S, D] the queries
+    get RoPE and the rotation and are returned in q's dtype (``q_rotated``, allocated if not
+    given); otherwise None is returned."""
+    torch = _torch()
+    _require_cuda(k, v, k_cache, k_cache_scales, v_cache, v_cache_scales)
+    if k.dim() != 4 or v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must be [B, Hkv, S, D] tensors of one shape and dtype")
+    B, Hkv, S, D = k.shape
+    cap = k_cache.shape[2] if k_cache.dim() == 4 else -1
+    dev = k.device
+    _require_buffer("k_cache", k_cache, (B, Hkv, cap, D // 2), (torch.uint8,), dev)
+    _require_buffer("v_cache", v_cache, (B, Hkv, cap, D // 2), (torch.uint8,), dev)
+    _require_buffer("k_cache_scales", k_cache_scales, (B, Hkv, cap), (torch.float16, torch.float32), dev)
+    _require_buffer("v_cache_scales", v_cache_scales, (B, Hkv, cap), (k_cache_scales.dtype,), dev)
+    H = Hkv
+    if q is not None:
+        _require_cuda(q)
+        if q.dim() != 4 or q.shape[0] != B or q.shape[2] != S or q.shape[3] != D or q.dtype != k.dtype:
+            raise ValueError("q must be [B, H, S, D] in k's dtype")
+        H = q.shape[1]
+        if q_rotated is None:
+            q_rotated = torch.empty((B, H, S, D), dtype=q.dtype, device=dev)
+        _require_buffer("q_rotated", q_rotated, (B, H, S, D), (q.dtype,), dev)
+    elif q_rotated is not None:
+        raise ValueError("q_rotated needs q")
+    P = 0
+    if rope_cos is not None or rope_sin is not None:
+        if rope_cos is None or rope_sin is None:
+            raise ValueError("rope_cos and rope_sin go together")
+        _require_cuda(rope_cos, rope_sin)
+        P = rope_cos.shape[0] if rope_cos.dim() == 2 else -1
+        _require_buffer("rope_cos", rope_cos, (P, D // 2), (torch.float32,), dev)
+        _require_buffer("rope_sin", rope_sin, (P, D // 2), (torch.float32,), dev)
+    qs = (ctypes.c_int64 * 4)(*q.stride()) if q is not None else None
+    ks = (ctypes.c_int64 * 4)(*k.stride())
+    vs = (ctypes.c_int64 * 4)(*v.stride())
+    st = lib().kv_cache_append_int4(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(k.dtype), B, H, Hkv, S, D, qs, ks, vs, _ptr(rope_cos),
+        _ptr(rope_sin), P, int(pos0), cap, _ptr(q_rotated), _ptr(k_cache), _ptr(k_cache_scales), _ptr(v_cache),
+        _ptr(v_cache_scales), _dtype_code(k_cache_scales.dtype), _stream(stream, dev))
+    _check("kv_cache_append_int4", st)
+    return q_rotated
 
 
 def w4a4_gemm(qa, sa, qw, sw, *, out=None, acc=None, return_acc=False, stream=None):

@@ -53,11 +53,15 @@ struct TensorArgs {
   const float* rope_sin;   // pairing element i with i + n/2 at position rope_pos0 + s
   uint32_t rope_pos0;
   uint32_t mode;
+  int64_t rows;            // rows of this tensor
+  uint32_t out_cap;        // 0: codes and scales rows follow the input rows; else the rows
+                           // of (batch, head) pair bh go to bh * out_cap + s (a cache of
+                           // capacity out_cap per head, its base pointers at the first
+                           // position written)
 };
 
 struct KArgs {
   TensorArgs t[2];
-  int64_t rows;       // rows per tensor
   uint32_t blocks0;   // row blocks of tensor 0 (blocks past it belong to tensor 1)
   uint32_t nblocks;   // row blocks in total; workgroups loop over them with a stride
   uint32_t opts;
@@ -158,6 +162,55 @@ RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
   }
 }
 
+// output row (codes, scales) of input row r: r itself, or with CACHE and t.out_cap != 0 row
+// s of (batch, head) pair bh = r / seq in a cache of t.out_cap rows per pair
+template <bool CACHE>
+RBQ_HD int64_t out_row(const TensorArgs& t, int64_t r) {
+  if constexpr (CACHE) {
+    if (t.out_cap != 0u)
+      return r + (int64_t)fastdiv((uint32_t)r, t.div_s) * (int64_t)(t.out_cap - t.seq);
+  }
+  return r;
+}
+
+// RoPE on one row held whole in this lane's registers (rows of at most 64 elements): w holds
+// the row's 16-bit values two per word, element i in half i % 2 of word i / 2; element i
+// pairs with i + n/2. Same arithmetic as apply_rope below.
+template <int K, int IN, class Ctx>
+RBQ_HD void apply_rope_in_lane(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t (&w)[1 << (K - 1)]) {
+  constexpr uint32_t H = 1u << (K - 1);  // pairs, and the words of one half
+  const uint32_t srow = row - fastdiv(row, t.div_s) * t.seq;
+  const float* cp = t.rope_cos + (int64_t)(t.rope_pos0 + srow) * H;
+  const float* sp = t.rope_sin + (int64_t)(t.rope_pos0 + srow) * H;
+  static_for<0, (int)(H / 8)>([&](auto G) {  // eight pairs at a time: four words of each half
+    constexpr int g = G.value;
+    const f32x4 c0 = c.template load<f32x4>(cp + 8 * g), c1 = c.template load<f32x4>(cp + 8 * g + 4);
+    const f32x4 s0 = c.template load<f32x4>(sp + 8 * g), s1 = c.template load<f32x4>(sp + 8 * g + 4);
+    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    static_for<0, 4>([&](auto D) {
+      constexpr int lo = 4 * g + D.value, hi = lo + (int)(H / 2);
+      float rl[2], rh[2];
+      static_for<0, 2>([&](auto HALF) {
+        constexpr int j = 2 * D.value + HALF.value;
+        const uint32_t ab = (w[lo] >> (16 * HALF.value)) & 0xFFFFu;
+        const uint32_t bb = (w[hi] >> (16 * HALF.value)) & 0xFFFFu;
+        const float a = (IN == IN_F16) ? f16_to_f32(ab) : bits_f32(ab << 16);
+        const float b = (IN == IN_F16) ? f16_to_f32(bb) : bits_f32(bb << 16);
+        rl[HALF.value] = a * cs[j] - b * sn[j];
+        rh[HALF.value] = b * cs[j] + a * sn[j];
+      });
+      if constexpr (IN == IN_F16) {
+        w[lo] = f32_to_f16(rl[0]) | (f32_to_f16(rl[1]) << 16);
+        w[hi] = f32_to_f16(rh[0]) | (f32_to_f16(rh[1]) << 16);
+      } else {
+        w[lo] = f32x2_to_bf16x2(rl[0], rl[1]);
+        w[hi] = f32x2_to_bf16x2(rh[0], rh[1]);
+      }
+    });
+  });
+}
+
 // ------------------------------------------------------------------ load (phase 0)
 
 // address of element `el` of row `row0 + rw` (rw < 2^r): a uniform 64-bit block base plus
@@ -174,7 +227,7 @@ RBQ_HD const char* in_addr(const TensorArgs& t, int64_t row0, uint32_t rw, uint3
   }
 }
 
-template <int K, bool MF, int IN, bool ROT, bool FOURD, class Ctx>
+template <int K, bool MF, int IN, bool ROT, bool FOURD, bool ROPE, class Ctx>
 RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                         Regs<K, MF>& v) {
   constexpr int C0 = run_log(RBQ_PLAN, 0);
@@ -226,6 +279,10 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
         sw[0] = c.template load<uint32_t>(sp);
       }
       static_for<0, BYTES / 4>([&](auto I) { w[I.value] ^= sw[I.value] & SIGN; });
+    }
+    if constexpr (ROPE) {
+      static_assert(IN != IN_F32 && C0 == K && NRUN == 1, "RoPE in the load needs a whole 16-bit row per lane");
+      apply_rope_in_lane<K, IN>(c, t, (uint32_t)(row0 + rw), w);
     }
     if constexpr (IN == IN_F32) {
       static_for<0, L>([&](auto I) { v[rb + I.value] = bits_f32(w[I.value]); });
@@ -411,7 +468,7 @@ RBQ_HD float round_quotient_exact(float u, float mk, float d) {
 
 // FAST: only packed codes and scales are written (no unpacked codes, no rotated rows), so
 // the kernel carries no registers for the other outputs
-template <int K, bool MF, int PH, bool ROT, int IN, bool FAST, class Ctx>
+template <int K, bool MF, int PH, bool ROT, int IN, bool FAST, bool CACHE, class Ctx>
 RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
                    Regs<K, MF>& v) {
   constexpr int E = 1 << RBQ_PLAN.e;
@@ -479,9 +536,10 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     if (FAST || (mode & MODE_QUANT)) {
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
       const uint32_t rw = ONE_ROW ? 0u : ((lp | rp) >> K);
-      if (leader && (ONE_ROW || row0 + rw < a.rows)) {
-        if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + row0 + rw, (uint16_t)h16);
-        else c.template store<float>((float*)t.scales + row0 + rw, s_st);
+      if (leader && (ONE_ROW || row0 + rw < t.rows)) {
+        const int64_t orow = out_row<CACHE>(t, row0 + rw);
+        if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + orow, (uint16_t)h16);
+        else c.template store<float>((float*)t.scales + orow, s_st);
       }
     }
   });
@@ -505,7 +563,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       const uint32_t idx = lp | rp;
       const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row0 + rw >= a.rows) return;
+      if (!ONE_ROW && row0 + rw >= t.rows) return;
       const float mk = mul[ci];
       uint32_t out[NW];
       static_for<0, NW>([&](auto D) {
@@ -523,7 +581,9 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       });
       constexpr int RUN_BYTES = PACKED ? L / 2 : L;
       constexpr uint32_t ROWB = PACKED ? N / 2 : N;
-      uint8_t* dst = (uint8_t*)t.codes + row0 * (int64_t)ROWB + (rw * ROWB + (PACKED ? el / 2 : el));
+      uint8_t* dst;
+      if constexpr (CACHE) dst = (uint8_t*)t.codes + out_row<CACHE>(t, row0 + rw) * (int64_t)ROWB + (PACKED ? el / 2 : el);
+      else dst = (uint8_t*)t.codes + row0 * (int64_t)ROWB + (rw * ROWB + (PACKED ? el / 2 : el));
       if constexpr (RUN_BYTES >= 16) {
         static_for<0, RUN_BYTES / 16>([&](auto Q) {
           c.template store<u32x4>(dst + 16 * Q.value, u32x4{out[4 * Q.value], out[4 * Q.value + 1], out[4 * Q.value + 2], out[4 * Q.value + 3]});
@@ -559,7 +619,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       const uint32_t idx = lp | rp;
       const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row0 + rw >= a.rows) return;
+      if (!ONE_ROW && row0 + rw >= t.rows) return;
       float* dst = t.rot32 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       if constexpr (L >= 4) {
         static_for<0, L / 4>([&](auto Q) {
@@ -578,7 +638,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       const uint32_t idx = lp | rp;
       const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
-      if (!ONE_ROW && row0 + rw >= a.rows) return;
+      if (!ONE_ROW && row0 + rw >= t.rows) return;
       uint16_t* dst = t.rot16 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       constexpr int NW = (L >= 2) ? L / 2 : 1;
       uint32_t out[NW];
@@ -613,7 +673,7 @@ RBQ_HD Block block_of(const KArgs& a, uint32_t blk) {
 }
 
 // the transform after phase 0, the reduction, the scale and the stores of one block
-template <int K, bool MF, int IN, bool ROT, bool FAST, class Ctx>
+template <int K, bool MF, int IN, bool ROT, bool FAST, bool CACHE, class Ctx>
 RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v) {
   if constexpr (ROT) {
     if constexpr (RBQ_PLAN.nph >= 2) {
@@ -624,9 +684,9 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
       transpose<K, MF, 1>(c, v);
       stages<K, MF, 2, false>(v);
     }
-    finish<K, MF, RBQ_PLAN.nph - 1, true, IN, FAST>(c, *b.t, a, b.row0, v);
+    finish<K, MF, RBQ_PLAN.nph - 1, true, IN, FAST, CACHE>(c, *b.t, a, b.row0, v);
   } else {
-    finish<K, MF, 0, false, IN, FAST>(c, *b.t, a, b.row0, v);
+    finish<K, MF, 0, false, IN, FAST, CACHE>(c, *b.t, a, b.row0, v);
   }
 }
 
@@ -638,7 +698,7 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
 // RBQ_PREFETCH and matrix plans the next block's loads are issued as soon as the MFMAs
 // have consumed the current block's, so they are in flight while the current block is
 // transformed.
-template <int K, int IN, bool ROT, bool FOURD, bool FAST, bool ROPE, class Ctx>
+template <int K, int IN, bool ROT, bool FOURD, bool FAST, bool ROPE, bool CACHE, class Ctx>
 RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32_t step) {
   constexpr bool MF = use_matrix_plan(K, IN, ROT);
   const uint32_t nb = a.nblocks;
@@ -647,17 +707,17 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       c.refresh_ids();
       const Block b = block_of<K, MF>(a, blk);
       uint32_t raw[kMatrixLoads<K, MF>][4];
-      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, a.rows, b.row0, raw);
+      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, b.t->rows, b.row0, raw);
       Regs<K, MF> v;
       matrix_apply<K, MF, IN>(c, raw, v);
       stages<K, MF, 0, false>(v);
-      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
     }
   } else if constexpr (MF) {
     uint32_t raw[kMatrixLoads<K, MF>][4];
     if (first < nb) {
       const Block b = block_of<K, MF>(a, first);
-      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, a.rows, b.row0, raw);
+      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, b.t->rows, b.row0, raw);
     }
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
@@ -667,19 +727,19 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       const uint32_t nxt = blk + step;
       if (nxt < nb) {
         const Block bn = block_of<K, MF>(a, nxt);
-        matrix_issue<K, MF, FOURD, IN, ROPE>(c, *bn.t, a.rows, bn.row0, raw);
+        matrix_issue<K, MF, FOURD, IN, ROPE>(c, *bn.t, bn.t->rows, bn.row0, raw);
       }
       stages<K, MF, 0, false>(v);
-      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
     }
   } else {
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
       const Block b = block_of<K, MF>(a, blk);
       Regs<K, MF> v;
-      load_phase0<K, MF, IN, ROT, FOURD>(c, *b.t, a.rows, b.row0, v);
+      load_phase0<K, MF, IN, ROT, FOURD, ROPE>(c, *b.t, b.t->rows, b.row0, v);
       if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
-      rest_of_block<K, MF, IN, ROT, FAST>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
     }
   }
 }

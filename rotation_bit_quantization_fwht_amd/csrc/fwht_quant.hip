@@ -16,26 +16,27 @@
 namespace rbq {
 
 template <int K>
-hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope, hipStream_t s);
+hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope, bool cache,
+                       hipStream_t s);
 
 static hipError_t dispatch(int k, const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope,
-                           hipStream_t s) {
+                           hipStream_t s, bool cache = false) {
   switch (k) {
-    case 1: return fwht_launch<1>(a, in, rot, fourd, fast, rope, s);
-    case 2: return fwht_launch<2>(a, in, rot, fourd, fast, rope, s);
-    case 3: return fwht_launch<3>(a, in, rot, fourd, fast, rope, s);
-    case 4: return fwht_launch<4>(a, in, rot, fourd, fast, rope, s);
-    case 5: return fwht_launch<5>(a, in, rot, fourd, fast, rope, s);
-    case 6: return fwht_launch<6>(a, in, rot, fourd, fast, rope, s);
-    case 7: return fwht_launch<7>(a, in, rot, fourd, fast, rope, s);
-    case 8: return fwht_launch<8>(a, in, rot, fourd, fast, rope, s);
-    case 9: return fwht_launch<9>(a, in, rot, fourd, fast, rope, s);
-    case 10: return fwht_launch<10>(a, in, rot, fourd, fast, rope, s);
-    case 11: return fwht_launch<11>(a, in, rot, fourd, fast, rope, s);
-    case 12: return fwht_launch<12>(a, in, rot, fourd, fast, rope, s);
-    case 13: return fwht_launch<13>(a, in, rot, fourd, fast, rope, s);
-    case 14: return fwht_launch<14>(a, in, rot, fourd, fast, rope, s);
-    case 15: return fwht_launch<15>(a, in, rot, fourd, fast, rope, s);
+    case 1: return fwht_launch<1>(a, in, rot, fourd, fast, rope, cache, s);
+    case 2: return fwht_launch<2>(a, in, rot, fourd, fast, rope, cache, s);
+    case 3: return fwht_launch<3>(a, in, rot, fourd, fast, rope, cache, s);
+    case 4: return fwht_launch<4>(a, in, rot, fourd, fast, rope, cache, s);
+    case 5: return fwht_launch<5>(a, in, rot, fourd, fast, rope, cache, s);
+    case 6: return fwht_launch<6>(a, in, rot, fourd, fast, rope, cache, s);
+    case 7: return fwht_launch<7>(a, in, rot, fourd, fast, rope, cache, s);
+    case 8: return fwht_launch<8>(a, in, rot, fourd, fast, rope, cache, s);
+    case 9: return fwht_launch<9>(a, in, rot, fourd, fast, rope, cache, s);
+    case 10: return fwht_launch<10>(a, in, rot, fourd, fast, rope, cache, s);
+    case 11: return fwht_launch<11>(a, in, rot, fourd, fast, rope, cache, s);
+    case 12: return fwht_launch<12>(a, in, rot, fourd, fast, rope, cache, s);
+    case 13: return fwht_launch<13>(a, in, rot, fourd, fast, rope, cache, s);
+    case 14: return fwht_launch<14>(a, in, rot, fourd, fast, rope, cache, s);
+    case 15: return fwht_launch<15>(a, in, rot, fourd, fast, rope, cache, s);
   }
   return hipErrorInvalidValue;
 }
@@ -71,8 +72,8 @@ static rbq_status hq_launch(const void* x, rbq_dtype x_dtype, int64_t n, int64_t
   t.rot32 = rotated;
   t.signs = signs;
   t.mode = MODE_QUANT | (rotated ? MODE_ROT32 : 0u);
+  t.rows = tokens;
   a.t[1] = t;
-  a.rows = tokens;
   a.blocks0 = (uint32_t)blocks;
   a.nblocks = (uint32_t)blocks;
   a.opts = ((flags & RBQ_PACKED) ? OPT_PACKED : 0u) | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u) |
@@ -152,6 +153,7 @@ static rbq_status kv_launch(const void* q, const void* k, rbq_dtype dtype, int64
     t.rope_cos = rope_cos;
     t.rope_sin = rope_sin;
     t.rope_pos0 = (uint32_t)rope_pos0;
+    t.rows = rows;
   }
   a.t[0].codes = q_codes;
   a.t[0].scales = q_scales;
@@ -160,7 +162,6 @@ static rbq_status kv_launch(const void* q, const void* k, rbq_dtype dtype, int64
   a.t[1].codes = k_codes;
   a.t[1].scales = k_scales;
   a.t[1].mode = MODE_QUANT;
-  a.rows = rows;
   a.blocks0 = (uint32_t)blocks;
   a.nblocks = (uint32_t)(2 * blocks);
   a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
@@ -203,3 +204,92 @@ extern "C" rbq_status kv_rope_rotate_quant(const void* q, const void* k, rbq_dty
                    q_rotated, flags, stream);
 }
 
+
+// ------------------------------------------------------------------ KV4 cache append
+
+namespace rbq {
+
+// the (batch, head, token) addressing of one [B, heads, S, D] tensor
+static void set_bhs(TensorArgs& t, const void* x, int64_t heads, int64_t seq, const int64_t st[4]) {
+  t.x = x;
+  t.row_stride = st[2];
+  t.sb = st[0];
+  t.sh = st[1];
+  t.ss = st[2];
+  t.seq = (uint32_t)seq;
+  t.heads = (uint32_t)heads;
+  t.div_s = make_fastdiv((uint32_t)seq);
+  t.div_h = make_fastdiv((uint32_t)heads);
+}
+
+}  // namespace rbq
+
+extern "C" rbq_status kv_cache_append_int4(const void* q, const void* k, const void* v, rbq_dtype dtype,
+                                           int64_t batch, int64_t heads, int64_t kv_heads, int64_t seq,
+                                           int64_t head_dim, const int64_t q_strides[4],
+                                           const int64_t k_strides[4], const int64_t v_strides[4],
+                                           const float* rope_cos, const float* rope_sin,
+                                           int64_t rope_positions, int64_t pos0, int64_t seq_cap,
+                                           void* q_rotated, uint8_t* k_cache, void* k_cache_scales,
+                                           uint8_t* v_cache, void* v_cache_scales,
+                                           rbq_dtype scale_dtype, hipStream_t stream) {
+  const CacheCheck chk = check_cache_append(q, k, v, dtype, batch, heads, kv_heads, seq, head_dim, q_strides,
+                                            k_strides, v_strides, rope_cos, rope_sin, rope_positions, pos0,
+                                            seq_cap, q_rotated, k_cache, k_cache_scales, v_cache,
+                                            v_cache_scales, scale_dtype);
+  if (chk.status != RBQ_OK || batch == 0 || kv_heads == 0 || seq == 0) return chk.status;
+  const bool rope = rope_cos != nullptr;
+  const int in = in_kind(dtype);
+  const int rl = rows_log(chk.k, in, true);
+  const int64_t rows_q = q ? batch * heads * seq : 0, rows_kv = batch * kv_heads * seq;
+  const int64_t bq = (rows_q + (int64_t{1} << rl) - 1) >> rl, bk = (rows_kv + (int64_t{1} << rl) - 1) >> rl;
+  const int64_t ssz = dtype_size(scale_dtype), half = head_dim / 2;
+  // launch 1: Q (RoPE, rotation, 16-bit output) and K (RoPE, rotation, INT4 into the cache)
+  KArgs a{};
+  TensorArgs& tq = a.t[0];
+  TensorArgs& tk = a.t[1];
+  if (q) {
+    set_bhs(tq, q, heads, seq, q_strides);
+    tq.rot16 = (uint16_t*)q_rotated;
+    tq.mode = MODE_ROT16;
+    tq.rows = rows_q;
+  }
+  set_bhs(tk, k, kv_heads, seq, k_strides);
+  tk.codes = k_cache + pos0 * half;
+  tk.scales = (char*)k_cache_scales + pos0 * ssz;
+  tk.mode = MODE_QUANT;
+  tk.rows = rows_kv;
+  tk.out_cap = (uint32_t)seq_cap;
+  for (TensorArgs* t : {&tq, &tk}) {
+    t->rope_cos = rope_cos;
+    t->rope_sin = rope_sin;
+    t->rope_pos0 = (uint32_t)pos0;
+  }
+  a.blocks0 = (uint32_t)bq;
+  a.nblocks = (uint32_t)(bq + bk);
+  a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
+  // launch 2: V (INT4 without rotation into the cache)
+  const int rlv = rows_log(chk.k, in, false);
+  const int64_t bv = (rows_kv + (int64_t{1} << rlv) - 1) >> rlv;
+  KArgs av{};
+  TensorArgs& tv = av.t[0];
+  set_bhs(tv, v, kv_heads, seq, v_strides);
+  tv.codes = v_cache + pos0 * half;
+  tv.scales = (char*)v_cache_scales + pos0 * ssz;
+  tv.mode = MODE_QUANT;
+  tv.rows = rows_kv;
+  tv.out_cap = (uint32_t)seq_cap;
+  av.t[1] = tv;
+  av.blocks0 = (uint32_t)bv;
+  av.nblocks = (uint32_t)bv;
+  av.opts = a.opts;
+  if (diag_log())
+    fprintf(stderr, "rbq: kv_cache_append B=%lld H=%lld Hkv=%lld S=%lld D=%lld pos0=%lld cap=%lld rope=%d q=%d "
+            "blocks=%lld+%lld\n", (long long)batch, (long long)heads, (long long)kv_heads, (long long)seq,
+            (long long)head_dim, (long long)pos0, (long long)seq_cap, (int)rope, q != nullptr,
+            (long long)(bq + bk), (long long)bv);
+  if (diag_fail_launch()) return RBQ_EHIP;
+  if (dispatch(chk.k, a, in, true, true, false, rope, stream, true) != hipSuccess) return RBQ_EHIP;
+  if (dispatch(chk.k, av, in, false, true, false, false, stream, true) != hipSuccess) return RBQ_EHIP;
+  return RBQ_OK;
+}

@@ -126,8 +126,8 @@ inline KvCheck check_kv(const void* q, const void* k, int dtype, int64_t B, int6
 }
 
 // RoPE tables: fp32 [rope_positions, head_dim / 2], 16-byte aligned, covering positions
-// rope_pos0 .. rope_pos0 + seq - 1; head_dim 128 (the layout whose load registers leave
-// room for each element's cos and sin)
+// rope_pos0 .. rope_pos0 + seq - 1; head_dim 64, 128 or 256 (the layouts that hold each
+// load's partner elements and table values)
 inline rbq_status check_rope(int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                              const float* cos, const float* sin, int64_t positions,
                              int64_t pos0) {
@@ -136,8 +136,57 @@ inline rbq_status check_rope(int dtype, int64_t B, int64_t H, int64_t S, int64_t
   if (!cos || !sin || !aligned(cos, 16) || !aligned(sin, 16)) return RBQ_EINVAL;
   if (pos0 + S > positions || positions > (int64_t{1} << 30)) return RBQ_EINVAL;
   if (dtype != RBQ_BF16 && dtype != RBQ_F16) return RBQ_EINVAL;
-  if (D != 128) return RBQ_ENOTSUP;
+  if (D != 64 && D != 128 && D != 256) return RBQ_ENOTSUP;
   return RBQ_OK;
+}
+
+struct CacheCheck {
+  rbq_status status;
+  int k;  // log2 head_dim
+};
+
+// kv_cache_append_int4: [B, heads, S, D] Q (optional), [B, kv_heads, S, D] K and V with any
+// element strides (d stride 1, 16-byte aligned vectors); caches [B, kv_heads, seq_cap, D/2]
+// and [B, kv_heads, seq_cap] receiving positions pos0 .. pos0 + S - 1
+inline CacheCheck check_cache_append(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                                     int64_t H, int64_t Hkv, int64_t S, int64_t D, const int64_t* qs,
+                                     const int64_t* ks, const int64_t* vs, const float* cos,
+                                     const float* sin, int64_t positions, int64_t pos0, int64_t cap,
+                                     const void* q_rot, const void* kc, const void* ksc, const void* vc,
+                                     const void* vsc, int scale_dtype) {
+  CacheCheck r{RBQ_EINVAL, 0};
+  if (dtype != RBQ_BF16 && dtype != RBQ_F16) return r;
+  if (!valid_scale_dtype(scale_dtype)) return r;
+  if (B < 0 || H < 0 || Hkv < 0 || S < 0 || pos0 < 0 || cap < 0) return r;
+  if (pos0 + S > cap) return r;
+  if (Hkv > 0 && H % Hkv != 0) return r;
+  if ((cos == nullptr) != (sin == nullptr)) return r;
+  if (D != 64 && D != 128 && D != 256) {
+    r.status = (is_pow2(D) && D >= 8 && D <= 32768) ? RBQ_ENOTSUP : RBQ_EINVAL;
+    return r;
+  }
+  r.k = ilog2(D);
+  if (B == 0 || Hkv == 0 || S == 0) { r.status = RBQ_OK; return r; }
+  if (B * H > (int64_t{1} << 31) || B * H * S >= (int64_t{1} << 31) || B * Hkv * cap >= (int64_t{1} << 31))
+    return r;
+  if (cos) {
+    const rbq_status rs = check_rope(dtype, B, Hkv, S, D, cos, sin, positions, pos0);
+    if (rs != RBQ_OK) { r.status = rs; return r; }
+  }
+  if ((q == nullptr) != (q_rot == nullptr)) return r;
+  if (q && (!qs || !aligned(q, 16) || !aligned(q_rot, 16))) return r;
+  if (!k || !v || !ks || !vs || !aligned(k, 16) || !aligned(v, 16)) return r;
+  if (!kc || !vc || !ksc || !vsc || !aligned(kc, 16) || !aligned(vc, 16)) return r;
+  const uint64_t ssz = (uint64_t)dtype_size((rbq_dtype)scale_dtype);
+  if (!aligned(ksc, ssz) || !aligned(vsc, ssz)) return r;
+  for (const int64_t* st : {qs, ks, vs}) {
+    if (!st) continue;
+    if (st[3] != 1) return r;
+    for (int i = 0; i < 3; ++i)
+      if (st[i] < 0 || (st[i] * 2) % 16 != 0) return r;
+  }
+  r.status = RBQ_OK;
+  return r;
 }
 
 inline rbq_status check_gemm(const void* qA, const void* sA, const void* qW, const void* sW,

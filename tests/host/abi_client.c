@@ -87,6 +87,15 @@ int main(int argc, char **argv) {
   EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 3, 16, 16, 128, 0.1f, PX, NULL),
          RBQ_EINVAL);
   EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4000, PX, NULL, NULL), RBQ_ENOTSUP);
+  EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, H / 2, S, D, st, st, st, NULL, NULL, 0, 8, S + 7,
+                              PS, PC, PS, PC, PS, RBQ_F16, NULL),
+         RBQ_EINVAL);  /* pos0 + seq beyond the capacity */
+  EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, 3, S, D, st, st, st, NULL, NULL, 0, 0, S,
+                              PS, PC, PS, PC, PS, RBQ_F16, NULL),
+         RBQ_EINVAL);  /* heads not a multiple of kv_heads */
+  EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, H, S, 32, st, st, st, NULL, NULL, 0, 0, S,
+                              PS, PC, PS, PC, PS, RBQ_F16, NULL),
+         RBQ_ENOTSUP);
   EXPECT(rbq_hbm_probe(PX, 4000, PC, 4096, 8, NULL), RBQ_EINVAL);
   EXPECT(rbq_hbm_probe(PX, 0, PC, 0, 8, NULL), RBQ_EINVAL);
   EXPECT(rbq_hbm_probe(PX, 4096, NULL, 4096, 8, NULL), RBQ_EINVAL);
@@ -113,6 +122,9 @@ int main(int argc, char **argv) {
     EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
     EXPECT(w4a8_gemm((const int8_t *)PC, PS, PC, PS, RBQ_F16, 64, 64, 4096, PX, NULL, NULL), launched);
     EXPECT(rbq_hbm_probe(PX, 65536, PC, 16384, 8, NULL), launched);
+    EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, H / 2, S, D, st, st, st, (const float *)PS,
+                                (const float *)PS, 2 * S, 3, S + 3, PS, PC, PS, PC, PS, RBQ_F16, NULL),
+           launched);
   }
 
   printf("%s: %d failure(s)\n", inject ? "inject" : "validate", failures);

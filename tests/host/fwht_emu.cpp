@@ -6,6 +6,7 @@
 //
 // usage: fwht_emu K IN ROT FOURD rows opts mode0 x.bin x_elems row_stride
 //                 codes.bin scales.bin [B H S sb sh ss]
+// environment: RBQ_EMU_GRID, RBQ_EMU_FAST, RBQ_EMU_SIGNS, RBQ_EMU_ROPE, RBQ_EMU_CACHE
 // (the rotated output, when requested by mode0, is written to codes.bin + ".rot")
 #include <barrier>
 #include <cstdio>
@@ -33,15 +34,29 @@ static void run(const KArgs& a, uint32_t grid) {
       th.emplace_back([&, t] {
         HostCtx c{(uint32_t)(t & 63), (uint32_t)(t >> 6), &sh};
         const bool fast = getenv("RBQ_EMU_FAST") != nullptr;
-        if constexpr (K == 7 && IN != IN_F32 && ROT) {
-          if (a.t[0].rope_cos) {
-            if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, true>(c, a, wg, grid);
-            else fwht_quant_persistent<K, IN, ROT, FOURD, false, true>(c, a, wg, grid);
-            return;
+        const bool rope = a.t[0].rope_cos != nullptr;
+        if constexpr (K >= 6 && K <= 8 && IN != IN_F32) {
+          if constexpr (FOURD) {
+            if (a.t[0].out_cap != 0u) {  // the per-head cache output (kv_cache_append_int4)
+              if constexpr (ROT) {
+                if (rope) fwht_quant_persistent<K, IN, ROT, FOURD, false, true, true>(c, a, wg, grid);
+                else fwht_quant_persistent<K, IN, ROT, FOURD, false, false, true>(c, a, wg, grid);
+              } else {
+                fwht_quant_persistent<K, IN, ROT, FOURD, false, false, true>(c, a, wg, grid);
+              }
+              return;
+            }
+          }
+          if constexpr (ROT) {
+            if (rope) {
+              if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, true, false>(c, a, wg, grid);
+              else fwht_quant_persistent<K, IN, ROT, FOURD, false, true, false>(c, a, wg, grid);
+              return;
+            }
           }
         }
-        if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, false>(c, a, wg, grid);
-        else fwht_quant_persistent<K, IN, ROT, FOURD, false, false>(c, a, wg, grid);
+        if (fast) fwht_quant_persistent<K, IN, ROT, FOURD, true, false, false>(c, a, wg, grid);
+        else fwht_quant_persistent<K, IN, ROT, FOURD, false, false, false>(c, a, wg, grid);
       });
     for (auto& x : th) x.join();
   }
@@ -50,8 +65,8 @@ static void run(const KArgs& a, uint32_t grid) {
 template <int K>
 static void run_k(const KArgs& a, uint32_t grid, int in, bool rot, bool fourd) {
   if (fourd) {
-    if (in == IN_BF16) run<K, IN_BF16, true, true>(a, grid);
-    else run<K, IN_F16, true, true>(a, grid);
+    if (in == IN_BF16) { if (rot) run<K, IN_BF16, true, true>(a, grid); else run<K, IN_BF16, false, true>(a, grid); }
+    else { if (rot) run<K, IN_F16, true, true>(a, grid); else run<K, IN_F16, false, true>(a, grid); }
     return;
   }
   if (in == IN_F32) { if (rot) run<K, IN_F32, true, false>(a, grid); else run<K, IN_F32, false, false>(a, grid); }
@@ -89,8 +104,16 @@ int main(int argc, char** argv) {
   auto alloc = [](size_t bytes) { return (char*)aligned_alloc(64, ((bytes + 63) / 64) * 64 + 64); };
   char* xb = alloc(x.size());
   memcpy(xb, x.data(), x.size());
-  const size_t code_bytes = (size_t)rows * ((opts & OPT_PACKED) ? n / 2 : n);
-  const size_t scale_bytes = (size_t)rows * ((opts & OPT_SCALE_F16) ? 2 : 4);
+  // RBQ_EMU_CACHE="cap pos0": codes and scales go to a cache of cap rows per (batch, head)
+  // at positions pos0 .. pos0 + S - 1 (needs the B H S arguments)
+  long long cache_cap = 0, cache_pos0 = 0, out_rows = rows;
+  if (const char* cp = getenv("RBQ_EMU_CACHE")) {
+    if (sscanf(cp, "%lld %lld", &cache_cap, &cache_pos0) != 2 || argc < 19) { fprintf(stderr, "bad RBQ_EMU_CACHE\n"); return 2; }
+    out_rows = atoll(argv[13]) * atoll(argv[14]) * cache_cap;
+  }
+  const size_t code_row = (size_t)((opts & OPT_PACKED) ? n / 2 : n), scale_size = (opts & OPT_SCALE_F16) ? 2 : 4;
+  const size_t code_bytes = (size_t)out_rows * code_row;
+  const size_t scale_bytes = (size_t)out_rows * scale_size;
   const size_t rot_bytes = (size_t)rows * n * ((mode0 & MODE_ROT16) ? 2 : 4);
   char* codes = alloc(code_bytes);
   char* scales = alloc(scale_bytes);
@@ -136,8 +159,13 @@ int main(int argc, char** argv) {
     t.div_s = make_fastdiv((uint32_t)S); t.div_h = make_fastdiv((uint32_t)H);
     (void)B;
   }
+  if (cache_cap) {
+    t.out_cap = (uint32_t)cache_cap;
+    t.codes = codes + cache_pos0 * code_row;
+    t.scales = scales + cache_pos0 * scale_size;
+  }
+  t.rows = rows;
   a.t[1] = t;
-  a.rows = rows;
   const int rl = make_plan(K, use_matrix_plan(K, in, rot != 0)).r;
   const uint32_t nblocks = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
   a.blocks0 = nblocks;

@@ -343,13 +343,13 @@ def rope_tables(positions, d, base=10000.0):
     # shapes whose rows fill whole 64-row blocks, several blocks per workgroup loop
     ("bfloat16", "contiguous", 3, (2, 6, 80)), ("bfloat16", "bshd_view", 0, (4, 5, 48)),
     ("float16", "contiguous", 0, (1, 4, 16)), ("float16", "bshd_view", 9, (8, 2, 272))])
-def test_kv_rope_small(rbq, dtype, layout, pos0, bhs):
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_kv_rope_small(rbq, dtype, layout, pos0, bhs, D):
     """kv_rope_rotate_quant: RoPE (half-split; the oracle evaluates it exactly and rounds it
     once to the 16-bit format, accepting the other neighbour only where float32 evaluation
     error reaches a rounding midpoint) then R3 and INT4, on Q and K."""
     B, H, S = bhs
-    D = 128
-    print(f"case kv rope {dtype} {layout} pos0={pos0} B,H,S={bhs}", flush=True)
+    print(f"case kv rope D={D} {dtype} {layout} pos0={pos0} B,H,S={bhs}", flush=True)
     q_bits, k_bits, _ = workloads.gen_kv(seed=17, batch=B, heads=H, seq=S, head_dim=D)
     if dtype == "float16":
         q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
@@ -417,7 +417,7 @@ def test_kv_rope_full_size_and_errors(rbq):
     assert np.all(np.max(np.abs(qa), axis=1) == 7) and not np.any(qa == -8)
     with pytest.raises(rbq.RBQError):   # tables too short for rope_pos0 + seq
         rbq.kv_rotate_quant(qd, kd, rope_cos=cd, rope_sin=sd, rope_pos0=65)
-    q256 = torch.zeros((1, 1, 4, 256), dtype=torch.bfloat16, device="cuda")
-    c256 = torch.zeros((8, 128), dtype=torch.float32, device="cuda")
-    with pytest.raises(rbq.RBQError):   # head_dim 256 is not fused
-        rbq.kv_rotate_quant(q256, q256.clone(), rope_cos=c256, rope_sin=c256)
+    q32 = torch.zeros((1, 1, 4, 32), dtype=torch.bfloat16, device="cuda")
+    c32 = torch.zeros((8, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(rbq.RBQError):   # head_dim 32 is not fused (64, 128 and 256 are)
+        rbq.kv_rotate_quant(q32, q32.clone(), rope_cos=c32, rope_sin=c32)

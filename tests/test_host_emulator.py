@@ -51,7 +51,8 @@ def emu():
 
 
 def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, mode=MODE_QUANT | MODE_ROT32,
-            row_stride=None, fourd=None, fast=False, grid=3, signs=None, int8=False, rope=None, bhs=None):
+            row_stride=None, fourd=None, fast=False, grid=3, signs=None, int8=False, rope=None, bhs=None,
+            cache=None):
     n = 1 << k
     xb = np.ascontiguousarray(x)
     xpath = str(tmp_path / "x.bin")
@@ -75,13 +76,16 @@ def run_emu(exe, tmp_path, x, dtype, k, rows, rot=True, packed=True, f16=True, m
         env["RBQ_EMU_ROPE"] = f"{cpath_r} {spath_r} {int(pos0)}"
     if fast:
         env["RBQ_EMU_FAST"] = "1"
+    if cache is not None:  # (capacity, first position): codes/scales rows of a per-head cache
+        env["RBQ_EMU_CACHE"] = f"{cache[0]} {cache[1]}"
     if signs is not None:
         signs_path = str(tmp_path / "signs.bin")
         np.ascontiguousarray(signs).tofile(signs_path)
         env["RBQ_EMU_SIGNS"] = signs_path
     r = subprocess.run(args, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, r.stderr
-    codes = np.fromfile(cpath, dtype=np.uint8).reshape(rows, -1)
+    out_rows = rows if cache is None else fourd[0] * fourd[1] * cache[0]
+    codes = np.fromfile(cpath, dtype=np.uint8).reshape(out_rows, -1)
     scales = np.fromfile(spath, dtype=np.float16 if f16 else np.float32).astype(np.float64)
     rot_out = None
     if mode & MODE_ROT32:
@@ -254,6 +258,7 @@ def rope_tables(positions, d, base=10000.0):
     return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype,layout,pos0,fast,bhs", [
     ("bfloat16", "flat", 0, True, (2, 3, 37)), ("bfloat16", "bshd", 5, False, (2, 3, 37)),
     ("float16", "flat", 3, False, (2, 3, 37)), ("float16", "bshd", 0, True, (2, 3, 37)),
@@ -261,12 +266,12 @@ def rope_tables(positions, d, base=10000.0):
     # workgroup loop
     ("bfloat16", "flat", 7, False, (2, 2, 48)), ("bfloat16", "bshd", 0, True, (1, 8, 32)),
     ("float16", "bshd", 2, False, (4, 3, 16)), ("float16", "flat", 0, True, (3, 4, 64))])
-def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
+def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs, D):
     """RoPE (half-split pairs, the oracle's exact map rounded once to the 16-bit format,
     either neighbour accepted where float32 error reaches a rounding midpoint) ahead of R3,
     on flat and strided [B, H, S, D] addressing, against the oracle's RoPE + rotation."""
     B, H, S = bhs
-    D = 128
+    k = D.bit_length() - 1
     q_bits, _, _ = workloads.gen_kv(seed=9, batch=B, heads=H, seq=S, head_dim=D)
     if dtype == "float16":
         q_bits = workloads.bf16_bits_to_f32(q_bits).astype(np.float16).view(np.uint16)
@@ -275,10 +280,10 @@ def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
     mode = MODE_QUANT if fast else MODE_QUANT | MODE_ROT32
     if layout == "bshd":
         mem = np.ascontiguousarray(q_bits.transpose(0, 2, 1, 3))
-        codes, scales, yr = run_emu(emu, tmp_path, mem, dtype, 7, rows, mode=mode, fast=fast,
+        codes, scales, yr = run_emu(emu, tmp_path, mem, dtype, k, rows, mode=mode, fast=fast,
                                     fourd=(B, H, S, S * H * D, D, H * D), rope=(cos, sin, pos0))
     else:
-        codes, scales, yr = run_emu(emu, tmp_path, q_bits.reshape(rows, D), dtype, 7, rows, mode=mode,
+        codes, scales, yr = run_emu(emu, tmp_path, q_bits.reshape(rows, D), dtype, k, rows, mode=mode,
                                     fast=fast, bhs=(B, H, S), rope=(cos, sin, pos0))
     x = workloads.to_float64(q_bits, dtype).reshape(rows, D)
     pos = pos0 + np.arange(S)
@@ -286,3 +291,40 @@ def test_rope_before_r3(emu, tmp_path, dtype, layout, pos0, fast, bhs):
     sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
     check_rope_quant(oracle.unpack_nibbles(codes), scales, x, cr, sr, dtype, y_gpu=None if fast else yr)
 
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("what", ["k_rope", "k_plain", "v"])
+def test_cache_rows_emulated(emu, tmp_path, D, what):
+    """kv_cache_append_int4's kernels: [B, S, H, D]-laid rows (a strided view) quantized into a
+    per-head cache of 64 rows at positions 20 .. 56 -- K with RoPE and the rotation, K with
+    the rotation only, V without rotation; every other cache row keeps its sentinel."""
+    B, H, S, cap, pos0 = 2, 3, 37, 64, 20
+    k = D.bit_length() - 1
+    dtype = "bfloat16"
+    q_bits, _, _ = workloads.gen_kv(seed=D + 5, batch=B, heads=H, seq=S, head_dim=D)
+    mem = np.ascontiguousarray(q_bits.transpose(0, 2, 1, 3))
+    rows = B * H * S
+    cos, sin = rope_tables(pos0 + S + 3, D)
+    rot = what != "v"
+    codes, scales, _ = run_emu(emu, tmp_path, mem, dtype, k, rows, rot=rot, mode=MODE_QUANT,
+                               fourd=(B, H, S, S * H * D, D, H * D), cache=(cap, pos0),
+                               rope=(cos, sin, pos0) if what == "k_rope" else None)
+    codes = codes.reshape(B, H, cap, D // 2)
+    sraw = np.fromfile(str(tmp_path / "scales.bin"), dtype=np.uint16).reshape(B, H, cap)
+    inside = np.zeros((B, H, cap), dtype=bool)
+    inside[:, :, pos0:pos0 + S] = True
+    assert np.all(codes[~inside] == 0xEE) and np.all(sraw[~inside] == 0xEEEE)
+    got_q = oracle.unpack_nibbles(codes[:, :, pos0:pos0 + S].reshape(rows, D // 2))
+    got_s = scales.reshape(B, H, cap)[:, :, pos0:pos0 + S].reshape(rows)
+    x = workloads.to_float64(q_bits, dtype).reshape(rows, D)
+    if what == "k_rope":
+        pos = pos0 + np.arange(S)
+        cr = np.broadcast_to(cos[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+        sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(rows, D // 2)
+        check_rope_quant(got_q, got_s, x, cr, sr, dtype)
+    else:
+        ref = oracle.hadamard_quant_int4(x, "float16", packed=False, rotate_input=rot)
+        st = check_quant(got_q, got_s, ref, "float16", x, rotate=rot)
+        if not rot:
+            assert st["code_flips"] == 0
