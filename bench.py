@@ -617,7 +617,54 @@ def main():
             "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2),
             "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": load_traffic("attention_decode_int4kv", kernel_source_hash(("common.h", "attention.hip")))}
-        del vcodes, vscales, aout
+        # the same attention with each head's 2048 tokens cut into ranges taken by separate
+        # workgroups (512 (batch, head) pairs fill only two workgroups per CU); both kernels,
+        # split and merge, inside the timed launches
+        split_rates = {}
+        ws = torch.empty((rbq.attention_split_workspace_bytes(B, H, 16),), dtype=torch.uint8, device=dev)
+        for splits in (2, 4, 8, 16):
+            fn = lambda sp=splits: rbq.attention_decode_int4kv_split(  # noqa
+                qdec, kc, ks, vcodes, vscales, 1.0 / math.sqrt(D), sp, out=aout, workspace=ws)
+            fn()
+            ts = time_back_to_back(torch, [fn], 20) * 1e-6
+            split_rates[splits] = ts
+        best = min(split_rates, key=split_rates.get)
+        ts = split_rates[best]
+        extras["attention_decode_int4kv_split"] = {
+            "workload": "as attention_decode_int4kv, each head's tokens in `splits` ranges + a merge kernel",
+            "splits": best, "avg_us": round(ts * 1e6, 3), "GB_s": round(nbytes / ts / 1e9, 2),
+            "frac_hbm_peak": round(nbytes / ts / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_us_by_splits": {str(k): round(v * 1e6, 3) for k, v in split_rates.items()}}
+        del vcodes, vscales, aout, ws
+        # long-context decode: one sequence of 32768 tokens, 32 heads (the same cache bytes
+        # in 32 (batch, head) pairs): unsplit, 32 workgroups for 256 CUs
+        LB, LH, LS = 1, 32, 32768
+        lk = torch.from_numpy(workloads.gen_packed_codes(33, LB * LH * LS, D)).to(dev).reshape(LB, LH, LS, D // 2)
+        lv = torch.from_numpy(workloads.gen_packed_codes(34, LB * LH * LS, D)).to(dev).reshape(LB, LH, LS, D // 2)
+        lks = torch.from_numpy(workloads.gen_scales(35, LB * LH * LS, "float16")).to(dev).reshape(LB, LH, LS)
+        lvs = torch.from_numpy(workloads.gen_scales(36, LB * LH * LS, "float16")).to(dev).reshape(LB, LH, LS)
+        lq = qdec[:LB].contiguous()
+        lout = torch.empty_like(lq)
+        lbytes = 2 * LB * LH * LS * (D // 2 + 2) + 2 * LB * LH * D * 2
+        fn = lambda: rbq.attention_decode_int4kv(lq, lk, lks, lv, lvs, 1.0 / math.sqrt(D), out=lout)  # noqa
+        fn()
+        t_one = time_back_to_back(torch, [fn], 20) * 1e-6
+        ws = torch.empty((rbq.attention_split_workspace_bytes(LB, LH, 256),), dtype=torch.uint8, device=dev)
+        long_rates = {}
+        for splits in (16, 32, 64, 128, 256):
+            fn = lambda sp=splits: rbq.attention_decode_int4kv_split(  # noqa
+                lq, lk, lks, lv, lvs, 1.0 / math.sqrt(D), sp, out=lout, workspace=ws)
+            fn()
+            long_rates[splits] = time_back_to_back(torch, [fn], 20) * 1e-6
+        best = min(long_rates, key=long_rates.get)
+        extras["attention_decode_long_context"] = {
+            "workload": "one query per head over INT4 K and V caches [1, 32, 32768, 128], fp16 scales",
+            "unsplit_avg_us": round(t_one * 1e6, 3), "unsplit_GB_s": round(lbytes / t_one / 1e9, 2),
+            "split_splits": best, "split_avg_us": round(long_rates[best] * 1e6, 3),
+            "split_GB_s": round(lbytes / long_rates[best] / 1e9, 2),
+            "split_frac_hbm_peak": round(lbytes / long_rates[best] / 1e9 / HBM_PEAK_GBS, 4),
+            "split_avg_us_by_splits": {str(k): round(v * 1e6, 3) for k, v in long_rates.items()}}
+        del lk, lv, lks, lvs, lq, lout, ws
     if args.only == "kron" or (args.only == "all" and not args.no_extras):
         # a row length that is not a power of two: the down-projection input of width
         # 14336 = 28 * 512 (Paley factor of the second kind, q = 13), R4's recipe

@@ -295,6 +295,41 @@ rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8
                                    hipStream_t stream);
 
 /*
+ * attention_decode_int4kv_split -- attention_decode_int4kv with each (batch, head)'s tokens
+ * cut into `splits` ranges of ceil(seq / splits) tokens, one workgroup per range, so that
+ * few (batch, head) pairs still fill the device. Each range's workgroup writes its partial
+ * maximum m, sum l and unnormalised output o (fp32, [batch * heads, splits, 2 + 128]) to
+ * `workspace`; a second kernel on the same stream combines the ranges in order,
+ *   out[d] = sum_r e^(m_r - M) o_r[d] / sum_r e^(m_r - M) l_r,  M = max_r m_r,
+ * the softmax of attention_decode_int4kv summed in another grouping (the same real value;
+ * fp32 rounding differs). The attention itself is the one the pages define for K and V
+ * cached in INT4; the split is a scheduling choice of this library, not theirs.
+ *
+ *  all arguments as attention_decode_int4kv, plus:
+ *  splits           1 .. 4096; ranges past the sequence's end contribute nothing.
+ *  workspace        device memory of at least workspace_bytes, 16-byte aligned, owned by the
+ *                   caller; not read before it is written; free for reuse once the call's
+ *                   kernels have finished on `stream`.
+ *  workspace_bytes  at least rbq_attention_split_workspace_bytes(batch, heads, splits).
+ * Errors: as attention_decode_int4kv, plus RBQ_EINVAL for splits outside 1 .. 4096 or a
+ * NULL, misaligned or short workspace; RBQ_ENOTSUP when batch * heads * splits > 2^31 - 1.
+ */
+rbq_status attention_decode_int4kv_split(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
+                                         const void *k_scales, const uint8_t *v_codes,
+                                         const void *v_scales, rbq_dtype scale_dtype, int64_t batch,
+                                         int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap,
+                                         int64_t head_dim, float softmax_scale, int64_t splits,
+                                         void *workspace, int64_t workspace_bytes, void *out,
+                                         hipStream_t stream);
+
+/*
+ * rbq_attention_split_workspace_bytes -- the workspace attention_decode_int4kv_split needs:
+ * batch * heads * splits * 130 * 4 bytes, written to *bytes. RBQ_EINVAL for a NULL `bytes`,
+ * negative sizes or splits outside 1 .. 4096; RBQ_ENOTSUP if batch * heads > 2^31 - 1.
+ */
+rbq_status rbq_attention_split_workspace_bytes(int64_t batch, int64_t heads, int64_t splits, int64_t *bytes);
+
+/*
  * w4a8_gemm_grouped -- W4A8 with group-wise weight scales: one scale per run of `group`
  * consecutive K elements of each weight row ("SpinQuant, when rotations are worth
  * learning": its ExecuTorch export uses 4-bit weights in groups of 256 or 32 input

@@ -16,7 +16,9 @@ The calls have the same names and meaning as the C functions declared in
   accumulation and a bf16 dequantization epilogue;
 * ``quantize_groups_int4`` / ``w4a8_gemm_grouped`` -- group-wise weight scales: the
   quantizer (one scale per run of ``group`` elements) and the W4A8 GEMM that consumes it;
-* ``attention_decode_int4kv`` -- decode attention over the INT4 key/value cache.
+* ``attention_decode_int4kv`` -- decode attention over the INT4 key/value cache;
+  ``attention_decode_int4kv_split`` the same with each sequence cut into ranges taken by
+  separate workgroups, their partials combined through a caller's workspace.
 
 This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
 memory, allocates outputs with torch when the caller does not pass them, and hands raw
@@ -44,6 +46,8 @@ __all__ = [
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
     "attention_decode_int4kv",
+    "attention_decode_int4kv_split",
+    "attention_split_workspace_bytes",
     "hbm_probe",
     "RBQ_OK",
     "RBQ_EINVAL",
@@ -76,6 +80,8 @@ EXPORTED_SYMBOLS = (
     "w4a8_gemm_grouped",
     "quantize_groups_int4",
     "attention_decode_int4kv",
+    "attention_decode_int4kv_split",
+    "rbq_attention_split_workspace_bytes",
     "rbq_hbm_probe",
     "rbq_status_string",
     "rbq_version",
@@ -144,6 +150,11 @@ def lib():
     L.attention_decode_int4kv.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
                                           ctypes.c_float, vp, vp]
     L.attention_decode_int4kv.restype = ci
+    L.attention_decode_int4kv_split.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
+                                                ctypes.c_float, i64, vp, i64, vp, vp]
+    L.attention_decode_int4kv_split.restype = ci
+    L.rbq_attention_split_workspace_bytes.argtypes = [i64, i64, i64, p64]
+    L.rbq_attention_split_workspace_bytes.restype = ci
     L.rbq_hbm_probe.argtypes = [vp, i64, vp, i64, i64, vp]
     L.rbq_hbm_probe.restype = ci
     L.rbq_status_string.argtypes = [ci]
@@ -578,6 +589,15 @@ def attention_decode_int4kv(q, k_codes, k_scales, v_codes, v_scales, softmax_sca
     k_codes / v_codes uint8 [B, Hkv, S_cap, 64], k_scales / v_scales [B, Hkv, S_cap];
     the first ``seq`` tokens (default S_cap) are attended. Returns out [B, H, 128] in q's
     dtype."""
+    (B, H, Hkv, seq, S_cap, D), out = _attention_operands(q, k_codes, k_scales, v_codes, v_scales, seq, out)
+    st = lib().attention_decode_int4kv(_ptr(q), _dtype_code(q.dtype), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                       _ptr(v_scales), _dtype_code(k_scales.dtype), B, H, Hkv, seq, S_cap, D,
+                                       float(softmax_scale), _ptr(out), _stream(stream, q.device))
+    _check("attention_decode_int4kv", st)
+    return out
+
+
+def _attention_operands(q, k_codes, k_scales, v_codes, v_scales, seq, out):
     torch = _torch()
     _require_cuda(q, k_codes, k_scales, v_codes, v_scales)
     B, H, D = q.shape
@@ -594,10 +614,37 @@ def attention_decode_int4kv(q, k_codes, k_scales, v_codes, v_scales, softmax_sca
     if v_scales.dtype != k_scales.dtype:
         raise ValueError("k_scales and v_scales must share a dtype")
     _require_buffer("out", out, (B, H, D), (q.dtype,), dev)
-    st = lib().attention_decode_int4kv(_ptr(q), _dtype_code(q.dtype), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
-                                       _ptr(v_scales), _dtype_code(k_scales.dtype), B, H, Hkv, seq, S_cap, D,
-                                       float(softmax_scale), _ptr(out), _stream(stream, dev))
-    _check("attention_decode_int4kv", st)
+    return (B, H, Hkv, seq, S_cap, D), out
+
+
+def attention_split_workspace_bytes(batch, heads, splits):
+    """Bytes of workspace attention_decode_int4kv_split needs (its partials, fp32)."""
+    n = ctypes.c_int64(0)
+    _check("rbq_attention_split_workspace_bytes",
+           lib().rbq_attention_split_workspace_bytes(int(batch), int(heads), int(splits), ctypes.byref(n)))
+    return n.value
+
+
+def attention_decode_int4kv_split(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, splits, *, seq=None,
+                                  out=None, workspace=None, stream=None):
+    """attention_decode_int4kv with each (batch, head)'s first ``seq`` tokens cut into
+    ``splits`` ranges (one workgroup each) whose partials are combined by a second kernel.
+    ``workspace`` is a GPU tensor of at least attention_split_workspace_bytes(B, H, splits)
+    bytes (allocated here when omitted). Returns out [B, H, 128] in q's dtype."""
+    torch = _torch()
+    (B, H, Hkv, seq, S_cap, D), out = _attention_operands(q, k_codes, k_scales, v_codes, v_scales, seq, out)
+    need = attention_split_workspace_bytes(B, H, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _require_cuda(workspace)
+    if not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    have = workspace.numel() * workspace.element_size()
+    st = lib().attention_decode_int4kv_split(_ptr(q), _dtype_code(q.dtype), _ptr(k_codes), _ptr(k_scales),
+                                             _ptr(v_codes), _ptr(v_scales), _dtype_code(k_scales.dtype), B, H, Hkv,
+                                             seq, S_cap, D, float(softmax_scale), int(splits), _ptr(workspace), have,
+                                             _ptr(out), _stream(stream, q.device))
+    _check("attention_decode_int4kv_split", st)
     return out
 
 

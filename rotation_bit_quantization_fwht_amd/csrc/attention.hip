@@ -26,6 +26,8 @@
 namespace rbq {
 
 struct AttnArgs {
+  float* part;          // split kernel: [B * H, splits, 2 + 128] partial (max, sum, output)
+  int splits, chunk;    // split kernel: token ranges [sp * chunk, (sp + 1) * chunk)
   const void* q;        // [B, H, 128] bf16 or fp16
   const uint8_t* kc;    // [B, Hkv, S_cap, 64]
   const void* ks;       // [B, Hkv, S_cap]
@@ -115,11 +117,15 @@ __device__ __forceinline__ void attn_fetch(AttnBatch& r, const AttnRsrc& rs, int
   }
 }
 
-template <int SF16>
+// SPLIT: workgroup x takes the tokens [sp * chunk, (sp + 1) * chunk) of pair bh (x = bh *
+// splits + sp) and writes its (maximum, sum, unnormalised output) to a.part instead of the
+// output; attention_merge_kernel combines the splits
+template <int SF16, bool SPLIT>
 __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs a) {
   __shared__ float part[kAttnGroups][kAttnD];
   __shared__ float gmax[kAttnGroups], gsum[kAttnGroups];
-  const int bh = blockIdx.x;
+  const int bh = SPLIT ? (int)blockIdx.x / a.splits : (int)blockIdx.x;
+  const int sp = SPLIT ? (int)blockIdx.x - bh * a.splits : 0;
   const int b = bh / a.H, h = bh - b * a.H;
   const int kvh = h / (a.H / a.Hkv);
   const int tid = threadIdx.x, c = tid & 15, tg = tid >> 4;
@@ -131,11 +137,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 
   const int64_t head = (int64_t)b * a.Hkv + kvh;
   const uint32_t ssz = SF16 ? 2u : 4u;
+  // this workgroup's tokens: [t_begin, t_begin + n) of the head (all S without splits)
+  const int t_begin = SPLIT ? sp * a.chunk : 0;
+  const int n = SPLIT ? max(0, min(a.chunk, a.S - t_begin)) : a.S;
+  const int64_t tok0 = head * a.S_cap + t_begin;
   AttnRsrc rs;
-  rs.kc = attn_rsrc(a.kc + head * a.S_cap * 64, (uint32_t)a.S * 64u);
-  rs.vc = attn_rsrc(a.vc + head * a.S_cap * 64, (uint32_t)a.S * 64u);
-  rs.ks = attn_rsrc((const char*)a.ks + head * a.S_cap * ssz, (uint32_t)a.S * ssz);
-  rs.vs = attn_rsrc((const char*)a.vs + head * a.S_cap * ssz, (uint32_t)a.S * ssz);
+  rs.kc = attn_rsrc(a.kc + tok0 * 64, (uint32_t)n * 64u);
+  rs.vc = attn_rsrc(a.vc + tok0 * 64, (uint32_t)n * 64u);
+  rs.ks = attn_rsrc((const char*)a.ks + tok0 * ssz, (uint32_t)n * ssz);
+  rs.vs = attn_rsrc((const char*)a.vs + tok0 * ssz, (uint32_t)n * ssz);
 
   // the group's running maximum and sum (equal on its sixteen lanes) and its output dims
   float m_run = -INFINITY, l_run = 0.0f;
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
   // and output, then the value rows weighted by the probabilities. The batch's loads are
   // all issued before any is used; the other waves of the CU hide their latency. The
   // batch's first token is always in range.
-  for (int t0 = tg; t0 < a.S; t0 += kAttnU * kAttnGroups) {
+  for (int t0 = tg; t0 < n; t0 += kAttnU * kAttnGroups) {
     AttnBatch r;
     attn_fetch<SF16>(r, rs, t0, c);
     float sc[kAttnU];
@@ -161,7 +171,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], kc[i], dot);
       dot = attn_row16_sum(dot);
-      sc[u] = (t0 + u * kAttnGroups < a.S) ? dot * r.ks[u] : -INFINITY;
+      sc[u] = (t0 + u * kAttnGroups < n) ? dot * r.ks[u] : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
     const float m_new = fmaxf(m_run, bmax);
@@ -183,7 +193,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
   }
 
   // ---- merge the groups: out = sum_g e^(m_g - M) acc_g / sum_g e^(m_g - M) l_g; groups
-  // without tokens hold (-inf, 0, 0) and weigh 0 (group 0 always has token 0)
+  // without tokens hold (-inf, 0, 0) and weigh 0 (group 0 always has token 0, except in
+  // a split past the sequence's end, whose triple is then (-inf, 0, 0))
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[tg][8 * c + i] = acc[i];
   if (c == 0) {
@@ -196,11 +207,22 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 #pragma unroll
     for (int g = 1; g < kAttnGroups; ++g) mx = fmaxf(mx, gmax[g]);
     float o = 0.0f, l = 0.0f;
+    if (mx != -INFINITY) {
 #pragma unroll
-    for (int g = 0; g < kAttnGroups; ++g) {
-      const float w = __expf(gmax[g] - mx);
-      o = fmaf(part[g][tid], w, o);
-      l = fmaf(gsum[g], w, l);
+      for (int g = 0; g < kAttnGroups; ++g) {
+        const float w = __expf(gmax[g] - mx);
+        o = fmaf(part[g][tid], w, o);
+        l = fmaf(gsum[g], w, l);
+      }
+    }
+    if constexpr (SPLIT) {
+      float* pp = a.part + ((int64_t)bh * a.splits + sp) * (2 + kAttnD);
+      pp[2 + tid] = o;
+      if (tid == 0) {
+        pp[0] = mx;
+        pp[1] = l;
+      }
+      return;
     }
     o /= l;
     uint16_t bits;
@@ -210,16 +232,33 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
   }
 }
 
-}  // namespace rbq
+// the splits of pair bh (one workgroup of 128 threads, one output dim each), in split
+// order: out = sum_sp e^(m_sp - M) o_sp / sum_sp e^(m_sp - M) l_sp, M the largest maximum
+// (split 0 always holds token 0, so M is finite); rounded to the query's format
+__global__ __launch_bounds__(kAttnD) void attention_merge_kernel(AttnArgs a) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* pp = a.part + (int64_t)bh * a.splits * (2 + kAttnD);
+  float mx = pp[0];
+  for (int sp = 1; sp < a.splits; ++sp) mx = fmaxf(mx, pp[sp * (2 + kAttnD)]);
+  float o = 0.0f, l = 0.0f;
+  for (int sp = 0; sp < a.splits; ++sp) {
+    const float* ps = pp + sp * (2 + kAttnD);
+    const float w = __expf(ps[0] - mx);  // 0 for a split without tokens (maximum -inf)
+    o = fmaf(ps[2 + d], w, o);
+    l = fmaf(ps[1], w, l);
+  }
+  o /= l;
+  uint16_t bits;
+  if (a.q_f16) bits = __builtin_bit_cast(uint16_t, (_Float16)o);
+  else bits = (uint16_t)f32_to_bf16(o);
+  ((uint16_t*)a.out)[(int64_t)bh * kAttnD + d] = bits;
+}
 
-using namespace rbq;
-
-extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes,
-                                              const void* k_scales, const uint8_t* v_codes,
-                                              const void* v_scales, rbq_dtype scale_dtype, int64_t batch,
-                                              int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap,
-                                              int64_t head_dim, float softmax_scale, void* out,
-                                              hipStream_t stream) {
+// checks shared by the attention entry points; RBQ_OK when a launch should follow
+static rbq_status attn_check(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes, const void* k_scales,
+                             const uint8_t* v_codes, const void* v_scales, rbq_dtype scale_dtype, int64_t batch,
+                             int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap, int64_t head_dim,
+                             float softmax_scale, const void* out) {
   if (q_dtype != RBQ_BF16 && q_dtype != RBQ_F16) return RBQ_EINVAL;
   if (!valid_scale_dtype(scale_dtype)) return RBQ_EINVAL;
   if (batch < 0 || heads < 0 || kv_heads < 1 || seq < 1 || seq_cap < seq) return RBQ_EINVAL;
@@ -233,19 +272,98 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
   // buffer offsets within one head's cache are 32-bit: seq * 64 bytes must fit
   if (batch * heads > 0x7FFFFFFF || heads > 0x7FFFFFFF || seq_cap > (int64_t{1} << 30) || seq >= (int64_t{1} << 26))
     return RBQ_ENOTSUP;
+  return RBQ_OK;
+}
+
+static AttnArgs attn_args(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes, const void* k_scales,
+                          const uint8_t* v_codes, const void* v_scales, rbq_dtype scale_dtype, int64_t heads,
+                          int64_t kv_heads, int64_t seq, int64_t seq_cap, float softmax_scale, void* out) {
   AttnArgs a{};
   a.q = q; a.kc = k_codes; a.ks = k_scales; a.vc = v_codes; a.vs = v_scales; a.out = out;
   a.H = (int)heads; a.Hkv = (int)kv_heads; a.S = (int)seq; a.S_cap = (int)seq_cap;
   a.scale = softmax_scale;
   a.q_f16 = q_dtype == RBQ_F16;
   a.scale_f16 = scale_dtype == RBQ_F16;
+  return a;
+}
+
+// bytes of split partials for batch * heads pairs and `splits` ranges
+static int64_t attn_split_bytes(int64_t batch, int64_t heads, int64_t splits) {
+  return batch * heads * splits * (2 + kAttnD) * (int64_t)sizeof(float);
+}
+
+// the split kernels on a workspace of at least attn_split_bytes bytes
+static rbq_status attn_split_launch(AttnArgs a, int64_t batch, int64_t heads, int64_t splits, float* part,
+                                    hipStream_t stream) {
+  a.splits = (int)splits;
+  a.chunk = (int)((a.S + splits - 1) / splits);
+  a.part = part;
+  const uint32_t grid = (uint32_t)(batch * heads * splits);
+  if (a.scale_f16)
+    hipLaunchKernelGGL((attention_decode_kernel<1, true>), dim3(grid), dim3(kAttnThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attention_decode_kernel<0, true>), dim3(grid), dim3(kAttnThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return RBQ_EHIP;
+  hipLaunchKernelGGL(attention_merge_kernel, dim3((uint32_t)(batch * heads)), dim3(kAttnD), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+}
+
+}  // namespace rbq
+
+using namespace rbq;
+
+extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes,
+                                              const void* k_scales, const uint8_t* v_codes,
+                                              const void* v_scales, rbq_dtype scale_dtype, int64_t batch,
+                                              int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap,
+                                              int64_t head_dim, float softmax_scale, void* out,
+                                              hipStream_t stream) {
+  const rbq_status st = attn_check(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, batch, heads,
+                                   kv_heads, seq, seq_cap, head_dim, softmax_scale, out);
+  if (st != RBQ_OK || batch == 0 || heads == 0) return st;
+  const AttnArgs a = attn_args(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, heads, kv_heads, seq,
+                               seq_cap, softmax_scale, out);
   if (diag_log())
     fprintf(stderr, "rbq: attention_decode_int4kv B=%lld H=%lld Hkv=%lld S=%lld cap=%lld\n", (long long)batch,
             (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap);
   if (diag_fail_launch()) return RBQ_EHIP;
   if (a.scale_f16)
-    hipLaunchKernelGGL(attention_decode_kernel<1>, dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<1, false>), dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(attention_decode_kernel<0>, dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<0, false>), dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0,
+                       stream, a);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+}
+
+extern "C" rbq_status rbq_attention_split_workspace_bytes(int64_t batch, int64_t heads, int64_t splits,
+                                                          int64_t* bytes) {
+  if (!bytes || batch < 0 || heads < 0 || splits < 1 || splits > 4096) return RBQ_EINVAL;
+  if (batch * heads > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  *bytes = attn_split_bytes(batch, heads, splits);
+  return RBQ_OK;
+}
+
+extern "C" rbq_status attention_decode_int4kv_split(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes,
+                                                    const void* k_scales, const uint8_t* v_codes,
+                                                    const void* v_scales, rbq_dtype scale_dtype, int64_t batch,
+                                                    int64_t heads, int64_t kv_heads, int64_t seq, int64_t seq_cap,
+                                                    int64_t head_dim, float softmax_scale, int64_t splits,
+                                                    void* workspace, int64_t workspace_bytes, void* out,
+                                                    hipStream_t stream) {
+  if (splits < 1 || splits > 4096) return RBQ_EINVAL;
+  const rbq_status st = attn_check(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, batch, heads,
+                                   kv_heads, seq, seq_cap, head_dim, softmax_scale, out);
+  if (st != RBQ_OK || batch == 0 || heads == 0) return st;
+  if (batch * heads * splits > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < attn_split_bytes(batch, heads, splits))
+    return RBQ_EINVAL;
+  const AttnArgs a = attn_args(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, heads, kv_heads, seq,
+                               seq_cap, softmax_scale, out);
+  if (diag_log())
+    fprintf(stderr, "rbq: attention_decode_int4kv_split B=%lld H=%lld Hkv=%lld S=%lld cap=%lld splits=%lld\n",
+            (long long)batch, (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap,
+            (long long)splits);
+  if (diag_fail_launch()) return RBQ_EHIP;
+  return attn_split_launch(a, batch, heads, splits, (float*)workspace, stream);
 }

@@ -3,7 +3,8 @@
 // contiguous slice). It is the measured ceiling the HBM-bound kernels are compared with,
 // beside the published peak; it computes nothing of the method.
 //
-// 256 threads per workgroup, 16-byte loads and stores, four loads in flight per lane.
+// 256 threads per workgroup, 16-byte loads and stores, up to sixteen loads in flight per
+// lane (all of a workgroup's slice when it is 64 KiB or less).
 // The loaded words are folded with xor into one value that every store writes, so the
 // loads cannot be dropped; with no write slice, one word per workgroup is written only if
 // the fold hits a value the caller's fill never produces.
@@ -19,24 +20,21 @@ typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kProbeThreads = 256;
 constexpr int kProbeChunk = kProbeThreads * 16;  // bytes one pass of the workgroup moves
 
+// P: 16-byte loads per lane per batch, all issued before any is used (a row kernel loads
+// its whole row that way)
+template <int P>
 __global__ __launch_bounds__(kProbeThreads) void hbm_probe_kernel(const char* src, int64_t rd, char* dst,
                                                                   int64_t wr, uint32_t marker) {
   const int64_t b = blockIdx.x;
   const probe_u32x4* s = (const probe_u32x4*)(src + b * rd) + threadIdx.x;
   uint32_t fold = 0;
   const int64_t passes = rd / kProbeChunk;
-  int64_t p = 0;
-  for (; p + 4 <= passes; p += 4) {
-    probe_u32x4 v0 = s[(p + 0) * kProbeThreads];
-    probe_u32x4 v1 = s[(p + 1) * kProbeThreads];
-    probe_u32x4 v2 = s[(p + 2) * kProbeThreads];
-    probe_u32x4 v3 = s[(p + 3) * kProbeThreads];
-    probe_u32x4 x = v0 ^ v1 ^ v2 ^ v3;
-    fold ^= x[0] ^ x[1] ^ x[2] ^ x[3];
-  }
-  for (; p < passes; ++p) {
-    probe_u32x4 v = s[p * kProbeThreads];
-    fold ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  for (int64_t p = 0; p < passes; p += P) {
+    probe_u32x4 v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = s[(p + i) * kProbeThreads];
+#pragma unroll
+    for (int i = 0; i < P; ++i) fold ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
   }
   if (wr == 0) {
     if (fold == marker) *(uint32_t*)(dst + b * 16 + (threadIdx.x & 3) * 4) = fold;
@@ -65,7 +63,17 @@ extern "C" rbq_status rbq_hbm_probe(const void* src, int64_t read_bytes_per_bloc
     fprintf(stderr, "rbq: hbm_probe read=%lld write=%lld blocks=%lld\n", (long long)read_bytes_per_block,
             (long long)write_bytes_per_block, (long long)blocks);
   if (diag_fail_launch()) return RBQ_EHIP;
-  hipLaunchKernelGGL(hbm_probe_kernel, dim3((uint32_t)blocks), dim3(kProbeThreads), 0, stream, (const char*)src,
-                     read_bytes_per_block, (char*)dst, write_bytes_per_block, 0x9E3779B9u);
+  // as many loads in flight per lane as the block's slice allows, up to 16
+  const int64_t passes = read_bytes_per_block / kProbeChunk;
+  const dim3 grid((uint32_t)blocks), block(kProbeThreads);
+  const uint32_t marker = 0x9E3779B9u;
+  const char* sp = (const char*)src;
+  char* dp = (char*)dst;
+  const int64_t rd = read_bytes_per_block, wr = write_bytes_per_block;
+  if (passes % 16 == 0 && passes > 0) hipLaunchKernelGGL(hbm_probe_kernel<16>, grid, block, 0, stream, sp, rd, dp, wr, marker);
+  else if (passes % 8 == 0 && passes > 0) hipLaunchKernelGGL(hbm_probe_kernel<8>, grid, block, 0, stream, sp, rd, dp, wr, marker);
+  else if (passes % 4 == 0 && passes > 0) hipLaunchKernelGGL(hbm_probe_kernel<4>, grid, block, 0, stream, sp, rd, dp, wr, marker);
+  else if (passes % 2 == 0 && passes > 0) hipLaunchKernelGGL(hbm_probe_kernel<2>, grid, block, 0, stream, sp, rd, dp, wr, marker);
+  else hipLaunchKernelGGL(hbm_probe_kernel<1>, grid, block, 0, stream, sp, rd, dp, wr, marker);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }

@@ -86,6 +86,32 @@ int main(int argc, char **argv) {
          RBQ_ENOTSUP);
   EXPECT(attention_decode_int4kv(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 3, 16, 16, 128, 0.1f, PX, NULL),
          RBQ_EINVAL);
+  /* split attention: bad split counts, a short or missing workspace, head_dim 64 */
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 0, PS,
+                                       1 << 20, PX, NULL),
+         RBQ_EINVAL);
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4097, PS,
+                                       1 << 30, PX, NULL),
+         RBQ_EINVAL);
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4, PS,
+                                       2 * 8 * 4 * 130 * 4 - 4, PX, NULL),
+         RBQ_EINVAL);
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4, NULL,
+                                       1 << 20, PX, NULL),
+         RBQ_EINVAL);
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 64, 0.1f, 4, PS,
+                                       1 << 20, PX, NULL),
+         RBQ_ENOTSUP);
+  EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 0, 8, 2, 16, 16, 128, 0.1f, 4, NULL,
+                                       0, PX, NULL),
+         RBQ_OK); /* empty batch: nothing to do, no workspace needed */
+  {
+    int64_t bytes = 0;
+    EXPECT(rbq_attention_split_workspace_bytes(2, 8, 4, &bytes), RBQ_OK);
+    if (bytes != 2 * 8 * 4 * 130 * 4) { printf("FAIL split workspace bytes: %lld\n", (long long)bytes); ++failures; }
+    EXPECT(rbq_attention_split_workspace_bytes(2, 8, 0, &bytes), RBQ_EINVAL);
+    EXPECT(rbq_attention_split_workspace_bytes(2, 8, 4, NULL), RBQ_EINVAL);
+  }
   EXPECT(w4a4_gemm(PC, PS, PC, PS, RBQ_F16, 64, 64, 4000, PX, NULL, NULL), RBQ_ENOTSUP);
   EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, H / 2, S, D, st, st, st, NULL, NULL, 0, 8, S + 7,
                               PS, PC, PS, PC, PS, RBQ_F16, NULL),
@@ -124,6 +150,9 @@ int main(int argc, char **argv) {
     EXPECT(rbq_hbm_probe(PX, 65536, PC, 16384, 8, NULL), launched);
     EXPECT(kv_cache_append_int4(PX, PX, PX, RBQ_BF16, B, H, H / 2, S, D, st, st, st, (const float *)PS,
                                 (const float *)PS, 2 * S, 3, S + 3, PS, PC, PS, PC, PS, RBQ_F16, NULL),
+           launched);
+    EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4, PS,
+                                         2 * 8 * 4 * 130 * 4, PX, NULL),
            launched);
   }
 

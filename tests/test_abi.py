@@ -238,7 +238,7 @@ def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 14, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 15, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
@@ -251,6 +251,7 @@ def test_dispatch_log(abi_client):
     assert lines[11].startswith("rbq: w4a8_gemm M=64")
     assert lines[12].startswith("rbq: hbm_probe read=65536 write=16384 blocks=8")
     assert lines[13].startswith("rbq: kv_cache_append B=2 H=4 Hkv=2 S=16 D=128 pos0=3 cap=19 rope=1 q=1")
+    assert lines[14].startswith("rbq: attention_decode_int4kv_split B=2 H=8 Hkv=2 S=16 cap=16 splits=4")
 
 
 def test_kron_validation_and_factor(L):
@@ -329,3 +330,25 @@ def test_attention_validation(L):
     assert at(D=64) == NS
     assert at(S=1 << 26, cap=1 << 26) == NS  # one head's codes past 32-bit byte offsets
     assert at(S=16, cap=(1 << 30) + 1) == NS
+
+
+def test_attention_split_validation(L):
+    E, NS = rbq.RBQ_EINVAL, rbq.RBQ_ENOTSUP
+    need = 2 * 8 * 4 * 130 * 4
+
+    def sp(splits=4, ws=A16b, ws_bytes=need, B=2, H=8, Hkv=2, S=16, D=128):
+        return L.attention_decode_int4kv_split(A16, rbq.RBQ_BF16, A16b, A16c, A16b, A16c, rbq.RBQ_F16, B, H, Hkv, S,
+                                               S, D, 0.1, splits, ws, ws_bytes, A16, NULL)
+
+    assert sp(B=0, ws=NULL, ws_bytes=0) == rbq.RBQ_OK
+    assert sp(splits=0) == E
+    assert sp(splits=4097) == E
+    assert sp(ws=NULL) == E
+    assert sp(ws=ctypes.c_void_p(0x20008)) == E
+    assert sp(ws_bytes=need - 1) == E
+    assert sp(D=256) == NS
+    assert sp(H=6, Hkv=4) == E
+    n = ctypes.c_int64(0)
+    assert L.rbq_attention_split_workspace_bytes(2, 8, 4, ctypes.byref(n)) == rbq.RBQ_OK and n.value == need
+    assert L.rbq_attention_split_workspace_bytes(-1, 8, 4, ctypes.byref(n)) == E
+    assert rbq.attention_split_workspace_bytes(16, 32, 8) == 16 * 32 * 8 * 130 * 4

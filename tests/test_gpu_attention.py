@@ -1,12 +1,14 @@
-"""GPU parity of attention_decode_int4kv against the fp64 oracle, through the C ABI: the
-kernel and the oracle read the same INT4 key/value codes and scales.
+"""GPU parity of attention_decode_int4kv and attention_decode_int4kv_split against the fp64
+oracle, through the C ABI: the kernels and the oracle read the same INT4 key/value codes and
+scales.
 
 Tolerance, derived from the kernel's fp32 arithmetic: a score takes 8 fused multiply-adds,
 4 shuffle additions and one product with the key scale, so its error is at most
 d_s = 14 * 2^-24 * |scale| * k_scale[s] * sum_d |q_d code_sd|; the probabilities then err by
 at most 2 max(d_s) + 2^-20 relative (each is a product of at most S/256 + 3 exponentials:
-the token's own, its group's rescalings and the merge weight, whose arguments add up to the
-score's distance from the maximum), the sums over S tokens by S * 2^-23,
+the token's own, its group's rescalings and the merge weights (one more for the split
+kernel's ranges), whose arguments add up to the score's distance from the maximum), the sums
+over S tokens by S * 2^-23,
 the output is rounded to bf16 (2^-8 relative covers it), and probabilities below the
 fp32 normal range (2^-126) are flushed to zero:
     |out - ref| <= 2^-8 |ref| + (2 max_s d_s + 2^-20 + S 2^-23) * sum_s p_s |v_sd|
@@ -71,11 +73,15 @@ def make(seed, B, H, Hkv, S, cap, scale_dtype=np.float16):
     return q, kc, ks, vc, vs
 
 
-def run(rbq, q, kc, ks, vc, vs, scale, seq):
+def run(rbq, q, kc, ks, vc, vs, scale, seq, splits=None):
+    """splits: None for attention_decode_int4kv, else attention_decode_int4kv_split."""
     qd = torch.from_numpy(workloads.f32_to_bf16_bits(q.astype(np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
     pk = lambda c: torch.from_numpy(oracle.pack_nibbles(c.reshape(-1, 128)).reshape(c.shape[:-1] + (64,))).cuda()
-    out = rbq.attention_decode_int4kv(qd, pk(kc), torch.from_numpy(ks).cuda(), pk(vc), torch.from_numpy(vs).cuda(),
-                                      scale, seq=seq)
+    args = (qd, pk(kc), torch.from_numpy(ks).cuda(), pk(vc), torch.from_numpy(vs).cuda(), scale)
+    if splits is None:
+        out = rbq.attention_decode_int4kv(*args, seq=seq)
+    else:
+        out = rbq.attention_decode_int4kv_split(*args, splits, seq=seq)
     torch.cuda.synchronize()
     return out
 
@@ -156,3 +162,48 @@ def test_attention_full_decode_shape_sampled(rbq):
     rng = np.random.default_rng(3)
     pairs = [(0, 0), (15, 31)] + [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(10)]
     check(out, q, kc, ks, vc, vs, 1.0 / math.sqrt(128), heads=pairs)
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,cap,splits", [(1, 1, 1, 1, 1, 1), (1, 1, 1, 1, 1, 5), (2, 4, 2, 37, 40, 3),
+                                                  (2, 4, 2, 37, 40, 64), (1, 8, 8, 1024, 1024, 4),
+                                                  (2, 32, 8, 3000, 3072, 7), (3, 6, 3, 1025, 1100, 16)])
+def test_attention_split_random_codes(rbq, B, H, Hkv, S, cap, splits):
+    """ranges of ceil(S / splits) tokens; with splits > S the last ranges are empty"""
+    print(f"case attention split B={B} H={H} Hkv={Hkv} S={S} cap={cap} splits={splits}", flush=True)
+    q, kc, ks, vc, vs = make(B * 100 + S, B, H, Hkv, S, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = run(rbq, q, kc, ks, vc, vs, scale, S, splits=splits)
+    check(out, q, kc[:, :, :S], ks[:, :, :S], vc[:, :, :S], vs[:, :, :S], scale)
+
+
+def test_attention_split_peaked_scores_fp32_scales(rbq):
+    # nearly one-hot softmax: the ranges' maxima differ widely and all but one weigh ~0
+    print("case attention split peaked", flush=True)
+    q, kc, ks, vc, vs = make(7, 2, 4, 4, 2500, 2500, np.float32)
+    out = run(rbq, q, kc, ks, vc, vs, 4.0, 2500, splits=9)
+    check(out, q, kc, ks, vc, vs, 4.0)
+
+
+def test_attention_split_full_decode_shape_sampled(rbq):
+    """B = 16, H = 32, S = 2048 with 8 ranges per head, in a reused workspace; heads sampled
+    against the oracle, and the whole output within a few bf16 steps of the unsplit kernel's."""
+    B, H, S = 16, 32, 2048
+    print("case attention split full decode shape", flush=True)
+    q, kc, ks, vc, vs = make(99, B, H, H, S, S)
+    scale = 1.0 / math.sqrt(128)
+    ws = torch.full((rbq.attention_split_workspace_bytes(B, H, 8),), 0xFF, dtype=torch.uint8, device="cuda")
+    qd = torch.from_numpy(workloads.f32_to_bf16_bits(q.astype(np.float32)).view(np.int16)).view(torch.bfloat16).cuda()
+    pk = lambda c: torch.from_numpy(oracle.pack_nibbles(c.reshape(-1, 128)).reshape(c.shape[:-1] + (64,))).cuda()
+    args = (qd, pk(kc), torch.from_numpy(ks).cuda(), pk(vc), torch.from_numpy(vs).cuda(), scale)
+    out = rbq.attention_decode_int4kv_split(*args, 8, workspace=ws)
+    out2 = rbq.attention_decode_int4kv_split(*args, 8, workspace=ws)  # the workspace as the first call left it
+    ref = rbq.attention_decode_int4kv(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    rng = np.random.default_rng(3)
+    pairs = [(0, 0), (15, 31)] + [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(10)]
+    check(out, q, kc, ks, vc, vs, scale, heads=pairs)
+    # the two kernels' fp32 values differ by rounding only, so their bf16 outputs by at most
+    # about one bf16 step (2^-7 relative); 2^-6 leaves room for a binade edge
+    a, b = out.float(), ref.float()
+    assert bool(((a - b).abs() <= b.abs() * 2.0 ** -6 + 2.0 ** -20).all())
