@@ -330,6 +330,28 @@ rbq_status attention_decode_int4kv_split(const void *q, rbq_dtype q_dtype, const
 rbq_status rbq_attention_split_workspace_bytes(int64_t batch, int64_t heads, int64_t splits, int64_t *bytes);
 
 /*
+ * attention_decode_int4kv_split_noalloc -- attention_decode_int4kv_split for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the ranges' partials go to a fixed array of 8 MiB that
+ * the library holds on each GPU it runs on until the process ends, so the call takes no
+ * workspace and allocates nothing. Its device address is looked up once per device (with
+ * that device current), on the first call there.
+ *
+ *  all other arguments as attention_decode_int4kv_split.
+ *  limit   batch * heads * splits * 130 * 4 <= 8 MiB (else RBQ_ENOTSUP, nothing launched).
+ * The array keeps the last call's partials; nothing in it needs to start at zero. Calls
+ * that overlap on one GPU (other streams, other threads) share the array and race: the
+ * caller serialises them. Errors: as attention_decode_int4kv_split, plus RBQ_ENOTSUP above
+ * the limit and RBQ_EHIP if the array's address cannot be found.
+ */
+rbq_status attention_decode_int4kv_split_noalloc(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
+                                                 const void *k_scales, const uint8_t *v_codes,
+                                                 const void *v_scales, rbq_dtype scale_dtype, int64_t batch,
+                                                 int64_t heads, int64_t kv_heads, int64_t seq,
+                                                 int64_t seq_cap, int64_t head_dim, float softmax_scale,
+                                                 int64_t splits, void *out, hipStream_t stream);
+
+/*
  * w4a8_gemm_grouped -- W4A8 with group-wise weight scales: one scale per run of `group`
  * consecutive K elements of each weight row ("SpinQuant, when rotations are worth
  * learning": its ExecuTorch export uses 4-bit weights in groups of 256 or 32 input

@@ -18,7 +18,9 @@ The calls have the same names and meaning as the C functions declared in
   quantizer (one scale per run of ``group`` elements) and the W4A8 GEMM that consumes it;
 * ``attention_decode_int4kv`` -- decode attention over the INT4 key/value cache;
   ``attention_decode_int4kv_split`` the same with each sequence cut into ranges taken by
-  separate workgroups, their partials combined through a caller's workspace.
+  separate workgroups, their partials combined through a caller's workspace
+  (``attention_decode_int4kv_split_noalloc``: through the library's fixed device array,
+  for callers that cannot allocate).
 
 This module only marshals arguments: it takes ``torch.Tensor`` objects that live in GPU
 memory, allocates outputs with torch when the caller does not pass them, and hands raw
@@ -47,6 +49,7 @@ __all__ = [
     "quantize_groups_int4",
     "attention_decode_int4kv",
     "attention_decode_int4kv_split",
+    "attention_decode_int4kv_split_noalloc",
     "attention_split_workspace_bytes",
     "hbm_probe",
     "RBQ_OK",
@@ -81,6 +84,7 @@ EXPORTED_SYMBOLS = (
     "quantize_groups_int4",
     "attention_decode_int4kv",
     "attention_decode_int4kv_split",
+    "attention_decode_int4kv_split_noalloc",
     "rbq_attention_split_workspace_bytes",
     "rbq_hbm_probe",
     "rbq_status_string",
@@ -153,6 +157,9 @@ def lib():
     L.attention_decode_int4kv_split.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
                                                 ctypes.c_float, i64, vp, i64, vp, vp]
     L.attention_decode_int4kv_split.restype = ci
+    L.attention_decode_int4kv_split_noalloc.argtypes = [vp, ci, vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64,
+                                                        ctypes.c_float, i64, vp, vp]
+    L.attention_decode_int4kv_split_noalloc.restype = ci
     L.rbq_attention_split_workspace_bytes.argtypes = [i64, i64, i64, p64]
     L.rbq_attention_split_workspace_bytes.restype = ci
     L.rbq_hbm_probe.argtypes = [vp, i64, vp, i64, i64, vp]
@@ -645,6 +652,28 @@ def attention_decode_int4kv_split(q, k_codes, k_scales, v_codes, v_scales, softm
                                              seq, S_cap, D, float(softmax_scale), int(splits), _ptr(workspace), have,
                                              _ptr(out), _stream(stream, q.device))
     _check("attention_decode_int4kv_split", st)
+    return out
+
+
+NOALLOC_PARTIAL_BYTES = 8 << 20  # the library's fixed partials array per GPU
+
+
+def attention_decode_int4kv_split_noalloc(q, k_codes, k_scales, v_codes, v_scales, softmax_scale, splits, *,
+                                          seq=None, out, stream=None):
+    """attention_decode_int4kv_split with the partials in the library's fixed device array
+    (8 MiB per GPU: batch * heads * splits * 520 bytes at most): nothing is allocated, so
+    ``out`` [B, H, 128] in q's dtype must be passed. Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("attention_decode_int4kv_split_noalloc allocates nothing: pass out")
+    if q.dim() == 3 and q.shape[0] * q.shape[1] * int(splits) * 520 > NOALLOC_PARTIAL_BYTES:
+        raise ValueError(f"attention_decode_int4kv_split_noalloc: batch * heads * splits * 520 bytes of partials "
+                         f"exceed the library's fixed {NOALLOC_PARTIAL_BYTES} bytes")
+    (B, H, Hkv, seq, S_cap, D), out = _attention_operands(q, k_codes, k_scales, v_codes, v_scales, seq, out)
+    st = lib().attention_decode_int4kv_split_noalloc(_ptr(q), _dtype_code(q.dtype), _ptr(k_codes), _ptr(k_scales),
+                                                     _ptr(v_codes), _ptr(v_scales), _dtype_code(k_scales.dtype), B,
+                                                     H, Hkv, seq, S_cap, D, float(softmax_scale), int(splits),
+                                                     _ptr(out), _stream(stream, q.device))
+    _check("attention_decode_int4kv_split_noalloc", st)
     return out
 
 

@@ -18,6 +18,8 @@
 // groups' (maximum, sum, output) triples are merged in LDS.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/rbq.h"
 #include "common.h"
 #include "diag.h"
@@ -287,6 +289,32 @@ static AttnArgs attn_args(const void* q, rbq_dtype q_dtype, const uint8_t* k_cod
   return a;
 }
 
+// ---- the split partials of attention_decode_int4kv_split_noalloc: a fixed device array,
+// for callers that cannot allocate (one per GPU the library runs on, held until the process
+// ends). Host code never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address): it uses the address hipGetSymbolAddress returns, once per device.
+// Nothing in it must start at zero (the split kernel writes every partial the merge reads);
+// calls that overlap on one GPU share it and race.
+constexpr int64_t kAttnScratchBytes = int64_t{8} << 20;
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+constexpr int kAttnMaxDevices = 64;
+
+// the device address of `scratch` on the current device; nullptr if it cannot be found
+static float* attn_scratch_ptr() {
+  static std::mutex mu;
+  static float* ptrs[kAttnMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kAttnMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = (float*)p;
+  }
+  return ptrs[dev];
+}
+
 // bytes of split partials for batch * heads pairs and `splits` ranges
 static int64_t attn_split_bytes(int64_t batch, int64_t heads, int64_t splits) {
   return batch * heads * splits * (2 + kAttnD) * (int64_t)sizeof(float);
@@ -366,4 +394,30 @@ extern "C" rbq_status attention_decode_int4kv_split(const void* q, rbq_dtype q_d
             (long long)splits);
   if (diag_fail_launch()) return RBQ_EHIP;
   return attn_split_launch(a, batch, heads, splits, (float*)workspace, stream);
+}
+
+extern "C" rbq_status attention_decode_int4kv_split_noalloc(const void* q, rbq_dtype q_dtype, const uint8_t* k_codes,
+                                                            const void* k_scales, const uint8_t* v_codes,
+                                                            const void* v_scales, rbq_dtype scale_dtype,
+                                                            int64_t batch, int64_t heads, int64_t kv_heads,
+                                                            int64_t seq, int64_t seq_cap, int64_t head_dim,
+                                                            float softmax_scale, int64_t splits, void* out,
+                                                            hipStream_t stream) {
+  if (splits < 1 || splits > 4096) return RBQ_EINVAL;
+  const rbq_status st = attn_check(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, batch, heads,
+                                   kv_heads, seq, seq_cap, head_dim, softmax_scale, out);
+  if (st != RBQ_OK || batch == 0 || heads == 0) return st;
+  if (batch * heads * splits > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (attn_split_bytes(batch, heads, splits) > kAttnScratchBytes) return RBQ_ENOTSUP;  // beyond the fixed array
+  const AttnArgs a = attn_args(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, heads, kv_heads, seq,
+                               seq_cap, softmax_scale, out);
+  if (diag_log())
+    fprintf(stderr,
+            "rbq: attention_decode_int4kv_split_noalloc B=%lld H=%lld Hkv=%lld S=%lld cap=%lld splits=%lld\n",
+            (long long)batch, (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap,
+            (long long)splits);
+  if (diag_fail_launch()) return RBQ_EHIP;
+  float* part = attn_scratch_ptr();
+  if (!part) return RBQ_EHIP;
+  return attn_split_launch(a, batch, heads, splits, part, stream);
 }

@@ -105,6 +105,16 @@ int main(int argc, char **argv) {
   EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 0, 8, 2, 16, 16, 128, 0.1f, 4, NULL,
                                        0, PX, NULL),
          RBQ_OK); /* empty batch: nothing to do, no workspace needed */
+  /* the allocation-free variant: its array holds 8 MiB of partials (520 bytes per range) */
+  EXPECT(attention_decode_int4kv_split_noalloc(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 64, 64, 64, 16, 16, 128, 0.1f,
+                                               4, PX, NULL),
+         RBQ_ENOTSUP);
+  EXPECT(attention_decode_int4kv_split_noalloc(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f,
+                                               0, PX, NULL),
+         RBQ_EINVAL);
+  EXPECT(attention_decode_int4kv_split_noalloc(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 64, 0.1f, 4,
+                                               PX, NULL),
+         RBQ_ENOTSUP);
   {
     int64_t bytes = 0;
     EXPECT(rbq_attention_split_workspace_bytes(2, 8, 4, &bytes), RBQ_OK);
@@ -153,6 +163,9 @@ int main(int argc, char **argv) {
            launched);
     EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4, PS,
                                          2 * 8 * 4 * 130 * 4, PX, NULL),
+           launched);
+    EXPECT(attention_decode_int4kv_split_noalloc(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 64, 64, 64, 16, 16, 128,
+                                                 0.1f, 3, PX, NULL),
            launched);
   }
 
