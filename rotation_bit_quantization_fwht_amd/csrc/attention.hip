@@ -9,13 +9,14 @@
 // scores equal those of the unrotated pair ("SpinQuant, when rotations are worth
 // learning", section "Four rotation sites": R3 is there so that K can be cached in INT4).
 //
-// One 512-thread workgroup per (batch, head), one pass over the cache. Sixteen lanes share
-// one cached token: lane c takes dims 8c .. 8c + 7, i.e. one dword of codes of the token's
-// 64-byte row, so a wave reads four consecutive rows (256 contiguous bytes) per load. Each
-// 16-lane group runs its own online softmax over its tokens (every 32nd token): per batch
-// of kAttnU tokens it takes the scores, raises its running maximum, rescales its sum and
-// output, and accumulates the value rows with the probabilities. At the end the 32
-// groups' (maximum, sum, output) triples are merged in LDS.
+// One 256-thread workgroup per (batch, head), or per range of its tokens in the split form,
+// one pass over the cache. Four lanes share one cached token: lane c takes dims
+// 32c .. 32c + 31, i.e. bytes 16c .. 16c + 15 of the token's 64-byte code row, so a wave
+// reads sixteen consecutive rows (1 KiB contiguous) per 16-byte load. Each four-lane group
+// runs its own online softmax over its tokens (every 64th token): per batch of kAttnU
+// tokens it takes the scores, raises its running maximum, rescales its sum and output, and
+// accumulates the value rows with the probabilities. At the end the 64 groups' (maximum,
+// sum, output) triples are merged in LDS.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -41,10 +42,10 @@ struct AttnArgs {
   int q_f16, scale_f16;
 };
 
-constexpr int kAttnThreads = 512;  // (256: 48 us, 1024: 40 us on the [16, 32, 2048, 128] cache)
-constexpr int kAttnGroups = kAttnThreads / 16;  // token groups of sixteen lanes
+constexpr int kAttnThreads = 256;
+constexpr int kAttnGroups = kAttnThreads / 4;  // token groups of four lanes
 constexpr int kAttnD = 128;
-constexpr int kAttnU = 8;  // tokens per group and batch
+constexpr int kAttnU = 4;  // tokens per group and batch
 
 __device__ __forceinline__ float attn_load16(const void* p, int64_t i, int f16) {
   const uint32_t h = ((const uint16_t*)p)[i];
@@ -64,33 +65,11 @@ __device__ __forceinline__ void attn_codes16(uint32_t w, float (&c)[8]) {
   }
 }
 
-// the value of another lane of the same 16-lane row, by a DPP move (CTRL: the DPP
-// control word)
+// the value of another lane of the same quad, by a DPP move (CTRL: the DPP control word)
 template <int CTRL>
 __device__ __forceinline__ float attn_dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
-
-// sum over each row of sixteen lanes, the same bits on every lane of the row: four DPP
-// steps (pairs, quads, the two quads of each half, the two halves), each adding the values
-// of two lanes that then hold the same sum in swapped order. A row is one token group, so
-// its lanes are active or inactive together.
-__device__ __forceinline__ float attn_row16_sum(float v) {
-  v += attn_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += attn_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += attn_dpp<0x141>(v);  // row_half_mirror
-  v += attn_dpp<0x140>(v);  // row_mirror
-  return v;
-}
-
-// one batch of a group's tokens: the lane's dword of each key and value row and the
-// tokens' scales. The loads are buffer loads range-checked against the head's first S
-// tokens: a token past the sequence reads zeros (its score is then set to -inf, so it
-// weighs 0), and no load is predicated.
-struct AttnBatch {
-  uint32_t kw[kAttnU], vw[kAttnU];
-  float ks[kAttnU], vs[kAttnU];
-};
 
 struct AttnRsrc {
   __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
@@ -102,13 +81,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+typedef uint32_t attn_u32x4 __attribute__((ext_vector_type(4)));
+
+struct AttnBatch {
+  attn_u32x4 kw[kAttnU], vw[kAttnU];
+  float ks[kAttnU], vs[kAttnU];
+};
+
 template <int SF16>
 __device__ __forceinline__ void attn_fetch(AttnBatch& r, const AttnRsrc& rs, int t0, int c) {
 #pragma unroll
   for (int u = 0; u < kAttnU; ++u) {
     const uint32_t t = (uint32_t)(t0 + u * kAttnGroups);
-    r.kw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, t * 64u + 4u * c, 0, 0);
-    r.vw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs.vc, t * 64u + 4u * c, 0, 0);
+    r.kw[u] = __builtin_bit_cast(attn_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.kc, t * 64u + 16u * c, 0, 0));
+    r.vw[u] = __builtin_bit_cast(attn_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.vc, t * 64u + 16u * c, 0, 0));
     if constexpr (SF16) {
       r.ks[u] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.ks, t * 2u, 0, 0));
       r.vs[u] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.vs, t * 2u, 0, 0));
@@ -119,27 +105,31 @@ __device__ __forceinline__ void attn_fetch(AttnBatch& r, const AttnRsrc& rs, int
   }
 }
 
-// SPLIT: workgroup x takes the tokens [sp * chunk, (sp + 1) * chunk) of pair bh (x = bh *
-// splits + sp) and writes its (maximum, sum, unnormalised output) to a.part instead of the
-// output; attention_merge_kernel combines the splits
+// sum over each quad of lanes (one token group), the same bits on its four lanes
+__device__ __forceinline__ float attn_quad_sum(float v) {
+  v += attn_dpp<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += attn_dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  return v;
+}
+
 template <int SF16, bool SPLIT>
-__global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void attention_decode_kernel(AttnArgs a) {
   __shared__ float part[kAttnGroups][kAttnD];
-  __shared__ float gmax[kAttnGroups], gsum[kAttnGroups];
+  __shared__ float gmax[kAttnGroups], gsum[kAttnGroups], gw[kAttnGroups], gm;
   const int bh = SPLIT ? (int)blockIdx.x / a.splits : (int)blockIdx.x;
   const int sp = SPLIT ? (int)blockIdx.x - bh * a.splits : 0;
   const int b = bh / a.H, h = bh - b * a.H;
   const int kvh = h / (a.H / a.Hkv);
-  const int tid = threadIdx.x, c = tid & 15, tg = tid >> 4;
+  const int tid = threadIdx.x, c = tid & 3, tg = tid >> 2;
 
-  // the query times the softmax scale, then over 16 (exact) for the codes' factor 16
-  float qd[8];
+  // the lane's 32 query dims times the softmax scale, over 16 (exact) for the codes' 16
+  float qd[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) qd[i] = (attn_load16(a.q, (int64_t)bh * kAttnD + 8 * c + i, a.q_f16) * a.scale) * 0.0625f;
+  for (int i = 0; i < 32; ++i) qd[i] = (attn_load16(a.q, (int64_t)bh * kAttnD + 32 * c + i, a.q_f16) * a.scale) * 0.0625f;
 
   const int64_t head = (int64_t)b * a.Hkv + kvh;
   const uint32_t ssz = SF16 ? 2u : 4u;
-  // this workgroup's tokens: [t_begin, t_begin + n) of the head (all S without splits)
   const int t_begin = SPLIT ? sp * a.chunk : 0;
   const int n = SPLIT ? max(0, min(a.chunk, a.S - t_begin)) : a.S;
   const int64_t tok0 = head * a.S_cap + t_begin;
@@ -149,79 +139,84 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
   rs.ks = attn_rsrc((const char*)a.ks + tok0 * ssz, (uint32_t)n * ssz);
   rs.vs = attn_rsrc((const char*)a.vs + tok0 * ssz, (uint32_t)n * ssz);
 
-  // the group's running maximum and sum (equal on its sixteen lanes) and its output dims
   float m_run = -INFINITY, l_run = 0.0f;
-  float acc[8];
+  float acc[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
 
-  // per batch: scores (eight products per lane, summed over the sixteen lanes with the
-  // same bits on every lane), the raised maximum, the rescaled sum
-  // and output, then the value rows weighted by the probabilities. The batch's loads are
-  // all issued before any is used; the other waves of the CU hide their latency. The
-  // batch's first token is always in range.
+  // a batch's loads are all issued before any is used, and its first token is in range.
+  // Loads are buffer loads range-checked against the workgroup's tokens: a token past them
+  // reads zeros and its score is set to -inf (it weighs 0), so no load is predicated.
   for (int t0 = tg; t0 < n; t0 += kAttnU * kAttnGroups) {
     AttnBatch r;
     attn_fetch<SF16>(r, rs, t0, c);
+    // keep the batch's loads ahead of its arithmetic (the scheduler would otherwise sink
+    // each load to its first use, leaving one token's loads in flight at a time)
+    __builtin_amdgcn_sched_barrier(0);
     float sc[kAttnU];
     float bmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kAttnU; ++u) {
-      float kc[8];
-      attn_codes16(r.kw[u], kc);
       float dot = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dot = fmaf(qd[i], kc[i], dot);
-      dot = attn_row16_sum(dot);
+      for (int j = 0; j < 4; ++j) {
+        float kc[8];
+        attn_codes16(r.kw[u][j], kc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf(qd[8 * j + i], kc[i], dot);
+      }
+      dot = attn_quad_sum(dot);
       sc[u] = (t0 + u * kAttnGroups < n) ? dot * r.ks[u] : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
     const float m_new = fmaxf(m_run, bmax);
-    const float corr = __expf(m_run - m_new);  // 0 on the group's first batch
+    const float corr = __expf(m_run - m_new);
     l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= corr;
+    for (int i = 0; i < 32; ++i) acc[i] *= corr;
 #pragma unroll
     for (int u = 0; u < kAttnU; ++u) {
-      const float p = __expf(sc[u] - m_new);  // 0 past the sequence
+      const float p = __expf(sc[u] - m_new);
       l_run += p;
       const float pv = (p * r.vs[u]) * 0.0625f;
-      float vc[8];
-      attn_codes16(r.vw[u], vc);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pv, vc[i], acc[i]);
+      for (int j = 0; j < 4; ++j) {
+        float vc[8];
+        attn_codes16(r.vw[u][j], vc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[8 * j + i] = fmaf(pv, vc[i], acc[8 * j + i]);
+      }
     }
     m_run = m_new;
   }
 
-  // ---- merge the groups: out = sum_g e^(m_g - M) acc_g / sum_g e^(m_g - M) l_g; groups
-  // without tokens hold (-inf, 0, 0) and weigh 0 (group 0 always has token 0, except in
-  // a split past the sequence's end, whose triple is then (-inf, 0, 0))
+  // ---- merge the 64 groups: weights e^(m_g - M) first, then one output dim per thread
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part[tg][8 * c + i] = acc[i];
+  for (int i = 0; i < 32; ++i) part[tg][32 * c + i] = acc[i];
   if (c == 0) {
     gmax[tg] = m_run;
     gsum[tg] = l_run;
   }
   __syncthreads();
-  if (tid < kAttnD) {
+  if (tid < kAttnGroups) {
     float mx = gmax[0];
-#pragma unroll
     for (int g = 1; g < kAttnGroups; ++g) mx = fmaxf(mx, gmax[g]);
+    gw[tid] = mx == -INFINITY ? 0.0f : __expf(gmax[tid] - mx);
+    if (tid == 0) gm = mx;
+  }
+  __syncthreads();
+  if (tid < kAttnD) {
     float o = 0.0f, l = 0.0f;
-    if (mx != -INFINITY) {
-#pragma unroll
-      for (int g = 0; g < kAttnGroups; ++g) {
-        const float w = __expf(gmax[g] - mx);
-        o = fmaf(part[g][tid], w, o);
-        l = fmaf(gsum[g], w, l);
-      }
+#pragma unroll 8
+    for (int g = 0; g < kAttnGroups; ++g) {
+      o = fmaf(part[g][tid], gw[g], o);
+      l = fmaf(gsum[g], gw[g], l);
     }
     if constexpr (SPLIT) {
       float* pp = a.part + ((int64_t)bh * a.splits + sp) * (2 + kAttnD);
       pp[2 + tid] = o;
       if (tid == 0) {
-        pp[0] = mx;
+        pp[0] = gm;
         pp[1] = l;
       }
       return;
@@ -236,18 +231,37 @@ __global__ __launch_bounds__(kAttnThreads) void attention_decode_kernel(AttnArgs
 
 // the splits of pair bh (one workgroup of 128 threads, one output dim each), in split
 // order: out = sum_sp e^(m_sp - M) o_sp / sum_sp e^(m_sp - M) l_sp, M the largest maximum
-// (split 0 always holds token 0, so M is finite); rounded to the query's format
+// (split 0 always holds token 0, so M is finite); rounded to the query's format. The
+// ranges' maxima and sums are staged in LDS (the threads share the loads), so each
+// thread's loop has only independent loads of its output dim.
+constexpr int kMergeChunk = 512;  // ranges staged per pass
 __global__ __launch_bounds__(kAttnD) void attention_merge_kernel(AttnArgs a) {
+  __shared__ float sm[kMergeChunk], sl[kMergeChunk];
+  __shared__ float red[kAttnD];
   const int bh = blockIdx.x, d = threadIdx.x;
   const float* pp = a.part + (int64_t)bh * a.splits * (2 + kAttnD);
-  float mx = pp[0];
-  for (int sp = 1; sp < a.splits; ++sp) mx = fmaxf(mx, pp[sp * (2 + kAttnD)]);
+  float mx = -INFINITY;
+  for (int sp = d; sp < a.splits; sp += kAttnD) mx = fmaxf(mx, pp[(int64_t)sp * (2 + kAttnD)]);
+  red[d] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int i = 1; i < kAttnD; ++i) mx = fmaxf(mx, red[i]);
   float o = 0.0f, l = 0.0f;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const float* ps = pp + sp * (2 + kAttnD);
-    const float w = __expf(ps[0] - mx);  // 0 for a split without tokens (maximum -inf)
-    o = fmaf(ps[2 + d], w, o);
-    l = fmaf(ps[1], w, l);
+  for (int base = 0; base < a.splits; base += kMergeChunk) {
+    const int cnt = min(kMergeChunk, a.splits - base);
+    __syncthreads();  // the previous pass's reads of sm / sl are done
+    for (int i = d; i < cnt; i += kAttnD) {
+      const float* ps = pp + (int64_t)(base + i) * (2 + kAttnD);
+      sm[i] = __expf(ps[0] - mx);  // 0 for a split without tokens (maximum -inf)
+      sl[i] = ps[1];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int i = 0; i < cnt; ++i) {
+      const float w = sm[i];
+      o = fmaf(pp[(int64_t)(base + i) * (2 + kAttnD) + 2 + d], w, o);
+      l = fmaf(sl[i], w, l);
+    }
   }
   o /= l;
   uint16_t bits;
@@ -355,12 +369,11 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
     fprintf(stderr, "rbq: attention_decode_int4kv B=%lld H=%lld Hkv=%lld S=%lld cap=%lld\n", (long long)batch,
             (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap);
   if (diag_fail_launch()) return RBQ_EHIP;
+  const dim3 grid((uint32_t)(batch * heads));
   if (a.scale_f16)
-    hipLaunchKernelGGL((attention_decode_kernel<1, false>), dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<1, false>), grid, dim3(kAttnThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attention_decode_kernel<0, false>), dim3((uint32_t)(batch * heads)), dim3(kAttnThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<0, false>), grid, dim3(kAttnThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
 

@@ -2,9 +2,10 @@
 oracle, through the C ABI: the kernels and the oracle read the same INT4 key/value codes and
 scales.
 
-Tolerance, derived from the kernel's fp32 arithmetic: a score takes 8 fused multiply-adds,
-4 shuffle additions and one product with the key scale, so its error is at most
-d_s = 14 * 2^-24 * |scale| * k_scale[s] * sum_d |q_d code_sd|; the probabilities then err by
+Tolerance, derived from the kernel's fp32 arithmetic: a score takes the rounded product of
+the query with the softmax scale, 32 fused multiply-adds per lane, 2 shuffle additions
+across the four lanes of a token and one product with the key scale, so its error is at most
+d_s = 36 * 2^-24 * |scale| * k_scale[s] * sum_d |q_d code_sd|; the probabilities then err by
 at most 2 max(d_s) + 2^-20 relative (each is a product of at most S/256 + 3 exponentials:
 the token's own, its group's rescalings and the merge weights (one more for the split
 kernel's ranges), whose arguments add up to the score's distance from the maximum), the sums
@@ -54,7 +55,7 @@ def check(out_dev, q, kc, ks, vc, vs, scale, heads=None):
         ref, p = ref[0, 0], p[0, 0]
         S = p.shape[0]
         dots = np.abs(kc[b, kvh].astype(np.float64) * q[b, h][None, :]).sum(axis=1)
-        d_max = float(np.max(14 * 2.0 ** -24 * abs(scale) * ks[b, kvh].astype(np.float64) * dots))
+        d_max = float(np.max(36 * 2.0 ** -24 * abs(scale) * ks[b, kvh].astype(np.float64) * dots))
         vmag = (p[:, None] * np.abs(vc[b, kvh] * vs[b, kvh][:, None].astype(np.float64))).sum(axis=0)
         vmax = float(np.max(np.abs(vc[b, kvh] * vs[b, kvh][:, None].astype(np.float64))))
         bound = (2.0 ** -8 * np.abs(ref) + (2 * d_max + 2.0 ** -20 + S * 2.0 ** -23) * vmag
