@@ -87,6 +87,17 @@ struct DevCtx {
   // compiler from moving LDS accesses across the point.
   __device__ __forceinline__ void wave_sync() const { __builtin_amdgcn_wave_barrier(); }
   __device__ __forceinline__ float shfl_xor(float v, int m) const { return __shfl_xor(v, m); }
+  // the same with a constant mask: masks 1 and 2 stay within a quad of lanes and take one
+  // DPP move (quad permutes [1, 0, 3, 2] and [2, 3, 0, 1]) instead of an LDS permute
+  template <int M>
+  __device__ __forceinline__ float shfl_xor_c(float v) const {
+    if constexpr (M == 1 || M == 2) {
+      constexpr int ctrl = (M == 1) ? 0xB1 : 0x4E;
+      return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+    } else {
+      return __shfl_xor(v, M);
+    }
+  }
 
   template <class T>
   __device__ __forceinline__ T load(const void* p) const {

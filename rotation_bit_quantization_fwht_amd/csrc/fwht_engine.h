@@ -54,6 +54,9 @@ struct TensorArgs {
   uint32_t rope_pos0;
   uint32_t mode;
   int64_t rows;            // rows of this tensor
+  uint32_t hs;             // RoPE, matrix plans: 1 = blocks in head-group order (hs_coords)
+  uint32_t nsb, nhh;       // head-group order: token blocks per head, head groups per batch
+  FastDiv div_nsb, div_nhh;
   uint32_t out_cap;        // 0: codes and scales rows follow the input rows; else the rows
                            // of (batch, head) pair bh go to bh * out_cap + s (a cache of
                            // capacity out_cap per head, its base pointers at the first
@@ -162,6 +165,87 @@ RBQ_HD int64_t row_offset(const TensorArgs& t, int64_t row) {
   }
 }
 
+// Head-group order (RoPE kernels of the matrix plans, when t.hs is set). Each block of 2^r
+// rows covers HG heads x 2^r / HG consecutive tokens of one batch, the blocks running over
+// the tokens, then the head groups, then the batch. The rows of one lane's loads (the row
+// bits its register index selects) are then HG heads at one token, which share their RoPE
+// angles, and each head's rows in the block are consecutive tokens, read as one contiguous
+// run. (A block of 64 rows over 32 heads at 2 tokens, 512 bytes per head, read ~1.6x
+// slower on the R3 workload; 4 heads x 16 tokens about as fast as the natural order.)
+// Without t.hs rows keep their natural (batch, head, token) order.
+struct Bhs {
+  uint32_t b, h, s;
+};
+
+// the row bits of a block that a lane's register index selects in phase 0
+template <int K, bool MF>
+constexpr uint32_t hs_jbits() {
+  return reg_part(RBQ_PLAN, 0, ((1u << RBQ_PLAN.e) - 1u) & ~7u) >> K;
+}
+
+// (batch, head, token) of block row r in head-group order
+template <int K, bool MF>
+RBQ_HD Bhs hs_coords(const TensorArgs& t, uint32_t r) {
+  constexpr uint32_t JB = hs_jbits<K, MF>();
+  constexpr int RB = RBQ_PLAN.r;
+  constexpr int HB = popcount_c(JB);
+  const uint32_t blk = r >> RB, rw = r & ((1u << RB) - 1u);
+  const uint32_t q = fastdiv(blk, t.div_nsb);  // batch * head groups + head group
+  const uint32_t b = fastdiv(q, t.div_nhh);
+  uint32_t hl = 0u, sl = 0u;
+  static_for<0, RB>([&](auto I) {
+    constexpr uint32_t below = (1u << I.value) - 1u;
+    const uint32_t bit = (rw >> I.value) & 1u;
+    if constexpr ((JB >> I.value) & 1u) hl |= bit << popcount_c(JB & below);
+    else sl |= bit << popcount_c(~JB & below);
+  });
+  return Bhs{b, ((q - b * t.nhh) << HB) | hl, ((blk - q * t.nsb) << (RB - HB)) | sl};
+}
+
+// the natural (batch, head, token) tensor row that block row r stands for
+template <int K, bool MF, bool RMAP>
+RBQ_HD int64_t tensor_row(const TensorArgs& t, int64_t r) {
+  if constexpr (RMAP && MF) {
+    if (t.hs) {
+      const Bhs x = hs_coords<K, MF>(t, (uint32_t)r);
+      return ((int64_t)x.b * t.heads + x.h) * t.seq + x.s;
+    }
+  }
+  return r;
+}
+
+// element offset of row (b, h, s): 4-D strides, or the natural rows of a 2-D tensor
+template <bool FOURD>
+RBQ_HD int64_t bhs_offset(const TensorArgs& t, const Bhs& x) {
+  if constexpr (FOURD) return (int64_t)x.b * t.sb + (int64_t)x.h * t.sh + (int64_t)x.s * t.ss;
+  else return ((int64_t)x.b * t.heads + x.h) * t.seq * t.row_stride + (int64_t)x.s * t.row_stride;
+}
+
+// host: head-group order for a RoPE launch at row length 2^k, when the heads and tokens
+// divide into whole blocks (so every block is full); else the natural order
+template <int K, bool MF>
+inline void set_rope_order(TensorArgs& t) {
+  t.hs = 0u;
+  if constexpr (MF) {
+    constexpr uint32_t HG = 1u << popcount_c(hs_jbits<K, MF>());
+    constexpr uint32_t SG = (1u << RBQ_PLAN.r) / HG;
+    if (t.heads > 0u && t.seq > 0u && t.heads % HG == 0u && t.seq % SG == 0u) {
+      t.hs = 1u;
+      t.nsb = t.seq / SG;
+      t.nhh = t.heads / HG;
+      t.div_nsb = make_fastdiv(t.nsb);
+      t.div_nhh = make_fastdiv(t.nhh);
+    }
+  }
+}
+
+// host: the order of a RoPE launch at row length 2^k (the matrix plans serve k = 7, 8)
+inline void set_rope_order_rt(TensorArgs& t, int k) {
+  if (k == 7) set_rope_order<7, true>(t);
+  else if (k == 8) set_rope_order<8, true>(t);
+  else t.hs = 0u;
+}
+
 // output row (codes, scales) of input row r: r itself, or with CACHE and t.out_cap != 0 row
 // s of (batch, head) pair bh = r / seq in a cache of t.out_cap rows per pair
 template <bool CACHE>
@@ -175,11 +259,11 @@ RBQ_HD int64_t out_row(const TensorArgs& t, int64_t r) {
 
 // RoPE on one row held whole in this lane's registers (rows of at most 64 elements): w holds
 // the row's 16-bit values two per word, element i in half i % 2 of word i / 2; element i
-// pairs with i + n/2. Same arithmetic as apply_rope below.
+// pairs with i + n/2. Same arithmetic as apply_rope below: x cos -+ p sin in fp32 as a
+// rounded product p sin and a fused multiply-add, rounded back to the 16-bit format.
 template <int K, int IN, class Ctx>
-RBQ_HD void apply_rope_in_lane(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t (&w)[1 << (K - 1)]) {
+RBQ_HD void apply_rope_in_lane(Ctx& c, const TensorArgs& t, uint32_t srow, uint32_t (&w)[1 << (K - 1)]) {
   constexpr uint32_t H = 1u << (K - 1);  // pairs, and the words of one half
-  const uint32_t srow = row - fastdiv(row, t.div_s) * t.seq;
   const float* cp = t.rope_cos + (int64_t)(t.rope_pos0 + srow) * H;
   const float* sp = t.rope_sin + (int64_t)(t.rope_pos0 + srow) * H;
   static_for<0, (int)(H / 8)>([&](auto G) {  // eight pairs at a time: four words of each half
@@ -197,8 +281,9 @@ RBQ_HD void apply_rope_in_lane(Ctx& c, const TensorArgs& t, uint32_t row, uint32
         const uint32_t bb = (w[hi] >> (16 * HALF.value)) & 0xFFFFu;
         const float a = (IN == IN_F16) ? f16_to_f32(ab) : bits_f32(ab << 16);
         const float b = (IN == IN_F16) ? f16_to_f32(bb) : bits_f32(bb << 16);
-        rl[HALF.value] = a * cs[j] - b * sn[j];
-        rh[HALF.value] = b * cs[j] + a * sn[j];
+        // x cos -+ p sin as one product and one fused multiply-add
+        rl[HALF.value] = fmaf(a, cs[j], b * -sn[j]);
+        rh[HALF.value] = fmaf(b, cs[j], a * sn[j]);
       });
       if constexpr (IN == IN_F16) {
         w[lo] = f32_to_f16(rl[0]) | (f32_to_f16(rl[1]) << 16);
@@ -282,7 +367,8 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
     }
     if constexpr (ROPE) {
       static_assert(IN != IN_F32 && C0 == K && NRUN == 1, "RoPE in the load needs a whole 16-bit row per lane");
-      apply_rope_in_lane<K, IN>(c, t, (uint32_t)(row0 + rw), w);
+      const uint32_t row = (uint32_t)(row0 + rw);
+      apply_rope_in_lane<K, IN>(c, t, row - fastdiv(row, t.div_s) * t.seq, w);
     }
     if constexpr (IN == IN_F32) {
       static_for<0, L>([&](auto I) { v[rb + I.value] = bits_f32(w[I.value]); });
@@ -313,27 +399,34 @@ constexpr int rope_partner_lane_bit() {
   return -1;
 }
 
-// RoPE on the 8 16-bit values of one lane (elements el .. el + 7 of tensor row `row`):
-// x' = x cos - p sin below n/2 and x cos + p sin above, p the partner i +- n/2, computed in
-// fp32 (products and sum rounded separately) and rounded back to the 16-bit format.
-template <int K, bool MF, int IN, class Ctx>
-RBQ_HD void apply_rope(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t el, u32x4& q4) {
-  constexpr int PB = rope_partner_lane_bit<K, MF>();
-  static_assert(PB >= 0, "RoPE needs the half-split partner in another lane");
+// the RoPE angles of elements el .. el + 7 (mod n/2) at token srow of a row: cos, and sin
+// negated below n/2 (x' = x cos - p sin there, x cos + p sin above)
+template <int K, class Ctx>
+RBQ_HD void rope_tables(Ctx& c, const TensorArgs& t, uint32_t srow, uint32_t el, float (&cs)[8], float (&sn)[8]) {
   constexpr uint32_t H = 1u << (K - 1);
-  uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
-  uint32_t p[4];
-  static_for<0, 4>([&](auto D) {
-    p[D.value] = f32_bits(c.shfl_xor(bits_f32(w[D.value]), 1 << PB));
-  });
-  const uint32_t srow = row - fastdiv(row, t.div_s) * t.seq;
   const float* cp = t.rope_cos + (int64_t)(t.rope_pos0 + srow) * H + (el & (H - 1));
   const float* sp = t.rope_sin + (int64_t)(t.rope_pos0 + srow) * H + (el & (H - 1));
   const f32x4 c0 = c.template load<f32x4>(cp), c1 = c.template load<f32x4>(cp + 4);
   const f32x4 s0 = c.template load<f32x4>(sp), s1 = c.template load<f32x4>(sp + 4);
-  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-  const bool upper = (el & H) != 0;
+  cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w; cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+  sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w; sn[4] = s1.x; sn[5] = s1.y; sn[6] = s1.z; sn[7] = s1.w;
+  const uint32_t neg = (el & H) ? 0u : 0x80000000u;
+  static_for<0, 8>([&](auto I) { sn[I.value] = bits_f32(f32_bits(sn[I.value]) ^ neg); });
+}
+
+// RoPE on the 8 16-bit values of one lane (8 consecutive elements of a row, angles cs and sn
+// from rope_tables): x' = x cos - p sin below n/2 and x cos + p sin above, p the partner
+// i +- n/2, computed in fp32 as a rounded product p sn and a fused multiply-add, and
+// rounded back to the 16-bit format.
+template <int K, bool MF, int IN, class Ctx>
+RBQ_HD void apply_rope(Ctx& c, const float (&cs)[8], const float (&sn)[8], u32x4& q4) {
+  constexpr int PB = rope_partner_lane_bit<K, MF>();
+  static_assert(PB >= 0, "RoPE needs the half-split partner in another lane");
+  uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
+  uint32_t p[4];
+  static_for<0, 4>([&](auto D) {
+    p[D.value] = f32_bits(c.template shfl_xor_c<1 << PB>(bits_f32(w[D.value])));
+  });
   static_for<0, 4>([&](auto D) {
     float r[2];
     static_for<0, 2>([&](auto HALF) {
@@ -342,9 +435,7 @@ RBQ_HD void apply_rope(Ctx& c, const TensorArgs& t, uint32_t row, uint32_t el, u
       const uint32_t pb = (p[D.value] >> (16 * HALF.value)) & 0xFFFFu;
       const float x = (IN == IN_F16) ? f16_to_f32(xb) : bits_f32(xb << 16);
       const float pv = (IN == IN_F16) ? f16_to_f32(pb) : bits_f32(pb << 16);
-      const float t1 = x * cs[j];
-      const float t2 = pv * sn[j];
-      r[HALF.value] = upper ? t1 + t2 : t1 - t2;
+      r[HALF.value] = fmaf(x, cs[j], pv * sn[j]);
     });
     w[D.value] = (IN == IN_F16) ? (f32_to_f16(r[0]) | (f32_to_f16(r[1]) << 16)) : f32x2_to_bf16x2(r[0], r[1]);
   });
@@ -356,6 +447,47 @@ RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0
                          uint32_t (&raw)[kMatrixLoads<K, MF>][4]) {
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
   const uint32_t last = (uint32_t)(rows - 1 - row0);  // last valid row of the block
+  if constexpr (ROPE) {
+    // A lane's loads are one column of several rows (its register index selects the row
+    // bits hs_jbits). In head-group order those rows are consecutive heads at one token:
+    // one fetch of the angles serves them all, and their addresses are one head stride
+    // apart. In the natural order each row has its own token and angles. Every load of the
+    // block is issued before RoPE uses any. (No RoPE entry point takes signs.)
+    constexpr int NJ = kMatrixLoads<K, MF>;
+    const uint32_t el = lp & ((1u << K) - 1u);  // the register index selects rows only
+    u32x4 q4[NJ];
+    float cs[8], sn[8];
+    if (t.hs) {
+      // every block is full in this order (the host checks that heads and tokens divide)
+      const Bhs x = hs_coords<K, MF>(t, (uint32_t)(row0 + (lp >> K)));
+      const int64_t head_step = FOURD ? t.sh : (int64_t)t.seq * t.row_stride;
+      const char* src = (const char*)t.x + (bhs_offset<FOURD>(t, x) + (int64_t)el) * 2;
+      static_for<0, NJ>([&](auto J) {
+        q4[J.value] = c.template load<u32x4>(src + (int64_t)J.value * head_step * 2);
+      });
+      rope_tables<K>(c, t, x.s, el, cs, sn);
+      static_for<0, NJ>([&](auto J) { apply_rope<K, MF, IN>(c, cs, sn, q4[J.value]); });
+    } else {
+      uint32_t srow[NJ];
+      static_for<0, NJ>([&](auto J) {
+        constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, (uint32_t)J.value << 3);
+        // rows past the end re-read the last row (their results are never stored)
+        const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : min_u32((lp | rp) >> K, last);
+        const uint32_t row = (uint32_t)(row0 + rw);
+        srow[J.value] = row - fastdiv(row, t.div_s) * t.seq;
+        q4[J.value] = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
+      });
+      static_for<0, NJ>([&](auto J) {
+        rope_tables<K>(c, t, srow[J.value], el, cs, sn);
+        apply_rope<K, MF, IN>(c, cs, sn, q4[J.value]);
+      });
+    }
+    static_for<0, NJ>([&](auto J) {
+      raw[J.value][0] = q4[J.value].x; raw[J.value][1] = q4[J.value].y;
+      raw[J.value][2] = q4[J.value].z; raw[J.value][3] = q4[J.value].w;
+    });
+    return;
+  }
   static_for<0, kMatrixLoads<K, MF>>([&](auto J) {
     constexpr uint32_t rp = reg_part(RBQ_PLAN, 0, (uint32_t)J.value << 3);
     const uint32_t idx = lp | rp;
@@ -368,7 +500,6 @@ RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0
       q4.x ^= s4.x & 0x80008000u; q4.y ^= s4.y & 0x80008000u;
       q4.z ^= s4.z & 0x80008000u; q4.w ^= s4.w & 0x80008000u;
     }
-    if constexpr (ROPE) apply_rope<K, MF, IN>(c, t, (uint32_t)(row0 + rw), el, q4);
     raw[J.value][0] = q4.x; raw[J.value][1] = q4.y; raw[J.value][2] = q4.z; raw[J.value][3] = q4.w;
   });
 }
@@ -468,7 +599,7 @@ RBQ_HD float round_quotient_exact(float u, float mk, float d) {
 
 // FAST: only packed codes and scales are written (no unpacked codes, no rotated rows), so
 // the kernel carries no registers for the other outputs
-template <int K, bool MF, int PH, bool ROT, int IN, bool FAST, bool CACHE, class Ctx>
+template <int K, bool MF, int PH, bool ROT, int IN, bool FAST, bool CACHE, bool RMAP, class Ctx>
 RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
                    Regs<K, MF>& v) {
   constexpr int E = 1 << RBQ_PLAN.e;
@@ -498,7 +629,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   static_for<0, 6>([&](auto B) {
     if constexpr ((LEM >> B.value) & 1u) {
       static_for<0, NC>([&](auto C) {
-        m[C.value] = fmaxf(m[C.value], c.shfl_xor(m[C.value], 1 << B.value));
+        m[C.value] = fmaxf(m[C.value], c.template shfl_xor_c<1 << B.value>(m[C.value]));
       });
     }
   });
@@ -519,6 +650,7 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
   const bool leader = ((c.lane & LEM) == 0) && ((c.wave & WEM) == 0);
   float mul[NC];
   float divv[NC];
+  int64_t orows[NC];  // output rows (CACHE or RMAP): tensor row, then cache row
   bool any_clamp = false;
   static_for<0, NC>([&](auto C) {
     const float mu = m[C.value];
@@ -533,11 +665,16 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
     divv[C.value] = s_st * SQRTN;
     // subnormal fp16 scales can sit far below max/qmax: then codes need the clamp
     any_clamp = any_clamp || ((mu * mk) > qmax + 0.25f);
+    if constexpr (CACHE || RMAP) {
+      constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
+      const uint32_t rw = ONE_ROW ? 0u : ((lp | rp) >> K);
+      orows[C.value] = out_row<CACHE>(t, tensor_row<K, MF, RMAP>(t, row0 + rw));
+    }
     if (FAST || (mode & MODE_QUANT)) {
       constexpr uint32_t rp = reg_part(RBQ_PLAN, PH, pdep_c((uint32_t)C.value, RRM));
       const uint32_t rw = ONE_ROW ? 0u : ((lp | rp) >> K);
       if (leader && (ONE_ROW || row0 + rw < t.rows)) {
-        const int64_t orow = out_row<CACHE>(t, row0 + rw);
+        const int64_t orow = (CACHE || RMAP) ? orows[C.value] : row0 + rw;
         if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + orow, (uint16_t)h16);
         else c.template store<float>((float*)t.scales + orow, s_st);
       }
@@ -582,7 +719,8 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       constexpr int RUN_BYTES = PACKED ? L / 2 : L;
       constexpr uint32_t ROWB = PACKED ? N / 2 : N;
       uint8_t* dst;
-      if constexpr (CACHE) dst = (uint8_t*)t.codes + out_row<CACHE>(t, row0 + rw) * (int64_t)ROWB + (PACKED ? el / 2 : el);
+      if constexpr (CACHE || RMAP)
+        dst = (uint8_t*)t.codes + orows[ci] * (int64_t)ROWB + (PACKED ? el / 2 : el);
       else dst = (uint8_t*)t.codes + row0 * (int64_t)ROWB + (rw * ROWB + (PACKED ? el / 2 : el));
       if constexpr (RUN_BYTES >= 16) {
         static_for<0, RUN_BYTES / 16>([&](auto Q) {
@@ -620,7 +758,9 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
       if (!ONE_ROW && row0 + rw >= t.rows) return;
-      float* dst = t.rot32 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
+      float* dst;
+      if constexpr (RMAP) dst = t.rot32 + tensor_row<K, MF, RMAP>(t, row0 + rw) * (int64_t)N + el;
+      else dst = t.rot32 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       if constexpr (L >= 4) {
         static_for<0, L / 4>([&](auto Q) {
           constexpr int o = 4 * Q.value;
@@ -639,7 +779,9 @@ RBQ_HD void finish(Ctx& c, const TensorArgs& t, const KArgs& a, int64_t row0,
       const uint32_t rw = ONE_ROW ? 0u : (idx >> K);
       const uint32_t el = idx & (uint32_t)(N - 1);
       if (!ONE_ROW && row0 + rw >= t.rows) return;
-      uint16_t* dst = t.rot16 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
+      uint16_t* dst;
+      if constexpr (RMAP) dst = t.rot16 + tensor_row<K, MF, RMAP>(t, row0 + rw) * (int64_t)N + el;
+      else dst = t.rot16 + row0 * (int64_t)N + (rw * (uint32_t)N + el);
       constexpr int NW = (L >= 2) ? L / 2 : 1;
       uint32_t out[NW];
       static_for<0, NW>([&](auto D) {
@@ -673,7 +815,7 @@ RBQ_HD Block block_of(const KArgs& a, uint32_t blk) {
 }
 
 // the transform after phase 0, the reduction, the scale and the stores of one block
-template <int K, bool MF, int IN, bool ROT, bool FAST, bool CACHE, class Ctx>
+template <int K, bool MF, int IN, bool ROT, bool FAST, bool CACHE, bool RMAP, class Ctx>
 RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v) {
   if constexpr (ROT) {
     if constexpr (RBQ_PLAN.nph >= 2) {
@@ -684,9 +826,9 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
       transpose<K, MF, 1>(c, v);
       stages<K, MF, 2, false>(v);
     }
-    finish<K, MF, RBQ_PLAN.nph - 1, true, IN, FAST, CACHE>(c, *b.t, a, b.row0, v);
+    finish<K, MF, RBQ_PLAN.nph - 1, true, IN, FAST, CACHE, RMAP>(c, *b.t, a, b.row0, v);
   } else {
-    finish<K, MF, 0, false, IN, FAST, CACHE>(c, *b.t, a, b.row0, v);
+    finish<K, MF, 0, false, IN, FAST, CACHE, RMAP>(c, *b.t, a, b.row0, v);
   }
 }
 
@@ -694,7 +836,8 @@ RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v
 #define RBQ_PREFETCH 0
 #endif
 
-// Workgroup `first` processes blocks first, first + step, ... < a.nblocks. With
+// Workgroup `first` processes blocks first, first + step, ... < a.nblocks (with ROPE in
+// head-group order when t.hs is set, see hs_coords). With
 // RBQ_PREFETCH and matrix plans the next block's loads are issued as soon as the MFMAs
 // have consumed the current block's, so they are in flight while the current block is
 // transformed.
@@ -711,7 +854,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       Regs<K, MF> v;
       matrix_apply<K, MF, IN>(c, raw, v);
       stages<K, MF, 0, false>(v);
-      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
     }
   } else if constexpr (MF) {
     uint32_t raw[kMatrixLoads<K, MF>][4];
@@ -730,7 +873,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
         matrix_issue<K, MF, FOURD, IN, ROPE>(c, *bn.t, bn.t->rows, bn.row0, raw);
       }
       stages<K, MF, 0, false>(v);
-      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
     }
   } else {
     for (uint32_t blk = first; blk < nb; blk += step) {
@@ -739,7 +882,7 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       Regs<K, MF> v;
       load_phase0<K, MF, IN, ROT, FOURD, ROPE>(c, *b.t, b.t->rows, b.row0, v);
       if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
-      rest_of_block<K, MF, IN, ROT, FAST, CACHE>(c, a, b, v);
+      rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
     }
   }
 }

@@ -154,6 +154,7 @@ static rbq_status kv_launch(const void* q, const void* k, rbq_dtype dtype, int64
     t.rope_sin = rope_sin;
     t.rope_pos0 = (uint32_t)rope_pos0;
     t.rows = rows;
+    if (rope_cos) set_rope_order_rt(t, chk.k);
   }
   a.t[0].codes = q_codes;
   a.t[0].scales = q_scales;
@@ -264,6 +265,7 @@ extern "C" rbq_status kv_cache_append_int4(const void* q, const void* k, const v
     t->rope_cos = rope_cos;
     t->rope_sin = rope_sin;
     t->rope_pos0 = (uint32_t)pos0;
+    if (rope_cos) set_rope_order_rt(*t, chk.k);
   }
   a.blocks0 = (uint32_t)bq;
   a.nblocks = (uint32_t)(bq + bk);

@@ -164,6 +164,10 @@ int main(int argc, char **argv) {
     EXPECT(attention_decode_int4kv_split(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 2, 8, 2, 16, 16, 128, 0.1f, 4, PS,
                                          2 * 8 * 4 * 130 * 4, PX, NULL),
            launched);
+    /* RoPE into the cache without a query: the unused query tensor stays empty */
+    EXPECT(kv_cache_append_int4(NULL, PX, PX, RBQ_BF16, B, H, H / 2, S, D, st, st, st, (const float *)PS,
+                                (const float *)PS, 2 * S, 3, S + 3, NULL, PC, PS, PC, PS, RBQ_F16, NULL),
+           launched);
     EXPECT(attention_decode_int4kv_split_noalloc(PX, RBQ_BF16, PC, PS, PC, PS, RBQ_F16, 64, 64, 64, 16, 16, 128,
                                                  0.1f, 3, PX, NULL),
            launched);

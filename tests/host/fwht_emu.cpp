@@ -158,6 +158,7 @@ int main(int argc, char** argv) {
     t.seq = (uint32_t)S; t.heads = (uint32_t)H;
     t.div_s = make_fastdiv((uint32_t)S); t.div_h = make_fastdiv((uint32_t)H);
     (void)B;
+    if (t.rope_cos) set_rope_order_rt(t, K);  // as the library does for RoPE launches
   }
   if (cache_cap) {
     t.out_cap = (uint32_t)cache_cap;

@@ -62,6 +62,7 @@ struct HostCtx {
     s->wave_bar[wave]->arrive_and_wait();
     return r;
   }
+  template <int M> float shfl_xor_c(float v) { return shfl_xor(v, M); }
   template <class T> T load(const void* p) {
     check_ptr(p, sizeof(T), "load");
     if ((uintptr_t)p % alignof(T)) { fprintf(stderr, "MISALIGNED load\n"); std::abort(); }

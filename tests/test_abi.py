@@ -238,7 +238,7 @@ def test_dispatch_log(abi_client):
     p = _run_client(abi_client, "inject", RBQ_FAULT_INJECT="launch", RBQ_LOG="1")
     assert p.returncode == 0, p.stdout + p.stderr
     lines = [l for l in p.stderr.splitlines() if l.startswith("rbq: ")]
-    assert len(lines) == 16, p.stderr  # one line per valid call, none for rejected ones
+    assert len(lines) == 17, p.stderr  # one line per valid call, none for rejected ones
     assert lines[0].startswith("rbq: hadamard_quant n=4096 tokens=8 dtype=1 rotate=1 signs=0 int8=0 packed=1")
     assert "signs=1" in lines[1] and "int8=1 packed=0" in lines[2]
     assert "rope=0" in lines[3] and "rope=1" in lines[4]
@@ -252,7 +252,8 @@ def test_dispatch_log(abi_client):
     assert lines[12].startswith("rbq: hbm_probe read=65536 write=16384 blocks=8")
     assert lines[13].startswith("rbq: kv_cache_append B=2 H=4 Hkv=2 S=16 D=128 pos0=3 cap=19 rope=1 q=1")
     assert lines[14].startswith("rbq: attention_decode_int4kv_split B=2 H=8 Hkv=2 S=16 cap=16 splits=4")
-    assert lines[15].startswith("rbq: attention_decode_int4kv_split_noalloc B=64 H=64 Hkv=64 S=16 cap=16 splits=3")
+    assert lines[15].startswith("rbq: kv_cache_append B=2 H=4 Hkv=2 S=16 D=128 pos0=3 cap=19 rope=1 q=0")
+    assert lines[16].startswith("rbq: attention_decode_int4kv_split_noalloc B=64 H=64 Hkv=64 S=16 cap=16 splits=3")
 
 
 def test_kron_validation_and_factor(L):

@@ -92,12 +92,15 @@ def assert_untouched(t, pos0, S, sentinel):
     assert np.all(a[:, :, outside] == sentinel)
 
 
+@pytest.mark.parametrize("shape", [(2, 6, 3, 37, 96, 29), (2, 8, 4, 32, 80, 16)])
 @pytest.mark.parametrize("rope", [True, False])
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_append_into_cache(rbq, D, dtype, rope):
-    B, H, Hkv, S, cap, pos0 = 2, 6, 3, 37, 96, 29
-    print(f"case kv_cache_append D={D} {dtype} rope={rope}", flush=True)
+def test_append_into_cache(rbq, D, dtype, rope, shape):
+    """shape = (B, H, Hkv, S, cap, pos0); the second takes the RoPE kernels' head-group
+    order for Q (and for K at head_dim 128)."""
+    B, H, Hkv, S, cap, pos0 = shape
+    print(f"case kv_cache_append D={D} {dtype} rope={rope} shape={shape}", flush=True)
     q_bits, _ = gen(D + 1, B, H, S, D, dtype)
     k_bits, v_bits = gen(D + 2, B, Hkv, S, D, dtype)
     q, k, v = bhsd_view(q_bits, dtype), bhsd_view(k_bits, dtype), bhsd_view(v_bits, dtype)

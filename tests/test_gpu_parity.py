@@ -342,7 +342,9 @@ def rope_tables(positions, d, base=10000.0):
     ("float16", "contiguous", 100, (2, 3, 45)), ("float16", "bshd_view", 0, (2, 3, 45)),
     # shapes whose rows fill whole 64-row blocks, several blocks per workgroup loop
     ("bfloat16", "contiguous", 3, (2, 6, 80)), ("bfloat16", "bshd_view", 0, (4, 5, 48)),
-    ("float16", "contiguous", 0, (1, 4, 16)), ("float16", "bshd_view", 9, (8, 2, 272))])
+    ("float16", "contiguous", 0, (1, 4, 16)), ("float16", "bshd_view", 9, (8, 2, 272)),
+    # head-group order (heads a multiple of 4, tokens of 16; for head_dim 256 of 8 and 8)
+    ("bfloat16", "contiguous", 5, (2, 8, 48)), ("float16", "bshd_view", 0, (3, 16, 32))])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_kv_rope_small(rbq, dtype, layout, pos0, bhs, D):
     """kv_rope_rotate_quant: RoPE (half-split; the oracle evaluates it exactly and rounds it
@@ -373,10 +375,11 @@ def test_kv_rope_small(rbq, dtype, layout, pos0, bhs, D):
         print(f"  {name}: {st}", flush=True)
 
 
-@pytest.mark.parametrize("bhs", [(1, 3, 37), (2, 2, 64)])
+@pytest.mark.parametrize("bhs", [(1, 3, 37), (2, 2, 64), (2, 8, 32)])
 def test_kv_rope_q_rotate_only(rbq, bhs):
     """RoPE + R3 with Q written rotated in bf16 (no codes): each rotated row lands at its
-    own (batch, head, token) place, with a ragged last block and with whole blocks."""
+    own (batch, head, token) place, with a ragged last block, with whole blocks, and with
+    blocks in head-group order."""
     B, H, S = bhs
     D = 128
     print(f"case kv rope q_rotate_only B,H,S={bhs}", flush=True)
