@@ -487,12 +487,20 @@ def main():
             "frac": headline["frac_hbm_peak"],
             "traffic": load_traffic("hadamard_quant_int4", fwht_hash),
         }
+        c = load_counters("hadamard_quant_int4", fwht_hash)
+        if c and "valu" in c:
+            # from the committed rocprofv3 pass: VALU instructions per element, and VALU
+            # issue cycles (4 per wave instruction) over the GPU's active cycles
+            roofline["valu_counters"] = c["valu"]
     extra_roofline = {}
     if "kv_rotate_quant" in kernels:
         k = kernels["kv_rotate_quant"]
         extra_roofline["kv_rotate_quant"] = {
             "bound": "hbm", "achieved": k["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": k["frac_hbm_peak"], "traffic": load_traffic("kv_rotate_quant", fwht_hash)}
+        c = load_counters("kv_rotate_quant", fwht_hash)
+        if c and "valu" in c:
+            extra_roofline["kv_rotate_quant"]["valu_counters"] = c["valu"]
     if "w4a4_gemm" in kernels:
         k = kernels["w4a4_gemm"]
         entry = {"bound": "mfma", "achieved": k["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
@@ -700,7 +708,8 @@ def main():
         extras["kron_r4_11008"] = {
             "workload": "bf16 [8192, 11008] = (H_172 (x) H_64) / sqrt(n), Goethals-Seidel H_172, packed INT4 + fp16 scales",
             "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2),
-            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("hadamard_kron_quant_int4_11008", kernel_source_hash(KRON_SOURCES))}
         del kx, kc, ks, k0
 
     cpu = None
