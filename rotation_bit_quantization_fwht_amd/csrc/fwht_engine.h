@@ -2,8 +2,9 @@
 //
 // One workgroup owns 2^r rows of length n = 2^k (see plan.h for the data layouts):
 //   load (global -> registers) and the first transform factor: for 16-bit inputs with
-//   k >= 7 a pair of 16x16x32 MFMAs multiplies every 32-element group by H_32 (exact:
-//   16-bit inputs, +-1 weights, fp32 accumulation); otherwise widen to fp32, fusing the
+//   k >= 7 a pair of 16x16x32 MFMAs multiplies every 32-element group by H_32 (the 32
+//   products of 16-bit inputs and +-1 weights are exact; their fp32 sum is rounded like any
+//   butterfly sum); otherwise widen to fp32, fusing the
 //   first butterfly into the widening of 16-bit pairs with a 2-term dot product
 //   -> register butterflies -> LDS transpose -> register butterflies [-> transpose ->
 //   butterflies] -> per-row absmax (registers, lane shuffles, LDS across waves)

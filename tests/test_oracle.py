@@ -624,14 +624,23 @@ def test_rope_16bit_rounds_the_exact_map_once():
     assert val[0, 0] == 1.0 + 2.0 ** -7 and not amb[0, 0]
 
 
-def _f32_eval_rope(x, c, s, fmt):
-    """The map evaluated in IEEE float32 (NumPy), each product and the sum rounded, then
-    rounded to the format (an implementation's arithmetic, used only to test the bound)."""
+def _f32_eval_rope(x, c, s, fmt, fused=False):
+    """The map evaluated in IEEE float32 (NumPy), then rounded to the format (an
+    implementation's arithmetic, used only to test the bound): each product and the sum
+    rounded, or (fused) one product rounded and added to the other, exact, product with one
+    rounding, as a fused multiply-add does. The 16-bit input times a float32 value is exact
+    in float64; the float64 sum before the rounding to float32 can add a double-rounding step
+    in rare cases, still inside the bound."""
     x = np.asarray(x, dtype=np.float32)
     d = x.shape[-1]
     a, b = x[..., : d // 2], x[..., d // 2:]
-    lo = (a * c).astype(np.float32) - (b * s).astype(np.float32)
-    hi = (b * c).astype(np.float32) + (a * s).astype(np.float32)
+    if fused:
+        f64 = lambda v: np.asarray(v, dtype=np.float64)
+        lo = (f64(a) * f64(c) + f64((b * -s).astype(np.float32))).astype(np.float32)
+        hi = (f64(b) * f64(c) + f64((a * s).astype(np.float32))).astype(np.float32)
+    else:
+        lo = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+        hi = (b * c).astype(np.float32) + (a * s).astype(np.float32)
     r = np.concatenate([lo, hi], axis=-1).astype(np.float32)
     if fmt == "float16":
         return r.astype(np.float16).astype(np.float64)
@@ -640,17 +649,19 @@ def _f32_eval_rope(x, c, s, fmt):
     return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("fmt", ["bfloat16", "float16"])
-def test_rope_ambiguity_covers_every_float32_evaluation(fmt):
-    """Where an element is not flagged, a float32 evaluation gives exactly the oracle's
-    value; where it is flagged, it gives the value or the flagged neighbour."""
+def test_rope_ambiguity_covers_every_float32_evaluation(fmt, fused):
+    """Where an element is not flagged, a float32 evaluation (products and sum rounded, or a
+    fused multiply-add) gives exactly the oracle's value; where it is flagged, it gives the
+    value or the flagged neighbour."""
     d = 128
     bits = workloads.gen_rows(5, 2048, d, fmt, n_outliers=2, factor=50)
     x = workloads.to_float64(bits, fmt)
     th = _angles(np.arange(2048), d)
     c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
     val, other, amb = oracle.rope_16bit_ambiguous(x, c, s, fmt)
-    f32 = _f32_eval_rope(x, c, s, fmt)
+    f32 = _f32_eval_rope(x, c, s, fmt, fused)
     assert np.array_equal(f32[~amb], val[~amb])
     assert np.all((f32[amb] == val[amb]) | (f32[amb] == other[amb]))
     assert 0 < np.mean(amb) < 5e-3  # rare, and the float32 result does differ somewhere
@@ -765,6 +776,16 @@ def test_goethals_seidel_order_172_is_hadamard():
     bad = np.block([[a, b @ r, c @ r, d @ r], [-b @ r, a, d @ r, -c.T @ r],
                     [-c @ r, -d.T @ r, a, b.T @ r], [-d @ r, c.T @ r, -b.T @ r, a]])
     assert not np.array_equal(bad @ bad.T, 172 * np.eye(172))
+
+
+def test_goethals_seidel_rows_are_constant_on_cosets():
+    """Each first row takes one sign on every coset of the order-7 subgroup of (Z/43)^*."""
+    sub = {1, 4, 11, 16, 21, 35, 41}
+    cosets = {frozenset((t * h) % 43 for h in sub) for t in range(1, 43)}
+    assert len(cosets) == 6
+    for row in oracle.gs_first_rows():
+        for cs in cosets:
+            assert len({int(row[t]) for t in cs}) == 1
 
 
 def test_periodic_autocorrelation_brute_force():
