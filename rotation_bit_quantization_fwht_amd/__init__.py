@@ -184,12 +184,18 @@ def _torch():
     return torch
 
 
+_DTYPE_CODES = None
+
+
 def _dtype_code(t):
-    torch = _torch()
-    m = {torch.float32: RBQ_F32, torch.bfloat16: RBQ_BF16, torch.float16: RBQ_F16}
-    if t not in m:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        torch = _torch()
+        _DTYPE_CODES = {torch.float32: RBQ_F32, torch.bfloat16: RBQ_BF16, torch.float16: RBQ_F16}
+    code = _DTYPE_CODES.get(t)
+    if code is None:
         raise TypeError(f"unsupported dtype {t}")
-    return m[t]
+    return code
 
 
 def _ptr(t):
@@ -197,8 +203,14 @@ def _ptr(t):
 
 
 def _stream(stream, device):
+    """The HIP stream to launch on: ``stream`` if given, else torch's current stream on
+    ``device``. The current stream's handle is read with torch's raw query where it has one
+    (a few hundredths of a microsecond, against about 2 us for building a Stream object)."""
     torch = _torch()
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(device.index if device.index is not None else torch.cuda.current_device()))
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
