@@ -644,6 +644,24 @@ def main():
             "frac_hbm_peak": round(nbytes / ts / 1e9 / HBM_PEAK_GBS, 4),
             "avg_us_by_splits": {str(k): round(v * 1e6, 3) for k, v in split_rates.items()}}
         del vcodes, vscales, aout, ws
+        # grouped key/value heads (32 query heads over 8 key/value heads, LLaMA-3 8B's
+        # decode shape): each key/value head's cache is read by 4 query heads' workgroups
+        GB_, GH, GHkv, GS = 16, 32, 8, 2048
+        gk = torch.from_numpy(workloads.gen_packed_codes(37, GB_ * GHkv * GS, D)).to(dev).reshape(GB_, GHkv, GS, D // 2)
+        gv = torch.from_numpy(workloads.gen_packed_codes(38, GB_ * GHkv * GS, D)).to(dev).reshape(GB_, GHkv, GS, D // 2)
+        gks = torch.from_numpy(workloads.gen_scales(39, GB_ * GHkv * GS, "float16")).to(dev).reshape(GB_, GHkv, GS)
+        gvs = torch.from_numpy(workloads.gen_scales(40, GB_ * GHkv * GS, "float16")).to(dev).reshape(GB_, GHkv, GS)
+        gq = qdec[:GB_, :GH].contiguous()
+        gout = torch.empty_like(gq)
+        gbytes = 2 * GB_ * GHkv * GS * (D // 2 + 2) + 2 * GB_ * GH * D * 2
+        fn = lambda: rbq.attention_decode_int4kv(gq, gk, gks, gv, gvs, 1.0 / math.sqrt(D), out=gout)  # noqa
+        fn()
+        tg = time_back_to_back(torch, [fn], 20) * 1e-6
+        extras["attention_decode_gqa"] = {
+            "workload": "one query per head, 32 query heads over INT4 K and V caches [16, 8, 2048, 128], fp16 scales",
+            "avg_us": round(tg * 1e6, 3), "unique_bytes": gbytes, "GB_s": round(gbytes / tg / 1e9, 2),
+            "frac_hbm_peak": round(gbytes / tg / 1e9 / HBM_PEAK_GBS, 4)}
+        del gk, gv, gks, gvs, gq, gout
         # long-context decode: one sequence of 32768 tokens, 32 heads (the same cache bytes
         # in 32 (batch, head) pairs): unsplit, 32 workgroups for 256 CUs
         LB, LH, LS = 1, 32, 32768

@@ -285,7 +285,7 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
  * Errors: RBQ_EINVAL for NULL or misaligned pointers, bad dtypes, seq < 1, seq_cap < seq,
  * heads not a multiple of kv_heads or a NaN scale; RBQ_ENOTSUP for head_dim != 128,
  * seq >= 2^26 (one head's codes are addressed with 32-bit byte offsets), seq_cap > 2^30
- * or batch * heads > 2^31 - 1.
+ * or (batch + 8) * heads > 2^31 - 1 (the grid is padded to whole groups of 8 key/value heads).
  */
 rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
                                    const void *k_scales, const uint8_t *v_codes,
@@ -312,7 +312,7 @@ rbq_status attention_decode_int4kv(const void *q, rbq_dtype q_dtype, const uint8
  *                   kernels have finished on `stream`.
  *  workspace_bytes  at least rbq_attention_split_workspace_bytes(batch, heads, splits).
  * Errors: as attention_decode_int4kv, plus RBQ_EINVAL for splits outside 1 .. 4096 or a
- * NULL, misaligned or short workspace; RBQ_ENOTSUP when batch * heads * splits > 2^31 - 1.
+ * NULL, misaligned or short workspace; RBQ_ENOTSUP when batch * heads * splits + 8 * heads > 2^31 - 1.
  */
 rbq_status attention_decode_int4kv_split(const void *q, rbq_dtype q_dtype, const uint8_t *k_codes,
                                          const void *k_scales, const uint8_t *v_codes,

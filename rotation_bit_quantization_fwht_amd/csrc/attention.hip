@@ -38,6 +38,7 @@ struct AttnArgs {
   const void* vs;
   void* out;            // [B, H, 128], the query's format
   int H, Hkv, S, S_cap;
+  int units;            // (batch, key/value head, split) triples: batch * Hkv * splits
   float scale;
   int q_f16, scale_f16;
 };
@@ -112,15 +113,41 @@ __device__ __forceinline__ float attn_quad_sum(float v) {
   return v;
 }
 
+// Workgroups are handed to the XCDs in turn (id mod 8), each XCD with its own L2. Unit u
+// and query head g of its group of G map to workgroup (u / 8) * 8 G + 8 g + u mod 8, so the
+// G workgroups that read one key/value head's cache share an XCD and are dispatched one
+// after another: the later ones find the cache lines in that XCD's L2. The grid holds
+// ceil(units / 8) * 8 G workgroups; those past the last unit return at once.
+// (Decode over a [16, 8, 2048, 128] cache with 32 query heads: 29.0-29.3 us, against
+// 30.4 us with the group's workgroups consecutive in id and so spread over all XCDs.)
+constexpr int kAttnXcds = 8;
+
+__host__ __device__ inline void attn_unit_of(int x, int G, int& u, int& g) {
+  const int t = x / kAttnXcds;
+  g = t % G;
+  u = (t / G) * kAttnXcds + x % kAttnXcds;
+}
+
+inline uint32_t attn_grid(int64_t units, int64_t G) {
+  return (uint32_t)((units + kAttnXcds - 1) / kAttnXcds * kAttnXcds * G);
+}
+
 template <int SF16, bool SPLIT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void attention_decode_kernel(AttnArgs a) {
   __shared__ float part[kAttnGroups][kAttnD];
   __shared__ float gmax[kAttnGroups], gsum[kAttnGroups], gw[kAttnGroups], gm;
-  const int bh = SPLIT ? (int)blockIdx.x / a.splits : (int)blockIdx.x;
-  const int sp = SPLIT ? (int)blockIdx.x - bh * a.splits : 0;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int kvh = h / (a.H / a.Hkv);
+  // workgroup -> (unit u = (batch, key/value head, split), query head g of the group):
+  // attn_unit_of keeps the G query heads of one key/value head on one XCD
+  const int G = a.H / a.Hkv;
+  int u, g;
+  attn_unit_of((int)blockIdx.x, G, u, g);
+  if (u >= a.units) return;  // the grid is padded to whole groups of eight units
+  const int sp = SPLIT ? u % a.splits : 0;
+  const int r = SPLIT ? u / a.splits : u;
+  const int b = r / a.Hkv, kvh = r - b * a.Hkv;
+  const int h = kvh * G + g;
+  const int bh = b * a.H + h;
   const int tid = threadIdx.x, c = tid & 3, tg = tid >> 2;
 
   // the lane's 32 query dims times the softmax scale, over 16 (exact) for the codes' 16
@@ -286,7 +313,8 @@ static rbq_status attn_check(const void* q, rbq_dtype q_dtype, const uint8_t* k_
   const uint64_t ssz = (uint64_t)dtype_size(scale_dtype);
   if (!aligned(k_scales, ssz) || !aligned(v_scales, ssz)) return RBQ_EINVAL;
   // buffer offsets within one head's cache are 32-bit: seq * 64 bytes must fit
-  if (batch * heads > 0x7FFFFFFF || heads > 0x7FFFFFFF || seq_cap > (int64_t{1} << 30) || seq >= (int64_t{1} << 26))
+  // (the grid is padded by up to 8 heads' worth of workgroups)
+  if (batch * heads + 8 * heads > 0x7FFFFFFF || seq_cap > (int64_t{1} << 30) || seq >= (int64_t{1} << 26))
     return RBQ_ENOTSUP;
   return RBQ_OK;
 }
@@ -340,7 +368,8 @@ static rbq_status attn_split_launch(AttnArgs a, int64_t batch, int64_t heads, in
   a.splits = (int)splits;
   a.chunk = (int)((a.S + splits - 1) / splits);
   a.part = part;
-  const uint32_t grid = (uint32_t)(batch * heads * splits);
+  a.units = (int)(batch * a.Hkv * splits);
+  const uint32_t grid = attn_grid(a.units, a.H / a.Hkv);
   if (a.scale_f16)
     hipLaunchKernelGGL((attention_decode_kernel<1, true>), dim3(grid), dim3(kAttnThreads), 0, stream, a);
   else
@@ -369,11 +398,13 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
     fprintf(stderr, "rbq: attention_decode_int4kv B=%lld H=%lld Hkv=%lld S=%lld cap=%lld\n", (long long)batch,
             (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap);
   if (diag_fail_launch()) return RBQ_EHIP;
-  const dim3 grid((uint32_t)(batch * heads));
+  AttnArgs au = a;
+  au.units = (int)(batch * kv_heads);
+  const dim3 grid(attn_grid(au.units, heads / kv_heads));
   if (a.scale_f16)
-    hipLaunchKernelGGL((attention_decode_kernel<1, false>), grid, dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<1, false>), grid, dim3(kAttnThreads), 0, stream, au);
   else
-    hipLaunchKernelGGL((attention_decode_kernel<0, false>), grid, dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL((attention_decode_kernel<0, false>), grid, dim3(kAttnThreads), 0, stream, au);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
 
@@ -396,7 +427,7 @@ extern "C" rbq_status attention_decode_int4kv_split(const void* q, rbq_dtype q_d
   const rbq_status st = attn_check(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, batch, heads,
                                    kv_heads, seq, seq_cap, head_dim, softmax_scale, out);
   if (st != RBQ_OK || batch == 0 || heads == 0) return st;
-  if (batch * heads * splits > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (batch * heads * splits + 8 * heads > 0x7FFFFFFF) return RBQ_ENOTSUP;
   if (!workspace || !aligned(workspace, 16) || workspace_bytes < attn_split_bytes(batch, heads, splits))
     return RBQ_EINVAL;
   const AttnArgs a = attn_args(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, heads, kv_heads, seq,
@@ -420,7 +451,7 @@ extern "C" rbq_status attention_decode_int4kv_split_noalloc(const void* q, rbq_d
   const rbq_status st = attn_check(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, batch, heads,
                                    kv_heads, seq, seq_cap, head_dim, softmax_scale, out);
   if (st != RBQ_OK || batch == 0 || heads == 0) return st;
-  if (batch * heads * splits > 0x7FFFFFFF) return RBQ_ENOTSUP;
+  if (batch * heads * splits + 8 * heads > 0x7FFFFFFF) return RBQ_ENOTSUP;
   if (attn_split_bytes(batch, heads, splits) > kAttnScratchBytes) return RBQ_ENOTSUP;  // beyond the fixed array
   const AttnArgs a = attn_args(q, q_dtype, k_codes, k_scales, v_codes, v_scales, scale_dtype, heads, kv_heads, seq,
                                seq_cap, softmax_scale, out);
