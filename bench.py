@@ -662,6 +662,33 @@ def main():
             "avg_us": round(tg * 1e6, 3), "unique_bytes": gbytes, "GB_s": round(gbytes / tg / 1e9, 2),
             "frac_hbm_peak": round(gbytes / tg / 1e9 / HBM_PEAK_GBS, 4)}
         del gk, gv, gks, gvs, gq, gout
+        # a decode step's cache write: one token per sequence, RoPE -> R3 -> INT4 keys and
+        # INT4 values appended at position 2047 of a 4096-row cache (LLaMA-3 8B heads), the
+        # query returned RoPE'd and rotated
+        DB, DH, DHkv, DCAP, DPOS = 16, 32, 8, 4096, 2047
+        dk = torch.randn((DB, DHkv, 1, D), device=dev).to(torch.bfloat16)
+        dv = torch.randn((DB, DHkv, 1, D), device=dev).to(torch.bfloat16)
+        dq = torch.randn((DB, DH, 1, D), device=dev).to(torch.bfloat16)
+        dkc = torch.zeros((DB, DHkv, DCAP, D // 2), dtype=torch.uint8, device=dev)
+        dvc = torch.zeros_like(dkc)
+        dks = torch.zeros((DB, DHkv, DCAP), dtype=torch.float16, device=dev)
+        dvs = torch.zeros_like(dks)
+        dqr = torch.empty_like(dq)
+        tth = torch.outer(torch.arange(DCAP, dtype=torch.float64, device=dev), inv)
+        tcos, tsin = torch.cos(tth).float(), torch.sin(tth).float()
+        fn = lambda: rbq.kv_cache_append_int4(dk, dv, dkc, dks, dvc, dvs, DPOS, q=dq, q_rotated=dqr,  # noqa
+                                              rope_cos=tcos, rope_sin=tsin)
+        fn()
+        dev_us, host_us = time_calls(torch, fn, 200)
+        ref_kc, ref_q = dkc.clone(), dqr.clone()
+        g_us = time_graph(torch, fn)
+        extras["kv_cache_append_decode"] = {
+            "workload": "decode step: Q [16, 32, 1, 128], K and V [16, 8, 1, 128] bf16 -> RoPE, R3, INT4 into a "
+                        "[16, 8, 4096, 64] cache at position 2047",
+            "device_us": round(dev_us, 3), "host_us": round(host_us, 3), "graph_us": round(g_us, 3),
+            "graph_matches_eager": bool(torch.equal(dkc, ref_kc) and torch.equal(dqr, ref_q))}
+        del ref_kc, ref_q
+        del dk, dv, dq, dkc, dvc, dks, dvs, dqr, tth, tcos, tsin
         # long-context decode: one sequence of 32768 tokens, 32 heads (the same cache bytes
         # in 32 (batch, head) pairs): unsplit, 32 workgroups for 256 CUs
         LB, LH, LS = 1, 32, 32768

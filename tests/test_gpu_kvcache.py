@@ -188,3 +188,28 @@ def test_prefill_then_decode_chain_to_attention(rbq):
     vcode = oracle.unpack_nibbles(vc.cpu().numpy()[:, :, :n].reshape(-1, D // 2)).reshape(B, Hkv, n, D)
     check_attention(out, got_q.reshape(B, H, D), kcode, ks.cpu().numpy()[:, :, :n], vcode, vs.cpu().numpy()[:, :, :n],
                     1.0 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("S,pos0", [(16, 48), (1, 63)])
+def test_append_fills_the_cache_to_its_last_row(rbq, S, pos0):
+    """pos0 + seq == seq_cap: the last rows of every head's cache (a prefill that fills it,
+    and a one-token decode at the final position, with RoPE), rows before pos0 untouched."""
+    B, H, Hkv, D, cap = 2, 8, 4, 128, 64
+    print(f"case kv_cache_append to the last row S={S} pos0={pos0}", flush=True)
+    q_bits, _ = gen(300 + S, B, H, S, D, "bfloat16")
+    k_bits, v_bits = gen(301 + S, B, Hkv, S, D, "bfloat16")
+    cos, sin = rope_tables(cap, D)
+    kc, ks, vc, vs = empty_cache(B, Hkv, cap, D)
+    qr = rbq.kv_cache_append_int4(bhsd_view(k_bits, "bfloat16"), bhsd_view(v_bits, "bfloat16"), kc, ks, vc, vs,
+                                  pos0, q=bhsd_view(q_bits, "bfloat16"), rope_cos=torch.from_numpy(cos).cuda(),
+                                  rope_sin=torch.from_numpy(sin).cuda())
+    torch.cuda.synchronize()
+    for t in (kc, vc):
+        assert_untouched(t, pos0, S, SENTINEL)
+    check_rows((kc, ks), k_bits, "bfloat16", pos0, (cos, sin), True)
+    check_rows((vc, vs), v_bits, "bfloat16", pos0, None, False)
+    got = qr.float().cpu().numpy().astype(np.float64).reshape(B * H * S, D)
+    pos = pos0 + np.arange(S)
+    cr = np.broadcast_to(cos[pos][None, None], (B, H, S, D // 2)).reshape(-1, D // 2)
+    sr = np.broadcast_to(sin[pos][None, None], (B, H, S, D // 2)).reshape(-1, D // 2)
+    check_rope_rotated(got, workloads.to_float64(q_bits, "bfloat16").reshape(B * H * S, D), cr, sr, "bfloat16")
