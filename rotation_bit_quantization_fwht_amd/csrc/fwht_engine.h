@@ -313,7 +313,8 @@ RBQ_HD const char* in_addr(const TensorArgs& t, int64_t row0, uint32_t rw, uint3
   }
 }
 
-template <int K, bool MF, int IN, bool ROT, bool FOURD, bool ROPE, class Ctx>
+// SIGNS: t.signs is set (see matrix_issue)
+template <int K, bool MF, int IN, bool ROT, bool FOURD, bool ROPE, bool SIGNS, class Ctx>
 RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                         Regs<K, MF>& v) {
   constexpr int C0 = run_log(RBQ_PLAN, 0);
@@ -347,7 +348,7 @@ RBQ_HD void load_phase0(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
         w[0] = c.template load<uint32_t>(src);
       }
     }
-    if (t.signs) {
+    if constexpr (SIGNS) {
       // multiply by the +-1 diagonal: flip each value's sign bit where the sign is negative
       constexpr uint32_t SIGN = (IN == IN_F32) ? 0x80000000u : 0x80008000u;
       const char* sp = (const char*)t.signs + el * (uint32_t)ESZ;
@@ -443,7 +444,11 @@ RBQ_HD void apply_rope(Ctx& c, const float (&cs)[8], const float (&sn)[8], u32x4
   q4 = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int K, bool MF, bool FOURD, int IN, bool ROPE, class Ctx>
+// SIGNS: t.signs is set (the randomized transform; only 2-D rows without RoPE take it). It
+// is a template parameter so that the sign loads of a block are issued with its other
+// loads, with no branch between them: with a runtime branch per load, each flip waits for
+// its loads before the next load is issued.
+template <int K, bool MF, bool FOURD, int IN, bool ROPE, bool SIGNS, class Ctx>
 RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0,
                          uint32_t (&raw)[kMatrixLoads<K, MF>][4]) {
   const uint32_t lp = lane_part<K, MF, 0>(c.lane, c.wave);
@@ -495,9 +500,13 @@ RBQ_HD void matrix_issue(Ctx& c, const TensorArgs& t, int64_t rows, int64_t row0
     // rows past the end re-read the last row (their results are never stored)
     const uint32_t rw = (RBQ_PLAN.r == 0) ? 0u : min_u32(idx >> K, last);
     const uint32_t el = idx & ((1u << K) - 1u);
+    // randomized Hadamard: flip the 16-bit sign bits where the diagonal is -1. The sign
+    // load goes first, so the two variants differ from their first instruction on and no
+    // common load is moved above the branch that selects them.
+    u32x4 s4{0u, 0u, 0u, 0u};
+    if constexpr (SIGNS) s4 = c.template load<u32x4>((const char*)t.signs + el * 2u);
     u32x4 q4 = c.template load<u32x4>(in_addr<K, MF, 2, FOURD>(t, row0, rw, el));
-    if (t.signs) {  // randomized Hadamard: flip the 16-bit sign bits where the diagonal is -1
-      const u32x4 s4 = c.template load<u32x4>((const char*)t.signs + el * 2u);
+    if constexpr (SIGNS) {
       q4.x ^= s4.x & 0x80008000u; q4.y ^= s4.y & 0x80008000u;
       q4.z ^= s4.z & 0x80008000u; q4.w ^= s4.w & 0x80008000u;
     }
@@ -851,9 +860,16 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       c.refresh_ids();
       const Block b = block_of<K, MF>(a, blk);
       uint32_t raw[kMatrixLoads<K, MF>][4];
-      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, b.t->rows, b.row0, raw);
       Regs<K, MF> v;
-      matrix_apply<K, MF, IN>(c, raw, v);
+      // the branch holds the MFMAs too, so no load is still in flight where the two paths
+      // meet (a join with loads in flight makes the first use wait for all of them)
+      if (!ROPE && !FOURD && b.t->signs) {
+        matrix_issue<K, MF, FOURD, IN, ROPE, true>(c, *b.t, b.t->rows, b.row0, raw);
+        matrix_apply<K, MF, IN>(c, raw, v);
+      } else {
+        matrix_issue<K, MF, FOURD, IN, ROPE, false>(c, *b.t, b.t->rows, b.row0, raw);
+        matrix_apply<K, MF, IN>(c, raw, v);
+      }
       stages<K, MF, 0, false>(v);
       rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
     }
@@ -861,7 +877,8 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
     uint32_t raw[kMatrixLoads<K, MF>][4];
     if (first < nb) {
       const Block b = block_of<K, MF>(a, first);
-      matrix_issue<K, MF, FOURD, IN, ROPE>(c, *b.t, b.t->rows, b.row0, raw);
+      if (!ROPE && !FOURD && b.t->signs) matrix_issue<K, MF, FOURD, IN, ROPE, true>(c, *b.t, b.t->rows, b.row0, raw);
+      else matrix_issue<K, MF, FOURD, IN, ROPE, false>(c, *b.t, b.t->rows, b.row0, raw);
     }
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
@@ -871,7 +888,8 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       const uint32_t nxt = blk + step;
       if (nxt < nb) {
         const Block bn = block_of<K, MF>(a, nxt);
-        matrix_issue<K, MF, FOURD, IN, ROPE>(c, *bn.t, bn.t->rows, bn.row0, raw);
+        if (!ROPE && !FOURD && bn.t->signs) matrix_issue<K, MF, FOURD, IN, ROPE, true>(c, *bn.t, bn.t->rows, bn.row0, raw);
+        else matrix_issue<K, MF, FOURD, IN, ROPE, false>(c, *bn.t, bn.t->rows, bn.row0, raw);
       }
       stages<K, MF, 0, false>(v);
       rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
@@ -881,7 +899,8 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
       c.refresh_ids();
       const Block b = block_of<K, MF>(a, blk);
       Regs<K, MF> v;
-      load_phase0<K, MF, IN, ROT, FOURD, ROPE>(c, *b.t, b.t->rows, b.row0, v);
+      if (!ROPE && !FOURD && b.t->signs) load_phase0<K, MF, IN, ROT, FOURD, ROPE, true>(c, *b.t, b.t->rows, b.row0, v);
+      else load_phase0<K, MF, IN, ROT, FOURD, ROPE, false>(c, *b.t, b.t->rows, b.row0, v);
       if constexpr (ROT) stages<K, MF, 0, IN != IN_F32>(v);
       rest_of_block<K, MF, IN, ROT, FAST, CACHE, ROPE>(c, a, b, v);
     }
