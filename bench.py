@@ -661,7 +661,24 @@ def main():
             "workload": "one query per head, 32 query heads over INT4 K and V caches [16, 8, 2048, 128], fp16 scales",
             "avg_us": round(tg * 1e6, 3), "unique_bytes": gbytes, "GB_s": round(gbytes / tg / 1e9, 2),
             "frac_hbm_peak": round(gbytes / tg / 1e9 / HBM_PEAK_GBS, 4)}
-        del gk, gv, gks, gvs, gq, gout
+        # the same in token ranges: with at least 256 (batch, key/value head, range) triples
+        # the library takes the shared-load kernel (one workgroup loads each cached token once
+        # for the four query heads of its key/value head); split and merge kernels both timed
+        gws = torch.empty((rbq.attention_split_workspace_bytes(GB_, GH, 8),), dtype=torch.uint8, device=dev)
+        gq_rates = {}
+        for splits in (2, 4, 8):
+            fn = lambda sp=splits: rbq.attention_decode_int4kv_split(  # noqa
+                gq, gk, gks, gv, gvs, 1.0 / math.sqrt(D), sp, out=gout, workspace=gws)
+            fn()
+            gq_rates[splits] = time_back_to_back(torch, [fn], 20) * 1e-6
+        best = min(gq_rates, key=gq_rates.get)
+        tgs = gq_rates[best]
+        extras["attention_decode_gqa_split"] = {
+            "workload": "as attention_decode_gqa, each key/value head's tokens in `splits` ranges + a merge kernel",
+            "splits": best, "avg_us": round(tgs * 1e6, 3), "unique_bytes": gbytes,
+            "GB_s": round(gbytes / tgs / 1e9, 2), "frac_hbm_peak": round(gbytes / tgs / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_us_by_splits": {str(k): round(v * 1e6, 3) for k, v in gq_rates.items()}}
+        del gk, gv, gks, gvs, gq, gout, gws
         # a decode step's cache write: one token per sequence, RoPE -> R3 -> INT4 keys and
         # INT4 values appended at position 2047 of a 4096-row cache (LLaMA-3 8B heads), the
         # query returned RoPE'd and rotated

@@ -273,7 +273,11 @@ rbq_status w4a8_gemm(const int8_t *qA, const void *sA, const uint8_t *qW, const 
  *   score[s] = softmax_scale * sum_d q[d] * k_scale[s] * k_code[s, d]
  *   out[d]   = sum_s softmax(score)[s] * v_scale[s] * v_code[s, d]
  * with key/value head kvh = h / (heads / kv_heads). Arithmetic in fp32; the output is
- * rounded to the query's format.
+ * rounded to the query's format. With 2 or more query heads per key/value head (an even
+ * number of them) and at least 256 workgroups' worth of (batch, key/value head, set of 2 or
+ * 4 query heads), one workgroup reads each cached token once for its set of query heads;
+ * otherwise one workgroup per (batch, query head). The two orders round differently (both
+ * within the fp32 error the parity tests bound).
  *
  *  q         [batch, heads, head_dim] contiguous, BF16 or F16 (kv_rotate_quant's rotated Q
  *            with RBQ_Q_ROTATE_ONLY), 16-byte aligned.

@@ -256,6 +256,252 @@ void attention_decode_kernel(AttnArgs a) {
   }
 }
 
+// ---- grouped key/value heads, shared loads: one workgroup per (batch, key/value head,
+// set of GW query heads[, range]) takes all GW queries at once, so each cached token is
+// loaded once for them (the kernel above loads it once per query head and relies on L2).
+// Eight lanes share a token, each taking DL = 16 dims (8 bytes of codes per row); the
+// query and output registers take 2 * GW * DL = 64 or 128 per lane. Each token group
+// runs the online softmax of the kernel above for each of its GW heads over batches of U
+// tokens (256 tokens per batch and workgroup, as above); the code conversion of a token is
+// shared by the GW heads. Scores sum over fewer dims per lane and more lanes (16 fused
+// multiply-adds and 3 shuffle additions for GW = 4), so their rounding is within the
+// kernel above's.
+template <int GW>
+struct AttnShared {
+  static constexpr int L = 8;                       // lanes per token
+  static constexpr int DL = kAttnD / L;             // dims per lane
+  static constexpr int W = DL / 8;                  // code dwords per lane and token (2)
+  static constexpr int NG = kAttnThreads / L;       // token groups
+  static constexpr int STRIDE = 256;                // tokens per batch, as in the per-head kernel
+  static constexpr int U = STRIDE / NG;             // tokens per group and batch (4 or 8)
+};
+
+typedef uint32_t attn_u32x2 __attribute__((ext_vector_type(2)));
+
+// sum over the eight lanes of a token group (quads first, then the two quads of each
+// 8-lane half row against each other), the same bits on every lane of the group
+__device__ __forceinline__ float attn_octet_sum(float v) {
+  v = attn_quad_sum(v);
+  return v + attn_dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i
+}
+
+template <int SF16, bool SPLIT, int GW>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attention_shared_kernel(AttnArgs a) {
+  using S = AttnShared<GW>;
+  __shared__ float part[S::NG][GW][kAttnD];
+  __shared__ float gmax[S::NG][GW], gsum[S::NG][GW], gw[S::NG][GW], gm[GW];
+  // workgroup -> (batch, key/value head, set of GW query heads[, range])
+  const int sets = (a.H / a.Hkv) / GW;
+  const int u = (int)blockIdx.x;
+  const int sp = SPLIT ? u % a.splits : 0;
+  const int r = SPLIT ? u / a.splits : u;
+  const int st = r % sets, bk = r / sets;
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int64_t bh0 = (int64_t)b * a.H + (int64_t)kvh * (a.H / a.Hkv) + (int64_t)st * GW;  // first query head
+  const int tid = threadIdx.x, c = tid % S::L, tg = tid / S::L;
+
+  // the lane's 16 query dims of each head (two 16-byte loads), times the softmax scale,
+  // over 16 (exact) for the codes' 16
+  float qd[GW][S::DL];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    const attn_u32x4* qp = (const attn_u32x4*)((const uint16_t*)a.q + (bh0 + g) * kAttnD + S::DL * c);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const attn_u32x4 w = qp[h];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        const float x = a.q_f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)bits) : bits_f32(bits << 16);
+        qd[g][8 * h + i] = (x * a.scale) * 0.0625f;
+      }
+    }
+  }
+
+  const int64_t head = (int64_t)b * a.Hkv + kvh;
+  const uint32_t ssz = SF16 ? 2u : 4u;
+  const int t_begin = SPLIT ? sp * a.chunk : 0;
+  const int n = SPLIT ? max(0, min(a.chunk, a.S - t_begin)) : a.S;
+  const int64_t tok0 = head * a.S_cap + t_begin;
+  AttnRsrc rs;
+  rs.kc = attn_rsrc(a.kc + tok0 * 64, (uint32_t)n * 64u);
+  rs.vc = attn_rsrc(a.vc + tok0 * 64, (uint32_t)n * 64u);
+  rs.ks = attn_rsrc((const char*)a.ks + tok0 * ssz, (uint32_t)n * ssz);
+  rs.vs = attn_rsrc((const char*)a.vs + tok0 * ssz, (uint32_t)n * ssz);
+
+  float m_run[GW], l_run[GW], acc[GW][S::DL];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S::DL; ++i) acc[g][i] = 0.0f;
+  }
+
+  // as in the per-head kernel: range-checked buffer loads (tokens past the range read zeros
+  // and score -inf), all of a batch's loads issued before any is used
+  for (int t0 = tg; t0 < n; t0 += S::STRIDE) {
+    uint32_t kw[S::U][S::W], vw[S::U][S::W];
+    float ksc[S::U], vsc[S::U];
+#pragma unroll
+    for (int v = 0; v < S::U; ++v) {
+      const uint32_t t = (uint32_t)(t0 + v * S::NG);
+      const attn_u32x2 k2 =
+          __builtin_bit_cast(attn_u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs.kc, t * 64u + 8u * c, 0, 0));
+      const attn_u32x2 v2 =
+          __builtin_bit_cast(attn_u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs.vc, t * 64u + 8u * c, 0, 0));
+      kw[v][0] = k2.x; kw[v][1] = k2.y;
+      vw[v][0] = v2.x; vw[v][1] = v2.y;
+      if constexpr (SF16) {
+        ksc[v] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.ks, t * 2u, 0, 0));
+        vsc[v] = (float)__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs.vs, t * 2u, 0, 0));
+      } else {
+        ksc[v] = bits_f32(__builtin_amdgcn_raw_buffer_load_b32(rs.ks, t * 4u, 0, 0));
+        vsc[v] = bits_f32(__builtin_amdgcn_raw_buffer_load_b32(rs.vs, t * 4u, 0, 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the value scale over 16 (exact: a power of two) once per token for the GW heads
+#pragma unroll
+    for (int v = 0; v < S::U; ++v) vsc[v] *= 0.0625f;
+    float sc[GW][S::U];
+    float bmax[GW];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) bmax[g] = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < S::U; ++v) {
+      float kc[S::W][8];
+#pragma unroll
+      for (int j = 0; j < S::W; ++j) attn_codes16(kw[v][j], kc[j]);
+      const bool ok = t0 + v * S::NG < n;
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < S::W; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = fmaf(qd[g][8 * j + i], kc[j][i], dot);
+        dot = attn_octet_sum(dot);
+        sc[g][v] = ok ? dot * ksc[v] : -INFINITY;
+        bmax[g] = fmaxf(bmax[g], sc[g][v]);
+      }
+    }
+    float m_new[GW];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      m_new[g] = fmaxf(m_run[g], bmax[g]);
+      const float corr = __expf(m_run[g] - m_new[g]);
+      l_run[g] *= corr;
+#pragma unroll
+      for (int i = 0; i < S::DL; ++i) acc[g][i] *= corr;
+      m_run[g] = m_new[g];
+    }
+#pragma unroll
+    for (int v = 0; v < S::U; ++v) {
+      float vc[S::W][8];
+#pragma unroll
+      for (int j = 0; j < S::W; ++j) attn_codes16(vw[v][j], vc[j]);
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const float p = __expf(sc[g][v] - m_new[g]);
+        l_run[g] += p;
+        const float pv = p * vsc[v];
+#pragma unroll
+        for (int j = 0; j < S::W; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[g][8 * j + i] = fmaf(pv, vc[j][i], acc[g][8 * j + i]);
+      }
+    }
+  }
+
+  // ---- merge the token groups of each head, as in the per-head kernel
+#pragma unroll
+  for (int g = 0; g < GW; ++g)
+#pragma unroll
+    for (int i = 0; i < S::DL; ++i) part[tg][g][S::DL * c + i] = acc[g][i];
+  if (c == 0) {
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      gmax[tg][g] = m_run[g];
+      gsum[tg][g] = l_run[g];
+    }
+  }
+  __syncthreads();
+  if (tid < GW) {
+    float mx = gmax[0][tid];
+    for (int k = 1; k < S::NG; ++k) mx = fmaxf(mx, gmax[k][tid]);
+    gm[tid] = mx;
+  }
+  __syncthreads();
+  for (int e = tid; e < S::NG * GW; e += kAttnThreads) {
+    const int k = e / GW, g = e - k * GW;
+    gw[k][g] = gm[g] == -INFINITY ? 0.0f : __expf(gmax[k][g] - gm[g]);
+  }
+  __syncthreads();
+  for (int o = tid; o < GW * kAttnD; o += kAttnThreads) {
+    const int g = o / kAttnD, d = o - g * kAttnD;
+    float acc_o = 0.0f, l = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < S::NG; ++k) {
+      acc_o = fmaf(part[k][g][d], gw[k][g], acc_o);
+      l = fmaf(gsum[k][g], gw[k][g], l);
+    }
+    const int64_t bh = bh0 + g;
+    if constexpr (SPLIT) {
+      float* pp = a.part + (bh * a.splits + sp) * (2 + kAttnD);
+      pp[2 + d] = acc_o;
+      if (d == 0) {
+        pp[0] = gm[g];
+        pp[1] = l;
+      }
+    } else {
+      acc_o /= l;
+      uint16_t bits;
+      if (a.q_f16) bits = __builtin_bit_cast(uint16_t, (_Float16)acc_o);
+      else bits = (uint16_t)f32_to_bf16(acc_o);
+      ((uint16_t*)a.out)[bh * kAttnD + d] = bits;
+    }
+  }
+}
+
+// Query heads per workgroup of the shared-load kernel for G query heads per key/value
+// head (0: use the per-head kernel). The shared kernel needs a whole number of sets of
+// 2 or 4 heads, and enough workgroups to fill the device: with fewer than 256 it leaves
+// CUs idle, where the per-head kernel's G-times larger grid still streams at full rate.
+constexpr int64_t kAttnSharedMinWorkgroups = 256;
+
+inline int attn_shared_heads(int64_t G, int64_t units_per_set) {
+  const int gw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 0);
+  if (gw == 0 || units_per_set * (G / gw) < kAttnSharedMinWorkgroups) return 0;
+  return gw;
+}
+
+// one launch of the decode kernels over `units` (batch, key/value head[, range]) triples
+template <bool SPLIT>
+static hipError_t attn_decode_launch(const AttnArgs& a0, int64_t units, hipStream_t stream) {
+  AttnArgs a = a0;
+  const int64_t G = a.H / a.Hkv;
+  const int gw = attn_shared_heads(G, units);
+  if (gw) {
+    a.units = (int)(units * (G / gw));
+    const dim3 grid((uint32_t)a.units);
+    if (gw == 4) {
+      if (a.scale_f16) hipLaunchKernelGGL((attention_shared_kernel<1, SPLIT, 4>), grid, dim3(kAttnThreads), 0, stream, a);
+      else hipLaunchKernelGGL((attention_shared_kernel<0, SPLIT, 4>), grid, dim3(kAttnThreads), 0, stream, a);
+    } else {
+      if (a.scale_f16) hipLaunchKernelGGL((attention_shared_kernel<1, SPLIT, 2>), grid, dim3(kAttnThreads), 0, stream, a);
+      else hipLaunchKernelGGL((attention_shared_kernel<0, SPLIT, 2>), grid, dim3(kAttnThreads), 0, stream, a);
+    }
+  } else {
+    a.units = (int)units;
+    const dim3 grid(attn_grid(units, G));
+    if (a.scale_f16) hipLaunchKernelGGL((attention_decode_kernel<1, SPLIT>), grid, dim3(kAttnThreads), 0, stream, a);
+    else hipLaunchKernelGGL((attention_decode_kernel<0, SPLIT>), grid, dim3(kAttnThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 // the splits of pair bh (one workgroup of 128 threads, one output dim each), in split
 // order: out = sum_sp e^(m_sp - M) o_sp / sum_sp e^(m_sp - M) l_sp, M the largest maximum
 // (split 0 always holds token 0, so M is finite); rounded to the query's format. The
@@ -368,13 +614,7 @@ static rbq_status attn_split_launch(AttnArgs a, int64_t batch, int64_t heads, in
   a.splits = (int)splits;
   a.chunk = (int)((a.S + splits - 1) / splits);
   a.part = part;
-  a.units = (int)(batch * a.Hkv * splits);
-  const uint32_t grid = attn_grid(a.units, a.H / a.Hkv);
-  if (a.scale_f16)
-    hipLaunchKernelGGL((attention_decode_kernel<1, true>), dim3(grid), dim3(kAttnThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attention_decode_kernel<0, true>), dim3(grid), dim3(kAttnThreads), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return RBQ_EHIP;
+  if (attn_decode_launch<true>(a, batch * a.Hkv * splits, stream) != hipSuccess) return RBQ_EHIP;
   hipLaunchKernelGGL(attention_merge_kernel, dim3((uint32_t)(batch * heads)), dim3(kAttnD), 0, stream, a);
   return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
@@ -398,14 +638,7 @@ extern "C" rbq_status attention_decode_int4kv(const void* q, rbq_dtype q_dtype, 
     fprintf(stderr, "rbq: attention_decode_int4kv B=%lld H=%lld Hkv=%lld S=%lld cap=%lld\n", (long long)batch,
             (long long)heads, (long long)kv_heads, (long long)seq, (long long)seq_cap);
   if (diag_fail_launch()) return RBQ_EHIP;
-  AttnArgs au = a;
-  au.units = (int)(batch * kv_heads);
-  const dim3 grid(attn_grid(au.units, heads / kv_heads));
-  if (a.scale_f16)
-    hipLaunchKernelGGL((attention_decode_kernel<1, false>), grid, dim3(kAttnThreads), 0, stream, au);
-  else
-    hipLaunchKernelGGL((attention_decode_kernel<0, false>), grid, dim3(kAttnThreads), 0, stream, au);
-  return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+  return attn_decode_launch<false>(a, batch * kv_heads, stream) == hipSuccess ? RBQ_OK : RBQ_EHIP;
 }
 
 extern "C" rbq_status rbq_attention_split_workspace_bytes(int64_t batch, int64_t heads, int64_t splits,

@@ -10,10 +10,12 @@ at most 2 max(d_s) + 2^-20 relative (each is a product of at most S/256 + 3 expo
 the token's own, its group's rescalings and the merge weights (one more for the split
 kernel's ranges), whose arguments add up to the score's distance from the maximum), the sums
 over S tokens by S * 2^-23,
-the output is rounded to bf16 (2^-8 relative covers it), and probabilities below the
-fp32 normal range (2^-126) are flushed to zero:
+the output is rounded to bf16 (2^-8 relative covers it) or fp16 (2^-8 relative, plus
+2^-25 absolute: half the spacing of fp16's subnormals, which is all the precision left to
+an output below 2^-14, as in a peaked softmax whose winning value is 0 in some dim), and
+probabilities below the fp32 normal range (2^-126) are flushed to zero:
     |out - ref| <= 2^-8 |ref| + (2 max_s d_s + 2^-20 + S 2^-23) * sum_s p_s |v_sd|
-                   + S 2^-126 max_s |v_sd|."""
+                   + S 2^-126 max_s |v_sd|  (+ 2^-25 for fp16 outputs)."""
 
 import math
 
@@ -44,6 +46,7 @@ def bf16(x):
 
 def check(out_dev, q, kc, ks, vc, vs, scale, heads=None):
     """heads: optional list of (b, h) to check (the oracle then runs on those only)."""
+    floor = 2.0 ** -25 if out_dev.dtype == torch.float16 else 0.0
     got = out_dev.float().cpu().numpy().astype(np.float64)
     B, H, D = q.shape
     Hkv = kc.shape[1]
@@ -59,7 +62,7 @@ def check(out_dev, q, kc, ks, vc, vs, scale, heads=None):
         vmag = (p[:, None] * np.abs(vc[b, kvh] * vs[b, kvh][:, None].astype(np.float64))).sum(axis=0)
         vmax = float(np.max(np.abs(vc[b, kvh] * vs[b, kvh][:, None].astype(np.float64))))
         bound = (2.0 ** -8 * np.abs(ref) + (2 * d_max + 2.0 ** -20 + S * 2.0 ** -23) * vmag
-                 + S * 2.0 ** -126 * vmax)
+                 + S * 2.0 ** -126 * vmax + floor)
         err = np.abs(got[b, h] - ref)
         assert np.all(err <= bound), f"(b={b}, h={h}) worst {float(np.max(err / np.maximum(bound, 1e-300))):.3g}x bound"
 
@@ -208,3 +211,45 @@ def test_attention_split_full_decode_shape_sampled(rbq):
     # about one bf16 step (2^-7 relative); 2^-6 leaves room for a binade edge
     a, b = out.float(), ref.float()
     assert bool(((a - b).abs() <= b.abs() * 2.0 ** -6 + 2.0 ** -20).all())
+
+
+# Grouped key/value heads with enough (batch, key/value head[, range]) triples for the
+# shared-load kernel (one workgroup per set of 2 or 4 query heads loads each cached token
+# once for all of them): 2, 4 and 8 query heads per key/value head, ragged lengths.
+@pytest.mark.parametrize("B,H,Hkv,S,cap", [(32, 32, 8, 300, 320), (16, 32, 16, 129, 129), (16, 64, 8, 257, 300),
+                                           (32, 24, 4, 513, 520)])
+def test_attention_grouped_heads_shared_loads(rbq, B, H, Hkv, S, cap):
+    print(f"case attention shared B={B} H={H} Hkv={Hkv} S={S} cap={cap}", flush=True)
+    q, kc, ks, vc, vs = make(B * 7 + H + S, B, H, Hkv, S, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = run(rbq, q, kc, ks, vc, vs, scale, S)
+    rng = np.random.default_rng(S)
+    pairs = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(40)]
+    check(out, q, kc[:, :, :S], ks[:, :, :S], vc[:, :, :S], vs[:, :, :S], scale, heads=pairs)
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,cap,splits", [(4, 32, 8, 2000, 2048, 8), (4, 32, 8, 5, 8, 8),
+                                                  (8, 16, 8, 777, 800, 16)])
+def test_attention_split_grouped_heads_shared_loads(rbq, B, H, Hkv, S, cap, splits):
+    """the split form over the shared-load kernel, including ranges past the sequence's end"""
+    print(f"case attention split shared B={B} H={H} Hkv={Hkv} S={S} cap={cap} splits={splits}", flush=True)
+    q, kc, ks, vc, vs = make(B * 11 + S, B, H, Hkv, S, cap)
+    scale = 1.0 / math.sqrt(128)
+    out = run(rbq, q, kc, ks, vc, vs, scale, S, splits=splits)
+    check(out, q, kc[:, :, :S], ks[:, :, :S], vc[:, :, :S], vs[:, :, :S], scale)
+
+
+def test_attention_shared_loads_fp32_scales_peaked_fp16_query(rbq):
+    # nearly one-hot softmax, fp32 scales and an fp16 query through the shared-load kernel
+    B, H, Hkv, S = 32, 32, 8, 600
+    print("case attention shared peaked fp16", flush=True)
+    _, kc, ks, vc, vs = make(43, B, H, Hkv, S, S, np.float32)
+    q = np.random.default_rng(44).standard_normal((B, H, 128)).astype(np.float16).astype(np.float64)
+    pk = lambda c: torch.from_numpy(oracle.pack_nibbles(c.reshape(-1, 128)).reshape(c.shape[:-1] + (64,))).cuda()
+    qd = torch.from_numpy(q.astype(np.float16)).cuda()
+    out = rbq.attention_decode_int4kv(qd, pk(kc), torch.from_numpy(ks).cuda(), pk(vc), torch.from_numpy(vs).cuda(), 4.0)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16
+    rng = np.random.default_rng(45)
+    pairs = [(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(40)]
+    check(out, q, kc, ks, vc, vs, 4.0, heads=pairs)
