@@ -69,6 +69,10 @@ struct KArgs {
   uint32_t blocks0;   // row blocks of tensor 0 (blocks past it belong to tensor 1)
   uint32_t nblocks;   // row blocks in total; workgroups loop over them with a stride
   uint32_t opts;
+  // cache kernels only: blocks from blocks1 on quantize rows of tv as they are (no
+  // rotation), n / 8 lanes per row, into tv's per-head cache (see as_is_rows)
+  TensorArgs tv;
+  uint32_t blocks1;
 };
 
 // one block of rows: its tensor and first row
@@ -824,6 +828,50 @@ RBQ_HD Block block_of(const KArgs& a, uint32_t blk) {
   return b;
 }
 
+// Rows of a 4-D [B, H, S, n] 16-bit tensor quantized as they are (no rotation) into its
+// per-head cache: kv_cache_append_int4's values, in the launch that rotates its keys (and
+// query). n / 8 lanes take a row, 8 values (one 16-byte load) each; the row's absmax by
+// shuffles across them; then the scale and codes of finish() for an unrotated row: max / 7
+// floored at 1e-8, stored as fp16 (RNE) or fp32, codes u / scale rounded half to even by
+// round_quotient_exact and clamped to [-8, 7] (a no-op unless a subnormal fp16 scale sits
+// below max / 7), packed low nibble first. Block vblk covers nthreads / (n / 8) rows.
+template <int K, int IN, class Ctx>
+RBQ_HD void as_is_rows(Ctx& c, const TensorArgs& t, const KArgs& a, uint32_t vblk, uint32_t nthreads) {
+  static_assert(K >= 6 && K <= 8 && IN != IN_F32, "16-bit rows of 64, 128 or 256 values");
+  constexpr uint32_t LPR = (1u << K) / 8;  // lanes per row
+  const uint32_t tid = c.wave * 64u + c.lane;
+  const int64_t row = (int64_t)vblk * (nthreads / LPR) + tid / LPR;
+  const uint32_t el = (tid % LPR) * 8u;
+  const bool live = row < t.rows;
+  const int64_t r = live ? row : t.rows - 1;  // every lane takes part in the shuffles
+  const u32x4 q4 = c.template load<u32x4>((const char*)t.x + (row_offset<true>(t, r) + (int64_t)el) * 2);
+  const uint32_t w[4] = {q4.x, q4.y, q4.z, q4.w};
+  float v[8];
+  static_for<0, 4>([&](auto D) { c.template widen<IN>(w[D.value], v[2 * D.value], v[2 * D.value + 1]); });
+  float mu = 0.0f;
+  static_for<0, 8>([&](auto I) { mu = fmaxf(mu, fabsf(v[I.value])); });
+  static_for<0, K - 3>([&](auto B) { mu = fmaxf(mu, c.template shfl_xor_c<1 << B.value>(mu)); });
+  const bool scale_f16 = (a.opts & OPT_SCALE_F16) != 0;
+  float s = fmaxf(mu / 7.0f, 1e-8f);
+  uint32_t h16 = 0;
+  if (scale_f16) { h16 = f32_to_f16(s); s = f16_to_f32(h16); }
+  const float mk = (s == 0.0f) ? 0.0f : 1.0f / s;
+  uint32_t acc = 0u;
+  static_for<0, 8>([&](auto I) {
+    float q = round_quotient_exact(v[I.value], mk, s) + kMagic;
+    q = fminf(fmaxf(q, kMagic - 8.0f), kMagic + 7.0f);
+    acc = alignbit(f32_bits(q), acc, 4);
+  });
+  if (live) {
+    const int64_t orow = out_row<true>(t, r);
+    c.template store<uint32_t>((uint8_t*)t.codes + orow * (int64_t)(1u << (K - 1)) + el / 2, acc);
+    if (tid % LPR == 0) {
+      if (scale_f16) c.template store<uint16_t>((uint16_t*)t.scales + orow, (uint16_t)h16);
+      else c.template store<float>((float*)t.scales + orow, s);
+    }
+  }
+}
+
 // the transform after phase 0, the reduction, the scale and the stores of one block
 template <int K, bool MF, int IN, bool ROT, bool FAST, bool CACHE, bool RMAP, class Ctx>
 RBQ_HD void rest_of_block(Ctx& c, const KArgs& a, const Block& b, Regs<K, MF>& v) {
@@ -855,9 +903,14 @@ template <int K, int IN, bool ROT, bool FOURD, bool FAST, bool ROPE, bool CACHE,
 RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32_t step) {
   constexpr bool MF = use_matrix_plan(K, IN, ROT);
   const uint32_t nb = a.nblocks;
+  static_assert(!(CACHE && RBQ_PREFETCH), "cache launches use the one-block-at-a-time loop");
+  constexpr uint32_t NT = 64u << RBQ_PLAN.w;
   if constexpr (MF && !RBQ_PREFETCH) {
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
+      if constexpr (CACHE) {
+        if (blk >= a.blocks1) { as_is_rows<K, IN>(c, a.tv, a, blk - a.blocks1, NT); continue; }
+      }
       const Block b = block_of<K, MF>(a, blk);
       uint32_t raw[kMatrixLoads<K, MF>][4];
       Regs<K, MF> v;
@@ -897,6 +950,9 @@ RBQ_HD void fwht_quant_persistent(Ctx& c, const KArgs& a, uint32_t first, uint32
   } else {
     for (uint32_t blk = first; blk < nb; blk += step) {
       c.refresh_ids();
+      if constexpr (CACHE) {
+        if (blk >= a.blocks1) { as_is_rows<K, IN>(c, a.tv, a, blk - a.blocks1, NT); continue; }
+      }
       const Block b = block_of<K, MF>(a, blk);
       Regs<K, MF> v;
       if (!ROPE && !FOURD && b.t->signs) load_phase0<K, MF, IN, ROT, FOURD, ROPE, true>(c, *b.t, b.t->rows, b.row0, v);

@@ -74,19 +74,17 @@ static hipError_t launch_one(const KArgs& a, hipStream_t stream) {
 // fast: packed codes and scales are the only outputs (no rotated rows, no int8 codes)
 // rope: RoPE before the transform (16-bit Q/K of head_dim 64, 128 or 256)
 // cache: 16-bit rows of head_dim 64, 128 or 256 addressed as [B, H, S, D], codes and
-//        scales possibly written to a per-head cache; rot = false quantizes them as they are
+//        scales possibly written to a per-head cache; the blocks from a.blocks1 on quantize
+//        the rows of a.tv as they are
 template <int K>
 hipError_t fwht_launch(const KArgs& a, int in, bool rot, bool fourd, bool fast, bool rope, bool cache,
                        hipStream_t s) {
   if (cache) {
     if constexpr (K >= 6 && K <= 8) {
-      if (in == IN_F32 || !fourd || fast || (rope && !rot)) return hipErrorNotSupported;
-      if (in == IN_BF16) {
-        if (!rot) return launch_one<K, IN_BF16, false, true, false, false, true>(a, s);
+      if (in == IN_F32 || !fourd || fast || !rot) return hipErrorNotSupported;
+      if (in == IN_BF16)
         return rope ? launch_one<K, IN_BF16, true, true, false, true, true>(a, s)
                     : launch_one<K, IN_BF16, true, true, false, false, true>(a, s);
-      }
-      if (!rot) return launch_one<K, IN_F16, false, true, false, false, true>(a, s);
       return rope ? launch_one<K, IN_F16, true, true, false, true, true>(a, s)
                   : launch_one<K, IN_F16, true, true, false, false, true>(a, s);
     } else {

@@ -43,6 +43,8 @@ static hipError_t dispatch(int k, const KArgs& a, int in, bool rot, bool fourd, 
 
 // rows per workgroup (log2) of the plan a launch will use
 static int rows_log(int k, int in, bool rot) { return make_plan(k, use_matrix_plan(k, in, rot)).r; }
+// log2 of the waves of a kernel's workgroup (its threads are 64 << this)
+static int threads_log(int k, int in, bool rot) { return make_plan(k, use_matrix_plan(k, in, rot)).w; }
 
 static int in_kind(rbq_dtype d) { return d == RBQ_F32 ? IN_F32 : (d == RBQ_BF16 ? IN_BF16 : IN_F16); }
 
@@ -267,24 +269,22 @@ extern "C" rbq_status kv_cache_append_int4(const void* q, const void* k, const v
     t->rope_pos0 = (uint32_t)pos0;
     if (rope_cos) set_rope_order_rt(*t, chk.k);
   }
-  a.blocks0 = (uint32_t)bq;
-  a.nblocks = (uint32_t)(bq + bk);
-  a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
-  // launch 2: V (INT4 without rotation into the cache)
-  const int rlv = rows_log(chk.k, in, false);
-  const int64_t bv = (rows_kv + (int64_t{1} << rlv) - 1) >> rlv;
-  KArgs av{};
-  TensorArgs& tv = av.t[0];
+  // V (INT4 without rotation into the cache) in the same launch: the blocks after Q's and
+  // K's take n / 8 lanes per row (as_is_rows)
+  const int64_t vrows_per_block = (int64_t{64} << threads_log(chk.k, in, true)) / (head_dim / 8);
+  const int64_t bv = (rows_kv + vrows_per_block - 1) / vrows_per_block;
+  if (bq + bk + bv > 0x7FFFFFFF) return RBQ_EINVAL;
+  TensorArgs& tv = a.tv;
   set_bhs(tv, v, kv_heads, seq, v_strides);
   tv.codes = v_cache + pos0 * half;
   tv.scales = (char*)v_cache_scales + pos0 * ssz;
   tv.mode = MODE_QUANT;
   tv.rows = rows_kv;
   tv.out_cap = (uint32_t)seq_cap;
-  av.t[1] = tv;
-  av.blocks0 = (uint32_t)bv;
-  av.nblocks = (uint32_t)bv;
-  av.opts = a.opts;
+  a.blocks0 = (uint32_t)bq;
+  a.blocks1 = (uint32_t)(bq + bk);
+  a.nblocks = (uint32_t)(bq + bk + bv);
+  a.opts = OPT_PACKED | (scale_dtype == RBQ_F16 ? OPT_SCALE_F16 : 0u);
   if (diag_log())
     fprintf(stderr, "rbq: kv_cache_append B=%lld H=%lld Hkv=%lld S=%lld D=%lld pos0=%lld cap=%lld rope=%d q=%d "
             "blocks=%lld+%lld\n", (long long)batch, (long long)heads, (long long)kv_heads, (long long)seq,
@@ -292,6 +292,5 @@ extern "C" rbq_status kv_cache_append_int4(const void* q, const void* k, const v
             (long long)(bq + bk), (long long)bv);
   if (diag_fail_launch()) return RBQ_EHIP;
   if (dispatch(chk.k, a, in, true, true, false, rope, stream, true) != hipSuccess) return RBQ_EHIP;
-  if (dispatch(chk.k, av, in, false, true, false, false, stream, true) != hipSuccess) return RBQ_EHIP;
   return RBQ_OK;
 }

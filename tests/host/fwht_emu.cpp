@@ -93,7 +93,8 @@ static void write_file(const char* path, const void* p, size_t n) {
 
 int main(int argc, char** argv) {
   if (argc < 13) { fprintf(stderr, "bad args\n"); return 2; }
-  const int K = atoi(argv[1]), in = atoi(argv[2]), rot = atoi(argv[3]), fourd = atoi(argv[4]);
+  const int K = atoi(argv[1]), in = atoi(argv[2]), fourd = atoi(argv[4]);
+  int rot = atoi(argv[3]);
   const long long rows = atoll(argv[5]);
   const unsigned opts = (unsigned)atoi(argv[6]), mode0 = (unsigned)atoi(argv[7]);
   std::vector<char> x = read_file(argv[8]);
@@ -168,8 +169,22 @@ int main(int argc, char** argv) {
   t.rows = rows;
   a.t[1] = t;
   const int rl = make_plan(K, use_matrix_plan(K, in, rot != 0)).r;
-  const uint32_t nblocks = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
+  uint32_t nblocks = (uint32_t)((rows + (1ll << rl) - 1) >> rl);
   a.blocks0 = nblocks;
+  a.blocks1 = nblocks;
+  if (cache_cap && !rot) {
+    // values of kv_cache_append_int4: quantized as they are by the rotating cache kernel's
+    // as_is_rows blocks (n / 8 lanes per row), as the library launches them
+    const long long nt = 64ll << make_plan(K, use_matrix_plan(K, in, true)).w;
+    const long long per = nt / (n / 8);
+    a.tv = t;
+    a.t[0].rows = 0;
+    a.t[1].rows = 0;
+    a.blocks0 = 0;
+    a.blocks1 = 0;
+    nblocks = (uint32_t)((rows + per - 1) / per);
+    rot = 1;
+  }
   a.nblocks = nblocks;
   // a small grid so that workgroups loop over several blocks (RBQ_EMU_GRID overrides)
   const char* g = getenv("RBQ_EMU_GRID");
