@@ -79,14 +79,17 @@ RBQ_HD uint32_t kron_lds_words(uint32_t m, uint32_t p_log, uint32_t* rs, uint32_
 // Waves per workgroup and operand blocks per gather chunk for KB K blocks of the MFMA.
 // Rows with m <= 32 in a 16-bit format take 8 waves with chunks of 4 blocks: their
 // registers then fit 4 waves per SIMD, so two workgroups of 8 waves share a CU and twice
-// as many gathers are in flight. Otherwise 4 waves with chunks of 8 / KB blocks.
+// as many gathers are in flight. Orders 161 to 192 (six K blocks) in a 16-bit format also
+// take 8 waves (one block per chunk): their LDS (operand table and row buffer) leaves room
+// for one workgroup per CU, and 8 waves give each SIMD two within 256 VGPRs. Otherwise 4
+// waves with chunks of 8 / KB blocks.
 template <int IN, int KB>
-constexpr uint32_t kron_waves() { return (KB == 1 && IN != IN_F32) ? 8u : 4u; }
+constexpr uint32_t kron_waves() { return (IN != IN_F32 && (KB == 1 || KB == 6)) ? 8u : 4u; }
 
 template <int IN, int KB>
 constexpr int kron_chunk() {
   if (IN == IN_F32 || KB > 8) return 1;
-  return kron_waves<IN, KB>() == 8u ? 4 : 8 / KB;
+  return KB == 1 ? (kron_waves<IN, KB>() == 8u ? 4 : 8) : 8 / KB;
 }
 
 // quadratic character of GF(q) from the square mask: 0, +1 (nonzero square) or -1
@@ -246,11 +249,11 @@ RBQ_HD void kron_gather(Ctx& c, const KronArgs& a, const KronGatherOffsets<IN, K
 }
 
 template <int IN, int KB, class Ctx>
-RBQ_HD void kron_mma_store(Ctx& c, const KronArgs& a, uint32_t nb0, const KronFrag<IN, KB>& f) {
+RBQ_HD void kron_mma_store(Ctx& c, const KronArgs& a, uint32_t nb0, const KronFrag<IN, KB>& f, uint32_t mb_lo,
+                           uint32_t mb_hi) {
   using F = KronFrag<IN, KB>;
   constexpr int NPART = (IN == IN_F32) ? 3 : 1;  // bf16 parts of an MFMA operand
-  const uint32_t m = a.m, NB = (1u << a.p_log) >> 4;
-  const uint32_t MB = (m + 15) / 16;
+  const uint32_t NB = (1u << a.p_log) >> 4;
   const uint32_t col = c.lane & 15u, grp = c.lane >> 4;
   static_for<0, F::NBC>([&](auto JJ) {
     const uint32_t nb = nb0 + kron_waves<IN, KB>() * JJ.value;
@@ -282,7 +285,7 @@ RBQ_HD void kron_mma_store(Ctx& c, const KronArgs& a, uint32_t nb0, const KronFr
       });
       const uint32_t bcol = nb * 16 + col;
       const uint32_t cw = bcol + ((bcol >> 4) << 2);  // word of column bcol within a row
-      for (uint32_t mb = 0; mb < MB; ++mb) {
+      for (uint32_t mb = mb_lo; mb < mb_hi; ++mb) {
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         const uint32_t trow = a.tab0 + (16 * mb + col) * a.hs + 4 * grp;
         static_for<0, KB>([&](auto KBI) {
@@ -294,7 +297,7 @@ RBQ_HD void kron_mma_store(Ctx& c, const KronArgs& a, uint32_t nb0, const KronFr
         });
         static_for<0, 4>([&](auto J) {
           const uint32_t ar = 16 * mb + 4 * grp + J.value;
-          if (ar < m) c.lds_store(ar * a.rs + cw, acc[J.value]);
+          if (ar < a.m) c.lds_store(ar * a.rs + cw, acc[J.value]);
         });
       }
     }
@@ -330,19 +333,26 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
   const KronGatherOffsets<IN, KB> go = kron_gather_offsets<IN, KB>(c, a);
   auto row_ptr = [&](int64_t r) { return (const char*)a.x + r * a.row_stride * (int64_t)ESZ; };
   F pre;  // the first chunk of this wave's columns for the next row
-  if ((int64_t)wg < a.rows) kron_gather<IN, KB>(c, a, go, row_ptr(wg), c.wave, pre);
+  // With fewer column blocks than waves (NB < W), R = W / NB waves share each block, each
+  // taking a range of the 16-row blocks mb of H_m; waves whose range is empty take no block.
+  const uint32_t MB = (m + 15) / 16;
+  const uint32_t R = NB < W ? W / NB : 1u;
+  const uint32_t part = c.wave / (W / R);
+  const uint32_t mb_lo = part * MB / R, mb_hi = (part + 1) * MB / R;
+  const uint32_t nb_first = mb_lo < mb_hi ? c.wave % (W / R) : NB;
+  if ((int64_t)wg < a.rows) kron_gather<IN, KB>(c, a, go, row_ptr(wg), nb_first, pre);
 
   for (int64_t row = wg; row < a.rows; row += grid) {
     const char* xr = row_ptr(row);
 
     // ---- 1. H_m on the matrix cores
-    kron_mma_store<IN, KB>(c, a, c.wave, pre);
-    for (uint32_t nb0 = c.wave + W * F::NBC; nb0 < NB; nb0 += W * F::NBC) {
+    kron_mma_store<IN, KB>(c, a, nb_first, pre, mb_lo, mb_hi);
+    for (uint32_t nb0 = nb_first + W * F::NBC; nb0 < NB; nb0 += W * F::NBC) {
       F f;
       kron_gather<IN, KB>(c, a, go, xr, nb0, f);
-      kron_mma_store<IN, KB>(c, a, nb0, f);
+      kron_mma_store<IN, KB>(c, a, nb0, f, mb_lo, mb_hi);
     }
-    if (row + grid < a.rows) kron_gather<IN, KB>(c, a, go, row_ptr(row + grid), c.wave, pre);
+    if (row + grid < a.rows) kron_gather<IN, KB>(c, a, go, row_ptr(row + grid), nb_first, pre);
     c.barrier_lds();
 
     // ---- 2. H_p over the bits of b above bit 3: bits 4..8, then bits 9..10
@@ -430,11 +440,14 @@ RBQ_HD void kron_rows(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
   }
 }
 
-// KS 1: the kernel for one K block (m <= 32); KS 0: two to five (m <= 160); KS 2: six to
-// eight (m <= 256). Each range is its own kernel, so the register budget of the larger
-// orders does not weigh on the smaller ones.
+// KS 1: the kernel for one K block (m <= 32); KS 0: two to five (m <= 160); KS 2: six
+// (m <= 192); KS 3: seven and eight (m <= 256). Each range is its own kernel, so the
+// register budget and wave count of one does not weigh on the others.
 template <int IN, int KS>
-constexpr uint32_t kron_body_waves() { return KS == 1 ? kron_waves<IN, 1>() : kron_waves<IN, 2>(); }
+constexpr uint32_t kron_body_waves() {
+  return KS == 1 ? kron_waves<IN, 1>() : KS == 2 ? kron_waves<IN, 6>() : KS == 3 ? kron_waves<IN, 7>()
+                                                                                  : kron_waves<IN, 2>();
+}
 
 template <int IN, int KS, class Ctx>
 RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t grid) {
@@ -472,12 +485,11 @@ RBQ_HD void kron_quant_body(Ctx& c, const KronArgs& a, uint32_t wg, uint32_t gri
       case 4: kron_rows<IN, 4>(c, a, wg, grid); break;
       default: kron_rows<IN, 5>(c, a, wg, grid); break;
     }
+  } else if constexpr (KS == 2) {
+    kron_rows<IN, 6>(c, a, wg, grid);
   } else {
-    switch (KB) {
-      case 6: kron_rows<IN, 6>(c, a, wg, grid); break;
-      case 7: kron_rows<IN, 7>(c, a, wg, grid); break;
-      default: kron_rows<IN, 8>(c, a, wg, grid); break;
-    }
+    if (KB == 7) kron_rows<IN, 7>(c, a, wg, grid);
+    else kron_rows<IN, 8>(c, a, wg, grid);
   }
 }
 

@@ -16,11 +16,12 @@ namespace rbq {
 // LW: LDS words of the variant (32 KiB, 80 KiB or 160 KiB), the smallest that holds the
 // row buffer and the operand table; smaller variants keep more workgroups per CU.
 // KS 1: rows with one K block of the MFMA (m <= 32), KS 0: two to five (m <= 160), KS 2:
-// six to eight (m <= 256); each has its own wave count and register budget (8 waves at
-// up to 128 VGPRs, or 4 at up to 256).
+// six (m <= 192), KS 3: seven and eight (m <= 256); each has its own wave count and
+// register budget (for m <= 32, 8 waves at up to 128 VGPRs; otherwise up to 256: 4 waves,
+// or, for six K blocks, 8 in the one workgroup per CU that their LDS allows).
 template <int IN, uint32_t LW, int KS>
 __global__ __launch_bounds__((64 * kron_body_waves<IN, KS>()))
-__attribute__((amdgpu_waves_per_eu(kron_body_waves<IN, KS>() == 8u ? 4 : 2)))
+__attribute__((amdgpu_waves_per_eu((KS == 1 && kron_body_waves<IN, KS>() == 8u) ? 4 : 2)))
 void kron_quant_kernel(KronArgs a) {
   __shared__ float lds[LW];
   DevCtx c;
@@ -66,7 +67,8 @@ static hipError_t kron_launch_in(const KronArgs& a, uint32_t words, hipStream_t 
   if (a.m <= 32u) return kron_launch_ks<IN, 1>(a, words, s);
   if (a.m <= 160u) return kron_launch_ks<IN, 0>(a, words, s);
   // orders above 160: the operand table alone takes more than 80 KiB
-  return kron_launch_lw<IN, 40960u, 2>(a, s);
+  if (a.m <= 192u) return kron_launch_lw<IN, 40960u, 2>(a, s);
+  return kron_launch_lw<IN, 40960u, 3>(a, s);
 }
 
 }  // namespace rbq

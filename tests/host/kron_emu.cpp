@@ -37,7 +37,8 @@ template <int IN>
 static void run(const KronArgs& a, uint32_t words, uint32_t grid) {
   if (a.m <= 32u) run_ks<IN, 1>(a, words, grid);
   else if (a.m <= 160u) run_ks<IN, 0>(a, words, grid);
-  else run_ks<IN, 2>(a, words, grid);
+  else if (a.m <= 192u) run_ks<IN, 2>(a, words, grid);
+  else run_ks<IN, 3>(a, words, grid);
 }
 
 static std::vector<char> read_file(const char* path) {
