@@ -97,6 +97,14 @@ __device__ __forceinline__ void wait_copies_and_sync() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// As above, but leaving this wave's L newest LDS reads in flight: for a barrier that frees
+// a stage read by older reads only (the loop issues no other LDS or scalar-memory
+// operations, so the count covers exactly those reads); the later reads' uses wait for them.
+template <int N, int L>
+__device__ __forceinline__ void wait_copies_and_sync_keep_reads() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(N), "n"(L) : "memory");
+}
+
 __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
   __shared__ u32x4_g lds[kStages * kSlots];
 
@@ -204,8 +212,10 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
     mma_sub(xa[1], xw[1]);
     widen_sub(fa0, fw0, 0, xa[0], xw[0]);
     // publish step s + 2: this wave's copies for it are done when at most those of step
-    // s + 3 are in flight
-    wait_copies_and_sync<kLoads>();
+    // s + 3 are in flight. The barrier also frees step s's stage for the copies of step
+    // s + 4: its reads (chunk 1 above, chunk 0 in the previous iteration) must be done,
+    // while the 6 reads of step s + 1's chunk 0 just issued may stay in flight.
+    wait_copies_and_sync_keep_reads<kLoads, 6>();
   }
 
   // epilogue. Lane holds m = column (lane & 31) of each MFMA tile and, per group q of four
