@@ -529,6 +529,22 @@ def main():
             "workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], bf16 out",
             "avg_us": round(t * 1e6, 3), "TOPS": round(GEMM_OPS / t / 1e12, 2),
             "frac_int8_mfma_peak": round(GEMM_OPS / t / 1e12 / INT8_PEAK_TOPS, 4)}
+        # decode: 16 tokens against the same weights (the four rotated weight sets, so the
+        # 22.5 MB of codes come from HBM), the few-token kernel; bound by the weight bytes
+        dec = {}
+        for name, call, a16, s16 in (("w4a4", rbq.w4a4_gemm, qa[:16].contiguous(), sa[:16].contiguous()),
+                                     ("w4a8", rbq.w4a8_gemm, qa8[:16].contiguous(), sa8[:16].contiguous())):
+            o16 = torch.empty((16, GEMM_N), dtype=torch.bfloat16, device=dev)
+            fns = [lambda i=i, call=call, a16=a16, s16=s16, o16=o16: call(a16, s16, sets["gemm"][i][2], sets["gemm"][i][3],
+                                                                        out=o16) for i in range(NSETS)]
+            fns[0]()
+            td = time_back_to_back(torch, fns, 40) * 1e-6
+            wbytes = GEMM_N * GEMM_K // 2 + 2 * GEMM_N + 16 * (GEMM_K // (2 if name == "w4a4" else 1)) + 16 * GEMM_N * 2
+            dec[name] = {"avg_us": round(td * 1e6, 3), "GB_s": round(wbytes / td / 1e9, 2),
+                         "frac_hbm_peak": round(wbytes / td / 1e9 / HBM_PEAK_GBS, 4)}
+        extras["gemm_decode_16_tokens"] = {
+            "workload": "16 tokens x W packed INT4 [11008, 4096] (A INT4 or INT8), bf16 out, one launch",
+            **dec}
         del sets8
         # group-wise weight scales (groups of 256 codes along K) on the same shape: the
         # rotated weights quantized per group, the INT8 activation codes as above

@@ -198,3 +198,53 @@ def test_gemm_bitwise_deterministic(rbq, which):
     for out, acc in runs[1:]:
         assert torch.equal(acc, runs[0][1])
         assert torch.equal(out.view(torch.int16), runs[0][0].view(torch.int16))
+
+
+# Few tokens (M <= 64, decode): the kernel that streams the weights once, one workgroup per
+# 32 weight rows with the waves splitting K. Ragged N (not a multiple of 32), K from one
+# 128-code block to the FFN width, one and two 32-token blocks.
+SMALL_M = [(1, 11008, 4096), (5, 136, 128), (31, 264, 4096), (32, 8, 128), (33, 520, 2048),
+           (64, 11008, 256), (17, 4104, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_M)
+def test_gemm_few_tokens(rbq, M, N, K):
+    print(f"case w4a4_gemm few tokens M={M} N={N} K={K}", flush=True)
+    qa = workloads.gen_packed_codes(5, M, K)
+    qw = workloads.gen_packed_codes(6, N, K)
+    sa = workloads.gen_scales(7, M, "float16")
+    sw = workloads.gen_scales(8, N, "float16")
+    acc, out = run(rbq, qa, sa, qw, sw)
+    acc_ref = oracle.int_gemm(oracle.unpack_nibbles(qa), oracle.unpack_nibbles(qw))
+    check_out(acc, out, acc_ref, sa, sw)
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_M)
+def test_w4a8_few_tokens(rbq, M, N, K):
+    print(f"case w4a8_gemm few tokens M={M} N={N} K={K}", flush=True)
+    qa = gen_int8_codes(5, M, K)
+    qw = workloads.gen_packed_codes(6, N, K)
+    sa = workloads.gen_scales(7, M, "float32")
+    sw = workloads.gen_scales(8, N, "float32")
+    acc, out = run8(rbq, qa, sa, qw, sw)
+    acc_ref, _ = oracle.w4a8_gemm(qa, sa, oracle.unpack_nibbles(qw), sw)
+    check_out(acc, out, acc_ref, sa, sw)
+
+
+@pytest.mark.parametrize("which", ["w4a4", "w4a8"])
+def test_few_token_kernel_matches_tiled_kernel(rbq, which):
+    """64 tokens go to the few-token kernel, 65 to the tiled one: on the same first 64
+    tokens both give the same int32 sums and, with the same epilogue arithmetic, the same
+    bf16 bits."""
+    N, K = 1032, 2048
+    print(f"case {which} few-token vs tiled", flush=True)
+    qa = workloads.gen_packed_codes(9, 65, K) if which == "w4a4" else gen_int8_codes(9, 65, K)
+    qw = dev(workloads.gen_packed_codes(10, N, K))
+    sa = dev(workloads.gen_scales(11, 65, "float16"))
+    sw = dev(workloads.gen_scales(12, N, "float16"))
+    call = rbq.w4a4_gemm if which == "w4a4" else rbq.w4a8_gemm
+    big_out, big_acc = call(dev(qa), sa, qw, sw, return_acc=True)
+    small_out, small_acc = call(dev(qa[:64]), sa[:64].contiguous(), qw, sw, return_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(small_acc, big_acc[:64])
+    assert torch.equal(small_out.view(torch.int16), big_out[:64].view(torch.int16))
