@@ -746,55 +746,62 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
 // ------------------------------------------------------------------ few tokens (decode)
 // With at most 64 tokens (M) the 256 x 256 tiles leave almost every CU idle (43 workgroups
 // for N = 11008, each doing 256 rows of work for the few real ones), while the work is
-// bound by streaming the weights once. Here a workgroup of eight waves takes 32 weight rows
-// (n) and all M tokens in one or two 32-token blocks, and the waves split K: wave w takes
-// the 64-code steps w, w + 8, w + 16, ... In a step, lane (fr, fg) uses 16 bytes of weight
-// row n0 + fr (codes 64 s + 32 fg .. + 31) and the same codes of token fr of each block,
-// and runs two v_mfma_i32_32x32x32_i8 (16 codes each) per block, with the operands widened
-// as in the tiled kernel (so the products and int32 sums are the same). All weight and
-// activation loads of a chunk of steps are issued before its MFMAs; with K = 4096 a
-// wave's eight steps are one chunk, so a workgroup has its whole 64 KB weight slab in
-// flight at once. The waves' sums are added in LDS (exact) and wave 0 scales and stores
-// them with the tiled kernel's epilogue arithmetic.
+// bound by streaming the weights once. Here a workgroup of four waves takes 16 weight rows
+// (n) and all M tokens in blocks of 16, and the waves split K: wave w takes the 128-code
+// steps w, w + 4, w + 8, ... In a step, lane (r, g) = (lane & 15, lane >> 4) loads 16
+// bytes of weight row n0 + r (codes 128 s + 32 g .. + 31: a row's four lanes read 64
+// contiguous bytes) and the same codes of token r of each block, and runs two
+// v_mfma_i32_16x16x64_i8 (16 codes per lane each) per block, with the operands widened as
+// in the tiled kernel (the same products, the same int32 sums). All weight and activation
+// loads of a chunk of steps are issued before its MFMAs. The waves' sums are added in LDS
+// (exact) and wave 0 scales and stores them with the tiled kernel's epilogue arithmetic.
 constexpr int kSmallMaxM = 64;
-constexpr int kSmallWaves = 8;
+constexpr int kSmallWaves = 4;
 
 template <bool A8, int TB>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs g) {
-  constexpr int C = (A8 && TB == 2) ? 4 : 8;       // steps per chunk (register budget)
-  constexpr int AV = A8 ? 2 : 1;                   // 16-byte activation loads per step
-  __shared__ int32_t red[kSmallWaves - 1][TB][16][64];  // waves 1 .. 7's sums, [value][lane]
+  constexpr int AV = A8 ? 2 : 1;                             // 16-byte activation loads per step
+  // steps per chunk: 8 (a wave's share of K = 4096) for one token block, fewer for more
+  // blocks (their activation registers)
+  constexpr int C = 8 / TB;
+  __shared__ int32_t red[kSmallWaves - 1][TB][4][64];         // waves 1 .. 3's sums, [value][lane]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = (int)blockIdx.x * 32;
-  const int fr = lane & 31, fg = lane >> 5;
+  const int n0 = (int)blockIdx.x * 16;
+  const int r = lane & 15, kg = lane >> 4;
   // rows past the end re-read the last row (their sums are never stored)
-  const uint8_t* wp = g.qw + (int64_t)min(n0 + fr, g.N - 1) * (g.K / 2) + 16 * fg;
+  const uint8_t* wp = g.qw + (int64_t)min(n0 + r, g.N - 1) * (g.K / 2) + 16 * kg;
   const int64_t abytes = A8 ? g.K : g.K / 2;
   const uint8_t* ap[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) ap[t] = g.qa + (int64_t)min(t * 32 + fr, g.M - 1) * abytes + 16 * AV * fg;
+  for (int t = 0; t < TB; ++t) ap[t] = g.qa + (int64_t)min(t * 16 + r, g.M - 1) * abytes + 16 * AV * kg;
 
-  v16i_t acc[TB];
+  v4i_t acc[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = v16i_t{};
-  const int steps = g.K / 64;
+  for (int t = 0; t < TB; ++t) acc[t] = v4i_t{};
+  const int steps = g.K / 128;
   for (int s0 = wave; s0 < steps; s0 += kSmallWaves * C) {
     u32x4_g w[C], a[TB][C][AV];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       // steps past the end load the last step again (never used)
       const int s = min(s0 + kSmallWaves * c, steps - 1);
-      w[c] = *(const u32x4_g*)(wp + (int64_t)s * 32);
+      w[c] = *(const u32x4_g*)(wp + (int64_t)s * 64);
 #pragma unroll
       for (int t = 0; t < TB; ++t)
 #pragma unroll
-        for (int v = 0; v < AV; ++v) a[t][c][v] = *(const u32x4_g*)(ap[t] + (int64_t)s * 32 * AV + 16 * v);
+        for (int v = 0; v < AV; ++v) a[t][c][v] = *(const u32x4_g*)(ap[t] + (int64_t)s * 64 * AV + 16 * v);
     }
+    // every load of the chunk is issued before the first MFMA (the scheduler would
+    // otherwise interleave them and wait sooner)
+    __builtin_amdgcn_sched_barrier(0);
+    // straight-line from the loads to the MFMAs (a branch per step would let the compiler
+    // sink each step's loads next to their use, one memory latency per step): steps past
+    // the end take part with their weight codes masked to zero
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (s0 + kSmallWaves * c >= steps) break;
-      const v4i_t yw0 = widen(w[c][0], w[c][1]), yw1 = widen(w[c][2], w[c][3]);
+      const uint32_t keep = (s0 + kSmallWaves * c < steps) ? 0xFFFFFFFFu : 0u;
+      const v4i_t yw0 = widen(w[c][0] & keep, w[c][1] & keep), yw1 = widen(w[c][2] & keep, w[c][3] & keep);
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
         v4i_t ya0, ya1;
@@ -805,8 +812,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs
           ya0 = widen(a[t][c][0][0], a[t][c][0][1]);
           ya1 = widen(a[t][c][0][2], a[t][c][0][3]);
         }
-        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw0, ya0, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(yw1, ya1, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(yw0, ya0, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(yw1, ya1, acc[t], 0, 0, 0);
       }
     }
   }
@@ -815,35 +822,34 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs
 #pragma unroll
     for (int t = 0; t < TB; ++t)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) red[wave - 1][t][k][lane] = acc[t][k];
+      for (int k = 0; k < 4; ++k) red[wave - 1][t][k][lane] = acc[t][k];
   }
   __syncthreads();
   if (wave != 0) return;
-  // lane holds token m = 32 t + fr and, per group q of four sums, n = n0 + 8 q + 4 fg + e
+  // lane holds token m = 16 t + r and weight rows n = n0 + 4 kg + e, e = 0 .. 3
   constexpr int SH = A8 ? 4 : 8;  // the codes' factor 16 (W only) or 256 (both operands)
+  const int n = n0 + 4 * kg;
+  if (n >= g.N) return;  // N is a multiple of 8, so n .. n + 3 are all in range
+  float swv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) swv[e] = load_scale(g.sw, n + e, g.scale_f16);
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int v = 0; v < kSmallWaves - 1; ++v) acc[t][k] += red[v][t][k][lane];
-    const int m = t * 32 + fr;
+    const int m = t * 16 + r;
     if (m >= g.M) continue;
+    if (g.acc)
+      *(u32x4*)(g.acc + (int64_t)m * g.N + n) =
+          u32x4{(uint32_t)(acc[t][0] >> SH), (uint32_t)(acc[t][1] >> SH), (uint32_t)(acc[t][2] >> SH),
+                (uint32_t)(acc[t][3] >> SH)};
     const float sam = load_scale(g.sa, m, g.scale_f16);
+    float y[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 8 * q + 4 * fg;
-      if (n >= g.N) continue;  // N is a multiple of 8, so n .. n + 3 are all in range
-      if (g.acc)
-        *(u32x4*)(g.acc + (int64_t)m * g.N + n) =
-            u32x4{(uint32_t)(acc[t][4 * q] >> SH), (uint32_t)(acc[t][4 * q + 1] >> SH),
-                  (uint32_t)(acc[t][4 * q + 2] >> SH), (uint32_t)(acc[t][4 * q + 3] >> SH)};
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        y[e] = ((float)(acc[t][4 * q + e] >> SH) * sam) * load_scale(g.sw, n + e, g.scale_f16);
-      *(u32x2*)(g.out + (int64_t)m * g.N + n) = u32x2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
-    }
+    for (int e = 0; e < 4; ++e) y[e] = ((float)(acc[t][e] >> SH) * sam) * swv[e];
+    *(u32x2*)(g.out + (int64_t)m * g.N + n) = u32x2{f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
   }
 }
 
@@ -851,9 +857,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs
 template <bool A8>
 static bool gemm_small_m_launch(const GemmArgs& g, hipStream_t stream) {
   if (g.M > kSmallMaxM) return false;
-  const dim3 grid((uint32_t)((g.N + 31) / 32)), block(64 * kSmallWaves);
-  if (g.M <= 32) hipLaunchKernelGGL((gemm_small_m_kernel<A8, 1>), grid, block, 0, stream, g);
-  else hipLaunchKernelGGL((gemm_small_m_kernel<A8, 2>), grid, block, 0, stream, g);
+  const dim3 grid((uint32_t)((g.N + 15) / 16)), block(64 * kSmallWaves);
+  if (g.M <= 16) hipLaunchKernelGGL((gemm_small_m_kernel<A8, 1>), grid, block, 0, stream, g);
+  else if (g.M <= 32) hipLaunchKernelGGL((gemm_small_m_kernel<A8, 2>), grid, block, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_small_m_kernel<A8, 4>), grid, block, 0, stream, g);
   return true;
 }
 
