@@ -853,6 +853,98 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs
   }
 }
 
+// Few tokens with group-wise weight scales (w4a8_gemm_grouped, M <= 64): a workgroup of
+// four waves takes 32 weight rows and the tokens in blocks of 32, and the waves split K by
+// whole groups (group g to wave g mod 4), so each wave folds its own groups: after a
+// group's 32-code steps, the int32 sums are converted and multiplied by the group's scale
+// into fp32 sums, as in the tiled grouped kernel. Tokens are MFMA operand A and weight
+// rows operand B, so a lane's sixteen sums share one weight row (n0 + fr) and one scale per
+// group. Per 32-code step a lane loads 8 bytes of its weight row and 16 of its token row
+// (codes 32 s + 16 fg .. + 15); the loads of a chunk of steps are issued before its MFMAs.
+// The waves' fp32 sums are added in LDS in wave order; the output is bf16((sum / 16) * sa),
+// the tiled kernel's epilogue.
+constexpr int kSmallGChunk = 8;
+
+template <int TB>
+__global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_grouped_kernel(GemmArgs g) {
+  __shared__ float red[kSmallWaves - 1][TB][16][64];  // waves 1 .. 3's fp32 sums, [value][lane]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = (int)blockIdx.x * 32;
+  const int fr = lane & 31, fg = lane >> 5;
+  const int n = min(n0 + fr, g.N - 1);  // rows past the end re-read the last row (not stored)
+  const uint8_t* wp = g.qw + (int64_t)n * (g.K / 2) + 8 * fg;
+  const uint8_t* ap[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) ap[t] = g.qa + (int64_t)min(t * 32 + fr, g.M - 1) * g.K + 16 * fg;
+  const int ngroups = g.K / g.group, gs = g.group / 32;  // groups, 32-code steps per group
+  const int mygroups = ngroups > wave ? (ngroups - wave + kSmallWaves - 1) / kSmallWaves : 0;
+  const int nsteps = mygroups * gs;                       // this wave's steps, group by group
+
+  v16i_t acc[TB];
+  float facc[TB][16];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    acc[t] = v16i_t{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) facc[t][e] = 0.0f;
+  }
+  for (int j0 = 0; j0 < nsteps; j0 += kSmallGChunk) {
+    u32x2_g w[kSmallGChunk];
+    u32x4_g a[TB][kSmallGChunk];
+#pragma unroll
+    for (int c = 0; c < kSmallGChunk; ++c) {
+      // steps past the end load this wave's last step again (masked below)
+      const int j = min(j0 + c, nsteps - 1);
+      const int s = (wave + kSmallWaves * (j / gs)) * gs + j % gs;  // global 32-code step
+      w[c] = *(const u32x2_g*)(wp + (int64_t)s * 16);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) a[t][c] = *(const u32x4_g*)(ap[t] + (int64_t)s * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < kSmallGChunk; ++c) {
+      const int j = j0 + c;
+      const uint32_t keep = j < nsteps ? 0xFFFFFFFFu : 0u;
+      const v4i_t yw = widen(w[c][0] & keep, w[c][1] & keep);
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(order_like_widen(a[t][c]), yw, acc[t], 0, 0, 0);
+      if (j < nsteps && j % gs == gs - 1) {  // the group's last step: fold
+        const int grp = wave + kSmallWaves * (j / gs);
+        const float sw = load_scale(g.sw, (int64_t)n * ngroups + grp, g.scale_f16);
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) facc[t][e] = fmaf((float)acc[t][e], sw, facc[t][e]);
+          acc[t] = v16i_t{};
+        }
+      }
+    }
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave - 1][t][e][lane] = facc[t][e];
+  }
+  __syncthreads();
+  if (wave != 0 || n0 + fr >= g.N) return;
+  // lane holds weight row n0 + fr and, per group q of four sums, token m = 32 t + 8 q + 4 fg + e
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = facc[t][e];
+#pragma unroll
+      for (int u = 0; u < kSmallWaves - 1; ++u) v += red[u][t][e][lane];
+      const int m = t * 32 + 8 * (e / 4) + 4 * fg + (e % 4);
+      if (m < g.M)
+        g.out[(int64_t)m * g.N + n0 + fr] = (uint16_t)f32_to_bf16((v * 0.0625f) * load_scale(g.sa, m, g.scale_f16));
+    }
+}
+
 // the few-token kernel for M <= kSmallMaxM; returns false when M is larger
 template <bool A8>
 static bool gemm_small_m_launch(const GemmArgs& g, hipStream_t stream) {
@@ -938,6 +1030,12 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
     fprintf(stderr, "rbq: w4a8_gemm_grouped M=%lld N=%lld K=%lld group=%lld tiles=%lld\n", (long long)M,
             (long long)N, (long long)K, (long long)group, (long long)ntiles);
   if (diag_fail_launch()) return RBQ_EHIP;
+  if (M <= kSmallMaxM) {
+    const dim3 sgrid((uint32_t)((N + 31) / 32)), sblock(64 * kSmallWaves);
+    if (M <= 32) hipLaunchKernelGGL((gemm_small_m_grouped_kernel<1>), sgrid, sblock, 0, stream, g);
+    else hipLaunchKernelGGL((gemm_small_m_grouped_kernel<2>), sgrid, sblock, 0, stream, g);
+    return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
+  }
   const dim3 grid((uint32_t)ntiles), block(kGThreads);
   const int fs = group >= 128 ? 4 : (int)(group / 32);  // sub-steps per group
   if (g.scale_f16) {

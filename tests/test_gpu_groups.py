@@ -161,3 +161,19 @@ def test_w4a8_gemm_grouped_largest_k_extremes(rbq, group):
     partial, ref = oracle.w4a8_gemm_grouped(qa, sa, oracle.unpack_nibbles(qw), sw, group)
     assert np.all(partial == 1024 * group)
     check_grouped(out, partial, ref, sa, sw)
+
+
+# Few tokens (M <= 64, decode): the grouped product on the kernel where the waves split K
+# by whole groups and add their fp32 sums at the end; every group size class, ragged N.
+@pytest.mark.parametrize("M,N,K,group", [(16, 11008, 4096, 256), (16, 520, 4096, 32), (33, 264, 2048, 64),
+                                         (5, 136, 1024, 1024), (64, 1032, 4096, 128), (1, 8, 4096, 32)])
+def test_w4a8_gemm_grouped_few_tokens(rbq, M, N, K, group):
+    print(f"case w4a8_gemm_grouped few tokens M={M} N={N} K={K} group={group}", flush=True)
+    ra, rw = _weights_and_activations(M + N + K, M, N, K, group)
+    out = rbq.w4a8_gemm_grouped(torch.from_numpy(ra["q"].astype(np.int8)).cuda(),
+                                torch.from_numpy(ra["scales"]).cuda(),
+                                torch.from_numpy(rw["codes"]).cuda(),
+                                torch.from_numpy(rw["scales"]).cuda(), group)
+    torch.cuda.synchronize()
+    partial, ref = oracle.w4a8_gemm_grouped(ra["q"], ra["s_stored"], rw["q"], rw["s_stored"], group)
+    check_grouped(out, partial, ref, ra["s_stored"], rw["s_stored"])
