@@ -854,32 +854,37 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_kernel(GemmArgs
 }
 
 // Few tokens with group-wise weight scales (w4a8_gemm_grouped, M <= 64): a workgroup of
-// four waves takes 32 weight rows and the tokens in blocks of 32, and the waves split K by
-// whole groups (group g to wave g mod 4), so each wave folds its own groups: after a
-// group's 32-code steps, the int32 sums are converted and multiplied by the group's scale
-// into fp32 sums, as in the tiled grouped kernel. Tokens are MFMA operand A and weight
-// rows operand B, so a lane's sixteen sums share one weight row (n0 + fr) and one scale per
-// group. Per 32-code step a lane loads 8 bytes of its weight row and 16 of its token row
-// (codes 32 s + 16 fg .. + 15); the loads of a chunk of steps are issued before its MFMAs.
-// The waves' fp32 sums are added in LDS in wave order; the output is bf16((sum / 16) * sa),
-// the tiled kernel's epilogue.
-constexpr int kSmallGChunk = 8;
-
-template <int TB>
+// four waves takes 32 weight rows and the tokens in blocks of 32. Tokens are MFMA operand A
+// and weight rows operand B (v_mfma_i32_32x32x32_i8), so a lane's sixteen sums share one
+// weight row (n0 + fr) and one scale per group. A step is DS MFMAs over 32 DS codes: lane
+// (fr, fg) loads 8 DS bytes of its weight row and 16 DS bytes of its token row (codes
+// 32 DS s + 16 DS fg .. + 16 DS - 1, one MFMA per 16 of them), so with DS = 2 (groups of 64
+// or more codes) every load is 16 bytes; with DS = 1 (groups of 32) a step is one group.
+// Each wave takes a contiguous range of the steps and, at the end of every group and of its
+// range, converts its int32 sums and multiplies them by the group's scale into fp32 sums, as
+// in the tiled grouped kernel (a group cut by a range end is folded in two parts). The
+// loads of a chunk (8 KB of weights per wave, 4 KB with two token blocks, and the scale of
+// each step's group) are issued before its MFMAs. Token blocks
+// of eight rows that lie past M are never folded (their sums are never stored). The waves'
+// fp32 sums are added in LDS in wave order; the output is bf16((sum / 16) * sa), the tiled
+// kernel's epilogue.
+template <int TB, int DS, bool F16>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_grouped_kernel(GemmArgs g) {
+  constexpr int C = 16 / (DS * TB);                   // steps per chunk
   __shared__ float red[kSmallWaves - 1][TB][16][64];  // waves 1 .. 3's fp32 sums, [value][lane]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = (int)blockIdx.x * 32;
   const int fr = lane & 31, fg = lane >> 5;
   const int n = min(n0 + fr, g.N - 1);  // rows past the end re-read the last row (not stored)
-  const uint8_t* wp = g.qw + (int64_t)n * (g.K / 2) + 8 * fg;
+  const uint8_t* wp = g.qw + (int64_t)n * (g.K / 2) + 8 * DS * fg;
   const uint8_t* ap[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) ap[t] = g.qa + (int64_t)min(t * 32 + fr, g.M - 1) * g.K + 16 * fg;
-  const int ngroups = g.K / g.group, gs = g.group / 32;  // groups, 32-code steps per group
-  const int mygroups = ngroups > wave ? (ngroups - wave + kSmallWaves - 1) / kSmallWaves : 0;
-  const int nsteps = mygroups * gs;                       // this wave's steps, group by group
+  for (int t = 0; t < TB; ++t) ap[t] = g.qa + (int64_t)min(t * 32 + fr, g.M - 1) * g.K + 16 * DS * fg;
+  const int ngroups = g.K / g.group, gs = g.group / (32 * DS);  // groups, steps per group
+  const int steps = g.K / (32 * DS);
+  const int lo = wave * steps / kSmallWaves, nsteps = (wave + 1) * steps / kSmallWaves - lo;
+  const int64_t srow = (int64_t)n * ngroups;  // this row's first group scale
 
   v16i_t acc[TB];
   float facc[TB][16];
@@ -889,36 +894,47 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_small_m_grouped_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) facc[t][e] = 0.0f;
   }
-  for (int j0 = 0; j0 < nsteps; j0 += kSmallGChunk) {
-    u32x2_g w[kSmallGChunk];
-    u32x4_g a[TB][kSmallGChunk];
+  for (int j0 = 0; j0 < nsteps; j0 += C) {
+    using WV = typename std::conditional<DS == 2, u32x4_g, u32x2_g>::type;
+    WV w[C];
+    u32x4_g a[TB][C][DS];
+    float sc[C];
 #pragma unroll
-    for (int c = 0; c < kSmallGChunk; ++c) {
-      // steps past the end load this wave's last step again (masked below)
-      const int j = min(j0 + c, nsteps - 1);
-      const int s = (wave + kSmallWaves * (j / gs)) * gs + j % gs;  // global 32-code step
-      w[c] = *(const u32x2_g*)(wp + (int64_t)s * 16);
+    for (int c = 0; c < C; ++c) {
+      // steps past the range load its last step again (masked below)
+      const int s = lo + min(j0 + c, nsteps - 1);
+      w[c] = *(const WV*)(wp + (int64_t)s * 16 * DS);
+      if constexpr (F16) sc[c] = (float)((const _Float16*)g.sw)[srow + s / gs];
+      else sc[c] = ((const float*)g.sw)[srow + s / gs];
 #pragma unroll
-      for (int t = 0; t < TB; ++t) a[t][c] = *(const u32x4_g*)(ap[t] + (int64_t)s * 32);
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int d = 0; d < DS; ++d) a[t][c][d] = *(const u32x4_g*)(ap[t] + (int64_t)s * 32 * DS + 16 * d);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < kSmallGChunk; ++c) {
-      const int j = j0 + c;
+    for (int c = 0; c < C; ++c) {
+      const int j = j0 + c, s = lo + j;
       const uint32_t keep = j < nsteps ? 0xFFFFFFFFu : 0u;
-      const v4i_t yw = widen(w[c][0] & keep, w[c][1] & keep);
 #pragma unroll
-      for (int t = 0; t < TB; ++t)
-        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(order_like_widen(a[t][c]), yw, acc[t], 0, 0, 0);
-      if (j < nsteps && j % gs == gs - 1) {  // the group's last step: fold
-        const int grp = wave + kSmallWaves * (j / gs);
-        const float sw = load_scale(g.sw, (int64_t)n * ngroups + grp, g.scale_f16);
+      for (int d = 0; d < DS; ++d) {
+        const v4i_t yw = widen(w[c][2 * d] & keep, w[c][2 * d + 1] & keep);
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
+        for (int t = 0; t < TB; ++t)
+          acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(order_like_widen(a[t][c][d]), yw, acc[t], 0, 0, 0);
+      }
+      if (j < nsteps && (s % gs == gs - 1 || j == nsteps - 1)) {  // a group's or the range's end
 #pragma unroll
-          for (int e = 0; e < 16; ++e) facc[t][e] = fmaf((float)acc[t][e], sw, facc[t][e]);
-          acc[t] = v16i_t{};
-        }
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (32 * t + 8 * q < g.M) {  // tokens 32 t + 8 q .. + 7
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                facc[t][4 * q + i] = fmaf((float)acc[t][4 * q + i], sc[c], facc[t][4 * q + i]);
+                acc[t][4 * q + i] = 0;
+              }
+            }
       }
     }
   }
@@ -1032,8 +1048,14 @@ extern "C" rbq_status w4a8_gemm_grouped(const int8_t* qA, const void* sA, const 
   if (diag_fail_launch()) return RBQ_EHIP;
   if (M <= kSmallMaxM) {
     const dim3 sgrid((uint32_t)((N + 31) / 32)), sblock(64 * kSmallWaves);
-    if (M <= 32) hipLaunchKernelGGL((gemm_small_m_grouped_kernel<1>), sgrid, sblock, 0, stream, g);
-    else hipLaunchKernelGGL((gemm_small_m_grouped_kernel<2>), sgrid, sblock, 0, stream, g);
+    // instantiations: token blocks (1 or 2) x one or two MFMAs per step x fp16 or fp32 scales
+    const int v = (M <= 32 ? 0 : 4) + (group == 32 ? 0 : 2) + (g.scale_f16 ? 1 : 0);
+    void (*const kern[8])(GemmArgs) = {
+        gemm_small_m_grouped_kernel<1, 1, false>, gemm_small_m_grouped_kernel<1, 1, true>,
+        gemm_small_m_grouped_kernel<1, 2, false>, gemm_small_m_grouped_kernel<1, 2, true>,
+        gemm_small_m_grouped_kernel<2, 1, false>, gemm_small_m_grouped_kernel<2, 1, true>,
+        gemm_small_m_grouped_kernel<2, 2, false>, gemm_small_m_grouped_kernel<2, 2, true>};
+    hipLaunchKernelGGL(kern[v], sgrid, sblock, 0, stream, g);
     return hipGetLastError() == hipSuccess ? RBQ_OK : RBQ_EHIP;
   }
   const dim3 grid((uint32_t)ntiles), block(kGThreads);

@@ -82,12 +82,16 @@ def check_grouped(out_dev, partial, out_ref, sa, sw):
 
 
 def _weights_and_activations(seed, M, N, K, group):
-    """A: bf16 rows -> INT8 codes (the library's own per-token quantizer); W: fp32 rows,
-    rotated and quantized per group by the oracle (operands identical on both sides)."""
+    """A: bf16 rows -> INT8 codes per token; W: fp32 rows -> INT4 codes per group; both
+    rotated first when K is a power of two and quantized by the oracle (operands identical
+    on both sides; the product does not depend on how the codes were made)."""
+    rot = K & (K - 1) == 0
     a = workloads.gen_rows(seed, M, K, "bfloat16", n_outliers=1, factor=40)
     w = workloads.gen_rows(seed + 1, N, K, "float32", n_outliers=0) * np.float32(0.02)
-    rw = oracle.quantize_groups(oracle.rotate(w.astype(np.float64)), group, "float16", packed=True)
-    ra = oracle.hadamard_quant_int4(workloads.to_float64(a, "bfloat16"), "float16", packed=False, bits=8)
+    w64 = oracle.rotate(w.astype(np.float64)) if rot else w.astype(np.float64)
+    rw = oracle.quantize_groups(w64, group, "float16", packed=True)
+    ra = oracle.hadamard_quant_int4(workloads.to_float64(a, "bfloat16"), "float16", packed=False, bits=8,
+                                    rotate_input=rot)
     return ra, rw
 
 
@@ -163,10 +167,14 @@ def test_w4a8_gemm_grouped_largest_k_extremes(rbq, group):
     check_grouped(out, partial, ref, sa, sw)
 
 
-# Few tokens (M <= 64, decode): the grouped product on the kernel where the waves split K
-# by whole groups and add their fp32 sums at the end; every group size class, ragged N.
+# Few tokens (M <= 64, decode): the grouped product on the kernel where each wave takes a
+# contiguous range of K, folds at group and range ends, and the waves add their fp32 sums at
+# the end; every group size class, ragged N, ranges that cut groups (K = 11008 and a group
+# of all K), and waves with no steps (K = 128).
 @pytest.mark.parametrize("M,N,K,group", [(16, 11008, 4096, 256), (16, 520, 4096, 32), (33, 264, 2048, 64),
-                                         (5, 136, 1024, 1024), (64, 1032, 4096, 128), (1, 8, 4096, 32)])
+                                         (5, 136, 1024, 1024), (64, 1032, 4096, 128), (1, 8, 4096, 32),
+                                         (3, 264, 11008, 256), (7, 72, 11008, 32), (2, 40, 4096, 4096),
+                                         (9, 16, 128, 64), (40, 24, 128, 32)])
 def test_w4a8_gemm_grouped_few_tokens(rbq, M, N, K, group):
     print(f"case w4a8_gemm_grouped few tokens M={M} N={N} K={K} group={group}", flush=True)
     ra, rw = _weights_and_activations(M + N + K, M, N, K, group)
@@ -177,3 +185,19 @@ def test_w4a8_gemm_grouped_few_tokens(rbq, M, N, K, group):
     torch.cuda.synchronize()
     partial, ref = oracle.w4a8_gemm_grouped(ra["q"], ra["s_stored"], rw["q"], rw["s_stored"], group)
     check_grouped(out, partial, ref, ra["s_stored"], rw["s_stored"])
+
+
+@pytest.mark.parametrize("M,group", [(7, 256), (40, 32), (1, 64)])
+def test_w4a8_gemm_grouped_few_tokens_fp32_scales_random_codes(rbq, M, group):
+    # the few-token kernel with fp32 scales, codes over the full grids (-128 / -8 included)
+    N, K = 264, 2048
+    print(f"case w4a8_gemm_grouped few tokens fp32 scales M={M} group={group}", flush=True)
+    rng = np.random.default_rng(31 + M)
+    qa = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    qw = workloads.gen_packed_codes(32 + M, N, K)
+    sa = workloads.gen_scales(33 + M, M, "float32")
+    sw = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(N, K // group))).astype(np.float32)
+    out = rbq.w4a8_gemm_grouped(torch.from_numpy(qa).cuda(), torch.from_numpy(sa).cuda(),
+                                torch.from_numpy(qw).cuda(), torch.from_numpy(sw).cuda(), group)
+    partial, ref = oracle.w4a8_gemm_grouped(qa, sa, oracle.unpack_nibbles(qw), sw, group)
+    check_grouped(out, partial, ref, sa, sw)
