@@ -499,7 +499,12 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
 // chunk. Copies go through a four-stage LDS ring as in the W4A4 kernel (A chunks swizzled
 // by key8, W by key; the copies of a step are issued two steps ahead), and the operand
 // reads of the next sub-step (and of the next step's first one) overlap the MFMAs of the
-// current one.
+// current one. With groups of 64 codes or more, two sub-steps are read as one: lane half fg
+// takes the whole 16-byte W chunk 2 v + fg of half-step v (codes 64 v + 32 fg .. + 31) and
+// the two A chunks of the same codes, and runs one MFMA per 16 of them. Each MFMA's codes
+// then lie in one 64-code block, so in one group; the W reads are half as many and, whole
+// chunks under the row key, free of bank conflicts (an 8-byte read of half a chunk puts the
+// 32 lanes of a pass on half the banks).
 //
 // A rows are MFMA operand A and W rows operand B, so each lane holds one output column n
 // per W block (and sixteen rows m): the fold at a group's end multiplies the lane's
@@ -654,6 +659,26 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
     }
   };
 
+  // half-step v (groups of 64 codes or more): whole chunks, one MFMA per 16 codes of a lane
+  auto read_half = [&](int step, int v, u32x4_g (&da)[2][2], u32x4_g (&dw)[2]) {
+    const u32x4_g* sb = lds + (step % kGStages) * kGSlots;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) da[i][h] = sb[swz8(fa_row[i], 4 * v + 2 * fg + h)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dw[j] = sb[kGSlotsA + swz(fw_row[j], 2 * v + fg)];
+  };
+  auto prep_half = [&](const u32x4_g (&da)[2][2], const u32x4_g (&dw)[2], v4i_t (&ya)[2][2], v4i_t (&yw)[2][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ya[h][i] = order_like_widen(da[i][h]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) yw[h][j] = widen(dw[j][2 * h], dw[j][2 * h + 1]);
+    }
+  };
+
   // scales of the groups the current step ends (FS < 4: 4 / FS groups; FS = 4: the one
   // group that ends with some step), loaded a step ahead
   constexpr int GPS = FS == 4 ? 1 : 4 / FS;
@@ -673,7 +698,9 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
   u32x4_g ca[2];
   u32x2_g cw[2];
   v4i_t ya[2], yw[2];
-  read_sub(0, 0, ca, cw);
+  u32x4_g da[2][2], dw[2];
+  if constexpr (FS == 1) read_sub(0, 0, ca, cw);
+  else read_half(0, 0, da, dw);
   for (int s = 0; s < steps; ++s) {
     // the scales the next step needs, loaded a whole step before the barrier waits for them
     const bool fresh = FS == 4 ? (s & spg_mask) == 0 : true;       // a group starts with this step
@@ -685,18 +712,31 @@ __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g
       for (int j = 0; j < 2; ++j)
         swn[gi][j] = !ends ? 0u : load_sw(j, FS == 4 ? ((s + 1) >> spg_log) : (s + 1) * GPS + gi);
     issue_copies(s + 3);  // its stage last held step s - 1, finished before the last barrier
+    if constexpr (FS == 1) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      prep(ca, cw, ya, yw);
-      if (u < 3) read_sub(s, u + 1, ca, cw);
-      else read_sub(s + 1, 0, ca, cw);  // (after the last step: a stale stage, never used)
-      mma_sub(ya, yw, FS == 4 ? (fresh && u == 0) : (u % FS == 0));
-      if constexpr (FS < 4) {
-        if ((u + 1) % FS == 0) {
-          // (kept in place: spread among later MFMAs, the fold's temporaries would hold
-          // more registers than the workgroup has)
+      for (int u = 0; u < 4; ++u) {
+        prep(ca, cw, ya, yw);
+        if (u < 3) read_sub(s, u + 1, ca, cw);
+        else read_sub(s + 1, 0, ca, cw);  // (after the last step: a stale stage, never used)
+        mma_sub(ya, yw, true);
+        // (kept in place: spread among later MFMAs, the fold's temporaries would hold
+        // more registers than the workgroup has)
+        __builtin_amdgcn_sched_barrier(0);
+        fold(swc[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        v4i_t yah[2][2], ywh[2][2];
+        prep_half(da, dw, yah, ywh);
+        if (v == 0) read_half(s, 1, da, dw);
+        else read_half(s + 1, 0, da, dw);  // (after the last step: a stale stage, never used)
+        mma_sub(yah[0], ywh[0], FS == 4 ? (fresh && v == 0) : true);
+        mma_sub(yah[1], ywh[1], false);
+        if constexpr (FS == 2) {  // a group per half-step
           __builtin_amdgcn_sched_barrier(0);
-          fold(swc[u / FS]);
+          fold(swc[v]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
