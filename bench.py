@@ -555,12 +555,21 @@ def main():
         qwg, swg = rbq.quantize_groups_int4(wr, 256)
         qwg32, swg32 = rbq.quantize_groups_int4(wr, 32)  # the other group size of the ExecuTorch export
         outg = torch.empty_like(out)
+        a16, s16 = qa8[:16].contiguous(), sa8[:16].contiguous()
+        outg16 = torch.empty((16, GEMM_N), dtype=torch.bfloat16, device=dev)
         for name, fn in (("quantize_groups_int4", lambda: rbq.quantize_groups_int4(wr, 256, codes=qwg, scales=swg)),
                          ("w4a8_gemm_grouped", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg, swg, 256, out=outg)),
-                         ("w4a8_gemm_grouped_32", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg32, swg32, 32, out=outg))):
+                         ("w4a8_gemm_grouped_32", lambda: rbq.w4a8_gemm_grouped(qa8, sa8, qwg32, swg32, 32, out=outg)),
+                         ("w4a8_gemm_grouped_16_tokens",
+                          lambda: rbq.w4a8_gemm_grouped(a16, s16, qwg, swg, 256, out=outg16))):
             fn()
             t = time_back_to_back(torch, [fn], 20) * 1e-6
-            if name.startswith("w4a8_gemm_grouped"):
+            if name == "w4a8_gemm_grouped_16_tokens":
+                wbytes = GEMM_N * GEMM_K // 2 + GEMM_N * (GEMM_K // 256) * 2 + 16 * GEMM_K + 16 * GEMM_N * 2
+                extras[name] = {"workload": "16 tokens INT8 x W packed INT4 [11008, 4096], weight scales per 256 "
+                                            "codes, bf16 out (one weight set), the few-token kernel",
+                                "avg_us": round(t * 1e6, 3), "GB_s": round(wbytes / t / 1e9, 2)}
+            elif name.startswith("w4a8_gemm_grouped"):
                 gsz = 32 if name.endswith("_32") else 256
                 extras[name] = {"workload": "A INT8 [4096, 4096] x W packed INT4 [11008, 4096], weight scales per "
                                             f"{gsz} codes, bf16 out (one operand set)",
@@ -570,7 +579,7 @@ def main():
                 nbytes = GEMM_N * GEMM_K * 4 + GEMM_N * GEMM_K // 2 + GEMM_N * (GEMM_K // 256) * 2
                 extras[name] = {"workload": "rotated fp32 weights [11008, 4096] -> packed INT4, fp16 scales per 256",
                                 "avg_us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 2)}
-        del wr, qwg, swg, qwg32, swg32, outg
+        del wr, qwg, swg, qwg32, swg32, outg, a16, s16, outg16
         # context only: the vendor library's int8 GEMM (torch._int_mm, hipBLASLt) on the same
         # shape with the codes already unpacked to int8 and a plain int32 result (no scales)
         try:
