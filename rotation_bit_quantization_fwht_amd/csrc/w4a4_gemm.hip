@@ -276,7 +276,10 @@ __global__ __launch_bounds__(kThreads) void w4a4_gemm_kernel(GemmArgs g) {
       const u32x4 v = *(const u32x4*)(stage + rloc * kEpiStride + (lane & 7) * 16);
       const int m = m0 + wm0 + hh * 64 + rloc;
       const int n = n0 + wn0 + (lane & 7) * 8;
-      if (m < g.M && n < g.N) *(u32x4*)(g.out + (int64_t)m * g.N + n) = v;
+      // nontemporal: the whole output of a wave of tiles goes out at once, and it is not
+      // read again; streamed, it evicts less of the operand rows the next tiles read
+      if (m < g.M && n < g.N)
+        __builtin_nontemporal_store(u32x4_g{v.x, v.y, v.z, v.w}, (u32x4_g*)(g.out + (int64_t)m * g.N + n));
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -478,7 +481,10 @@ __global__ __launch_bounds__(kThreads) void w4a8_gemm_kernel(GemmArgs g) {
       const u32x4 v = *(const u32x4*)(stage + rloc * kEpiStride + (lane & 7) * 16);
       const int m = m0 + wm0 + hh * 64 + rloc;
       const int n = n0 + wn0 + (lane & 7) * 8;
-      if (m < g.M && n < g.N) *(u32x4*)(g.out + (int64_t)m * g.N + n) = v;
+      // nontemporal: the whole output of a wave of tiles goes out at once, and it is not
+      // read again; streamed, it evicts less of the operand rows the next tiles read
+      if (m < g.M && n < g.N)
+        __builtin_nontemporal_store(u32x4_g{v.x, v.y, v.z, v.w}, (u32x4_g*)(g.out + (int64_t)m * g.N + n));
     }
     __builtin_amdgcn_wave_barrier();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
