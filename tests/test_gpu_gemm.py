@@ -146,6 +146,30 @@ def test_w4a8_random_codes(rbq, M, N, K):
     check_out(acc, out, acc_ref, sa, sw)
 
 
+# Tile grids that exercise the workgroup -> tile order of the 256 x 256 kernels: tile counts
+# that are multiples of 8 (each XCD given an eighth of the sequence) with the last group of
+# 8 tile columns 1, 4 or 5 wide, ragged M and N, and a count that is not (plain order).
+TILE_GRIDS = [(2048, 2304, 256), (1024, 5120, 128), (1800, 2056, 128), (2048, 3328, 256), (1280, 4352, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_GRIDS)
+@pytest.mark.parametrize("which", ["w4a4", "w4a8"])
+def test_gemm_tile_grids_exact(rbq, M, N, K, which):
+    print(f"case {which} tile grid M={M} N={N} K={K} tiles={-(-M // 256)}x{-(-N // 256)}", flush=True)
+    qw = workloads.gen_packed_codes(2, N, K)
+    sa = workloads.gen_scales(3, M, "float16")
+    sw = workloads.gen_scales(4, N, "float16")
+    if which == "w4a4":
+        qa = workloads.gen_packed_codes(1, M, K)
+        acc, out = run(rbq, qa, sa, qw, sw)
+        acc_ref = oracle.int_gemm(oracle.unpack_nibbles(qa), oracle.unpack_nibbles(qw))
+    else:
+        qa = gen_int8_codes(1, M, K)
+        acc, out = run8(rbq, qa, sa, qw, sw)
+        acc_ref, _ = oracle.w4a8_gemm(qa, sa, oracle.unpack_nibbles(qw), sw)
+    check_out(acc, out, acc_ref, sa, sw)
+
+
 def test_w4a8_extreme_codes(rbq):
     """-128 x -8 everywhere at the largest supported K: the sums reach 1024 * 65536 = 2^26
     (2^30 with the kernel's factor 16) and must stay exact."""
