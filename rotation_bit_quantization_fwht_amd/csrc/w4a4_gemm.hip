@@ -75,7 +75,7 @@ static_assert(2 * kWavesN * 64 * kEpiStride <= kStages * kSlots * 16, "epilogue 
 __device__ __forceinline__ int swz_key(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int swz(int r, int j) { return r * kChunks + (j ^ swz_key(r)); }
 
-// Output tile (m, n) of workgroup b for the 256 x 256 kernels. Consecutive workgroup ids go
+// Output tile (m, n) of workgroup b for the tiled kernels. Consecutive workgroup ids go
 // to different XCDs (b % 8), so XCD x is given the x-th eighth of the tile sequence (a
 // bijection when the tile count is a multiple of 8; otherwise plain order). The sequence
 // walks groups of 8 tile columns, m-major inside a group: the 32 tiles an XCD runs at once
@@ -546,10 +546,9 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data, no swizzle, range-
 template <int SF16, int FS>
 __global__ __launch_bounds__(kGThreads) void w4a8_gemm_grouped_kernel(GemmArgs g) {
   __shared__ u32x4_g lds[kGRing / 16];
-  const int ntiles = g.tiles_m * g.tiles_n;
   const int b = blockIdx.x;
-  const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
-  const int tn = t / g.tiles_m, tm = t % g.tiles_m;
+  const int2 tt = tile_of(b, g.tiles_m, g.tiles_n);  // as in w4a4_gemm_kernel
+  const int tm = tt.x, tn = tt.y;
   const int m0 = tm * kGBM, n0 = tn * kGBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
