@@ -293,6 +293,40 @@ def copy_calibration(torch, args):
                       "copy_GB_s": round(2 * nbytes * args.steps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}))
 
 
+GEMM_SHAPES = ((4096, 4096, 4096), (4096, 4096, 16384), (4096, 8192, 4096), (4096, 11008, 4096),
+               (4096, 11008, 8192), (8192, 11008, 4096))
+
+
+def gemm_shapes(torch, rbq, dev, reps):
+    """W4A4 GEMM over tile grids of one, two and 2.69 waves and over K: where the time goes.
+    Seeded random packed codes (the values do not change the timing), four operand sets per
+    shape cycled back to back after a 300 ms pre-warm of their own; best of three runs."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    out = []
+    for (M, N, K) in GEMM_SHAPES:
+        sets = []
+        for _ in range(NSETS):
+            qa = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g)
+            qw = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+            sa = (torch.rand(M, device=dev, generator=g) * 0.01 + 0.001).half()
+            sw = (torch.rand(N, device=dev, generator=g) * 0.01 + 0.001).half()
+            sets.append((qa, sa, qw, sw, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        fns = [lambda s=s: rbq.w4a4_gemm(s[0], s[1], s[2], s[3], out=s[4]) for s in sets]
+        t0 = time.time()
+        while time.time() - t0 < 0.3:
+            for f in fns:
+                f()
+            torch.cuda.synchronize()
+        us = min(time_back_to_back(torch, fns, reps) for _ in range(3))
+        ops = 2 * M * N * K
+        out.append({"M": M, "N": N, "K": K, "tiles": -(-M // 256) * -(-N // 256), "avg_us": round(us, 2),
+                    "TOPS": round(ops / us / 1e6, 1), "frac_int8_mfma_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)})
+        del sets, fns
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,9 +337,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the reports beside the step (worked example, decode sweep, variants)")
-    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "kron", "copy", "stream"], default="all",
+    ap.add_argument("--only", choices=["all", "r4", "kv", "gemm", "kron", "copy", "stream", "gemm_shapes"], default="all",
                     help="restrict the step (for profiling one kernel); 'copy' runs a plain 1 GiB "
-                         "device copy used to calibrate the HBM byte counters; 'stream' runs the "
+                         "device copy used to calibrate the HBM byte counters; 'gemm_shapes' times the W4A4 GEMM over several tile grids and K; 'stream' runs the "
                          "HBM streaming probe")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -332,6 +366,10 @@ def main():
     rbq.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "gemm_shapes":
+        print(json.dumps({"w4a4_gemm_shapes": gemm_shapes(torch, rbq, dev, max(args.steps, 20))}), flush=True)
+        return
 
     if args.only == "stream":
         print(json.dumps({"hbm_probe": hbm_probe_rates(torch, rbq, dev, reps=args.steps),
