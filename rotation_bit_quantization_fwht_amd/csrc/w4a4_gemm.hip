@@ -79,9 +79,9 @@ __device__ __forceinline__ int swz(int r, int j) { return r * kChunks + (j ^ swz
 // to different XCDs (b % 8), so XCD x is given the x-th eighth of the tile sequence (a
 // bijection when the tile count is a multiple of 8; otherwise plain order). The sequence
 // walks groups of 8 tile columns, m-major inside a group: the 32 tiles an XCD runs at once
-// are then 4 A row strips by 8 W column strips (6 MB of operands for K = 4096) instead of
-// 16 by 2 (9 MB) in its 4 MB L2 (4096 x 11008 x 4096: 154.1 -> 152.2 us; 8192 rows: 312.1 ->
-// 301.1 us).
+// then share 4 A row strips and 8 W column strips. For the W4A4 kernel at K = 4096 that is
+// 6 MB of operands instead of 9 MB (16 by 2 strips) for its 4 MB L2 (4096 x 11008 x 4096:
+// 154.1 -> 152.2 us; 8192 rows: 312.1 -> 301.1 us).
 __device__ __forceinline__ int2 tile_of(int b, int tiles_m, int tiles_n) {
   const int ntiles = tiles_m * tiles_n;
   const int t = (ntiles % 8 == 0) ? (b % 8) * (ntiles / 8) + b / 8 : b;
