@@ -90,11 +90,18 @@ __device__ __forceinline__ int2 tile_of(int b, int tiles_m, int tiles_n) {
   return int2{r / gw, grp * 8 + r % gw};
 }
 
+// One 64-bit shift moves both dwords' even codes up a nibble (d1's low nibble receives d0's
+// top one, which the mask clears), one instruction fewer per 16 codes than two 32-bit
+// shifts; the compiler splits a 64-bit shift written in C back into two, hence the asm
+// (4096 x 11008 x 4096: 151.4 -> 148.4 us, results bit-identical).
 __device__ __forceinline__ v4i_t widen(uint32_t d0, uint32_t d1) {
+  const uint64_t x0 = ((uint64_t)d1 << 32) | d0;
+  uint64_t x;
+  asm("v_lshlrev_b64 %0, 4, %1" : "=v"(x) : "v"(x0));
   v4i_t r;
-  r[0] = (int)((d0 << 4) & 0xF0F0F0F0u);
+  r[0] = (int)((uint32_t)x & 0xF0F0F0F0u);
   r[1] = (int)(d0 & 0xF0F0F0F0u);
-  r[2] = (int)((d1 << 4) & 0xF0F0F0F0u);
+  r[2] = (int)((uint32_t)(x >> 32) & 0xF0F0F0F0u);
   r[3] = (int)(d1 & 0xF0F0F0F0u);
   return r;
 }
